@@ -1,0 +1,192 @@
+/*
+ * jetlong.h -- C ABI of libjetlong: Dynamic Bifocal RoPE attention (Jet-Long)
+ * on AMD Instinct MI355X (gfx950).
+ *
+ * The method (pages cited by title and section):
+ *   [BT] "Jet-Long: 具有动态双焦RoPE的高效长上下文扩展" (bittide.aicompass.dev):
+ *        §3.1 group size G = max(1, ceil(L / w_pretrained)) and remap
+ *        f(x) = floor(x / G); §3.2 inclusion-exclusion merge; §3.3 KV-cache
+ *        correction rotation; §3.4 one fused kernel for prefill and generation.
+ *   [TW] "NVIDIA研究团队找到了让AI“看清”超长文本的新方法" (techwalker.com):
+ *        §二 local window (standard RoPE) and remote window (remapped RoPE);
+ *        §三 cache keeps raw-RoPE keys, correction rotations at read time;
+ *        §四 three attention calls B, A, C merged with LogSumExp weights.
+ *
+ * Conventions shared by every entry point:
+ *   - Tensors are row-major and contiguous.  q, o: [T][Hq][d]; k, v: [T][Hkv][d]
+ *     (packed "varlen" layout); lse: float32.  d is 64 or 128; Hq % Hkv == 0 and
+ *     query head h reads kv head h / (Hq / Hkv).
+ *   - RoPE is the half-split form: pair (t, t + d/2) is turned by p * theta_t,
+ *     theta_t = rope_base^(-2t/d).
+ *   - Positions are 0-based within each sequence.  A key j is local to query i
+ *     iff 0 <= i - j < w_local and remote iff i - j >= w_local; keys j > i are
+ *     masked (causal).
+ *   - Scores are softmax_scale * <q_rot, k_rot>; lse is the natural log of the
+ *     sum of exp(score) over the keys of a row.
+ *   - All pointers except those marked "host" are device pointers owned by the
+ *     caller.  The library allocates no device memory, keeps no state other
+ *     than a thread-local error string, and never synchronizes: work is
+ *     enqueued on `stream` (a hipStream_t; NULL is the default stream) and is
+ *     complete when the caller synchronizes that stream.
+ *   - Every argument is validated on the host before any HIP call.  A failing
+ *     entry point launches nothing and returns a status; jl_last_error() then
+ *     holds a description.  Values that live in device memory (cu_seqlens,
+ *     seqlens_k, positions) cannot be checked on the host: if they break the
+ *     documented contract the outputs are unspecified, but no kernel reads or
+ *     writes outside the buffers whose sizes the host arguments describe.
+ *   - Outputs must not alias inputs (except in jl_rope_apply).
+ */
+#ifndef JETLONG_H
+#define JETLONG_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define JL_ABI_VERSION 1
+
+typedef enum {
+    JL_OK = 0,
+    JL_ERR_INVALID_ARGUMENT = 1, /* null pointer, bad size, inconsistent shapes        */
+    JL_ERR_UNSUPPORTED = 2,      /* legal request this build does not implement       */
+    JL_ERR_WORKSPACE_TOO_SMALL = 3,
+    JL_ERR_HIP = 4               /* a HIP runtime call or kernel launch failed        */
+} jl_status;
+
+typedef enum { JL_DTYPE_F32 = 0, JL_DTYPE_BF16 = 1 } jl_dtype;
+
+typedef struct {
+    int32_t w_pretrained;  /* >= 1: the model's pretraining window ([BT] §3.1)            */
+    int32_t w_local;       /* >= 0: local window size in tokens ([TW] §二; 2048 there)     */
+    double rope_base;      /* > 0: theta_t = rope_base^(-2t/d)                             */
+    float softmax_scale;   /* > 0 and finite                                               */
+    int32_t bifocal;       /* 1: Jet-Long; 0: plain RoPE causal attention (same kernels)   */
+} jl_params;
+
+/* JL_ABI_VERSION of the built library. */
+int jl_abi_version(void);
+
+/* Static, never-null text for a status value. */
+const char* jl_status_string(int status);
+
+/* Thread-local description of the last failure on this thread ("" if none). */
+const char* jl_last_error(void);
+
+/*
+ * [BT] §3.1: *G_out = max(1, ceil(L / w_pretrained)) computed in exact integer
+ * arithmetic on the host.  L >= 1, w_pretrained >= 1; G_out is a host pointer.
+ */
+jl_status jl_group_size(int64_t L, int32_t w_pretrained, int32_t* G_out);
+
+/*
+ * RoPE rotation: out[t][h][:] = R(floor(positions[t] / G)) x[t][h][:].
+ * G = 1 gives standard RoPE (what a KV cache stores, [TW] §三); G > 1 gives the
+ * remapped rotation of the remote window ([BT] §3.1).
+ *   x, out     [T][H][d] of `dtype`; out may equal x (in place).
+ *   positions  device int32 [T], each >= 0.
+ *   T >= 1, H >= 1, d in {64, 128}, rope_base > 0, G >= 1.
+ * Angles are reduced in fp64 before sin/cos, so positions up to 2^31 - 1 keep
+ * full fp32 accuracy; bf16 outputs are rounded to nearest even.
+ */
+jl_status jl_rope_apply(void* out, const void* x, const int32_t* positions, int64_t T, int32_t H,
+                        int32_t d, double rope_base, int32_t G, jl_dtype dtype, void* stream);
+
+/*
+ * Bytes of device workspace jl_bifocal_prefill needs for these sizes
+ * (host pointer `bytes`).  Depends only on the arguments, never on data.
+ */
+jl_status jl_bifocal_prefill_workspace(int64_t T, int32_t n_seqs, int32_t Hq, int32_t Hkv,
+                                       int32_t d, jl_dtype dtype, size_t* bytes);
+
+/*
+ * Causal bifocal prefill ([BT] §3.2, [TW] §四).  For query i of a sequence of
+ * length L (G = G(L), f(x) = floor(x/G)) and every key j <= i:
+ *     local  (i - j <  w_local): s = scale * <R(i) q_i,    R(j) k_j>
+ *     remote (i - j >= w_local): s = scale * <R(f(i)) q_i, R(f(j)) k_j>
+ * then o_i = softmax(s) v and lse_i = ln sum_j exp(s_ij).  This is exactly the
+ * pages' merge of full remote attention plus local-standard minus
+ * local-remapped; the kernel evaluates it tile by tile without a mask.
+ *   o          [T][Hq][d] of dtype (written).
+ *   lse        float32 [Hq][T] (written).
+ *   q, k, v    raw, un-rotated inputs, [T][Hq][d] and [T][Hkv][d].
+ *   cu_seqlens device int32 [n_seqs + 1]: 0 = cu[0] < cu[1] < ... < cu[n_seqs] = T
+ *              (each sequence non-empty, each length <= max_seqlen), or NULL
+ *              for a single sequence of T tokens (then n_seqs must be 1).
+ *   max_seqlen >= every sequence length (sizes the launch grid).
+ *   k_rot_out  optional (NULL to skip): [T][Hkv][d] of dtype receives R(j) k_j,
+ *              the standard-RoPE keys a KV cache stores for later decode.
+ *   workspace  device buffer of at least jl_bifocal_prefill_workspace() bytes,
+ *              256-byte aligned; contents need no initialisation and are
+ *              scratch after the call.
+ * Supported: dtype bf16 (MFMA path) or f32 (fp32 path), d in {64, 128}.
+ */
+jl_status jl_bifocal_prefill(void* o, float* lse, const void* q, const void* k, const void* v,
+                             const int32_t* cu_seqlens, int32_t n_seqs, int64_t T,
+                             int32_t max_seqlen, int32_t Hq, int32_t Hkv, int32_t d,
+                             const jl_params* params, jl_dtype dtype, void* k_rot_out,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of device workspace jl_bifocal_decode needs for these sizes. */
+jl_status jl_bifocal_decode_workspace(int32_t batch, int32_t max_seqlen_k, int32_t Hq,
+                                      int32_t Hkv, int32_t d, jl_dtype dtype, size_t* bytes);
+
+/*
+ * Bifocal decode ([TW] §三, [BT] §3.3): one new query per sequence against a
+ * KV cache that stores keys under standard RoPE at their original positions
+ * (k_cache[b][j] = R(j) k_j, e.g. written by jl_rope_apply with G = 1 or by
+ * jl_bifocal_prefill's k_rot_out).  The cache is read-only: it is never
+ * rewritten when G changes.  With L = seqlens_k[b] (the current token is
+ * already appended), p = L - 1, G = G(L):
+ *     local  (p - j <  w_local): s = scale * <R(p) q, k_cache[j]>
+ *     remote (p - j >= w_local): s = scale * <R(f(p)) q, R(f(j) - j) k_cache[j]>
+ * i.e. the query carries the correction f(p) - p and every remote key the
+ * correction f(j) - j, applied in registers.
+ *   o          [B][Hq][d] of dtype (written); lse float32 [B][Hq] (written).
+ *   q          raw (un-rotated) query [B][Hq][d].
+ *   k_cache, v_cache  [B][S_max][Hkv][d] of dtype, read-only.
+ *   seqlens_k  device int32 [B], 1 <= L_b <= max_seqlen_k <= S_max.
+ *   workspace  at least jl_bifocal_decode_workspace() bytes (scratch).
+ * Supported: dtype bf16 or f32, d in {64, 128}, Hq / Hkv <= 16.
+ */
+jl_status jl_bifocal_decode(void* o, float* lse, const void* q, const void* k_cache,
+                            const void* v_cache, const int32_t* seqlens_k, int32_t batch,
+                            int32_t max_seqlen_k, int64_t S_max, int32_t Hq, int32_t Hkv,
+                            int32_t d, const jl_params* params, jl_dtype dtype, void* workspace,
+                            size_t workspace_bytes, void* stream);
+
+/*
+ * Test export: runs the kernels' own device index functions for a sequence of
+ * length L (1 <= L) and writes
+ *   G_out     device int32 [1]    G(L)
+ *   f_out     device int32 [L]    f(x) for x = 0..L-1
+ *   band_out  device uint8 [n*n], n = min(L, 1024): band of (i, j) for
+ *             i, j < n: 0 masked (j > i), 1 local, 2 remote
+ *   tile_out  device uint8 [ceil(L/bm) * ceil(L/bn)]: class of the tile
+ *             rows [a*bm, min((a+1)*bm, L)) x keys [b*bn, min((b+1)*bn, L)):
+ *             bit 0 = holds a local pair, bit 1 = holds a remote pair,
+ *             bit 2 = holds a masked (j > i) pair; 0 = skipped (all masked).
+ * bm, bn in [1, 4096]; bifocal as in jl_params.
+ */
+jl_status jl_debug_index_math(int64_t L, int32_t w_pretrained, int32_t w_local, int32_t bifocal,
+                              int32_t bm, int32_t bn, int32_t* G_out, int32_t* f_out,
+                              uint8_t* band_out, uint8_t* tile_out, void* stream);
+
+/*
+ * Kernel timing (profiling aid).  While enabled, every kernel the library
+ * launches is bracketed by HIP events on its stream; jl_profile_read()
+ * synchronizes those events and reports, per kernel name, the launch count
+ * and the summed duration in milliseconds.  Enabling or disabling clears the
+ * record.  Host pointers; `names` receives static strings.
+ */
+jl_status jl_profile_enable(int32_t on);
+jl_status jl_profile_read(const char** names, int32_t* counts, double* total_ms, int32_t capacity,
+                          int32_t* n_out);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* JETLONG_H */

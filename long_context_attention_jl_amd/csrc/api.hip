@@ -1,0 +1,419 @@
+// api.hip -- the C ABI of libjetlong: argument validation, workspace layout,
+// dispatch to the gfx950 kernels, error reporting and kernel timing.
+//
+// Pages cited (title, section):
+//   [BT] "Jet-Long: 具有动态双焦RoPE的高效长上下文扩展" (bittide.aicompass.dev)
+//   [TW] "NVIDIA研究团队找到了让AI“看清”超长文本的新方法" (techwalker.com)
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/jetlong.h"
+#include "internal.h"
+
+namespace jl {
+
+// ---------------------------------------------------------------------------
+// errors
+
+static thread_local std::string g_err;
+
+static jl_status fail(jl_status st, const std::string& msg) {
+    g_err = msg;
+    if (getenv("JL_LOG")) fprintf(stderr, "libjetlong: %s\n", msg.c_str());
+    return st;
+}
+
+static jl_status hip_fail(hipError_t e, const char* where) {
+    return fail(JL_ERR_HIP, std::string(where) + ": " + hipGetErrorString(e));
+}
+
+static jl_status finish(hipStream_t s, const char* where) {
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail(e, where);
+    if (getenv("JL_DEBUG_SYNC")) {
+        e = hipStreamSynchronize(s);
+        if (e == hipSuccess) e = hipGetLastError();
+        if (e != hipSuccess) return hip_fail(e, where);
+    }
+    g_err.clear();
+    return JL_OK;
+}
+
+// ---------------------------------------------------------------------------
+// kernel timing
+
+namespace {
+struct Rec {
+    const char* name;
+    hipEvent_t start, stop;
+};
+std::mutex g_prof_mu;
+bool g_prof_on = false;
+std::vector<Rec> g_recs;
+std::vector<hipEvent_t> g_pool;
+
+hipEvent_t take_event() {
+    if (!g_pool.empty()) {
+        hipEvent_t e = g_pool.back();
+        g_pool.pop_back();
+        return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+}
+
+void clear_records() {
+    for (auto& r : g_recs) {
+        g_pool.push_back(r.start);
+        g_pool.push_back(r.stop);
+    }
+    g_recs.clear();
+}
+}  // namespace
+
+LaunchScope::LaunchScope(const char* name, hipStream_t s) : name_(name), stream_(s), slot_(-1) {
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    if (!g_prof_on) return;
+    Rec r{name, take_event(), take_event()};
+    if (!r.start || !r.stop) return;
+    if (hipEventRecord(r.start, s) != hipSuccess) return;
+    slot_ = (int)g_recs.size();
+    g_recs.push_back(r);
+}
+
+LaunchScope::~LaunchScope() {
+    if (slot_ < 0) return;
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    if (slot_ < (int)g_recs.size()) (void)hipEventRecord(g_recs[slot_].stop, stream_);
+}
+
+// ---------------------------------------------------------------------------
+// layouts
+
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+PrefillLayout prefill_layout(int64_t T, int32_t n_seqs, int32_t Hkv, int32_t d, int dtype) {
+    PrefillLayout L{};
+    L.T_pad = (T + (int64_t)n_seqs * (kBN - 1) + kBN - 1) / kBN * kBN;
+    int64_t lo = (int64_t)n_seqs * kPreciseRows;
+    if (lo > T) lo = T;
+    L.lo_pad = (lo + (int64_t)n_seqs * (kBN - 1) + kBN - 1) / kBN * kBN;
+    size_t off = 0;
+    L.plan = off;
+    off = align256(off + (size_t)(n_seqs + 1) * kPlanFields * sizeof(int32_t));
+    if (dtype == JL_DTYPE_BF16) {
+        const size_t kb = (size_t)Hkv * L.T_pad * d * 2;
+        const size_t lb = (size_t)Hkv * L.lo_pad * d * 2;
+        L.ks = off; off = align256(off + kb);
+        L.kr = off; off = align256(off + kb);
+        L.vt = off; off = align256(off + kb);
+        L.ks_lo = off; off = align256(off + lb);
+        L.kr_lo = off; off = align256(off + lb);
+    } else {
+        const size_t kb = (size_t)Hkv * T * d * 4;
+        L.ks32 = off; off = align256(off + kb);
+        L.kr32 = off; off = align256(off + kb);
+    }
+    L.total = off;
+    return L;
+}
+
+DecodeLayout decode_layout(int32_t B, int32_t max_seqlen_k, int32_t Hq, int32_t Hkv, int32_t d) {
+    DecodeLayout L{};
+    const int nw = Hkv < 8 ? Hkv : 8;
+    const int64_t groups = (Hkv + nw - 1) / nw;
+    const int64_t target = 512;  // about two workgroups per compute unit
+    int64_t want = (target + (int64_t)B * groups - 1) / ((int64_t)B * groups);
+    if (want < 1) want = 1;
+    int64_t chunk = (max_seqlen_k + want - 1) / want;
+    chunk = (chunk + 63) / 64 * 64;
+    if (chunk < 64) chunk = 64;
+    L.chunk = (int32_t)chunk;
+    L.n_splits = (int32_t)((max_seqlen_k + chunk - 1) / chunk);
+    size_t off = 0;
+    L.part_ml = off;
+    off = align256(off + (size_t)B * L.n_splits * Hq * 2 * sizeof(float));
+    L.part_o = off;
+    off = align256(off + (size_t)B * L.n_splits * Hq * d * sizeof(float));
+    L.total = off;
+    return L;
+}
+
+RopeTable make_rope_table(double base, int d) {
+    RopeTable t{};
+    for (int i = 0; i < d / 2 && i < 64; ++i)
+        t.rev[i] = pow(base, -2.0 * (double)i / (double)d) / (2.0 * 3.14159265358979323846);
+    return t;
+}
+
+}  // namespace jl
+
+using namespace jl;
+
+// ---------------------------------------------------------------------------
+// shared checks (pure host code: no HIP call happens before they pass)
+
+static jl_status check_dtype_d(jl_dtype dtype, int32_t d) {
+    if (dtype != JL_DTYPE_F32 && dtype != JL_DTYPE_BF16)
+        return fail(JL_ERR_UNSUPPORTED, "dtype must be JL_DTYPE_F32 or JL_DTYPE_BF16");
+    if (d <= 0 || (d & 1)) return fail(JL_ERR_INVALID_ARGUMENT, "d must be a positive even number");
+    if (d != 64 && d != 128) return fail(JL_ERR_UNSUPPORTED, "d must be 64 or 128");
+    return JL_OK;
+}
+
+static jl_status check_params(const jl_params* p) {
+    if (!p) return fail(JL_ERR_INVALID_ARGUMENT, "params is NULL");
+    if (p->w_pretrained < 1) return fail(JL_ERR_INVALID_ARGUMENT, "w_pretrained must be >= 1");
+    if (p->w_local < 0) return fail(JL_ERR_INVALID_ARGUMENT, "w_local must be >= 0");
+    if (!(p->rope_base > 0.0) || !isfinite(p->rope_base))
+        return fail(JL_ERR_INVALID_ARGUMENT, "rope_base must be finite and > 0");
+    if (!(p->softmax_scale > 0.0f) || !isfinite(p->softmax_scale))
+        return fail(JL_ERR_INVALID_ARGUMENT, "softmax_scale must be finite and > 0");
+    if (p->bifocal != 0 && p->bifocal != 1)
+        return fail(JL_ERR_INVALID_ARGUMENT, "bifocal must be 0 or 1");
+    return JL_OK;
+}
+
+static jl_status check_heads(int32_t Hq, int32_t Hkv) {
+    if (Hq < 1 || Hkv < 1) return fail(JL_ERR_INVALID_ARGUMENT, "Hq and Hkv must be >= 1");
+    if (Hq % Hkv) return fail(JL_ERR_INVALID_ARGUMENT, "Hq must be a multiple of Hkv");
+    if (Hq > 65535) return fail(JL_ERR_UNSUPPORTED, "Hq above 65535");
+    return JL_OK;
+}
+
+extern "C" {
+
+int jl_abi_version(void) { return JL_ABI_VERSION; }
+
+const char* jl_status_string(int status) {
+    switch (status) {
+        case JL_OK: return "JL_OK";
+        case JL_ERR_INVALID_ARGUMENT: return "JL_ERR_INVALID_ARGUMENT";
+        case JL_ERR_UNSUPPORTED: return "JL_ERR_UNSUPPORTED";
+        case JL_ERR_WORKSPACE_TOO_SMALL: return "JL_ERR_WORKSPACE_TOO_SMALL";
+        case JL_ERR_HIP: return "JL_ERR_HIP";
+        default: return "JL_UNKNOWN_STATUS";
+    }
+}
+
+const char* jl_last_error(void) { return g_err.c_str(); }
+
+jl_status jl_group_size(int64_t L, int32_t w_pretrained, int32_t* G_out) {
+    if (!G_out) return fail(JL_ERR_INVALID_ARGUMENT, "G_out is NULL");
+    if (L < 1) return fail(JL_ERR_INVALID_ARGUMENT, "L must be >= 1");
+    if (w_pretrained < 1) return fail(JL_ERR_INVALID_ARGUMENT, "w_pretrained must be >= 1");
+    const int64_t G = group_size(L, w_pretrained);
+    if (G > 2147483647LL) return fail(JL_ERR_INVALID_ARGUMENT, "G does not fit in int32");
+    *G_out = (int32_t)G;
+    g_err.clear();
+    return JL_OK;
+}
+
+jl_status jl_rope_apply(void* out, const void* x, const int32_t* positions, int64_t T, int32_t H,
+                        int32_t d, double rope_base, int32_t G, jl_dtype dtype, void* stream) {
+    if (!out || !x || !positions) return fail(JL_ERR_INVALID_ARGUMENT, "null pointer argument");
+    if (T < 1 || H < 1) return fail(JL_ERR_INVALID_ARGUMENT, "T and H must be >= 1");
+    jl_status st = check_dtype_d(dtype, d);
+    if (st != JL_OK) return st;
+    if (!(rope_base > 0.0) || !isfinite(rope_base))
+        return fail(JL_ERR_INVALID_ARGUMENT, "rope_base must be finite and > 0");
+    if (G < 1) return fail(JL_ERR_INVALID_ARGUMENT, "G must be >= 1");
+    if (T > (1LL << 40) / ((int64_t)H * d)) return fail(JL_ERR_INVALID_ARGUMENT, "T*H*d too large");
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e = launch_rope_apply(out, x, positions, T, H, d, make_rope_table(rope_base, d), G,
+                                     dtype, s);
+    if (e != hipSuccess) return hip_fail(e, "jl_rope_apply launch");
+    return finish(s, "jl_rope_apply");
+}
+
+jl_status jl_bifocal_prefill_workspace(int64_t T, int32_t n_seqs, int32_t Hq, int32_t Hkv,
+                                       int32_t d, jl_dtype dtype, size_t* bytes) {
+    if (!bytes) return fail(JL_ERR_INVALID_ARGUMENT, "bytes is NULL");
+    if (T < 1 || n_seqs < 1) return fail(JL_ERR_INVALID_ARGUMENT, "T and n_seqs must be >= 1");
+    jl_status st = check_heads(Hq, Hkv);
+    if (st != JL_OK) return st;
+    st = check_dtype_d(dtype, d);
+    if (st != JL_OK) return st;
+    if (T + (int64_t)n_seqs * kBN >= 2147483647LL)
+        return fail(JL_ERR_UNSUPPORTED, "T + 64 * n_seqs must stay below 2^31");
+    *bytes = prefill_layout(T, n_seqs, Hkv, d, dtype).total;
+    g_err.clear();
+    return JL_OK;
+}
+
+jl_status jl_bifocal_prefill(void* o, float* lse, const void* q, const void* k, const void* v,
+                             const int32_t* cu_seqlens, int32_t n_seqs, int64_t T,
+                             int32_t max_seqlen, int32_t Hq, int32_t Hkv, int32_t d,
+                             const jl_params* params, jl_dtype dtype, void* k_rot_out,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+    if (!o || !lse || !q || !k || !v || !workspace)
+        return fail(JL_ERR_INVALID_ARGUMENT, "null pointer argument");
+    jl_status st = check_params(params);
+    if (st != JL_OK) return st;
+    if (T < 1) return fail(JL_ERR_INVALID_ARGUMENT, "T must be >= 1");
+    if (n_seqs < 1) return fail(JL_ERR_INVALID_ARGUMENT, "n_seqs must be >= 1");
+    if (!cu_seqlens && n_seqs != 1)
+        return fail(JL_ERR_INVALID_ARGUMENT, "cu_seqlens == NULL requires n_seqs == 1");
+    if (max_seqlen < 1 || max_seqlen > T)
+        return fail(JL_ERR_INVALID_ARGUMENT, "max_seqlen must be in [1, T]");
+    if (!cu_seqlens && max_seqlen != T)
+        return fail(JL_ERR_INVALID_ARGUMENT, "a single sequence needs max_seqlen == T");
+    if ((int64_t)n_seqs > T) return fail(JL_ERR_INVALID_ARGUMENT, "n_seqs > T");
+    if (n_seqs > 65535) return fail(JL_ERR_UNSUPPORTED, "n_seqs above 65535");
+    if ((int64_t)max_seqlen > 65535LL * kBM)
+        return fail(JL_ERR_UNSUPPORTED, "max_seqlen above 65535 * 256");
+    st = check_heads(Hq, Hkv);
+    if (st != JL_OK) return st;
+    st = check_dtype_d(dtype, d);
+    if (st != JL_OK) return st;
+    if (T + (int64_t)n_seqs * kBN >= 2147483647LL)
+        return fail(JL_ERR_UNSUPPORTED, "T + 64 * n_seqs must stay below 2^31");
+    if (o == q || o == k || o == v || (void*)lse == q || (k_rot_out && (k_rot_out == k || k_rot_out == q || k_rot_out == v || k_rot_out == o)))
+        return fail(JL_ERR_INVALID_ARGUMENT, "outputs must not alias inputs");
+    if ((uintptr_t)workspace & 255) return fail(JL_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
+    const PrefillLayout lay = prefill_layout(T, n_seqs, Hkv, d, dtype);
+    if (workspace_bytes < lay.total)
+        return fail(JL_ERR_WORKSPACE_TOO_SMALL,
+                    "workspace needs " + std::to_string(lay.total) + " bytes");
+
+    PrefillArgs a{};
+    a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse; a.k_rot_out = k_rot_out; a.ws = workspace;
+    a.lay = lay;
+    a.n_seqs = n_seqs; a.Hq = Hq; a.Hkv = Hkv; a.d = d; a.max_seqlen = max_seqlen; a.T = T;
+    a.w_local = params->w_local; a.bifocal = params->bifocal;
+    a.softmax_scale = params->softmax_scale;
+    a.tab = make_rope_table(params->rope_base, d);
+
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e = launch_plan((int32_t*)((char*)workspace + lay.plan), cu_seqlens, n_seqs, T,
+                               max_seqlen, params->w_pretrained, s);
+    if (e != hipSuccess) return hip_fail(e, "plan launch");
+    e = launch_kv_prepass(a, dtype, s);
+    if (e != hipSuccess) return hip_fail(e, "key/value pre-pass launch");
+    e = dtype == JL_DTYPE_BF16 ? launch_prefill_bf16(a, s) : launch_prefill_f32(a, s);
+    if (e != hipSuccess) return hip_fail(e, "prefill launch");
+    return finish(s, "jl_bifocal_prefill");
+}
+
+jl_status jl_bifocal_decode_workspace(int32_t batch, int32_t max_seqlen_k, int32_t Hq,
+                                      int32_t Hkv, int32_t d, jl_dtype dtype, size_t* bytes) {
+    if (!bytes) return fail(JL_ERR_INVALID_ARGUMENT, "bytes is NULL");
+    if (batch < 1 || max_seqlen_k < 1)
+        return fail(JL_ERR_INVALID_ARGUMENT, "batch and max_seqlen_k must be >= 1");
+    jl_status st = check_heads(Hq, Hkv);
+    if (st != JL_OK) return st;
+    st = check_dtype_d(dtype, d);
+    if (st != JL_OK) return st;
+    *bytes = decode_layout(batch, max_seqlen_k, Hq, Hkv, d).total;
+    g_err.clear();
+    return JL_OK;
+}
+
+jl_status jl_bifocal_decode(void* o, float* lse, const void* q, const void* k_cache,
+                            const void* v_cache, const int32_t* seqlens_k, int32_t batch,
+                            int32_t max_seqlen_k, int64_t S_max, int32_t Hq, int32_t Hkv,
+                            int32_t d, const jl_params* params, jl_dtype dtype, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+    if (!o || !lse || !q || !k_cache || !v_cache || !seqlens_k || !workspace)
+        return fail(JL_ERR_INVALID_ARGUMENT, "null pointer argument");
+    jl_status st = check_params(params);
+    if (st != JL_OK) return st;
+    if (batch < 1 || max_seqlen_k < 1)
+        return fail(JL_ERR_INVALID_ARGUMENT, "batch and max_seqlen_k must be >= 1");
+    if (S_max < max_seqlen_k) return fail(JL_ERR_INVALID_ARGUMENT, "S_max < max_seqlen_k");
+    if (batch > 65535) return fail(JL_ERR_UNSUPPORTED, "batch above 65535");
+    st = check_heads(Hq, Hkv);
+    if (st != JL_OK) return st;
+    if (Hq / Hkv > 16) return fail(JL_ERR_UNSUPPORTED, "decode supports Hq / Hkv <= 16");
+    st = check_dtype_d(dtype, d);
+    if (st != JL_OK) return st;
+    if (S_max > (1LL << 40) / ((int64_t)batch * Hkv * d))
+        return fail(JL_ERR_INVALID_ARGUMENT, "cache too large");
+    if (o == q || o == k_cache || o == v_cache)
+        return fail(JL_ERR_INVALID_ARGUMENT, "outputs must not alias inputs");
+    if ((uintptr_t)workspace & 255) return fail(JL_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
+    const DecodeLayout lay = decode_layout(batch, max_seqlen_k, Hq, Hkv, d);
+    if (workspace_bytes < lay.total)
+        return fail(JL_ERR_WORKSPACE_TOO_SMALL,
+                    "workspace needs " + std::to_string(lay.total) + " bytes");
+    DecodeArgs a{};
+    a.q = q; a.kc = k_cache; a.vc = v_cache; a.o = o; a.lse = lse; a.seqlens = seqlens_k;
+    a.ws = workspace; a.lay = lay;
+    a.B = batch; a.max_seqlen_k = max_seqlen_k; a.Hq = Hq; a.Hkv = Hkv; a.d = d; a.S_max = S_max;
+    a.w_pretrained = params->w_pretrained; a.w_local = params->w_local;
+    a.bifocal = params->bifocal; a.softmax_scale = params->softmax_scale;
+    a.tab = make_rope_table(params->rope_base, d);
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e = launch_decode(a, dtype, s);
+    if (e != hipSuccess) return hip_fail(e, "decode launch");
+    return finish(s, "jl_bifocal_decode");
+}
+
+jl_status jl_debug_index_math(int64_t L, int32_t w_pretrained, int32_t w_local, int32_t bifocal,
+                              int32_t bm, int32_t bn, int32_t* G_out, int32_t* f_out,
+                              uint8_t* band_out, uint8_t* tile_out, void* stream) {
+    if (!G_out || !f_out || !band_out || !tile_out)
+        return fail(JL_ERR_INVALID_ARGUMENT, "null pointer argument");
+    if (L < 1 || L > 2147483647LL) return fail(JL_ERR_INVALID_ARGUMENT, "L must be in [1, 2^31)");
+    if (w_pretrained < 1 || w_local < 0)
+        return fail(JL_ERR_INVALID_ARGUMENT, "w_pretrained >= 1 and w_local >= 0 required");
+    if (bifocal != 0 && bifocal != 1) return fail(JL_ERR_INVALID_ARGUMENT, "bifocal must be 0 or 1");
+    if (bm < 1 || bm > 4096 || bn < 1 || bn > 4096)
+        return fail(JL_ERR_INVALID_ARGUMENT, "bm and bn must be in [1, 4096]");
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e = launch_debug_index(L, w_pretrained, w_local, bifocal, bm, bn, G_out, f_out,
+                                      band_out, tile_out, s);
+    if (e != hipSuccess) return hip_fail(e, "debug index launch");
+    return finish(s, "jl_debug_index_math");
+}
+
+jl_status jl_profile_enable(int32_t on) {
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    clear_records();
+    g_prof_on = on != 0;
+    g_err.clear();
+    return JL_OK;
+}
+
+jl_status jl_profile_read(const char** names, int32_t* counts, double* total_ms, int32_t capacity,
+                          int32_t* n_out) {
+    if (!n_out || (capacity > 0 && (!names || !counts || !total_ms)))
+        return fail(JL_ERR_INVALID_ARGUMENT, "null pointer argument");
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    std::vector<const char*> nm;
+    std::vector<int32_t> cnt;
+    std::vector<double> tot;
+    for (auto& r : g_recs) {
+        hipError_t e = hipEventSynchronize(r.stop);
+        if (e != hipSuccess) return hip_fail(e, "jl_profile_read");
+        float ms = 0.0f;
+        e = hipEventElapsedTime(&ms, r.start, r.stop);
+        if (e != hipSuccess) return hip_fail(e, "jl_profile_read");
+        size_t i = 0;
+        while (i < nm.size() && strcmp(nm[i], r.name) != 0) ++i;
+        if (i == nm.size()) {
+            nm.push_back(r.name);
+            cnt.push_back(0);
+            tot.push_back(0.0);
+        }
+        cnt[i] += 1;
+        tot[i] += ms;
+    }
+    clear_records();
+    *n_out = (int32_t)nm.size();
+    for (int32_t i = 0; i < capacity && i < (int32_t)nm.size(); ++i) {
+        names[i] = nm[i];
+        counts[i] = cnt[i];
+        total_ms[i] = tot[i];
+    }
+    g_err.clear();
+    return JL_OK;
+}
+
+}  // extern "C"

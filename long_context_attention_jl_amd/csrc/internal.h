@@ -1,0 +1,88 @@
+// internal.h -- launchers shared between libjetlong's entry points and kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "common.h"
+
+namespace jl {
+
+// Records start/stop events around one launch when profiling is on.
+struct LaunchScope {
+    LaunchScope(const char* name, hipStream_t s);
+    ~LaunchScope();
+    const char* name_;
+    hipStream_t stream_;
+    int slot_;
+};
+
+// Byte layout of the prefill workspace; every region starts 256-byte aligned.
+struct PrefillLayout {
+    int64_t T_pad;    // padded key rows (multiple of kBN)
+    int64_t lo_pad;   // padded rows of the split-precision ("lo") key copies
+    size_t plan, ks, kr, vt, ks_lo, kr_lo;  // offsets (bf16 path)
+    size_t ks32, kr32;                      // offsets (f32 path)
+    size_t total;
+};
+PrefillLayout prefill_layout(int64_t T, int32_t n_seqs, int32_t Hkv, int32_t d, int dtype);
+
+struct DecodeLayout {
+    int32_t n_splits;
+    int32_t chunk;
+    size_t part_o, part_ml, total;
+};
+DecodeLayout decode_layout(int32_t batch, int32_t max_seqlen_k, int32_t Hq, int32_t Hkv, int32_t d);
+
+RopeTable make_rope_table(double base, int d);
+
+hipError_t launch_rope_apply(void* out, const void* x, const int32_t* pos, int64_t T, int32_t H,
+                             int32_t d, const RopeTable& tab, int32_t G, int dtype,
+                             hipStream_t s);
+
+hipError_t launch_plan(int32_t* plan, const int32_t* cu, int32_t n_seqs, int64_t T,
+                       int32_t max_seqlen, int32_t w_pretrained, hipStream_t s);
+
+struct PrefillArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    void* o;
+    float* lse;
+    void* k_rot_out;
+    void* ws;
+    PrefillLayout lay;
+    int32_t n_seqs, Hq, Hkv, d, max_seqlen;
+    int64_t T;
+    int32_t w_local, bifocal;
+    float softmax_scale;
+    RopeTable tab;
+};
+
+hipError_t launch_kv_prepass(const PrefillArgs& a, int dtype, hipStream_t s);
+hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t s);
+hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t s);
+
+struct DecodeArgs {
+    const void* q;
+    const void* kc;
+    const void* vc;
+    void* o;
+    float* lse;
+    const int32_t* seqlens;
+    void* ws;
+    DecodeLayout lay;
+    int32_t B, max_seqlen_k, Hq, Hkv, d;
+    int64_t S_max;
+    int32_t w_pretrained, w_local, bifocal;
+    float softmax_scale;
+    RopeTable tab;
+};
+hipError_t launch_decode(const DecodeArgs& a, int dtype, hipStream_t s);
+
+hipError_t launch_debug_index(int64_t L, int32_t w_pretrained, int32_t w_local, int32_t bifocal,
+                              int32_t bm, int32_t bn, int32_t* G_out, int32_t* f_out,
+                              uint8_t* band_out, uint8_t* tile_out, hipStream_t s);
+
+}  // namespace jl

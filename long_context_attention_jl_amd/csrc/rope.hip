@@ -1,0 +1,353 @@
+// rope.hip -- RoPE rotation kernels, the prefill plan and the key/value
+// pre-pass that lays K and V out for the attention kernels.
+//
+// Pages cited (title, section):
+//   [BT] "Jet-Long: 具有动态双焦RoPE的高效长上下文扩展" (bittide.aicompass.dev)
+//   [TW] "NVIDIA研究团队找到了让AI“看清”超长文本的新方法" (techwalker.com)
+#include "internal.h"
+
+namespace jl {
+
+// ---------------------------------------------------------------------------
+// out[t][h] = R(floor(pos[t] / G)) x[t][h]; one thread per (token, pair t),
+// the angle computed once and reused for all H heads of the token.
+template <typename T>
+__global__ __launch_bounds__(256) void rope_apply_kernel(T* __restrict__ out,
+                                                         const T* __restrict__ x,
+                                                         const int32_t* __restrict__ pos,
+                                                         int64_t ntok, int32_t H, int32_t d,
+                                                         RopeTable tab, int32_t G) {
+    const int half = d / 2;
+    const int64_t item = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (item >= ntok * half) return;
+    const int64_t tok = item / half;
+    const int t = (int)(item % half);
+    const int32_t p = remap(pos[tok], G);
+    float c, s;
+    rope_cs(p, tab.rev[t], c, s);
+    for (int h = 0; h < H; ++h) {
+        const int64_t base = (tok * H + h) * (int64_t)d;
+        const float x0 = (float)x[base + t];
+        const float x1 = (float)x[base + t + half];
+        out[base + t] = (T)(x0 * c - x1 * s);
+        out[base + t + half] = (T)(x1 * c + x0 * s);
+    }
+}
+
+hipError_t launch_rope_apply(void* out, const void* x, const int32_t* pos, int64_t T, int32_t H,
+                             int32_t d, const RopeTable& tab, int32_t G, int dtype,
+                             hipStream_t s) {
+    const int64_t items = T * (d / 2);
+    const dim3 grid((unsigned)((items + 255) / 256));
+    LaunchScope scope("rope_apply", s);
+    if (dtype == 1)
+        hipLaunchKernelGGL(rope_apply_kernel<bf16>, grid, dim3(256), 0, s, (bf16*)out,
+                           (const bf16*)x, pos, T, H, d, tab, G);
+    else
+        hipLaunchKernelGGL(rope_apply_kernel<float>, grid, dim3(256), 0, s, (float*)out,
+                           (const float*)x, pos, T, H, d, tab, G);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Plan: per-sequence start, length, G ([BT] §3.1: one G per sequence from its
+// own length) and the offsets of the padded key layouts.  One thread; the
+// number of sequences is small next to the attention work.  If cu_seqlens
+// breaks its contract every length is set to 0 (all kernels then do nothing)
+// and the "bad" flag is raised, so no kernel leaves its buffers.
+__global__ void plan_kernel(int32_t* __restrict__ plan, const int32_t* __restrict__ cu,
+                            int32_t n_seqs, int64_t T, int32_t max_seqlen, int32_t w_pretrained) {
+    if (threadIdx.x != 0 || blockIdx.x != 0) return;
+    bool bad = false;
+    if (cu) {
+        if (cu[0] != 0 || (int64_t)cu[n_seqs] != T) bad = true;
+        for (int s = 0; s < n_seqs && !bad; ++s) {
+            const int64_t len = (int64_t)cu[s + 1] - cu[s];
+            if (len < 1 || len > max_seqlen) bad = true;
+        }
+    }
+    int64_t pad = 0, lo = 0;
+    for (int s = 0; s < n_seqs; ++s) {
+        int32_t* e = plan + s * kPlanFields;
+        const int32_t start = cu ? cu[s] : 0;
+        const int32_t len = bad ? 0 : (cu ? cu[s + 1] - cu[s] : (int32_t)T);
+        e[kPlanStart] = bad ? 0 : start;
+        e[kPlanLen] = len;
+        e[kPlanG] = (int32_t)group_size(len, w_pretrained);
+        e[kPlanPadOff] = (int32_t)pad;
+        e[kPlanLoOff] = (int32_t)lo;
+        e[kPlanTile0] = (int32_t)(pad / kBN);
+        e[kPlanLoTile0] = (int32_t)(lo / kBN);
+        e[kPlanBad] = 0;
+        pad += (len + kBN - 1) / kBN * kBN;
+        const int32_t nlo = len < kPreciseRows ? len : kPreciseRows;
+        lo += (nlo + kBN - 1) / kBN * kBN;
+    }
+    int32_t* e = plan + n_seqs * kPlanFields;
+    e[kPlanStart] = (int32_t)T;
+    e[kPlanLen] = 0;
+    e[kPlanG] = 1;
+    e[kPlanPadOff] = (int32_t)pad;
+    e[kPlanLoOff] = (int32_t)lo;
+    e[kPlanTile0] = (int32_t)(pad / kBN);
+    e[kPlanLoTile0] = (int32_t)(lo / kBN);
+    e[kPlanBad] = bad ? 1 : 0;
+}
+
+hipError_t launch_plan(int32_t* plan, const int32_t* cu, int32_t n_seqs, int64_t T,
+                       int32_t max_seqlen, int32_t w_pretrained, hipStream_t s) {
+    LaunchScope scope("plan", s);
+    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(64), 0, s, plan, cu, n_seqs, T, max_seqlen,
+                       w_pretrained);
+    return hipGetLastError();
+}
+
+// Sequence owning padded key tile `tile` (plan tile0 is non-decreasing);
+// -1 if the tile is beyond the last sequence.
+__device__ inline int seq_of_tile(const int32_t* plan, int n_seqs, int tile) {
+    if (tile >= plan[n_seqs * kPlanFields + kPlanTile0]) return -1;
+    int lo = 0, hi = n_seqs - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) / 2;
+        if (plan[mid * kPlanFields + kPlanTile0] <= tile) lo = mid;
+        else hi = mid - 1;
+    }
+    return lo;
+}
+
+// Order of keys inside each group of 16 in the transposed V tile.  The
+// prefill kernel's P operand holds, in lane half h, the keys
+// {4h..4h+3, 8+4h..8+4h+3} of a 16-key step; storing the group as
+// [0..3, 8..11, 4..7, 12..15] lets that half read its 8 keys as one 16-byte
+// vector.  The permutation is its own inverse.
+__host__ __device__ constexpr int vt_perm16(int p) {
+    return (p & 4) != ((p >> 1) & 4) ? (p ^ 12) : p;
+}
+
+// ---------------------------------------------------------------------------
+// Key/value pre-pass of the bf16 prefill (one workgroup per padded key tile,
+// looping over kv heads so each (position, pair) angle is computed once):
+//   KS[g][row]  = R(n) k_n            (standard RoPE, [TW] §二), fp16
+//   KR[g][row]  = R(f(n)) k_n         (remapped RoPE, [BT] §3.1; only if G > 1), fp16
+//   KS_lo/KR_lo = f16(x - f16(x))     for n < kPreciseRows (split precision)
+//   VT[g][tile][d][key']              V tile transposed, keys in vt_perm16 order
+//   k_rot_out[tok][g] = KS row        (optional, the caller's cache layout)
+// Pad rows (n >= L) are written as zeros so masked keys never meet NaNs.
+template <int D>
+__global__ __launch_bounds__(256) void kv_prepass_bf16_kernel(PrefillArgs a) {
+    constexpr int HALF = D / 2;
+    constexpr int TPC = D / 8;  // pairs per thread: 4 threads per key row
+    __shared__ bf16 vs[kBN * (D + 2)];
+
+    const int32_t* plan = (const int32_t*)((char*)a.ws + a.lay.plan);
+    f16* KS = (f16*)((char*)a.ws + a.lay.ks);
+    f16* KR = (f16*)((char*)a.ws + a.lay.kr);
+    bf16* VT = (bf16*)((char*)a.ws + a.lay.vt);
+    f16* KSlo = (f16*)((char*)a.ws + a.lay.ks_lo);
+    f16* KRlo = (f16*)((char*)a.ws + a.lay.kr_lo);
+    const bf16* k = (const bf16*)a.k;
+    const bf16* v = (const bf16*)a.v;
+    bf16* krot = (bf16*)a.k_rot_out;
+
+    const int tile = blockIdx.x;
+    const int s = seq_of_tile(plan, a.n_seqs, tile);
+    if (s < 0) return;
+    const int32_t* e = plan + s * kPlanFields;
+    const int32_t start = e[kPlanStart], len = e[kPlanLen], G = e[kPlanG];
+    const bool bif = a.bifocal && G > 1;
+    const int32_t n0 = (tile - e[kPlanTile0]) * kBN;  // first position of the tile
+    const int64_t prow0 = (int64_t)tile * kBN;          // first padded row
+
+    // ---- keys: thread (r, c) rotates pairs [c*TPC, (c+1)*TPC) of row r ----
+    const int r = threadIdx.x / 4, c = threadIdx.x % 4;
+    const int32_t n = n0 + r;
+    const bool valid = n < len;
+    const bool lo_row = n < kPreciseRows;
+    float cs[TPC], sn[TPC], cr[TPC], sr[TPC];
+    if (valid) {
+        const int32_t fn = remap(n, G);
+#pragma unroll
+        for (int u = 0; u < TPC; ++u) {
+            rope_cs(n, a.tab.rev[c * TPC + u], cs[u], sn[u]);
+            if (bif) rope_cs(fn, a.tab.rev[c * TPC + u], cr[u], sr[u]);
+        }
+    }
+    for (int g = 0; g < a.Hkv; ++g) {
+        f16 ys0[TPC], ys1[TPC], yr0[TPC], yr1[TPC];
+        f16 ls0[TPC], ls1[TPC], lr0[TPC], lr1[TPC];
+        bf16 kb0[TPC], kb1[TPC];
+        if (valid) {
+            const bf16* src = k + ((int64_t)(start + n) * a.Hkv + g) * D + c * TPC;
+#pragma unroll
+            for (int u = 0; u < TPC; ++u) {
+                const float x0 = (float)src[u], x1 = (float)src[u + HALF];
+                const float s0 = x0 * cs[u] - x1 * sn[u];
+                const float s1 = x1 * cs[u] + x0 * sn[u];
+                ys0[u] = (f16)s0;
+                ys1[u] = (f16)s1;
+                ls0[u] = (f16)(s0 - (float)ys0[u]);
+                ls1[u] = (f16)(s1 - (float)ys1[u]);
+                kb0[u] = (bf16)s0;
+                kb1[u] = (bf16)s1;
+                if (bif) {
+                    const float r0 = x0 * cr[u] - x1 * sr[u];
+                    const float r1 = x1 * cr[u] + x0 * sr[u];
+                    yr0[u] = (f16)r0;
+                    yr1[u] = (f16)r1;
+                    lr0[u] = (f16)(r0 - (float)yr0[u]);
+                    lr1[u] = (f16)(r1 - (float)yr1[u]);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int u = 0; u < TPC; ++u) {
+                ys0[u] = ys1[u] = yr0[u] = yr1[u] = (f16)0.0f;
+                ls0[u] = ls1[u] = lr0[u] = lr1[u] = (f16)0.0f;
+                kb0[u] = kb1[u] = (bf16)0.0f;
+            }
+        }
+        const int64_t drow = ((int64_t)g * a.lay.T_pad + prow0 + r) * D + c * TPC;
+#pragma unroll
+        for (int u = 0; u < TPC; ++u) {
+            KS[drow + u] = ys0[u];
+            KS[drow + u + HALF] = ys1[u];
+        }
+        if (bif) {
+#pragma unroll
+            for (int u = 0; u < TPC; ++u) {
+                KR[drow + u] = yr0[u];
+                KR[drow + u + HALF] = yr1[u];
+            }
+        }
+        if (lo_row) {
+            const int64_t lrow =
+                ((int64_t)g * a.lay.lo_pad + e[kPlanLoOff] + n) * D + c * TPC;
+#pragma unroll
+            for (int u = 0; u < TPC; ++u) {
+                KSlo[lrow + u] = ls0[u];
+                KSlo[lrow + u + HALF] = ls1[u];
+            }
+            if (bif) {
+#pragma unroll
+                for (int u = 0; u < TPC; ++u) {
+                    KRlo[lrow + u] = lr0[u];
+                    KRlo[lrow + u + HALF] = lr1[u];
+                }
+            }
+        }
+        if (krot && valid) {
+            bf16* dst = krot + ((int64_t)(start + n) * a.Hkv + g) * D + c * TPC;
+#pragma unroll
+            for (int u = 0; u < TPC; ++u) {
+                dst[u] = kb0[u];
+                dst[u + HALF] = kb1[u];
+            }
+        }
+    }
+
+    // ---- values: transpose each head's [kBN][D] tile through LDS ----
+    for (int g = 0; g < a.Hkv; ++g) {
+        __syncthreads();
+        for (int idx = threadIdx.x; idx < kBN * D; idx += 256) {
+            const int rr = idx / D, dd = idx % D;
+            const int32_t nn = n0 + rr;
+            vs[rr * (D + 2) + dd] =
+                nn < len ? v[((int64_t)(start + nn) * a.Hkv + g) * D + dd] : (bf16)0.0f;
+        }
+        __syncthreads();
+        bf16* dst = VT + ((int64_t)g * a.lay.T_pad + prow0) * D;
+        for (int idx = threadIdx.x; idx < kBN * D; idx += 256) {
+            const int dd = idx / kBN, p = idx % kBN;
+            const int key = (p & ~15) | vt_perm16(p & 15);
+            dst[dd * kBN + p] = vs[key * (D + 2) + dd];
+        }
+    }
+}
+
+// fp32 path: rotated keys in the caller's token order, [Hkv][T][D] fp32.
+__global__ __launch_bounds__(256) void kv_prepass_f32_kernel(PrefillArgs a) {
+    const int32_t* plan = (const int32_t*)((char*)a.ws + a.lay.plan);
+    float* KS = (float*)((char*)a.ws + a.lay.ks32);
+    float* KR = (float*)((char*)a.ws + a.lay.kr32);
+    const float* k = (const float*)a.k;
+    float* krot = (float*)a.k_rot_out;
+    const int half = a.d / 2;
+    const int64_t item = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (item >= a.T * half) return;
+    const int64_t tok = item / half;
+    const int t = (int)(item % half);
+    // sequence of this token (linear scan: the fp32 path serves small cases)
+    int s = 0;
+    while (s + 1 < a.n_seqs && tok >= plan[(s + 1) * kPlanFields + kPlanStart]) ++s;
+    const int32_t* e = plan + s * kPlanFields;
+    if (tok < e[kPlanStart] || tok >= (int64_t)e[kPlanStart] + e[kPlanLen]) return;
+    const int32_t n = (int32_t)(tok - e[kPlanStart]);
+    float cs, sn, cr, sr;
+    rope_cs(n, a.tab.rev[t], cs, sn);
+    rope_cs(remap(n, e[kPlanG]), a.tab.rev[t], cr, sr);
+    for (int g = 0; g < a.Hkv; ++g) {
+        const float* src = k + (tok * a.Hkv + g) * (int64_t)a.d;
+        const float x0 = src[t], x1 = src[t + half];
+        const int64_t dst = ((int64_t)g * a.T + tok) * a.d;
+        KS[dst + t] = x0 * cs - x1 * sn;
+        KS[dst + t + half] = x1 * cs + x0 * sn;
+        KR[dst + t] = x0 * cr - x1 * sr;
+        KR[dst + t + half] = x1 * cr + x0 * sr;
+        if (krot) {
+            float* o = krot + (tok * a.Hkv + g) * (int64_t)a.d;
+            o[t] = KS[dst + t];
+            o[t + half] = KS[dst + t + half];
+        }
+    }
+}
+
+hipError_t launch_kv_prepass(const PrefillArgs& a, int dtype, hipStream_t s) {
+    if (dtype == 1) {
+        LaunchScope scope("kv_prepass_bf16", s);
+        const dim3 grid((unsigned)(a.lay.T_pad / kBN));
+        if (a.d == 128)
+            hipLaunchKernelGGL(kv_prepass_bf16_kernel<128>, grid, dim3(256), 0, s, a);
+        else
+            hipLaunchKernelGGL(kv_prepass_bf16_kernel<64>, grid, dim3(256), 0, s, a);
+    } else {
+        LaunchScope scope("kv_prepass_f32", s);
+        const int64_t items = a.T * (a.d / 2);
+        hipLaunchKernelGGL(kv_prepass_f32_kernel, dim3((unsigned)((items + 255) / 256)),
+                           dim3(256), 0, s, a);
+    }
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Test export of the index math the kernels use.
+__global__ void debug_index_kernel(int64_t L, int32_t w_pretrained, int32_t w_local,
+                                   int32_t bifocal, int32_t bm, int32_t bn, int32_t* G_out,
+                                   int32_t* f_out, uint8_t* band_out, uint8_t* tile_out) {
+    const int64_t G = group_size(L, w_pretrained);
+    const bool bif = bifocal && G > 1;
+    const int64_t n = L < 1024 ? L : 1024;
+    const int64_t nt_i = (L + bm - 1) / bm, nt_j = (L + bn - 1) / bn;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    const int64_t id0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (id0 == 0) G_out[0] = (int32_t)G;
+    for (int64_t x = id0; x < L; x += stride) f_out[x] = remap((int32_t)x, (int32_t)G);
+    for (int64_t x = id0; x < n * n; x += stride)
+        band_out[x] = (uint8_t)band(x / n, x % n, w_local, bif);
+    for (int64_t x = id0; x < nt_i * nt_j; x += stride) {
+        const int64_t a = x / nt_j, b = x % nt_j;
+        const int64_t i0 = a * bm, i1 = (a + 1) * bm < L ? (a + 1) * bm : L;
+        const int64_t j0 = b * bn, j1 = (b + 1) * bn < L ? (b + 1) * bn : L;
+        tile_out[x] = (uint8_t)tile_class(i0, i1, j0, j1, w_local, bif);
+    }
+}
+
+hipError_t launch_debug_index(int64_t L, int32_t w_pretrained, int32_t w_local, int32_t bifocal,
+                              int32_t bm, int32_t bn, int32_t* G_out, int32_t* f_out,
+                              uint8_t* band_out, uint8_t* tile_out, hipStream_t s) {
+    LaunchScope scope("debug_index", s);
+    hipLaunchKernelGGL(debug_index_kernel, dim3(256), dim3(256), 0, s, L, w_pretrained, w_local,
+                       bifocal, bm, bn, G_out, f_out, band_out, tile_out);
+    return hipGetLastError();
+}
+
+}  // namespace jl

@@ -1,0 +1,273 @@
+"""ctypes binding of libjetlong (argument marshalling only).
+
+Every step of the computation runs in the HIP kernels of ``libjetlong.so``;
+this module converts torch tensors to pointers, allocates outputs and the
+workspace with torch (device memory plumbing) and passes the caller's current
+HIP stream.  There is no fallback: if the library is missing or a call fails,
+an exception is raised.
+
+Pages cited:
+  [BT] "Jet-Long: 具有动态双焦RoPE的高效长上下文扩展" (bittide.aicompass.dev)
+  [TW] "NVIDIA研究团队找到了让AI“看清”超长文本的新方法" (techwalker.com)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import List, Optional, Sequence, Tuple, Union
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libjetlong.so")
+
+JL_OK = 0
+JL_ERR_INVALID_ARGUMENT = 1
+JL_ERR_UNSUPPORTED = 2
+JL_ERR_WORKSPACE_TOO_SMALL = 3
+JL_ERR_HIP = 4
+JL_DTYPE_F32 = 0
+JL_DTYPE_BF16 = 1
+
+
+class JLError(RuntimeError):
+    def __init__(self, status: int, fn: str, msg: str):
+        super().__init__("%s failed: %s (%s)" % (fn, _STATUS.get(status, status), msg))
+        self.status = status
+
+
+_STATUS = {0: "JL_OK", 1: "JL_ERR_INVALID_ARGUMENT", 2: "JL_ERR_UNSUPPORTED",
+           3: "JL_ERR_WORKSPACE_TOO_SMALL", 4: "JL_ERR_HIP"}
+
+
+class jl_params(ctypes.Structure):
+    _fields_ = [("w_pretrained", ctypes.c_int32), ("w_local", ctypes.c_int32),
+                ("rope_base", ctypes.c_double), ("softmax_scale", ctypes.c_float),
+                ("bifocal", ctypes.c_int32)]
+
+
+_lib = None
+_vp = ctypes.c_void_p
+_i32 = ctypes.c_int32
+_i64 = ctypes.c_int64
+
+
+def lib() -> ctypes.CDLL:
+    """Load libjetlong.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libjetlong.so is not built; run __graft_entry__.build() "
+                               "or python long_context_attention_jl_amd/build.py")
+        L = ctypes.CDLL(LIB_PATH)
+        L.jl_abi_version.restype = ctypes.c_int
+        L.jl_status_string.restype = ctypes.c_char_p
+        L.jl_status_string.argtypes = [ctypes.c_int]
+        L.jl_last_error.restype = ctypes.c_char_p
+        L.jl_group_size.restype = ctypes.c_int
+        L.jl_group_size.argtypes = [_i64, _i32, ctypes.POINTER(_i32)]
+        L.jl_rope_apply.restype = ctypes.c_int
+        L.jl_rope_apply.argtypes = [_vp, _vp, _vp, _i64, _i32, _i32, ctypes.c_double, _i32, ctypes.c_int, _vp]
+        L.jl_bifocal_prefill_workspace.restype = ctypes.c_int
+        L.jl_bifocal_prefill_workspace.argtypes = [_i64, _i32, _i32, _i32, _i32, ctypes.c_int,
+                                                   ctypes.POINTER(ctypes.c_size_t)]
+        L.jl_bifocal_prefill.restype = ctypes.c_int
+        L.jl_bifocal_prefill.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i64, _i32, _i32, _i32,
+                                         _i32, ctypes.POINTER(jl_params), ctypes.c_int, _vp, _vp,
+                                         ctypes.c_size_t, _vp]
+        L.jl_bifocal_decode_workspace.restype = ctypes.c_int
+        L.jl_bifocal_decode_workspace.argtypes = [_i32, _i32, _i32, _i32, _i32, ctypes.c_int,
+                                                  ctypes.POINTER(ctypes.c_size_t)]
+        L.jl_bifocal_decode.restype = ctypes.c_int
+        L.jl_bifocal_decode.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i64, _i32, _i32,
+                                        _i32, ctypes.POINTER(jl_params), ctypes.c_int, _vp,
+                                        ctypes.c_size_t, _vp]
+        L.jl_debug_index_math.restype = ctypes.c_int
+        L.jl_debug_index_math.argtypes = [_i64, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp]
+        L.jl_profile_enable.restype = ctypes.c_int
+        L.jl_profile_enable.argtypes = [_i32]
+        L.jl_profile_read.restype = ctypes.c_int
+        L.jl_profile_read.argtypes = [ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(_i32),
+                                      ctypes.POINTER(ctypes.c_double), _i32, ctypes.POINTER(_i32)]
+        _lib = L
+    return _lib
+
+
+def _check(st: int, fn: str) -> None:
+    if st != JL_OK:
+        msg = lib().jl_last_error()
+        raise JLError(st, fn, msg.decode() if msg else "")
+
+
+def _dtype(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return JL_DTYPE_BF16
+    if t.dtype == torch.float32:
+        return JL_DTYPE_F32
+    raise TypeError("libjetlong takes bfloat16 or float32 tensors, got %s" % t.dtype)
+
+
+def _dev(t: torch.Tensor, name: str) -> int:
+    if not t.is_cuda:
+        raise ValueError("%s must be a GPU tensor" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    return t.data_ptr()
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _params(w_pretrained, w_local, rope_base, softmax_scale, bifocal) -> jl_params:
+    return jl_params(int(w_pretrained), int(w_local), float(rope_base), float(softmax_scale),
+                     1 if bifocal else 0)
+
+
+def abi_version() -> int:
+    return lib().jl_abi_version()
+
+
+def group_size(L: int, w_pretrained: int) -> int:
+    """[BT] §3.1: G = max(1, ceil(L / w_pretrained)) (host, exact)."""
+    g = _i32()
+    _check(lib().jl_group_size(int(L), int(w_pretrained), ctypes.byref(g)), "jl_group_size")
+    return g.value
+
+
+def rope_apply(x: torch.Tensor, positions: torch.Tensor, rope_base: float, G: int = 1,
+               out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """out[t, h] = R(floor(positions[t] / G)) x[t, h]; x is [T, H, d] (bf16 or fp32)."""
+    T, H, d = x.shape
+    if out is None:
+        out = torch.empty_like(x)
+    pos = positions.to(device=x.device, dtype=torch.int32).contiguous()
+    _check(lib().jl_rope_apply(_dev(out, "out"), _dev(x, "x"), _dev(pos, "positions"), T, H, d,
+                               float(rope_base), int(G), _dtype(x), _stream()), "jl_rope_apply")
+    return out
+
+
+def prefill_workspace_bytes(T: int, n_seqs: int, Hq: int, Hkv: int, d: int, dtype) -> int:
+    n = ctypes.c_size_t()
+    dt = JL_DTYPE_BF16 if dtype == torch.bfloat16 else JL_DTYPE_F32
+    _check(lib().jl_bifocal_prefill_workspace(T, n_seqs, Hq, Hkv, d, dt, ctypes.byref(n)),
+           "jl_bifocal_prefill_workspace")
+    return n.value
+
+
+def _workspace(nbytes: int, device, ws: Optional[torch.Tensor]) -> torch.Tensor:
+    if ws is not None and ws.numel() * ws.element_size() >= nbytes:
+        return ws
+    # 256-byte aligned (torch's caching allocator aligns to at least 512 bytes)
+    return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+
+
+def bifocal_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, w_pretrained: int,
+                    w_local: int, rope_base: float, softmax_scale: float, bifocal: bool = True,
+                    cu_seqlens: Union[None, Sequence[int], torch.Tensor] = None,
+                    max_seqlen: Optional[int] = None, k_rot_out: Optional[torch.Tensor] = None,
+                    workspace: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                    lse_out: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Causal bifocal prefill ([BT] §3.2): q [T, Hq, d], k/v [T, Hkv, d] raw.
+    Returns (o [T, Hq, d], lse [Hq, T] float32)."""
+    T, Hq, d = q.shape
+    Hkv = k.shape[1]
+    dev = q.device
+    if cu_seqlens is None:
+        cu_t, n_seqs = None, 1
+        if max_seqlen is None:
+            max_seqlen = T
+    else:
+        if isinstance(cu_seqlens, torch.Tensor):
+            cu_t = cu_seqlens.to(device=dev, dtype=torch.int32).contiguous()
+            if max_seqlen is None:
+                max_seqlen = int((cu_t[1:] - cu_t[:-1]).max().item())
+        else:
+            cu_list = [int(x) for x in cu_seqlens]
+            cu_t = torch.tensor(cu_list, dtype=torch.int32, device=dev)
+            if max_seqlen is None:
+                max_seqlen = max(b - a for a, b in zip(cu_list[:-1], cu_list[1:]))
+        n_seqs = cu_t.numel() - 1
+    o = out if out is not None else torch.empty_like(q)
+    lse = lse_out if lse_out is not None else torch.empty((Hq, T), dtype=torch.float32, device=dev)
+    nbytes = prefill_workspace_bytes(T, n_seqs, Hq, Hkv, d, q.dtype)
+    ws = _workspace(nbytes, dev, workspace)
+    p = _params(w_pretrained, w_local, rope_base, softmax_scale, bifocal)
+    _check(lib().jl_bifocal_prefill(
+        _dev(o, "o"), _dev(lse, "lse"), _dev(q, "q"), _dev(k, "k"), _dev(v, "v"),
+        None if cu_t is None else _dev(cu_t, "cu_seqlens"), n_seqs, T, int(max_seqlen), Hq, Hkv,
+        d, ctypes.byref(p), _dtype(q), None if k_rot_out is None else _dev(k_rot_out, "k_rot_out"),
+        _dev(ws, "workspace"), ws.numel() * ws.element_size(), _stream()), "jl_bifocal_prefill")
+    return o, lse
+
+
+def decode_workspace_bytes(B: int, max_seqlen_k: int, Hq: int, Hkv: int, d: int, dtype) -> int:
+    n = ctypes.c_size_t()
+    dt = JL_DTYPE_BF16 if dtype == torch.bfloat16 else JL_DTYPE_F32
+    _check(lib().jl_bifocal_decode_workspace(B, max_seqlen_k, Hq, Hkv, d, dt, ctypes.byref(n)),
+           "jl_bifocal_decode_workspace")
+    return n.value
+
+
+def bifocal_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                   seqlens_k: Union[Sequence[int], torch.Tensor], *, w_pretrained: int,
+                   w_local: int, rope_base: float, softmax_scale: float, bifocal: bool = True,
+                   max_seqlen_k: Optional[int] = None, workspace: Optional[torch.Tensor] = None,
+                   out: Optional[torch.Tensor] = None,
+                   lse_out: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Bifocal decode ([TW] §三, [BT] §3.3): q [B, Hq, d] raw; caches
+    [B, S_max, Hkv, d] of standard-RoPE keys.  Returns (o [B, Hq, d], lse [B, Hq])."""
+    B, Hq, d = q.shape
+    S_max, Hkv = k_cache.shape[1], k_cache.shape[2]
+    dev = q.device
+    if isinstance(seqlens_k, torch.Tensor):
+        sl = seqlens_k.to(device=dev, dtype=torch.int32).contiguous()
+        if max_seqlen_k is None:
+            max_seqlen_k = int(sl.max().item())
+    else:
+        lens = [int(x) for x in seqlens_k]
+        sl = torch.tensor(lens, dtype=torch.int32, device=dev)
+        if max_seqlen_k is None:
+            max_seqlen_k = max(lens)
+    o = out if out is not None else torch.empty_like(q)
+    lse = lse_out if lse_out is not None else torch.empty((B, Hq), dtype=torch.float32, device=dev)
+    nbytes = decode_workspace_bytes(B, int(max_seqlen_k), Hq, Hkv, d, q.dtype)
+    ws = _workspace(nbytes, dev, workspace)
+    p = _params(w_pretrained, w_local, rope_base, softmax_scale, bifocal)
+    _check(lib().jl_bifocal_decode(
+        _dev(o, "o"), _dev(lse, "lse"), _dev(q, "q"), _dev(k_cache, "k_cache"),
+        _dev(v_cache, "v_cache"), _dev(sl, "seqlens_k"), B, int(max_seqlen_k), S_max, Hq, Hkv, d,
+        ctypes.byref(p), _dtype(q), _dev(ws, "workspace"), ws.numel() * ws.element_size(),
+        _stream()), "jl_bifocal_decode")
+    return o, lse
+
+
+def debug_index_math(L: int, w_pretrained: int, w_local: int, bifocal: bool, bm: int, bn: int,
+                     device="cuda"):
+    """Runs the kernels' device index functions; returns (G, f, band, tile) on the host."""
+    n = min(L, 1024)
+    nti, ntj = (L + bm - 1) // bm, (L + bn - 1) // bn
+    G = torch.zeros(1, dtype=torch.int32, device=device)
+    f = torch.zeros(L, dtype=torch.int32, device=device)
+    band = torch.zeros(n * n, dtype=torch.uint8, device=device)
+    tile = torch.zeros(nti * ntj, dtype=torch.uint8, device=device)
+    _check(lib().jl_debug_index_math(int(L), int(w_pretrained), int(w_local), 1 if bifocal else 0,
+                                     int(bm), int(bn), G.data_ptr(), f.data_ptr(), band.data_ptr(),
+                                     tile.data_ptr(), _stream()), "jl_debug_index_math")
+    torch.cuda.synchronize(device)
+    return (int(G.item()), f.cpu().numpy(), band.cpu().numpy().reshape(n, n),
+            tile.cpu().numpy().reshape(nti, ntj))
+
+
+def profile_enable(on: bool) -> None:
+    _check(lib().jl_profile_enable(1 if on else 0), "jl_profile_enable")
+
+
+def profile_read() -> dict:
+    """{kernel name: (launch count, total ms)} since the last enable/read."""
+    cap = 64
+    names = (ctypes.c_char_p * cap)()
+    counts = (_i32 * cap)()
+    tot = (ctypes.c_double * cap)()
+    n = _i32()
+    _check(lib().jl_profile_read(names, counts, tot, cap, ctypes.byref(n)), "jl_profile_read")
+    return {names[i].decode(): (counts[i], tot[i]) for i in range(min(n.value, cap))}

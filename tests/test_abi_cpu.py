@@ -1,0 +1,154 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, and rejects bad arguments on the host before any HIP call
+(fake, never-dereferenced pointers are enough to reach each check)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from long_context_attention_jl_amd import jetlong as jlb
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "jetlong.h")
+
+FAKE = 0x100000  # 256-byte aligned, never dereferenced by a failing call
+
+
+def _declared():
+    text = open(HEADER, encoding="utf-8").read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(jl_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = _declared()
+    for must in ("jl_rope_apply", "jl_bifocal_prefill", "jl_bifocal_decode", "jl_group_size",
+                 "jl_bifocal_prefill_workspace", "jl_bifocal_decode_workspace"):
+        assert must in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(jlb.LIB_PATH)
+    missing = [n for n in _declared() if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+def test_abi_version_and_status_strings():
+    assert jlb.abi_version() == 1
+    L = jlb.lib()
+    assert L.jl_status_string(0) == b"JL_OK"
+    assert L.jl_status_string(4) == b"JL_ERR_HIP"
+    assert L.jl_status_string(99) == b"JL_UNKNOWN_STATUS"
+
+
+@pytest.mark.parametrize("L,w,G", [(65536, 32768, 2), (131072, 32768, 4), (32768, 32768, 1),
+                                   (32769, 32768, 2), (1, 1, 1), (512, 128, 4), (98304, 32768, 3)])
+def test_group_size_host(L, w, G):
+    assert jlb.group_size(L, w) == G
+
+
+def test_group_size_rejects():
+    with pytest.raises(jlb.JLError) as e:
+        jlb.group_size(0, 5)
+    assert e.value.status == jlb.JL_ERR_INVALID_ARGUMENT
+    with pytest.raises(jlb.JLError):
+        jlb.group_size(5, 0)
+
+
+def _params(**kw):
+    d = dict(w_pretrained=32768, w_local=2048, rope_base=1e6, softmax_scale=0.088, bifocal=1)
+    d.update(kw)
+    return jlb.jl_params(d["w_pretrained"], d["w_local"], d["rope_base"], d["softmax_scale"],
+                         d["bifocal"])
+
+
+def _prefill(**kw):
+    a = dict(o=FAKE, lse=FAKE * 2, q=FAKE * 3, k=FAKE * 4, v=FAKE * 5, cu=None, n_seqs=1, T=1024,
+             max_seqlen=1024, Hq=32, Hkv=8, d=128, params=_params(), dtype=1, krot=None,
+             ws=FAKE * 8, ws_bytes=1 << 40, stream=None)
+    a.update(kw)
+    p = a["params"]
+    return jlb.lib().jl_bifocal_prefill(
+        a["o"], a["lse"], a["q"], a["k"], a["v"], a["cu"], a["n_seqs"], a["T"], a["max_seqlen"],
+        a["Hq"], a["Hkv"], a["d"], None if p is None else ctypes.byref(p), a["dtype"], a["krot"],
+        a["ws"], a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(o=None), 1), (dict(q=None), 1), (dict(ws=None), 1), (dict(params=None), 1),
+    (dict(T=0), 1), (dict(n_seqs=0), 1), (dict(n_seqs=2), 1), (dict(max_seqlen=0), 1),
+    (dict(max_seqlen=2000), 1), (dict(max_seqlen=512), 1), (dict(Hq=30), 1), (dict(Hkv=0), 1),
+    (dict(d=96), 2), (dict(d=65), 1), (dict(dtype=7), 2),
+    (dict(params=_params(w_pretrained=0)), 1), (dict(params=_params(w_local=-1)), 1),
+    (dict(params=_params(rope_base=0.0)), 1), (dict(params=_params(softmax_scale=0.0)), 1),
+    (dict(params=_params(softmax_scale=float("inf"))), 1), (dict(params=_params(bifocal=2)), 1),
+    (dict(ws_bytes=1000), 3), (dict(ws=FAKE * 8 + 4), 1), (dict(o=FAKE * 3), 1),
+    (dict(krot=FAKE * 4), 1), (dict(cu=FAKE * 9, n_seqs=70000, T=1 << 20, max_seqlen=1024), 2),
+])
+def test_prefill_validation(kw, status):
+    assert _prefill(**kw) == status
+    assert jlb.lib().jl_last_error()
+
+
+def test_prefill_workspace_query():
+    n = ctypes.c_size_t()
+    L = jlb.lib()
+    assert L.jl_bifocal_prefill_workspace(131072, 1, 32, 8, 128, 1, ctypes.byref(n)) == 0
+    # three bf16 key/value layouts of the padded sequence dominate
+    assert n.value >= 3 * 8 * 131072 * 128 * 2
+    assert L.jl_bifocal_prefill_workspace(512, 1, 1, 1, 64, 0, ctypes.byref(n)) == 0
+    assert n.value >= 2 * 512 * 64 * 4
+    assert L.jl_bifocal_prefill_workspace(0, 1, 1, 1, 64, 0, ctypes.byref(n)) == 1
+    assert L.jl_bifocal_prefill_workspace(10, 1, 3, 2, 64, 0, ctypes.byref(n)) == 1
+    assert L.jl_bifocal_prefill_workspace(10, 1, 1, 1, 80, 0, ctypes.byref(n)) == 2
+
+
+def _decode(**kw):
+    a = dict(o=FAKE, lse=FAKE * 2, q=FAKE * 3, kc=FAKE * 4, vc=FAKE * 5, sl=FAKE * 6, B=1,
+             max_L=131072, S_max=131072, Hq=32, Hkv=8, d=128, params=_params(), dtype=1,
+             ws=FAKE * 8, ws_bytes=1 << 40, stream=None)
+    a.update(kw)
+    p = a["params"]
+    return jlb.lib().jl_bifocal_decode(
+        a["o"], a["lse"], a["q"], a["kc"], a["vc"], a["sl"], a["B"], a["max_L"], a["S_max"],
+        a["Hq"], a["Hkv"], a["d"], None if p is None else ctypes.byref(p), a["dtype"], a["ws"],
+        a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(o=None), 1), (dict(sl=None), 1), (dict(kc=None), 1), (dict(B=0), 1),
+    (dict(max_L=0), 1), (dict(S_max=100), 1), (dict(Hq=33), 1), (dict(Hq=34, Hkv=2), 2),
+    (dict(d=32), 2), (dict(dtype=3), 2), (dict(params=_params(w_local=-5)), 1),
+    (dict(ws_bytes=16), 3), (dict(ws=FAKE * 8 + 128), 1), (dict(o=FAKE * 4), 1),
+    (dict(B=70000), 2),
+])
+def test_decode_validation(kw, status):
+    assert _decode(**kw) == status
+
+
+def test_rope_validation():
+    L = jlb.lib()
+    assert L.jl_rope_apply(None, FAKE, FAKE, 10, 1, 64, 1e4, 1, 1, None) == 1
+    assert L.jl_rope_apply(FAKE, FAKE, FAKE, 0, 1, 64, 1e4, 1, 1, None) == 1
+    assert L.jl_rope_apply(FAKE, FAKE, FAKE, 10, 1, 48, 1e4, 1, 1, None) == 2
+    assert L.jl_rope_apply(FAKE, FAKE, FAKE, 10, 1, 64, -1.0, 1, 1, None) == 1
+    assert L.jl_rope_apply(FAKE, FAKE, FAKE, 10, 1, 64, 1e4, 0, 1, None) == 1
+
+
+def test_debug_and_profile_validation():
+    L = jlb.lib()
+    assert L.jl_debug_index_math(0, 8, 2, 1, 16, 16, FAKE, FAKE, FAKE, FAKE, None) == 1
+    assert L.jl_debug_index_math(10, 8, 2, 1, 0, 16, FAKE, FAKE, FAKE, FAKE, None) == 1
+    assert L.jl_debug_index_math(10, 8, 2, 1, 16, 16, None, FAKE, FAKE, FAKE, None) == 1
+    n = ctypes.c_int32()
+    assert L.jl_profile_read(None, None, None, 0, ctypes.byref(n)) == 0
+    assert n.value == 0
+    assert L.jl_profile_read(None, None, None, 0, None) == 1
+
+
+def test_binding_fails_loudly_without_library(monkeypatch):
+    monkeypatch.setattr(jlb, "_lib", None)
+    monkeypatch.setattr(jlb, "LIB_PATH", "/nonexistent/libjetlong.so")
+    with pytest.raises(RuntimeError):
+        jlb.lib()
