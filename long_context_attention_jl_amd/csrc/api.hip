@@ -108,11 +108,12 @@ PrefillLayout prefill_layout(int64_t T, int32_t n_seqs, int32_t Hkv, int32_t d, 
     L.plan = off;
     off = align256(off + (size_t)(n_seqs + 1) * kPlanFields * sizeof(int32_t));
     if (dtype == JL_DTYPE_BF16) {
-        const size_t kb = (size_t)Hkv * L.T_pad * d * 2;
-        const size_t lb = (size_t)Hkv * L.lo_pad * d * 2;
+        const size_t kb = (size_t)Hkv * (L.T_pad / kBN) * ktile_elems(d) * 2;
+        const size_t vb = (size_t)Hkv * (L.T_pad / kBN) * vtile_elems(d) * 2;
+        const size_t lb = (size_t)Hkv * (L.lo_pad / kBN) * ktile_elems(d) * 2;
         L.ks = off; off = align256(off + kb);
         L.kr = off; off = align256(off + kb);
-        L.vt = off; off = align256(off + kb);
+        L.vt = off; off = align256(off + vb);
         L.ks_lo = off; off = align256(off + lb);
         L.kr_lo = off; off = align256(off + lb);
     } else {
@@ -128,7 +129,13 @@ DecodeLayout decode_layout(int32_t B, int32_t max_seqlen_k, int32_t Hq, int32_t 
     DecodeLayout L{};
     const int nw = Hkv < 8 ? Hkv : 8;
     const int64_t groups = (Hkv + nw - 1) / nw;
-    const int64_t target = 512;  // about two workgroups per compute unit
+    // about one resident workgroup (8 waves) per compute unit; JL_DECODE_WGS
+    // overrides the target for tuning
+    int64_t target = 256;
+    if (const char* e = getenv("JL_DECODE_WGS")) {
+        const long v = strtol(e, nullptr, 10);
+        if (v >= 1 && v <= 65536) target = v;
+    }
     int64_t want = (target + (int64_t)B * groups - 1) / ((int64_t)B * groups);
     if (want < 1) want = 1;
     int64_t chunk = (max_seqlen_k + want - 1) / want;
@@ -145,11 +152,10 @@ DecodeLayout decode_layout(int32_t B, int32_t max_seqlen_k, int32_t Hq, int32_t 
     return L;
 }
 
-RopeTable make_rope_table(double base, int d) {
-    RopeTable t{};
-    for (int i = 0; i < d / 2 && i < 64; ++i)
-        t.rev[i] = pow(base, -2.0 * (double)i / (double)d) / (2.0 * 3.14159265358979323846);
-    return t;
+RopeFreq make_rope_freq(double base, int d) {
+    RopeFreq f;
+    f.c = -2.0 * log2(base) / (double)d;
+    return f;
 }
 
 }  // namespace jl
@@ -226,7 +232,7 @@ jl_status jl_rope_apply(void* out, const void* x, const int32_t* positions, int6
     if (G < 1) return fail(JL_ERR_INVALID_ARGUMENT, "G must be >= 1");
     if (T > (1LL << 40) / ((int64_t)H * d)) return fail(JL_ERR_INVALID_ARGUMENT, "T*H*d too large");
     hipStream_t s = (hipStream_t)stream;
-    hipError_t e = launch_rope_apply(out, x, positions, T, H, d, make_rope_table(rope_base, d), G,
+    hipError_t e = launch_rope_apply(out, x, positions, T, H, d, make_rope_freq(rope_base, d), G,
                                      dtype, s);
     if (e != hipSuccess) return hip_fail(e, "jl_rope_apply launch");
     return finish(s, "jl_rope_apply");
@@ -288,7 +294,7 @@ jl_status jl_bifocal_prefill(void* o, float* lse, const void* q, const void* k, 
     a.n_seqs = n_seqs; a.Hq = Hq; a.Hkv = Hkv; a.d = d; a.max_seqlen = max_seqlen; a.T = T;
     a.w_local = params->w_local; a.bifocal = params->bifocal;
     a.softmax_scale = params->softmax_scale;
-    a.tab = make_rope_table(params->rope_base, d);
+    a.tab = make_rope_freq(params->rope_base, d);
 
     hipStream_t s = (hipStream_t)stream;
     hipError_t e = launch_plan((int32_t*)((char*)workspace + lay.plan), cu_seqlens, n_seqs, T,
@@ -348,7 +354,7 @@ jl_status jl_bifocal_decode(void* o, float* lse, const void* q, const void* k_ca
     a.B = batch; a.max_seqlen_k = max_seqlen_k; a.Hq = Hq; a.Hkv = Hkv; a.d = d; a.S_max = S_max;
     a.w_pretrained = params->w_pretrained; a.w_local = params->w_local;
     a.bifocal = params->bifocal; a.softmax_scale = params->softmax_scale;
-    a.tab = make_rope_table(params->rope_base, d);
+    a.tab = make_rope_freq(params->rope_base, d);
     hipStream_t s = (hipStream_t)stream;
     hipError_t e = launch_decode(a, dtype, s);
     if (e != hipSuccess) return hip_fail(e, "decode launch");

@@ -15,6 +15,7 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16;
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -31,6 +32,14 @@ constexpr int kBM = kWaveRows * kWaves;  // 256 query rows per workgroup
 // score almost undiluted.  Keys they read are < kPreciseRows as well.
 constexpr int kPreciseRows = 2048;
 constexpr int kPlanFields = 8;      // int32 fields per sequence in the plan
+
+// Key and value tiles are stored in the workspace exactly as they sit in LDS
+// (rows padded by 8 halves against bank conflicts), so the prefill kernel
+// fills LDS with flat global->LDS DMA copies.
+__host__ __device__ constexpr int kstr(int d) { return d + 8; }       // K row stride (halves)
+constexpr int kVStr = kBN + 8;                                        // V^T row stride (halves)
+__host__ __device__ constexpr int ktile_elems(int d) { return kBN * kstr(d); }
+__host__ __device__ constexpr int vtile_elems(int d) { return d * kVStr; }
 
 // Plan fields (per sequence s, written by the plan kernel).
 enum PlanField {
@@ -83,14 +92,31 @@ __host__ __device__ inline uint32_t tile_class(int64_t i0, int64_t i1, int64_t j
     return c;
 }
 
+__host__ __device__ inline uint32_t tile_class32(int32_t i0, int32_t i1, int32_t j0, int32_t j1,
+                                                 int32_t w_local, bool bif) {
+    if (j0 > i1 - 1) return 0;
+    uint32_t c = (j1 - 1 > i0) ? kHasMasked : 0u;
+    const int32_t dmax = (i1 - 1) - j0;
+    const int32_t dmin = (i0 - (j1 - 1)) > 0 ? (i0 - (j1 - 1)) : 0;
+    if (!bif) return c | kHasLocal;
+    if (dmin < w_local) c |= kHasLocal;
+    if (dmax >= w_local) c |= kHasRemote;
+    return c;
+}
+
 // ---------------------------------------------------------------------------
-// RoPE angles.  theta_t = base^(-2t/d) is passed in revolutions
-// (theta_t / 2pi, computed on the host in fp64).  The angle p * theta_t is
-// reduced modulo one revolution in fp64, so sin/cos see |arg| <= pi and keep
-// fp32 accuracy for any position below 2^31.
-struct RopeTable {
-    double rev[64];  // theta_t / (2 pi), t < d/2 (d <= 128)
+// RoPE angles.  theta_t = base^(-2t/d) is formed on the device as
+// exp2(t * c), c = -2 log2(base) / d (fp64), and used in revolutions
+// (theta_t / 2pi).  The angle p * theta_t is reduced modulo one revolution in
+// fp64, so sin/cos see |arg| <= pi and keep fp32 accuracy for any position
+// below 2^31.
+struct RopeFreq {
+    double c;  // -2 log2(base) / d
 };
+
+__device__ __forceinline__ double rope_rev(const RopeFreq& f, int t) {
+    return exp2(f.c * (double)t) * 0.15915494309189533576888376337251;
+}
 
 __device__ __forceinline__ void rope_cs(int64_t p, double rev_t, float& c, float& s) {
     double x = (double)p * rev_t;
@@ -99,6 +125,14 @@ __device__ __forceinline__ void rope_cs(int64_t p, double rev_t, float& c, float
     sincosf(a, &s, &c);
 }
 
-__device__ __forceinline__ float bf16_to_f32(bf16 x) { return (float)x; }
+// Same angle through the hardware sine and cosine (v_sin_f32 / v_cos_f32 take
+// their argument in revolutions); used where many angles are needed per key.
+__device__ __forceinline__ void rope_cs_hw(int64_t p, double rev_t, float& c, float& s) {
+    double x = (double)p * rev_t;
+    x -= rint(x);
+    const float r = (float)x;
+    s = __builtin_amdgcn_sinf(r);
+    c = __builtin_amdgcn_cosf(r);
+}
 
 }  // namespace jl

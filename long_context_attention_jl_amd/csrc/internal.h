@@ -35,10 +35,10 @@ struct DecodeLayout {
 };
 DecodeLayout decode_layout(int32_t batch, int32_t max_seqlen_k, int32_t Hq, int32_t Hkv, int32_t d);
 
-RopeTable make_rope_table(double base, int d);
+RopeFreq make_rope_freq(double base, int d);
 
 hipError_t launch_rope_apply(void* out, const void* x, const int32_t* pos, int64_t T, int32_t H,
-                             int32_t d, const RopeTable& tab, int32_t G, int dtype,
+                             int32_t d, const RopeFreq& tab, int32_t G, int dtype,
                              hipStream_t s);
 
 hipError_t launch_plan(int32_t* plan, const int32_t* cu, int32_t n_seqs, int64_t T,
@@ -57,7 +57,7 @@ struct PrefillArgs {
     int64_t T;
     int32_t w_local, bifocal;
     float softmax_scale;
-    RopeTable tab;
+    RopeFreq tab;
 };
 
 hipError_t launch_kv_prepass(const PrefillArgs& a, int dtype, hipStream_t s);
@@ -77,7 +77,7 @@ struct DecodeArgs {
     int64_t S_max;
     int32_t w_pretrained, w_local, bifocal;
     float softmax_scale;
-    RopeTable tab;
+    RopeFreq tab;
 };
 hipError_t launch_decode(const DecodeArgs& a, int dtype, hipStream_t s);
 

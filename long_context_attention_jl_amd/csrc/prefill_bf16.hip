@@ -32,8 +32,10 @@
 // over the keys does not shrink (the softmax-weighted mean key points along
 // the query), so its size sets the LSE error directly.  The QK^T product
 // therefore uses fp16 operands (11-bit significand, same MFMA rate as bf16 on
-// gfx950): rotated q and k must stay below 65504 in magnitude.  P and V stay
-// bf16 for the PV product.  Rows below kPreciseRows, which see few keys, add
+// gfx950): rotated q and k must stay below 65504 in magnitude.  PV runs on
+// fp16 too: V (bf16 input, exact in fp16 within its range) and the
+// probabilities, whose row sum is taken from the same fp16 values with
+// v_dot2_f32_f16 so numerator and denominator agree.  Rows below kPreciseRows, which see few keys, add
 // the fp16 residuals of q and k (hi * hi + hi * lo + lo * hi).
 #include "internal.h"
 
@@ -53,10 +55,16 @@ struct Cfg {
     static constexpr int NK = PRECISE ? 4 : 2; // KS, KR (+ KS_lo, KR_lo)
     static constexpr int NBUF = PRECISE ? 1 : 2;
     static constexpr int BUF = NK * KSLOT + VSLOT;
-    static constexpr int LDS_BYTES = NBUF * BUF * 2;
+    static constexpr int QIMG = 2 * kBM * KSTR * 2;    // rotated-query images (prologue)
+    static constexpr int LDS_BYTES = (NBUF * BUF * 2) > QIMG ? (NBUF * BUF * 2) : QIMG;
     static constexpr int CH = D * kBN * 2 / 16 / 512;  // 16-byte chunks per thread per slot
     static constexpr int NS = D / 16;                   // k-steps of a QK^T product
     static constexpr int ND = D / 32;                   // 32-row blocks of O^T
+};
+
+template <bool B>
+struct BoolC {
+    static constexpr bool value = B;
 };
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
@@ -75,7 +83,11 @@ __global__ __launch_bounds__(512) void prefill_bf16_kernel(PrefillArgs a, int rb
     extern __shared__ __align__(16) char smem_raw[];
     bf16* lds = reinterpret_cast<bf16*>(smem_raw);
 
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    // the wave index is uniform per wave; readfirstlane tells the compiler so,
+    // which keeps every per-wave tile-class branch a scalar branch (otherwise
+    // all score paths would run under lane masks, MFMAs included)
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int qr = lane & 31, hh = lane >> 5;  // query column, lane half
 
     // ---- which (head, sequence, row block) ----
@@ -98,100 +110,104 @@ __global__ __launch_bounds__(512) void prefill_bf16_kernel(PrefillArgs a, int rb
     const int32_t myrow = wr0 + qr;
     const bool row_valid = myrow < len;
 
-    // ---- rotate this lane's query values into B-operand registers ----
-    // lane (qr, hh) holds d = 16*st + 8*hh + u for st < NS, u < 8; the RoPE
-    // partner of step st is step st + NS/2.
+    // ---- rotated, scaled queries as MFMA B operands ----
+    // The workgroup rotates its 256 query rows cooperatively into LDS (the
+    // K/V buffers are not in use yet): thread (t, r) handles pair t of rows
+    // r, r + 512/(D/2), ...; then lane (qr, hh) of each wave reads its
+    // operand registers, d = 16*st + 8*hh + u, as 16-byte vectors.
     f16x8 QS[C::NS], QR[C::NS], QSl[C::NS], QRl[C::NS];
     {
         const float qscale = a.softmax_scale * kLog2e;
-        float xq[C::NS][8];
-        const bf16* qp = (const bf16*)a.q + ((int64_t)(start + myrow) * a.Hq + head) * D + 8 * hh;
-#pragma unroll
-        for (int st = 0; st < C::NS; ++st) {
-            bf16x8 raw = {};
-            if (row_valid) raw = *reinterpret_cast<const bf16x8*>(qp + 16 * st);
-#pragma unroll
-            for (int u = 0; u < 8; ++u) xq[st][u] = (float)raw[u];
-        }
-        const int32_t fpos = remap(myrow, G);
-#pragma unroll
-        for (int st = 0; st < C::NS / 2; ++st) {
-#pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const int t = 16 * st + 8 * hh + u;
-                const float x0 = xq[st][u], x1 = xq[st + C::NS / 2][u];
+        constexpr int HALF = D / 2;
+        f16* qs_l = reinterpret_cast<f16*>(smem_raw);
+        f16* qr_l = qs_l + kBM * C::KSTR;
+        const int t = tid % HALF;
+        const double rv = rope_rev(a.tab, t);
+        const bf16* qg = (const bf16*)a.q + (int64_t)head * D;
+        for (int round = 0; round < (PRECISE ? 2 : 1); ++round) {
+#pragma unroll 1
+            for (int r = tid / HALF; r < kBM; r += 512 / HALF) {
+                const int32_t row = row0 + r;
+                float x0 = 0.0f, x1 = 0.0f;
+                if (row < len) {
+                    const bf16* qp = qg + (int64_t)(start + row) * a.Hq * D;
+                    x0 = (float)qp[t];
+                    x1 = (float)qp[t + HALF];
+                }
                 float c, sn;
-                rope_cs(myrow, a.tab.rev[t], c, sn);
+                rope_cs(row, rv, c, sn);
                 float y0 = (x0 * c - x1 * sn) * qscale, y1 = (x1 * c + x0 * sn) * qscale;
-                QS[st][u] = (f16)y0;
-                QS[st + C::NS / 2][u] = (f16)y1;
-                if constexpr (PRECISE) {
-                    QSl[st][u] = (f16)(y0 - (float)QS[st][u]);
-                    QSl[st + C::NS / 2][u] = (f16)(y1 - (float)QS[st + C::NS / 2][u]);
+                if (round == 0) {
+                    qs_l[r * C::KSTR + t] = (f16)y0;
+                    qs_l[r * C::KSTR + t + HALF] = (f16)y1;
+                } else {
+                    qs_l[r * C::KSTR + t] = (f16)(y0 - (float)(f16)y0);
+                    qs_l[r * C::KSTR + t + HALF] = (f16)(y1 - (float)(f16)y1);
                 }
                 if (bif) {
-                    rope_cs(fpos, a.tab.rev[t], c, sn);
+                    rope_cs(remap(row, G), rv, c, sn);
                     y0 = (x0 * c - x1 * sn) * qscale;
                     y1 = (x1 * c + x0 * sn) * qscale;
                 }
-                QR[st][u] = (f16)y0;
-                QR[st + C::NS / 2][u] = (f16)y1;
-                if constexpr (PRECISE) {
-                    QRl[st][u] = (f16)(y0 - (float)QR[st][u]);
-                    QRl[st + C::NS / 2][u] = (f16)(y1 - (float)QR[st + C::NS / 2][u]);
+                if (round == 0) {
+                    qr_l[r * C::KSTR + t] = (f16)y0;
+                    qr_l[r * C::KSTR + t + HALF] = (f16)y1;
+                } else {
+                    qr_l[r * C::KSTR + t] = (f16)(y0 - (float)(f16)y0);
+                    qr_l[r * C::KSTR + t + HALF] = (f16)(y1 - (float)(f16)y1);
                 }
             }
+            __syncthreads();
+            const int qoff = (wave * kWaveRows + qr) * C::KSTR + 8 * hh;
+#pragma unroll
+            for (int st = 0; st < C::NS; ++st) {
+                const f16x8 vs = *reinterpret_cast<const f16x8*>(qs_l + qoff + 16 * st);
+                const f16x8 vr = *reinterpret_cast<const f16x8*>(qr_l + qoff + 16 * st);
+                if (round == 0) {
+                    QS[st] = vs;
+                    QR[st] = vr;
+                } else {
+                    QSl[st] = vs;
+                    QRl[st] = vr;
+                }
+            }
+            __syncthreads();
         }
     }
 
-    // ---- global tile sources ----
-    const int64_t pad_off = e[kPlanPadOff];
-    const bf16* KSg = (const bf16*)((const char*)a.ws + a.lay.ks) + ((int64_t)g * a.lay.T_pad + pad_off) * D;
-    const bf16* KRg = (const bf16*)((const char*)a.ws + a.lay.kr) + ((int64_t)g * a.lay.T_pad + pad_off) * D;
-    const bf16* VTg = (const bf16*)((const char*)a.ws + a.lay.vt) + ((int64_t)g * a.lay.T_pad + pad_off) * D;
-    const bf16* KSlg = (const bf16*)((const char*)a.ws + a.lay.ks_lo) + ((int64_t)g * a.lay.lo_pad + e[kPlanLoOff]) * D;
-    const bf16* KRlg = (const bf16*)((const char*)a.ws + a.lay.kr_lo) + ((int64_t)g * a.lay.lo_pad + e[kPlanLoOff]) * D;
+    const int64_t ntp = a.lay.T_pad / kBN, ntl = a.lay.lo_pad / kBN;
+    const bf16* KSg = (const bf16*)((const char*)a.ws + a.lay.ks) + ((int64_t)g * ntp + e[kPlanTile0]) * C::KSLOT;
+    const bf16* KRg = (const bf16*)((const char*)a.ws + a.lay.kr) + ((int64_t)g * ntp + e[kPlanTile0]) * C::KSLOT;
+    const bf16* VTg = (const bf16*)((const char*)a.ws + a.lay.vt) + ((int64_t)g * ntp + e[kPlanTile0]) * C::VSLOT;
+    const bf16* KSlg = (const bf16*)((const char*)a.ws + a.lay.ks_lo) + ((int64_t)g * ntl + e[kPlanLoTile0]) * C::KSLOT;
+    const bf16* KRlg = (const bf16*)((const char*)a.ws + a.lay.kr_lo) + ((int64_t)g * ntl + e[kPlanLoTile0]) * C::KSLOT;
 
     const int ntiles = (row_end + kBN - 1) / kBN;
-    u32x4 rk[C::NK][C::CH];
-    u32x4 rv[C::CH];
 
     auto tile_need = [&](int tau) -> uint32_t {
-        return tile_class(row0, row_end, (int64_t)tau * kBN, (int64_t)tau * kBN + kBN, a.w_local, bif);
+        return tile_class32(row0, row_end, tau * kBN, tau * kBN + kBN, a.w_local, bif);
     };
-    auto gload = [&](int tau, uint32_t cls) {
-        const int64_t off = (int64_t)tau * kBN * D;
-#pragma unroll
-        for (int c = 0; c < C::CH; ++c) {
-            const int64_t ch = (int64_t)(tid + 512 * c) * 8;
-            if (cls & kHasLocal) {
-                rk[0][c] = *reinterpret_cast<const u32x4*>(KSg + off + ch);
-                if constexpr (PRECISE) rk[2][c] = *reinterpret_cast<const u32x4*>(KSlg + off + ch);
-            }
-            if (cls & kHasRemote) {
-                rk[1][c] = *reinterpret_cast<const u32x4*>(KRg + off + ch);
-                if constexpr (PRECISE) rk[3][c] = *reinterpret_cast<const u32x4*>(KRlg + off + ch);
-            }
-            rv[c] = *reinterpret_cast<const u32x4*>(VTg + off + ch);
+    // global -> LDS DMA of one tile image: each wave instruction moves 64 x 16
+    // contiguous bytes; the workspace holds the tiles in their LDS layout.
+    auto dma = [&](const bf16* src, bf16* dst, int elems) {
+        const int nchunk = elems / 8;
+        for (int c0 = wave * 64; c0 < nchunk; c0 += 512) {
+            if (c0 + lane < nchunk)
+                __builtin_amdgcn_global_load_lds((const void*)(src + (int64_t)(c0 + lane) * 8),
+                                                 (void*)(dst + c0 * 8), 16, 0, 0);
         }
     };
-    auto lstore = [&](int buf, uint32_t cls) {
+    auto load_tile = [&](int tau, int buf, uint32_t cls) {
         bf16* base = lds + buf * C::BUF;
-#pragma unroll
-        for (int c = 0; c < C::CH; ++c) {
-            const int ch = tid + 512 * c;
-            const int kr = ch / (D / 8), kc = (ch % (D / 8)) * 8;
-            const int vr = ch / (kBN / 8), vc = (ch % (kBN / 8)) * 8;
-            if (cls & kHasLocal) {
-                *reinterpret_cast<u32x4*>(base + 0 * C::KSLOT + kr * C::KSTR + kc) = rk[0][c];
-                if constexpr (PRECISE) *reinterpret_cast<u32x4*>(base + 2 * C::KSLOT + kr * C::KSTR + kc) = rk[2][c];
-            }
-            if (cls & kHasRemote) {
-                *reinterpret_cast<u32x4*>(base + 1 * C::KSLOT + kr * C::KSTR + kc) = rk[1][c];
-                if constexpr (PRECISE) *reinterpret_cast<u32x4*>(base + 3 * C::KSLOT + kr * C::KSTR + kc) = rk[3][c];
-            }
-            *reinterpret_cast<u32x4*>(base + C::NK * C::KSLOT + vr * C::VSTR + vc) = rv[c];
+        if (cls & kHasLocal) {
+            dma(KSg + (int64_t)tau * C::KSLOT, base, C::KSLOT);
+            if constexpr (PRECISE) dma(KSlg + (int64_t)tau * C::KSLOT, base + 2 * C::KSLOT, C::KSLOT);
         }
+        if (cls & kHasRemote) {
+            dma(KRg + (int64_t)tau * C::KSLOT, base + C::KSLOT, C::KSLOT);
+            if constexpr (PRECISE) dma(KRlg + (int64_t)tau * C::KSLOT, base + 3 * C::KSLOT, C::KSLOT);
+        }
+        dma(VTg + (int64_t)tau * C::VSLOT, base + C::NK * C::KSLOT, C::VSLOT);
     };
 
     // ---- running softmax state (log2 domain) and O^T accumulators ----
@@ -217,16 +233,104 @@ __global__ __launch_bounds__(512) void prefill_bf16_kernel(PrefillArgs a, int rb
         return acc;
     };
 
+    // Raises the running max when a score exceeds it by more than 8 (log2
+    // units).  Sums stay exact relative to whatever max they use, p stays
+    // below 2^8, and most tiles skip rescaling O entirely.
+    auto maybe_raise = [&](float mx) {
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const bool raise = mx > m_run + 8.0f;
+        if (__any(raise)) {
+            const float m_new = raise ? mx : m_run;
+            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+            m_run = m_new;
+            l_run *= alpha;
+#pragma unroll
+            for (int db = 0; db < C::ND; ++db)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) O[db][i] *= alpha;
+        }
+    };
+    const f16x2 ones = {(f16)1.0f, (f16)1.0f};
+    // p = exp2(s - m) as fp16 B operands, and their row sum
+    auto probs = [&](const f32x16& Sb, f16x8* Pb) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) Pb[i >> 3][i & 7] = (f16)__builtin_amdgcn_exp2f(Sb[i] - m_run);
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+            for (int i = 0; i < 8; i += 2) {
+                const f16x2 pp = {Pb[h2][i], Pb[h2][i + 1]};
+                l_run = __builtin_amdgcn_fdot2(pp, ones, l_run, false);
+            }
+    };
+    // O^T += V^T P^T for one 32-key block (two 16-key steps)
+    auto pv = [&](const bf16* vb, int b, const f16x8* Pb) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int db = 0; db < C::ND; ++db) {
+                const f16x8 vv = *reinterpret_cast<const f16x8*>(
+                    vb + (32 * db + qr) * C::VSTR + 32 * b + 16 * u + 8 * hh);
+                O[db] = mfma32h(vv, Pb[u], O[db]);
+            }
+    };
+
+    // Fast path: the wave's whole tile is local or remote and unmasked.  Both
+    // score blocks are issued first; then block 0's probabilities; then the
+    // block-0 PV products are interleaved with block 1's exponentials so the
+    // matrix unit and the vector ALU work at the same time.
+    auto fast_tile = [&](const bf16* base, auto remote_c) {
+        constexpr bool REMOTE = decltype(remote_c)::value;
+        const f16x8* Q = REMOTE ? QR : QS;
+        const bf16* kp = base + (REMOTE ? C::KSLOT : 0) + qr * C::KSTR + 8 * hh;
+        f32x16 S0 = {}, S1 = {};
+#pragma unroll
+        for (int st = 0; st < C::NS; ++st)
+            S0 = mfma32h(*reinterpret_cast<const f16x8*>(kp + 16 * st), Q[st], S0);
+#pragma unroll
+        for (int st = 0; st < C::NS; ++st)
+            S1 = mfma32h(*reinterpret_cast<const f16x8*>(kp + 32 * C::KSTR + 16 * st), Q[st], S1);
+        float mx = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, fmaxf(S0[i], S1[i]));
+        maybe_raise(mx);
+        const bf16* vb = base + C::NK * C::KSLOT;
+        f16x8 P0[2], P1[2];
+        probs(S0, P0);
+        pv(vb, 0, P0);
+        probs(S1, P1);
+        // PV(block 0): 8 x (1 LDS read + 1 MFMA) interleaved with the 48
+        // vector instructions of block 1's probabilities
+#pragma unroll
+        for (int g = 0; g < 8; ++g) {
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // VALU
+        }
+        pv(vb, 1, P1);
+    };
+
     auto compute = [&](int tau, int buf) {
         const bf16* base = lds + buf * C::BUF;
         const int32_t j0 = tau * kBN;
-        if (tile_class(wr0, wr_end, j0, j0 + kBN, a.w_local, bif) == 0) return;
+        const uint32_t tc = tile_class32(wr0, wr_end, j0, j0 + kBN, a.w_local, bif);
+        if (tc == 0) return;
+        if constexpr (!PRECISE) {
+            if (tc == kHasLocal) {
+                fast_tile(base, BoolC<false>{});
+                return;
+            }
+            if (tc == kHasRemote) {
+                fast_tile(base, BoolC<true>{});
+                return;
+            }
+        }
         f32x16 S[2];
         uint32_t bcls[2];
 #pragma unroll
         for (int b = 0; b < 2; ++b) {
             const int32_t jb = j0 + 32 * b;
-            bcls[b] = tile_class(wr0, wr_end, jb, jb + 32, a.w_local, bif);
+            bcls[b] = tile_class32(wr0, wr_end, jb, jb + 32, a.w_local, bif);
             if (bcls[b] == 0) {
 #pragma unroll
                 for (int i = 0; i < 16; ++i) S[b][i] = -INFINITY;
@@ -254,70 +358,36 @@ __global__ __launch_bounds__(512) void prefill_bf16_kernel(PrefillArgs a, int rb
                 }
             }
         }
-        // online softmax over this tile's 32 scores per lane (+ partner lane)
         float mx = -INFINITY;
 #pragma unroll
-        for (int b = 0; b < 2; ++b)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) mx = fmaxf(mx, S[b][i]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float m_new = fmaxf(m_run, mx);
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-        m_run = m_new;
-        float ls = 0.0f;
-        bf16x8 P[2][2];
-#pragma unroll
-        for (int b = 0; b < 2; ++b)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const float p = __builtin_amdgcn_exp2f(S[b][i] - m_new);
-                ls += p;
-                P[b][i >> 3][i & 7] = (bf16)p;
-            }
-        l_run = l_run * alpha + ls;
-#pragma unroll
-        for (int db = 0; db < C::ND; ++db)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) O[db][i] *= alpha;
-        // O^T += V^T P^T over the tile's four 16-key steps
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, fmaxf(S[0][i], S[1][i]));
+        maybe_raise(mx);
+        f16x8 P[2][2];
+        probs(S[0], P[0]);
+        probs(S[1], P[1]);
         const bf16* vb = base + C::NK * C::KSLOT;
-#pragma unroll
-        for (int b = 0; b < 2; ++b) {
-            if (bcls[b] == 0) continue;
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-#pragma unroll
-                for (int db = 0; db < C::ND; ++db) {
-                    const bf16x8 vv = *reinterpret_cast<const bf16x8*>(
-                        vb + (32 * db + qr) * C::VSTR + 32 * b + 16 * u + 8 * hh);
-                    O[db] = mfma32(vv, P[b][u], O[db]);
-                }
-            }
-        }
+        if (bcls[0] != 0) pv(vb, 0, P[0]);
+        if (bcls[1] != 0) pv(vb, 1, P[1]);
     };
 
     // ---- main loop over key tiles ----
-    {
-        const uint32_t c0 = tile_need(0);
-        gload(0, c0);
-        lstore(0, c0);
-        __syncthreads();
-    }
+    load_tile(0, 0, tile_need(0));
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
     for (int tau = 0; tau < ntiles; ++tau) {
         const int cur = (C::NBUF == 2) ? (tau & 1) : 0;
         const bool more = tau + 1 < ntiles;
-        uint32_t cn = 0;
-        if (more) cn = tile_need(tau + 1);
-        if (C::NBUF == 2 && more) gload(tau + 1, cn);
+        const uint32_t cn = more ? tile_need(tau + 1) : 0u;
+        // the other buffer was last read in iteration tau - 1, which every
+        // wave finished before the barrier that ended it
+        if (C::NBUF == 2 && more) load_tile(tau + 1, cur ^ 1, cn);
         if (wave_active) compute(tau, cur);
         if (more) {
-            if (C::NBUF == 2) {
-                lstore(cur ^ 1, cn);
-            } else {
+            if (C::NBUF == 1) {
                 __syncthreads();
-                gload(tau + 1, cn);
-                lstore(0, cn);
+                load_tile(tau + 1, 0, cn);
             }
+            __builtin_amdgcn_s_waitcnt(0);  // this wave's DMA writes have landed
             __syncthreads();
         }
     }

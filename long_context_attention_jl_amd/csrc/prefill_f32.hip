@@ -44,10 +44,11 @@ __global__ __launch_bounds__(64) void prefill_f32_kernel(PrefillArgs a) {
     if (lane < HALF) {
         const float x0 = q[lane], x1 = q[lane + HALF];
         float c, sn;
-        rope_cs(i, a.tab.rev[lane], c, sn);
+        const double rv = rope_rev(a.tab, lane);
+        rope_cs(i, rv, c, sn);
         qs[lane] = x0 * c - x1 * sn;
         qs[lane + HALF] = x1 * c + x0 * sn;
-        rope_cs(remap(i, G), a.tab.rev[lane], c, sn);
+        rope_cs(remap(i, G), rv, c, sn);
         qm[lane] = x0 * c - x1 * sn;
         qm[lane + HALF] = x1 * c + x0 * sn;
     }

@@ -16,7 +16,7 @@ __global__ __launch_bounds__(256) void rope_apply_kernel(T* __restrict__ out,
                                                          const T* __restrict__ x,
                                                          const int32_t* __restrict__ pos,
                                                          int64_t ntok, int32_t H, int32_t d,
-                                                         RopeTable tab, int32_t G) {
+                                                         RopeFreq tab, int32_t G) {
     const int half = d / 2;
     const int64_t item = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (item >= ntok * half) return;
@@ -24,7 +24,7 @@ __global__ __launch_bounds__(256) void rope_apply_kernel(T* __restrict__ out,
     const int t = (int)(item % half);
     const int32_t p = remap(pos[tok], G);
     float c, s;
-    rope_cs(p, tab.rev[t], c, s);
+    rope_cs(p, rope_rev(tab, t), c, s);
     for (int h = 0; h < H; ++h) {
         const int64_t base = (tok * H + h) * (int64_t)d;
         const float x0 = (float)x[base + t];
@@ -35,7 +35,7 @@ __global__ __launch_bounds__(256) void rope_apply_kernel(T* __restrict__ out,
 }
 
 hipError_t launch_rope_apply(void* out, const void* x, const int32_t* pos, int64_t T, int32_t H,
-                             int32_t d, const RopeTable& tab, int32_t G, int dtype,
+                             int32_t d, const RopeFreq& tab, int32_t G, int dtype,
                              hipStream_t s) {
     const int64_t items = T * (d / 2);
     const dim3 grid((unsigned)((items + 255) / 256));
@@ -130,7 +130,7 @@ __host__ __device__ constexpr int vt_perm16(int p) {
 //   KS[g][row]  = R(n) k_n            (standard RoPE, [TW] §二), fp16
 //   KR[g][row]  = R(f(n)) k_n         (remapped RoPE, [BT] §3.1; only if G > 1), fp16
 //   KS_lo/KR_lo = f16(x - f16(x))     for n < kPreciseRows (split precision)
-//   VT[g][tile][d][key']              V tile transposed, keys in vt_perm16 order
+//   VT[g][tile][d][key']              V tile transposed to fp16, keys in vt_perm16 order
 //   k_rot_out[tok][g] = KS row        (optional, the caller's cache layout)
 // Pad rows (n >= L) are written as zeros so masked keys never meet NaNs.
 template <int D>
@@ -142,7 +142,7 @@ __global__ __launch_bounds__(256) void kv_prepass_bf16_kernel(PrefillArgs a) {
     const int32_t* plan = (const int32_t*)((char*)a.ws + a.lay.plan);
     f16* KS = (f16*)((char*)a.ws + a.lay.ks);
     f16* KR = (f16*)((char*)a.ws + a.lay.kr);
-    bf16* VT = (bf16*)((char*)a.ws + a.lay.vt);
+    f16* VT = (f16*)((char*)a.ws + a.lay.vt);
     f16* KSlo = (f16*)((char*)a.ws + a.lay.ks_lo);
     f16* KRlo = (f16*)((char*)a.ws + a.lay.kr_lo);
     const bf16* k = (const bf16*)a.k;
@@ -156,7 +156,6 @@ __global__ __launch_bounds__(256) void kv_prepass_bf16_kernel(PrefillArgs a) {
     const int32_t start = e[kPlanStart], len = e[kPlanLen], G = e[kPlanG];
     const bool bif = a.bifocal && G > 1;
     const int32_t n0 = (tile - e[kPlanTile0]) * kBN;  // first position of the tile
-    const int64_t prow0 = (int64_t)tile * kBN;          // first padded row
 
     // ---- keys: thread (r, c) rotates pairs [c*TPC, (c+1)*TPC) of row r ----
     const int r = threadIdx.x / 4, c = threadIdx.x % 4;
@@ -168,8 +167,9 @@ __global__ __launch_bounds__(256) void kv_prepass_bf16_kernel(PrefillArgs a) {
         const int32_t fn = remap(n, G);
 #pragma unroll
         for (int u = 0; u < TPC; ++u) {
-            rope_cs(n, a.tab.rev[c * TPC + u], cs[u], sn[u]);
-            if (bif) rope_cs(fn, a.tab.rev[c * TPC + u], cr[u], sr[u]);
+            const double rv = rope_rev(a.tab, c * TPC + u);
+            rope_cs(n, rv, cs[u], sn[u]);
+            if (bif) rope_cs(fn, rv, cr[u], sr[u]);
         }
     }
     for (int g = 0; g < a.Hkv; ++g) {
@@ -206,7 +206,9 @@ __global__ __launch_bounds__(256) void kv_prepass_bf16_kernel(PrefillArgs a) {
                 kb0[u] = kb1[u] = (bf16)0.0f;
             }
         }
-        const int64_t drow = ((int64_t)g * a.lay.T_pad + prow0 + r) * D + c * TPC;
+        // tile image: row r of tile `tile`, stride kstr(D)
+        const int64_t drow = ((int64_t)g * (a.lay.T_pad / kBN) + tile) * ktile_elems(D) +
+                             (int64_t)r * kstr(D) + c * TPC;
 #pragma unroll
         for (int u = 0; u < TPC; ++u) {
             KS[drow + u] = ys0[u];
@@ -221,7 +223,8 @@ __global__ __launch_bounds__(256) void kv_prepass_bf16_kernel(PrefillArgs a) {
         }
         if (lo_row) {
             const int64_t lrow =
-                ((int64_t)g * a.lay.lo_pad + e[kPlanLoOff] + n) * D + c * TPC;
+                ((int64_t)g * (a.lay.lo_pad / kBN) + e[kPlanLoTile0] + n / kBN) * ktile_elems(D) +
+                (int64_t)(n % kBN) * kstr(D) + c * TPC;
 #pragma unroll
             for (int u = 0; u < TPC; ++u) {
                 KSlo[lrow + u] = ls0[u];
@@ -255,11 +258,11 @@ __global__ __launch_bounds__(256) void kv_prepass_bf16_kernel(PrefillArgs a) {
                 nn < len ? v[((int64_t)(start + nn) * a.Hkv + g) * D + dd] : (bf16)0.0f;
         }
         __syncthreads();
-        bf16* dst = VT + ((int64_t)g * a.lay.T_pad + prow0) * D;
+        f16* dst = VT + ((int64_t)g * (a.lay.T_pad / kBN) + tile) * vtile_elems(D);
         for (int idx = threadIdx.x; idx < kBN * D; idx += 256) {
             const int dd = idx / kBN, p = idx % kBN;
             const int key = (p & ~15) | vt_perm16(p & 15);
-            dst[dd * kBN + p] = vs[key * (D + 2) + dd];
+            dst[dd * kVStr + p] = (f16)(float)vs[key * (D + 2) + dd];
         }
     }
 }
@@ -283,8 +286,9 @@ __global__ __launch_bounds__(256) void kv_prepass_f32_kernel(PrefillArgs a) {
     if (tok < e[kPlanStart] || tok >= (int64_t)e[kPlanStart] + e[kPlanLen]) return;
     const int32_t n = (int32_t)(tok - e[kPlanStart]);
     float cs, sn, cr, sr;
-    rope_cs(n, a.tab.rev[t], cs, sn);
-    rope_cs(remap(n, e[kPlanG]), a.tab.rev[t], cr, sr);
+    const double rv = rope_rev(a.tab, t);
+    rope_cs(n, rv, cs, sn);
+    rope_cs(remap(n, e[kPlanG]), rv, cr, sr);
     for (int g = 0; g < a.Hkv; ++g) {
         const float* src = k + (tok * a.Hkv + g) * (int64_t)a.d;
         const float x0 = src[t], x1 = src[t + half];
