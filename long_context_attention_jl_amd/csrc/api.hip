@@ -12,7 +12,7 @@
 #include <string>
 #include <vector>
 
-#include "../../include/jetlong.h"
+#include "jetlong.h"
 #include "internal.h"
 
 namespace jl {
