@@ -63,6 +63,7 @@ struct Cfg {
     static_assert(KSLOT % 512 == 0 && VSLOT % 512 == 0, "tiles are whole 1 KB DMA rounds");
 };
 
+
 __device__ __forceinline__ f32x16 mfma32h(f16x8 a, f16x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
@@ -211,6 +212,13 @@ void prefill_bf16_kernel(PrefillArgs a, int rb_first, int n_rb) {
         f16x8 kv[C::NS];
 #pragma unroll
         for (int st = 0; st < C::NS; ++st) kv[st] = *reinterpret_cast<const f16x8*>(kp + 16 * st);
+        const bf16* vb = base + C::NK * C::KSLOT + qr * C::VSTR + 32 * b + 8 * hh;
+        f16x8 vv[2][C::ND];
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int db = 0; db < C::ND; ++db)
+                vv[u][db] = *reinterpret_cast<const f16x8*>(vb + 32 * db * C::VSTR + 16 * u);
         // all operand reads of the block are in flight before its MFMA chain
         __builtin_amdgcn_sched_barrier(0);
         f32x16 Sb = {};
@@ -257,15 +265,10 @@ void prefill_bf16_kernel(PrefillArgs a, int rb_first, int n_rb) {
                 const f16x2 pp = {Pb[h2][i], Pb[h2][i + 1]};
                 l_run = __builtin_amdgcn_fdot2(pp, ones, l_run, false);
             }
-        const bf16* vb = base + C::NK * C::KSLOT;
 #pragma unroll
         for (int u = 0; u < 2; ++u)
 #pragma unroll
-            for (int db = 0; db < C::ND; ++db) {
-                const f16x8 vv = *reinterpret_cast<const f16x8*>(
-                    vb + (32 * db + qr) * C::VSTR + 32 * b + 16 * u + 8 * hh);
-                O[db] = mfma32h(vv, Pb[u], O[db]);
-            }
+            for (int db = 0; db < C::ND; ++db) O[db] = mfma32h(vv[u][db], Pb[u], O[db]);
     };
 
     auto compute = [&](int tau, const bf16* base, bool remote_phase)  __attribute__((always_inline)) {
@@ -280,7 +283,8 @@ void prefill_bf16_kernel(PrefillArgs a, int rb_first, int n_rb) {
 
     // ---- one phase: tiles [t0, t1), unrolled by two so each step names its
     // LDS buffers statically ----
-    auto step = [&](int tau, int t1, bool remote_phase, const bf16* cur, bf16* nxt)  __attribute__((always_inline)) {
+    auto step = [&](int tau, int t1, bool remote_phase, const bf16* cur, bf16* nxt)
+        __attribute__((always_inline)) {
         const bool more = tau + 1 < t1;
         // the other buffer was last read in the previous step, which every
         // wave finished before the barrier that ended it
@@ -291,7 +295,7 @@ void prefill_bf16_kernel(PrefillArgs a, int rb_first, int n_rb) {
             __syncthreads();
         }
     };
-    auto run_phase = [&](int t0, int t1, bool remote_phase)  __attribute__((always_inline)) {
+    auto run_phase = [&](int t0, int t1, bool remote_phase) __attribute__((always_inline)) {
         load_tile(t0, remote_phase, lds0);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
