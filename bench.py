@@ -30,6 +30,34 @@ def _flops_rows(d, Hq, a, b):
     return 4.0 * d * Hq * ((b * (b + 1) - a * (a + 1)) / 2.0)
 
 
+def _profiled_traffic(summary: str):
+    """HBM bytes per launch recorded in a committed rocprofv3 counter summary
+    (FETCH_SIZE + WRITE_SIZE, scaled by a plain-copy calibration), or None when
+    the kernel's sources no longer hash to the value the counters were taken on."""
+    import hashlib
+
+    path = os.path.join(ROOT, "profiles", summary)
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        key, sep, val = line.partition(":")
+        if sep and key.strip() in ("traffic_bytes_per_launch", "sources", "source_sha256_16"):
+            fields[key.strip()] = val.strip()
+    if len(fields) != 3:
+        return None
+    h = hashlib.sha256()
+    for f in fields["sources"].split():
+        fp = os.path.join(ROOT, f)
+        if not os.path.exists(fp):
+            return None
+        with open(fp, "rb") as fh:
+            h.update(fh.read())
+    if h.hexdigest()[:16] != fields["source_sha256_16"]:
+        return None
+    return float(fields["traffic_bytes_per_launch"])
+
+
 def _copy_calibration(n_bytes: int, iters: int):
     import torch
 
@@ -135,7 +163,7 @@ def main():
         "roofline": {"bound": "mfma", "kernel": "prefill_bf16",
                      "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": None,
+                     "traffic": _profiled_traffic("traffic_prefill_bf16_qwen3_L131072.md"),
                      "algorithmic_flops_per_launch": main_flops},
     }
     del o, lse
@@ -204,6 +232,7 @@ def bench_decode(jl, inputs, torch, iters):
         "hbm_frac": round(nbytes / (t_bif * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4),
         "split_kernel_us": round(split_us, 2),
         "split_kernel_GBps": round(nbytes / (split_us * 1e-6) / 1e9, 1),
+        "split_kernel_traffic": _profiled_traffic("traffic_decode_split_L131072.md"),
         "kernels": {n: {"launches": c2, "avg_us": round(ms * 1e3 / max(c2, 1), 2)}
                     for n, (c2, ms) in sorted(prof.items())},
     }
@@ -226,7 +255,9 @@ def cpu_baseline(case):
     t0 = time.perf_counter()
     oracle.prefill(case.q, case.k, case.v, rows=[0], **kw)
     t_rot = time.perf_counter() - t0
-    rows = [T // 8, T // 4, T // 2, 3 * T // 4, T - 1]
+    # 256 rows evenly strided over the sequence (all heads): about 15 s of
+    # fp64 work on 16 cores, representative of every band and G boundary
+    rows = [int((r + 0.5) * T / 256) for r in range(256)]
     t0 = time.perf_counter()
     oracle.prefill(case.q, case.k, case.v, rows=rows, **kw)
     t_sample = time.perf_counter() - t0
@@ -236,9 +267,10 @@ def cpu_baseline(case):
     t_full = t_rot + t_rows * pairs_full / pairs_sample
     return {"value": round(T / t_full, 3), "unit": "tokens/s", "cores": threads,
             "kind": "oracle",
-            "sample": "rows %s x %d heads of qwen3_8b_L131072 (%d causal pairs per head); "
-                      "key rotation %.1f s + rows %.1f s measured, full run extrapolated to "
-                      "%.0f s by causal pairs" % (rows, Hq, pairs_sample, t_rot, t_rows, t_full)}
+            "sample": "%d rows evenly strided over qwen3_8b_L131072 x %d heads (%d causal "
+                      "pairs per head); key rotation %.1f s + rows %.1f s measured, full run "
+                      "extrapolated to %.0f s by causal pairs"
+                      % (len(rows), Hq, pairs_sample, t_rot, t_rows, t_full)}
 
 
 if __name__ == "__main__":

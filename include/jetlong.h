@@ -122,6 +122,10 @@ jl_status jl_bifocal_prefill_workspace(int64_t T, int32_t n_seqs, int32_t Hq, in
  *              256-byte aligned; contents need no initialisation and are
  *              scratch after the call.
  * Supported: dtype bf16 (MFMA path) or f32 (fp32 path), d in {64, 128}.
+ * The bf16 path forms q k^T and P v on fp16 MFMA operands (fp32 accumulate):
+ * inputs must be finite and the rotated q (times softmax_scale * log2 e), the
+ * rotated k and v must stay below 65504 in magnitude.  Device data is not
+ * range-checked; values outside that range give inf/NaN outputs.
  */
 jl_status jl_bifocal_prefill(void* o, float* lse, const void* q, const void* k, const void* v,
                              const int32_t* cu_seqlens, int32_t n_seqs, int64_t T,
