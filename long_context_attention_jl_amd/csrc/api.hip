@@ -125,24 +125,29 @@ PrefillLayout prefill_layout(int64_t T, int32_t n_seqs, int32_t Hkv, int32_t d, 
     return L;
 }
 
-DecodeLayout decode_layout(int32_t B, int32_t max_seqlen_k, int32_t Hq, int32_t Hkv, int32_t d) {
+DecodeLayout decode_layout(int32_t B, int32_t max_seqlen_k, int32_t Hq, int32_t Hkv, int32_t d,
+                           int dtype) {
     DecodeLayout L{};
-    const int nw = Hkv < 8 ? Hkv : 8;
+    // bf16: 8-wave workgroups (one per compute unit), 48-position stages;
+    // fp32: 4-wave workgroups (two per compute unit), 64-position stages
+    const bool b16 = dtype == JL_DTYPE_BF16;
+    const int wmax = b16 ? 8 : 4;
+    const int stage = b16 ? 48 : 64;
+    const int nw = Hkv < wmax ? Hkv : wmax;  // waves (kv heads) per decode workgroup
     const int64_t groups = (Hkv + nw - 1) / nw;
-    // about one resident workgroup (8 waves) per compute unit; JL_DECODE_WGS
-    // overrides the target for tuning
-    int64_t target = 256;
+    // JL_DECODE_WGS overrides the workgroup target for tuning
+    int64_t target = b16 ? 256 : 512;
     if (const char* e = getenv("JL_DECODE_WGS")) {
         const long v = strtol(e, nullptr, 10);
         if (v >= 1 && v <= 65536) target = v;
     }
+    const int64_t span = (int64_t)max_seqlen_k + stage - 1;
     int64_t want = (target + (int64_t)B * groups - 1) / ((int64_t)B * groups);
     if (want < 1) want = 1;
-    int64_t chunk = (max_seqlen_k + want - 1) / want;
-    chunk = (chunk + 63) / 64 * 64;
-    if (chunk < 64) chunk = 64;
+    int64_t chunk = (span + want - 1) / want;
+    chunk = (chunk + stage - 1) / stage * stage;
     L.chunk = (int32_t)chunk;
-    L.n_splits = (int32_t)((max_seqlen_k + chunk - 1) / chunk);
+    L.n_splits = (int32_t)((span + chunk - 1) / chunk);
     size_t off = 0;
     L.part_ml = off;
     off = align256(off + (size_t)B * L.n_splits * Hq * 2 * sizeof(float));
@@ -316,7 +321,7 @@ jl_status jl_bifocal_decode_workspace(int32_t batch, int32_t max_seqlen_k, int32
     if (st != JL_OK) return st;
     st = check_dtype_d(dtype, d);
     if (st != JL_OK) return st;
-    *bytes = decode_layout(batch, max_seqlen_k, Hq, Hkv, d).total;
+    *bytes = decode_layout(batch, max_seqlen_k, Hq, Hkv, d, dtype).total;
     g_err.clear();
     return JL_OK;
 }
@@ -344,7 +349,7 @@ jl_status jl_bifocal_decode(void* o, float* lse, const void* q, const void* k_ca
     if (o == q || o == k_cache || o == v_cache)
         return fail(JL_ERR_INVALID_ARGUMENT, "outputs must not alias inputs");
     if ((uintptr_t)workspace & 255) return fail(JL_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
-    const DecodeLayout lay = decode_layout(batch, max_seqlen_k, Hq, Hkv, d);
+    const DecodeLayout lay = decode_layout(batch, max_seqlen_k, Hq, Hkv, d, dtype);
     if (workspace_bytes < lay.total)
         return fail(JL_ERR_WORKSPACE_TOO_SMALL,
                     "workspace needs " + std::to_string(lay.total) + " bytes");

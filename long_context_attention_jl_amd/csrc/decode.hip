@@ -6,22 +6,19 @@
 //   [TW] "NVIDIA研究团队找到了让AI“看清”超长文本的新方法" (techwalker.com)
 //
 // The cache holds R(j) k_j and is never rewritten when G changes ([TW] §三).
-// At read time the query carries the correction f(p) - p, R(f(p)) q, and every
-// key older than the local window is turned by the correction f(j) - j in
-// registers before its dot product ([BT] §3.3).  Keys inside the window are
-// scored against the same R(f(p)) q after the query's correction is undone on
-// the key side, R(p - f(p)) inverted, i.e. turned by f(p) - p: <R(p) q, K_j> =
-// <R(f(p)) q, R(f(p) - p) K_j>.  One query operand then serves every key.
+// At read time a key older than the local window is scored as
+// <R(f(p)) q, R(f(j) - j) K_j>: the query carries the correction f(p) - p and
+// the key the correction f(j) - j, applied in registers ([BT] §3.3).  Keys
+// inside the window are scored as <R(p) q, K_j> on the stored values.
 //
 // Work decomposition: a workgroup owns a chunk of key positions of one
-// sequence and up to 8 kv heads (one wave each).  The correction angles depend
-// only on (position, pair), so the workgroup computes them once per 64
-// positions into LDS and every head's wave reuses them.  Per 16-key tile a
-// wave forms S^T (16 keys x the GQA group's query heads) = K Q^T on
-// v_mfma_f32_16x16x32_bf16 with both operands split into bf16 hi + lo parts
-// (hi*hi + hi*lo + lo*hi: about 16 significant bits, so the scores carry no
-// visible 16-bit rounding), then accumulates P V in fp32 on the vector ALU.
-// Two tiles' K and V loads stay in flight while a tile is processed.
+// sequence and up to 4 kv heads (one wave each).  Per 16-key tile a wave
+// forms S^T (16 keys x the GQA group's query heads) = K Q^T on
+// v_mfma_f32_16x16x32_bf16 with the query split into bf16 hi + lo parts and
+// rotated keys split the same way (about 16 significant bits, so the scores
+// carry no visible 16-bit rounding), then accumulates P V in fp32 on the
+// vector ALU.  One tile's K and V loads stay in flight while the previous
+// tile is processed; three workgroups share a compute unit.
 // Each chunk writes (m, l, O) partials; a second kernel merges the chunks
 // exactly (max-shifted sums).
 #include "internal.h"
@@ -33,6 +30,21 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kStage = 64;  // key positions per angle-table stage
 constexpr int kTile = 16;   // keys per wave step
+constexpr int kDecodeWaves = 4;  // fp32 kernel: waves (kv heads) per workgroup
+constexpr int kStageB = 48;      // bf16 kernel: positions per stage (three tiles)
+constexpr int kWavesB = 8;       // bf16 kernel: waves (kv heads) per workgroup
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// O^T-style P V product: A = P^T (16 query columns x 16 keys), B = V (16 keys
+// x 16 d), both bf16
+__device__ __forceinline__ f32x4 mfma16k16(s16x4 a, s16x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+
+// s_waitcnt vmcnt(n) (n < 64), other counters untouched
+#define JL_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(0x0F70 | ((n) & 15) | (((n) >> 4) << 14))
 
 __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -60,27 +72,37 @@ struct Vec8<float> {
     __device__ static float get(const T& x, int i) { return i < 4 ? x.a[i] : x.b[i - 4]; }
 };
 
-// DPL consecutive stored values (DPL in {1, 2, 4, 8}) kept in their storage
-// type until use.
-template <typename TIN, int DPL>
-struct VRow {
-    TIN x[DPL];
-    __device__ void load(const TIN* p) {
-#pragma unroll
-        for (int u = 0; u < DPL; ++u) x[u] = p[u];
-    }
-    __device__ void zero() {
-#pragma unroll
-        for (int u = 0; u < DPL; ++u) x[u] = (TIN)0.0f;
-    }
+// N (1 or 2) consecutive stored values loaded as one vector, kept in their
+// storage type until use.
+template <typename TIN, int N>
+struct VSmall;
+template <>
+struct VSmall<bf16, 2> {
+    bf16x2 x;
+    __device__ void load(const bf16* p) { x = *reinterpret_cast<const bf16x2*>(p); }
+    __device__ void zero() { x = bf16x2{}; }
     __device__ float get(int u) const { return (float)x[u]; }
 };
-template <typename TIN>
-struct VRow<TIN, 8> {
-    typename Vec8<TIN>::T x;
-    __device__ void load(const TIN* p) { x = Vec8<TIN>::load(p); }
-    __device__ void zero() { x = typename Vec8<TIN>::T{}; }
-    __device__ float get(int u) const { return Vec8<TIN>::get(x, u); }
+template <>
+struct VSmall<bf16, 1> {
+    bf16 x;
+    __device__ void load(const bf16* p) { x = *p; }
+    __device__ void zero() { x = (bf16)0.0f; }
+    __device__ float get(int) const { return (float)x; }
+};
+template <>
+struct VSmall<float, 2> {
+    float2 x;
+    __device__ void load(const float* p) { x = *reinterpret_cast<const float2*>(p); }
+    __device__ void zero() { x = make_float2(0.0f, 0.0f); }
+    __device__ float get(int u) const { return u ? x.y : x.x; }
+};
+template <>
+struct VSmall<float, 1> {
+    float x;
+    __device__ void load(const float* p) { x = *p; }
+    __device__ void zero() { x = 0.0f; }
+    __device__ float get(int) const { return x; }
 };
 
 }  // namespace
@@ -88,23 +110,39 @@ struct VRow<TIN, 8> {
 // BIF = false compiles the kernel with every bifocal step removed: plain RoPE
 // attention over the cache, the baseline the decode overhead is quoted on.
 // GQ >= Hq / Hkv is the padded GQA group (4, 8 or 16).
+//
+// Remote keys.  Within a stage of 64 positions starting at js, the key
+// correction angle is f(j) - j = (f(js) - js) - u_j with
+// u_j = (j - js) - (f(j) - f(js)) in [0, 64).  The score
+//   <R(f(p)) q, R(f(j) - j) K_j> = <R(f(p) - f(js) + js) q, R(-u_j) K_j>
+// so each wave turns its query once per stage and every key by a small angle
+// -u_j theta_t read from a table built once per workgroup: no per-stage
+// table, no workgroup barrier in the key loop.  Local keys are scored against
+// R(p) q directly on the stored (exact) cache values.
+//
+// Lanes.  Scores S^T = K Q^T come from v_mfma_f32_16x16x32_bf16: lane
+// (n, c) = (lane % 16, lane / 16) feeds key n of the tile and holds the scores
+// of keys 4c..4c+3 for query column n.  With GQ <= 8 the query's bf16 hi part
+// sits in columns [0, GQ) and its lo part in [GQ, 2 GQ) of one operand, so one
+// product gives both and a lane swap adds them.  For P V each lane owns D/64
+// consecutive d of every head and walks all 16 keys of the tile.
 template <int D, typename TIN, bool BIF, int GQ>
-__global__ __launch_bounds__(512) void decode_split_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(sizeof(TIN) == 2 ? 3 : 2)))
+void decode_split_kernel(DecodeArgs a) {
     constexpr int HALF = D / 2;
     constexpr int NST = D / 32;          // k-steps of the QK^T product
-    constexpr int DPL = (32 / GQ) < (D / 8) ? (32 / GQ) : (D / 8);  // d values per lane in PV
-    constexpr int DSL = D / DPL;         // lanes per key row in PV
-    constexpr int KSUB = 64 / DSL;       // keys processed side by side in PV
+    constexpr int NH = NST / 2;          // k-steps per RoPE half
+    constexpr int DPL = D / 64;          // d values per lane in P V
+    constexpr bool PACK = GQ <= 8;       // hi and lo query parts in one operand
     constexpr int TSTR = HALF + 2;       // LDS row stride of the angle table (float2)
-    static_assert(KSUB >= 1 && kTile % KSUB == 0, "PV lane split");
-    __shared__ float2 tab[BIF ? kStage * TSTR : 1];
-    __shared__ float pbuf[8][kTile][16];  // per wave: p[key][query column]
-    __shared__ float abuf[8][16];         // per wave: alpha per query column
+    __shared__ float2 tab[BIF ? kStage * TSTR : 1];  // R(-u theta_t): (cos, sin)
+    __shared__ double revs[HALF];                    // theta_t / 2 pi
+    __shared__ float pbuf[kDecodeWaves][kTile][16];  // per wave: p[key][query column]
+    __shared__ float abuf[kDecodeWaves][16];         // per wave: alpha per query column
 
     const int nw = blockDim.x >> 6;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-    const int n = lane & 15, c = lane >> 4;      // QK^T roles: column n, lane group c
-    const int ks = lane / DSL, ds = lane % DSL;  // PV roles: key subset, d slice
+    const int n = lane & 15, c = lane >> 4;
     const int b = blockIdx.z, split = blockIdx.x;
     const int kvh = blockIdx.y * nw + wave;
     const bool head_ok = kvh < a.Hkv;
@@ -117,7 +155,15 @@ __global__ __launch_bounds__(512) void decode_split_kernel(DecodeArgs a) {
     const bool bif = BIF && G > 1;
     const int32_t fp = remap(p, G);
     const int32_t rem_last = p - a.w_local;  // keys j <= rem_last are remote (if bif)
-    const int32_t kbeg = split * a.lay.chunk;
+    // Chunks start at z0 + split * chunk with z0 in (-64, 0] chosen so that the
+    // first local key rem_last + 1 starts a 64-key stage: every stage is then
+    // wholly remote or wholly local.  Positions below 0 are masked.
+    int32_t z0 = 0;
+    if (bif && rem_last >= 0) {
+        const int32_t m = (rem_last + 1) & (kStage - 1);
+        z0 = m ? m - kStage : 0;
+    }
+    const int32_t kbeg = z0 + split * a.lay.chunk;
     const int32_t kend = min(kbeg + a.lay.chunk, L);
 
     float* pm = (float*)((char*)a.ws + a.lay.part_ml);
@@ -135,102 +181,106 @@ __global__ __launch_bounds__(512) void decode_split_kernel(DecodeArgs a) {
         return;
     }
 
-    // ---- query operand: R(f(p)) q (or R(p) q without bifocal), scaled by
-    // softmax_scale * log2(e), split into bf16 hi + lo; lane (n, c) holds
-    // head n of the group at d = 32 s + 8 c + u.
-    bf16x8 Qh[NST], Ql[NST];
-    {
-        const float qscale = a.softmax_scale * kLog2e;
-        const bool qok = head_ok && n < grp;
-        const TIN* qp = (const TIN*)a.q + ((int64_t)b * a.Hq + kvh * grp + n) * D + 8 * c;
-        const int32_t qpos = bif ? fp : p;
-#pragma unroll
-        for (int s = 0; s < NST / 2; ++s) {
-#pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const float x0 = qok ? (float)qp[32 * s + u] : 0.0f;
-                const float x1 = qok ? (float)qp[32 * s + u + HALF] : 0.0f;
-                float cs, sn;
-                rope_cs(qpos, rope_rev(a.tab, 32 * s + 8 * c + u), cs, sn);
-                const float y0 = (x0 * cs - x1 * sn) * qscale;
-                const float y1 = (x1 * cs + x0 * sn) * qscale;
-                Qh[s][u] = (bf16)y0;
-                Ql[s][u] = (bf16)(y0 - (float)Qh[s][u]);
-                Qh[s + NST / 2][u] = (bf16)y1;
-                Ql[s + NST / 2][u] = (bf16)(y1 - (float)Qh[s + NST / 2][u]);
-            }
-        }
-    }
-
     const TIN* kc = (const TIN*)a.kc + (int64_t)b * a.S_max * a.Hkv * D + (int64_t)kvh * D;
     const TIN* vc = (const TIN*)a.vc + (int64_t)b * a.S_max * a.Hkv * D + (int64_t)kvh * D;
     const int64_t rstride = (int64_t)a.Hkv * D;
 
-    // register-staged tile loads (zero beyond the chunk)
+    // tile loads into registers (zero beyond the chunk): K as MFMA operands,
+    // V as one 64-lane row read per key
     typedef typename Vec8<TIN>::T KV8;
-    KV8 kbuf[NST];
-    VRow<TIN, DPL> vbuf[kTile / KSUB];
-    auto load_tile = [&](int32_t j0) {
+    typedef VSmall<TIN, DPL> VV;
+    KV8 kA[NST], kB[NST];
+    VV vA[kTile], vB[kTile];
+    auto load_tile = [&](int32_t j0, KV8* kd, VV* vd) __attribute__((always_inline)) {
         const int32_t kj = j0 + n;
-        const bool okk = kj < kend;
+        const bool okk = kj >= 0 && kj < kend;
 #pragma unroll
-        for (int s = 0; s < NST; ++s) {
-            if (okk) kbuf[s] = Vec8<TIN>::load(kc + (int64_t)kj * rstride + 32 * s + 8 * c);
-            else kbuf[s] = KV8{};
-        }
+        for (int s = 0; s < NST; ++s)
+            kd[s] = okk ? Vec8<TIN>::load(kc + (int64_t)kj * rstride + 32 * s + 8 * c) : KV8{};
 #pragma unroll
-        for (int r = 0; r < kTile / KSUB; ++r) {
-            const int32_t key = j0 + KSUB * r + ks;
-            if (key < kend) vbuf[r].load(vc + (int64_t)key * rstride + DPL * ds);
-            else vbuf[r].zero();
+        for (int r = 0; r < kTile; ++r) {
+            if (j0 + r >= 0 && j0 + r < kend) vd[r].load(vc + (int64_t)(j0 + r) * rstride + DPL * lane);
+            else vd[r].zero();
         }
     };
+    if (head_ok) load_tile(kbeg, kA, vA);
 
-    float m_run = -INFINITY, l_part = 0.0f;
-    float O[GQ][DPL];
-#pragma unroll
-    for (int h = 0; h < GQ; ++h)
-#pragma unroll
-        for (int u = 0; u < DPL; ++u) O[h][u] = 0.0f;
-
-    // one 16-key tile: scores, online softmax, P V
-    auto process = [&](int32_t j0, int32_t js, const KV8* kcur, const VRow<TIN, DPL>* vcur) {
-        // ---- S^T = K Q^T with hi/lo operands ----
-        f32x4 sacc = {};
+    // ---- theta_t / 2 pi and the small-angle table, once per workgroup (the
+    // only barrier) ----
+    {
+        const double rv = rope_rev(a.tab, threadIdx.x % HALF);  // blockDim is a multiple of HALF
+        if (threadIdx.x < HALF) revs[threadIdx.x] = rv;
         if (BIF && bif) {
-            const float2* tp = tab + (j0 + n - js) * TSTR + 8 * c;
+            for (int x = threadIdx.x; x < kStage * HALF; x += blockDim.x) {
+                float cs, sn;
+                rope_cs_hw(-(int64_t)(x / HALF), rv, cs, sn);
+                tab[(x / HALF) * TSTR + x % HALF] = make_float2(cs, sn);
+            }
+        }
+        __syncthreads();
+    }
+    if (!head_ok) return;
+
+    // ---- query.  Lane column n carries head hq; with PACK, columns
+    // [GQ, 2 GQ) carry the lo parts.  Raw values at d = 32 s + 8 c + u stay
+    // in the input type; Q holds the rotated query the current keys use.
+    const float qscale = a.softmax_scale * kLog2e;
+    const int hq = PACK ? (n & (GQ - 1)) : n;
+    const bool qlo = PACK && n >= GQ;
+    KV8 qraw[NST];
+    {
+        const bool qok = hq < grp && (!PACK || n < 2 * GQ);
+        const TIN* qp = (const TIN*)a.q + ((int64_t)b * a.Hq + kvh * grp + hq) * D + 8 * c;
 #pragma unroll
-            for (int s = 0; s < NST / 2; ++s) {
-                bf16x8 h0, l0, h1, l1;
+        for (int s = 0; s < NST; ++s) qraw[s] = qok ? Vec8<TIN>::load(qp + 32 * s) : KV8{};
+    }
+    bf16x8 Q[NST];
+    bf16x8 Qlo[PACK ? 1 : NST];
+    auto rotate_q = [&](int64_t pos) __attribute__((always_inline)) {
 #pragma unroll
-                for (int x = 0; x < 8; ++x) {
-                    const float2 cs = tp[32 * s + x];
-                    const float k0 = Vec8<TIN>::get(kcur[s], x);
-                    const float k1 = Vec8<TIN>::get(kcur[s + NST / 2], x);
-                    const float y0 = k0 * cs.x - k1 * cs.y;
-                    const float y1 = k1 * cs.x + k0 * cs.y;
-                    h0[x] = (bf16)y0;
-                    l0[x] = (bf16)(y0 - (float)h0[x]);
-                    h1[x] = (bf16)y1;
-                    l1[x] = (bf16)(y1 - (float)h1[x]);
+        for (int s = 0; s < NH; ++s)
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int t = 32 * s + 8 * c + u;
+                float cs, sn;
+                rope_cs_hw(pos, revs[t], cs, sn);
+                const float x0 = Vec8<TIN>::get(qraw[s], u), x1 = Vec8<TIN>::get(qraw[s + NH], u);
+                const float y0 = (x0 * cs - x1 * sn) * qscale;
+                const float y1 = (x1 * cs + x0 * sn) * qscale;
+                const bf16 h0 = (bf16)y0, h1 = (bf16)y1;
+                const bf16 l0 = (bf16)(y0 - (float)h0), l1 = (bf16)(y1 - (float)h1);
+                if constexpr (PACK) {
+                    Q[s][u] = qlo ? l0 : h0;
+                    Q[s + NH][u] = qlo ? l1 : h1;
+                } else {
+                    Q[s][u] = h0;
+                    Q[s + NH][u] = h1;
+                    Qlo[s][u] = l0;
+                    Qlo[s + NH][u] = l1;
                 }
-                sacc = mfma16(h0, Qh[s], sacc);
-                sacc = mfma16(h0, Ql[s], sacc);
-                sacc = mfma16(l0, Qh[s], sacc);
-                sacc = mfma16(h1, Qh[s + NST / 2], sacc);
-                sacc = mfma16(h1, Ql[s + NST / 2], sacc);
-                sacc = mfma16(l1, Qh[s + NST / 2], sacc);
             }
-        } else if constexpr (sizeof(TIN) == 2) {
-            // stored bf16 keys are exact MFMA operands
+    };
+    // Q is set at every stage start: remote stages turn it to the stage's
+    // angle, local stages use R(p) q (kept once set)
+    bool q_local = false;
+
+    auto finish = [&](f32x4 acc) __attribute__((always_inline)) -> f32x4 {
+        if constexpr (PACK) {
 #pragma unroll
-            for (int s = 0; s < NST; ++s) {
-                sacc = mfma16(kcur[s], Qh[s], sacc);
-                sacc = mfma16(kcur[s], Ql[s], sacc);
-            }
-        } else {
+            for (int i = 0; i < 4; ++i) acc[i] += __shfl_xor(acc[i], GQ);
+        }
+        return acc;
+    };
+    // scores of a tile on the stored keys (Q = R(p) q)
+    auto scores_local = [&](const KV8* kcur) __attribute__((always_inline)) -> f32x4 {
+        f32x4 acc = {};
 #pragma unroll
-            for (int s = 0; s < NST; ++s) {
+        for (int s = 0; s < NST; ++s) {
+            if constexpr (sizeof(TIN) == 2) {
+                // stored bf16 keys are exact MFMA operands
+                acc = mfma16(kcur[s], Q[s], acc);
+                if constexpr (!PACK) acc = mfma16(kcur[s], Qlo[s], acc);
+            } else {
                 bf16x8 h0, l0;
 #pragma unroll
                 for (int x = 0; x < 8; ++x) {
@@ -238,18 +288,63 @@ __global__ __launch_bounds__(512) void decode_split_kernel(DecodeArgs a) {
                     h0[x] = (bf16)k0;
                     l0[x] = (bf16)(k0 - (float)h0[x]);
                 }
-                sacc = mfma16(h0, Qh[s], sacc);
-                sacc = mfma16(h0, Ql[s], sacc);
-                sacc = mfma16(l0, Qh[s], sacc);
+                acc = mfma16(h0, Q[s], acc);
+                acc = mfma16(l0, Q[s], acc);
+                if constexpr (!PACK) acc = mfma16(h0, Qlo[s], acc);
             }
         }
-        // ---- online softmax per query column n (keys 4c + i here).  The
-        // running max is only raised when a score exceeds it by more than
-        // 2^8 (log2 units): the partial sums stay exact relative to whatever
-        // max they use, and most tiles then skip rescaling O.
+        return finish(acc);
+    };
+    // scores of a tile of remote keys: key n turned by -u theta (Q = stage query)
+    auto scores_remote = [&](const KV8* kcur, int32_t u) __attribute__((always_inline)) -> f32x4 {
+        f32x4 acc = {};
+        const float2* tp = tab + u * TSTR + 8 * c;
+#pragma unroll
+        for (int s = 0; s < NH; ++s) {
+            bf16x8 h0, l0, h1, l1;
+#pragma unroll
+            for (int x = 0; x < 8; ++x) {
+                const float2 cs = tp[32 * s + x];
+                const float k0 = Vec8<TIN>::get(kcur[s], x);
+                const float k1 = Vec8<TIN>::get(kcur[s + NH], x);
+                const float y0 = k0 * cs.x - k1 * cs.y;
+                const float y1 = k1 * cs.x + k0 * cs.y;
+                h0[x] = (bf16)y0;
+                l0[x] = (bf16)(y0 - (float)h0[x]);
+                h1[x] = (bf16)y1;
+                l1[x] = (bf16)(y1 - (float)h1[x]);
+            }
+            acc = mfma16(h0, Q[s], acc);
+            acc = mfma16(l0, Q[s], acc);
+            acc = mfma16(h1, Q[s + NH], acc);
+            acc = mfma16(l1, Q[s + NH], acc);
+            if constexpr (!PACK) {
+                acc = mfma16(h0, Qlo[s], acc);
+                acc = mfma16(h1, Qlo[s + NH], acc);
+            }
+        }
+        return finish(acc);
+    };
+
+    float m_run = -INFINITY, l_part = 0.0f;
+    float O[GQ][DPL];
+#pragma unroll
+    for (int h = 0; h < GQ; ++h)
+#pragma unroll
+        for (int x = 0; x < DPL; ++x) O[h][x] = 0.0f;
+
+    // online softmax and P V of one tile.  The running max is only raised
+    // when a score exceeds it by more than 2^8 (log2 units): the partial sums
+    // stay exact relative to whatever max they use, and most tiles then skip
+    // rescaling O.
+    auto process = [&](int32_t j0, const f32x4& sacc, const VV* vcur) __attribute__((always_inline)) {
+        const bool col = n < GQ;  // lanes of packed lo parts carry no scores
         float sc[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sc[i] = (j0 + 4 * c + i < kend) ? sacc[i] : -INFINITY;
+        for (int i = 0; i < 4; ++i) {
+            const int32_t kk = j0 + 4 * c + i;
+            sc[i] = (col && kk >= 0 && kk < kend) ? sacc[i] : -INFINITY;
+        }
         float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
         mx = fmaxf(mx, __shfl_xor(mx, 16));
         mx = fmaxf(mx, __shfl_xor(mx, 32));
@@ -262,7 +357,8 @@ __global__ __launch_bounds__(512) void decode_split_kernel(DecodeArgs a) {
         float ps = 0.0f;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const float pv = __builtin_amdgcn_exp2f(sc[i] - m_run);
+            // masked keys weigh exactly 0 (also while m_run is still -inf)
+            const float pv = sc[i] != -INFINITY ? __builtin_amdgcn_exp2f(sc[i] - m_run) : 0.0f;
             ps += pv;
             pbuf[wave][4 * c + i][n] = pv;
         }
@@ -272,7 +368,6 @@ __global__ __launch_bounds__(512) void decode_split_kernel(DecodeArgs a) {
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        // ---- O[h][d] = alpha_h O[h][d] + sum_keys p[key][h] V[key][d] ----
         if (any_raise) {
 #pragma unroll
             for (int h = 0; h < GQ; ++h) {
@@ -282,11 +377,10 @@ __global__ __launch_bounds__(512) void decode_split_kernel(DecodeArgs a) {
             }
         }
 #pragma unroll
-        for (int r = 0; r < kTile / KSUB; ++r) {
-            const float* prow = &pbuf[wave][KSUB * r + ks][0];
+        for (int r = 0; r < kTile; ++r) {
 #pragma unroll
             for (int h = 0; h < GQ; ++h) {
-                const float ph = prow[h];
+                const float ph = pbuf[wave][r][h];
 #pragma unroll
                 for (int x = 0; x < DPL; ++x) O[h][x] += ph * vcur[r].get(x);
             }
@@ -296,83 +390,51 @@ __global__ __launch_bounds__(512) void decode_split_kernel(DecodeArgs a) {
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     };
 
-    // two tiles in flight: tile t is staged in buffer t & 1
-    KV8 kb1[NST];
-    VRow<TIN, DPL> vb1[kTile / KSUB];
-    if (head_ok) {
-        load_tile(kbeg);
-#pragma unroll
-        for (int s = 0; s < NST; ++s) kb1[s] = kbuf[s];
-#pragma unroll
-        for (int r = 0; r < kTile / KSUB; ++r) vb1[r] = vbuf[r];
-        // kb1/vb1 now hold tile 0; kbuf/vbuf receive tile 1
-        if (kbeg + kTile < kend) load_tile(kbeg + kTile);
-    }
-    for (int32_t js = kbeg; js < kend; js += kStage) {
-        if (BIF && bif) {
-            // angle table: remote keys f(j) - j, local keys f(p) - p
-            __syncthreads();
-            for (int x = threadIdx.x; x < kStage * HALF; x += blockDim.x) {
-                const int r = x / HALF, t = x % HALF;
-                const int32_t j = js + r;
-                float cs = 1.0f, sn = 0.0f;
-                if (j < kend) {
-                    const int64_t ang = j <= rem_last ? (int64_t)remap(j, G) - j : (int64_t)fp - p;
-                    rope_cs_hw(ang, rope_rev(a.tab, t), cs, sn);
-                }
-                tab[r * TSTR + t] = make_float2(cs, sn);
-            }
-            __syncthreads();
+    const float invG = 1.0f / (float)G;
+    int32_t jb = 0, r0 = 0;     // angle base of the stage (>= 0) and jb mod G
+    bool stage_remote = false;
+    auto tile = [&](int32_t j0, const KV8* kcur, const VV* vcur) __attribute__((always_inline)) {
+        f32x4 sacc;
+        if (BIF && stage_remote) {
+            // u of key n: (j - jb) - (f(j) - f(jb)), f(j) - f(jb) = floor((r0 + j - jb) / G)
+            const int32_t dl = max(j0 + n - jb, 0);
+            int32_t fd = (int32_t)((float)(r0 + dl) * invG);
+            if ((fd + 1) * G <= r0 + dl) ++fd;
+            if (fd * G > r0 + dl) --fd;
+            const int32_t uu = min(max(dl - fd, 0), kStage - 1);
+            sacc = scores_remote(kcur, uu);
+        } else {
+            sacc = scores_local(kcur);
         }
-        if (!head_ok) continue;
-#pragma unroll
-        for (int u = 0; u < kStage / kTile; ++u) {
+        process(j0, sacc, vcur);
+    };
+
+    // stages of 64 positions; within a stage one tile stays in flight while
+    // the previous one is processed (even tiles in kA/vA, odd ones in kB/vB)
+    for (int32_t js = kbeg; js < kend; js += kStage) {
+        stage_remote = BIF && bif && js <= rem_last;
+        jb = max(js, 0);
+        const int32_t fjb = remap(jb, G);
+        r0 = jb - fjb * G;
+        if (stage_remote || !q_local) {
+            rotate_q(stage_remote ? (int64_t)fp - fjb + jb : (int64_t)p);
+            q_local = !stage_remote;
+        }
+#pragma unroll 1
+        for (int u = 0; u < kStage / kTile; u += 2) {
             const int32_t j0 = js + kTile * u;
             if (j0 < kend) {
-                // even tiles live in kb1/vb1, odd ones in kbuf/vbuf; after use the
-                // buffer is refilled with the tile two steps ahead
-                KV8 kcur[NST];
-                VRow<TIN, DPL> vcur[kTile / KSUB];
-                if ((u & 1) == 0) {
-#pragma unroll
-                    for (int s = 0; s < NST; ++s) kcur[s] = kb1[s];
-#pragma unroll
-                    for (int r = 0; r < kTile / KSUB; ++r) vcur[r] = vb1[r];
-                } else {
-#pragma unroll
-                    for (int s = 0; s < NST; ++s) kcur[s] = kbuf[s];
-#pragma unroll
-                    for (int r = 0; r < kTile / KSUB; ++r) vcur[r] = vbuf[r];
+                const bool more = j0 + kTile < kend;
+                if (more) load_tile(j0 + kTile, kB, vB);
+                tile(j0, kA, vA);
+                if (more) {
+                    if (j0 + 2 * kTile < kend) load_tile(j0 + 2 * kTile, kA, vA);
+                    tile(j0 + kTile, kB, vB);
                 }
-                if (j0 + 2 * kTile < kend) {
-                    if ((u & 1) == 0) {
-                        // load into kbuf/vbuf via a temporary swap
-                        KV8 tk[NST];
-                        VRow<TIN, DPL> tv[kTile / KSUB];
-#pragma unroll
-                        for (int s = 0; s < NST; ++s) tk[s] = kbuf[s];
-#pragma unroll
-                        for (int r = 0; r < kTile / KSUB; ++r) tv[r] = vbuf[r];
-                        load_tile(j0 + 2 * kTile);
-#pragma unroll
-                        for (int s = 0; s < NST; ++s) {
-                            kb1[s] = kbuf[s];
-                            kbuf[s] = tk[s];
-                        }
-#pragma unroll
-                        for (int r = 0; r < kTile / KSUB; ++r) {
-                            vb1[r] = vbuf[r];
-                            vbuf[r] = tv[r];
-                        }
-                    } else {
-                        load_tile(j0 + 2 * kTile);
-                    }
-                }
-                process(j0, js, kcur, vcur);
             }
         }
     }
-    if (!head_ok) return;
+
     // ---- partial (m, l, unnormalised O) of this chunk ----
     float l_tot = l_part + __shfl_xor(l_part, 16);
     l_tot += __shfl_xor(l_tot, 32);
@@ -380,85 +442,427 @@ __global__ __launch_bounds__(512) void decode_split_kernel(DecodeArgs a) {
         pm[2 * (pbase + n)] = m_run;
         pm[2 * (pbase + n) + 1] = l_tot;
     }
-    // sum the KSUB key subsets (lanes ds, ds + DSL, ...)
 #pragma unroll
-    for (int off = DSL; off < 64; off <<= 1)
+    for (int h = 0; h < GQ; ++h)
+        if (h < grp) {
 #pragma unroll
-        for (int h = 0; h < GQ; ++h)
-#pragma unroll
-            for (int x = 0; x < DPL; ++x) O[h][x] += __shfl_xor(O[h][x], off);
-    if (ks == 0) {
-#pragma unroll
-        for (int h = 0; h < GQ; ++h)
-            if (h < grp) {
-#pragma unroll
-                for (int x = 0; x < DPL; ++x) po[(pbase + h) * D + DPL * ds + x] = O[h][x];
-            }
-    }
+            for (int x = 0; x < DPL; ++x) po[(pbase + h) * D + DPL * lane + x] = O[h][x];
+        }
 }
 
-// Merge of the chunk partials: o = sum 2^(m_c - M) O_c / sum 2^(m_c - M) l_c,
-// lse = (M + log2 sum ...) ln 2 -- the LogSumExp combination of [TW] §四.
-// Workgroup (head, sequence, 32-wide slice of d) with 256 threads = 32 d
-// values x 8 chunk groups; chunk g, g + 8, ... are summed by one thread and
-// the 8 groups combined through LDS.
+// bf16 decode.  Same scoring as above; P V runs on MFMA and V never enters
+// registers: each wave streams its V tiles into a 3-slot LDS ring with
+// global->LDS DMA, and the transposing LDS read ds_read_b64_tr_b16 hands every
+// lane its B operand (4 keys x 1 d per 16-d block) directly.  The
+// probabilities are already in the A operand layout (lane (n, c) holds keys
+// 4c..4c+3 of query column n), rounded to bf16; the row sums use the same
+// rounded values.  K tiles stay two ahead in registers.
+template <int D, bool BIF, int GQ>
+__global__ __launch_bounds__(512) void decode_split_bf16_kernel(DecodeArgs a) {
+    constexpr int HALF = D / 2;
+    constexpr int NST = D / 32;          // k-steps of the QK^T product
+    constexpr int NH = NST / 2;          // k-steps per RoPE half
+    constexpr bool PACK = GQ <= 8;       // hi and lo query parts in one operand
+    constexpr int TSTR = HALF + 2;       // LDS row stride of the angle table (float2)
+    constexpr int ROWB = D * 2;          // bytes of one key row of V
+    constexpr int CPR = ROWB / 16;       // 16-byte chunks per row
+    constexpr int RPI = 64 / CPR;        // rows per DMA instruction
+    constexpr int NI = kTile / RPI;      // DMA instructions per tile
+    constexpr int GSTR = RPI * ROWB + 32;  // bytes per instruction group (+32 spreads LDS banks)
+    constexpr int SLOT = NI * GSTR;      // bytes of one wave's V tile
+    constexpr int NDB = D / 16;          // 16-wide d blocks of O
+    constexpr int OPS = NST + NI;        // memory instructions per tile
+    __shared__ float2 tab[BIF ? kStageB * TSTR : 1];  // R(-u theta_t): (cos, sin)
+    __shared__ double revs[HALF];                     // theta_t / 2 pi
+    __shared__ __align__(16) char vs0[kWavesB * SLOT];
+    __shared__ __align__(16) char vs1[kWavesB * SLOT];
+    __shared__ __align__(16) char vs2[kWavesB * SLOT];
+
+    const int nw = blockDim.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int n = lane & 15, c = lane >> 4;
+    const int b = blockIdx.z, split = blockIdx.x;
+    const int kvh = blockIdx.y * nw + wave;
+    const bool head_ok = kvh < a.Hkv;
+    const int grp = a.Hq / a.Hkv;
+
+    int32_t L = a.seqlens[b];
+    L = L < 0 ? 0 : (L > a.max_seqlen_k ? a.max_seqlen_k : L);
+    const int32_t p = L - 1;
+    const int32_t G = (int32_t)group_size(L, a.w_pretrained);
+    const bool bif = BIF && G > 1;
+    const int32_t fp = remap(p, G);
+    const int32_t rem_last = p - a.w_local;  // keys j <= rem_last are remote (if bif)
+    // chunks start at z0 + split * chunk, z0 in (-kStageB, 0], so that the
+    // first local key starts a stage; positions below 0 are masked
+    int32_t z0 = 0;
+    if (bif && rem_last >= 0) {
+        const int32_t m = (rem_last + 1) % kStageB;
+        z0 = m ? m - kStageB : 0;
+    }
+    const int32_t kbeg = z0 + split * a.lay.chunk;
+    const int32_t kend = min(kbeg + a.lay.chunk, L);
+
+    float* pm = (float*)((char*)a.ws + a.lay.part_ml);
+    float* po = (float*)((char*)a.ws + a.lay.part_o);
+    const int64_t pbase = ((int64_t)b * a.lay.n_splits + split) * a.Hq + (int64_t)kvh * grp;
+
+    if (kbeg >= kend) {  // empty chunk: neutral partial
+        if (head_ok) {
+            if (c == 0 && n < grp) {
+                pm[2 * (pbase + n)] = -INFINITY;
+                pm[2 * (pbase + n) + 1] = 0.0f;
+            }
+            for (int x = lane; x < grp * D; x += 64) po[pbase * D + x] = 0.0f;
+        }
+        return;
+    }
+
+    // every load below is unconditional (branch-free memory stream, exact
+    // waits): indices are clamped to valid rows, masked keys weigh 0
+    const int kvh_c = min(kvh, a.Hkv - 1);
+    const bf16* kc = (const bf16*)a.kc + (int64_t)b * a.S_max * a.Hkv * D + (int64_t)kvh_c * D;
+    const bf16* vc = (const bf16*)a.vc + (int64_t)b * a.S_max * a.Hkv * D + (int64_t)kvh_c * D;
+    const int64_t rstride = (int64_t)a.Hkv * D;
+    char* const slot0 = vs0 + wave * SLOT;
+    char* const slot1 = vs1 + wave * SLOT;
+    char* const slot2 = vs2 + wave * SLOT;
+
+    const int32_t klo = max(kbeg, 0), khi = kend - 1;
+    // K of key j0 + n into registers (keys outside the chunk read a row
+    // inside it; their scores are masked)
+    auto load_k = [&](int32_t j0, bf16x8* kd) __attribute__((always_inline)) {
+        const int32_t kj = min(max(j0 + n, klo), khi);
+#pragma unroll
+        for (int s = 0; s < NST; ++s)
+            kd[s] = *reinterpret_cast<const bf16x8*>(kc + (int64_t)kj * rstride + 32 * s + 8 * c);
+    };
+    // V rows of a tile into a slot: instruction r moves keys r + NI q
+    // (q = lane / CPR) to slot + r * GSTR + q * ROWB (same clamping)
+    auto dma_v = [&](int32_t j0, char* slot) __attribute__((always_inline)) {
+        const int q = lane / CPR, ch = lane % CPR;
+        // a rolled loop: one DMA instruction per call site keeps the
+        // compiler's LDS-DMA dependency tracking exact
+#pragma unroll 1
+        for (int r = 0; r < NI; ++r) {
+            const int32_t key = min(max(j0 + r + NI * q, klo), khi);
+            __builtin_amdgcn_global_load_lds((const void*)(vc + (int64_t)key * rstride + 8 * ch),
+                                             (void*)(slot + r * GSTR), 16, 0, 0);
+        }
+    };
+
+    bf16x8 kA[NST], kB[NST], kC[NST];
+    load_k(kbeg, kA);
+    dma_v(kbeg, slot0);
+    load_k(kbeg + kTile, kB);
+    dma_v(kbeg + kTile, slot1);
+
+    // ---- theta_t / 2 pi and the small-angle table, once per workgroup (the
+    // only barrier) ----
+    {
+        const double rv = rope_rev(a.tab, threadIdx.x % HALF);  // blockDim is a multiple of HALF
+        if (threadIdx.x < HALF) revs[threadIdx.x] = rv;
+        if (BIF && bif) {
+            for (int x = threadIdx.x; x < kStageB * HALF; x += blockDim.x) {
+                float cs, sn;
+                rope_cs_hw(-(int64_t)(x / HALF), rv, cs, sn);
+                tab[(x / HALF) * TSTR + x % HALF] = make_float2(cs, sn);
+            }
+        }
+        __syncthreads();
+    }
+    if (!head_ok) return;
+
+    // ---- query (as in the generic kernel) ----
+    const float qscale = a.softmax_scale * kLog2e;
+    const int hq = PACK ? (n & (GQ - 1)) : n;
+    const bool qlo = PACK && n >= GQ;
+    bf16x8 qraw[NST];
+    {
+        const bool qok = hq < grp && (!PACK || n < 2 * GQ);
+        const bf16* qp = (const bf16*)a.q + ((int64_t)b * a.Hq + kvh * grp + hq) * D + 8 * c;
+#pragma unroll
+        for (int s = 0; s < NST; ++s)
+            qraw[s] = qok ? *reinterpret_cast<const bf16x8*>(qp + 32 * s) : bf16x8{};
+    }
+    bf16x8 Q[NST];
+    bf16x8 Qlo[PACK ? 1 : NST];
+    auto rotate_q = [&](int64_t pos) __attribute__((always_inline)) {
+#pragma unroll
+        for (int s = 0; s < NH; ++s)
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int t = 32 * s + 8 * c + u;
+                float cs, sn;
+                rope_cs_hw(pos, revs[t], cs, sn);
+                const float x0 = (float)qraw[s][u], x1 = (float)qraw[s + NH][u];
+                const float y0 = (x0 * cs - x1 * sn) * qscale;
+                const float y1 = (x1 * cs + x0 * sn) * qscale;
+                const bf16 h0 = (bf16)y0, h1 = (bf16)y1;
+                const bf16 l0 = (bf16)(y0 - (float)h0), l1 = (bf16)(y1 - (float)h1);
+                if constexpr (PACK) {
+                    Q[s][u] = qlo ? l0 : h0;
+                    Q[s + NH][u] = qlo ? l1 : h1;
+                } else {
+                    Q[s][u] = h0;
+                    Q[s + NH][u] = h1;
+                    Qlo[s][u] = l0;
+                    Qlo[s + NH][u] = l1;
+                }
+            }
+    };
+    bool q_local = false;
+
+    auto finish = [&](f32x4 acc) __attribute__((always_inline)) -> f32x4 {
+        if constexpr (PACK) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[i] += __shfl_xor(acc[i], GQ);
+        }
+        return acc;
+    };
+    auto scores_local = [&](const bf16x8* kcur) __attribute__((always_inline)) -> f32x4 {
+        f32x4 acc = {};
+#pragma unroll
+        for (int s = 0; s < NST; ++s) {
+            acc = mfma16(kcur[s], Q[s], acc);
+            if constexpr (!PACK) acc = mfma16(kcur[s], Qlo[s], acc);
+        }
+        return finish(acc);
+    };
+    auto scores_remote = [&](const bf16x8* kcur, int32_t u) __attribute__((always_inline)) -> f32x4 {
+        f32x4 acc = {};
+        const float2* tp = tab + u * TSTR + 8 * c;
+#pragma unroll
+        for (int s = 0; s < NH; ++s) {
+            bf16x8 h0, l0, h1, l1;
+#pragma unroll
+            for (int x = 0; x < 8; ++x) {
+                const float2 cs = tp[32 * s + x];
+                const float k0 = (float)kcur[s][x];
+                const float k1 = (float)kcur[s + NH][x];
+                const float y0 = k0 * cs.x - k1 * cs.y;
+                const float y1 = k1 * cs.x + k0 * cs.y;
+                h0[x] = (bf16)y0;
+                l0[x] = (bf16)(y0 - (float)h0[x]);
+                h1[x] = (bf16)y1;
+                l1[x] = (bf16)(y1 - (float)h1[x]);
+            }
+            acc = mfma16(h0, Q[s], acc);
+            acc = mfma16(l0, Q[s], acc);
+            acc = mfma16(h1, Q[s + NH], acc);
+            acc = mfma16(l1, Q[s + NH], acc);
+            if constexpr (!PACK) {
+                acc = mfma16(h0, Qlo[s], acc);
+                acc = mfma16(h1, Qlo[s + NH], acc);
+            }
+        }
+        return finish(acc);
+    };
+
+    // running softmax state per query column (log2 domain; a finite floor so
+    // masked keys give exp2(-inf) = 0, never NaN) and O^T blocks: lane (n, c)
+    // of block bd holds O[query 4c + i][d = 16 bd + n]
+    float m_run = -1e30f, l_part = 0.0f;
+    f32x4 O[NDB];
+#pragma unroll
+    for (int bd = 0; bd < NDB; ++bd) O[bd] = f32x4{};
+    // the lane's transposing-read address in a slot: it supplies the 4 d of
+    // key 4c + n/4 starting at d = 4 (n % 4) of each 16-d block
+    const int vkey = 4 * c + (n >> 2);
+    const int voff = (vkey % NI) * GSTR + (vkey / NI) * ROWB + (n & 3) * 8;
+
+    auto process = [&](int32_t j0, const f32x4& sacc, const char* slot) __attribute__((always_inline)) {
+        const bool col = n < GQ;  // lanes of packed lo parts carry no scores
+        float sc[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int32_t kk = j0 + 4 * c + i;
+            sc[i] = (col && kk >= 0 && kk < kend) ? sacc[i] : -INFINITY;
+        }
+        float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const bool raise = mx > m_run + 8.0f;
+        float alpha = 1.0f;
+        if (raise) {
+            alpha = __builtin_amdgcn_exp2f(m_run - mx);
+            m_run = mx;
+        }
+        s16x4 pa;
+        float ps = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const bf16 pb = (bf16)__builtin_amdgcn_exp2f(sc[i] - m_run);
+            ps += (float)pb;
+            pa[i] = __builtin_bit_cast(short, pb);
+        }
+        l_part = l_part * alpha + ps;
+        if (__any(raise)) {
+            // row 4c + i of O belongs to query column 4c + i
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float ai = __shfl(alpha, 4 * c + i);
+#pragma unroll
+                for (int bd = 0; bd < NDB; ++bd) O[bd][i] *= ai;
+            }
+        }
+#pragma unroll
+        for (int bd = 0; bd < NDB; ++bd) {
+            const s16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(slot + voff + 32 * bd));
+            O[bd] = mfma16k16(pa, vb, O[bd]);
+        }
+    };
+
+    const float invG = 1.0f / (float)G;
+    int32_t jb = 0, r0 = 0;  // angle base of the stage (>= 0) and jb mod G
+    bool stage_remote = false;
+    // one tile: issue the loads two tiles ahead, wait for this tile's, score, P V
+    auto step = [&](int32_t j0, const bf16x8* kcur, const char* scur, bf16x8* knext, char* snext)
+        __attribute__((always_inline)) {
+        load_k(j0 + 2 * kTile, knext);
+        dma_v(j0 + 2 * kTile, snext);
+        JL_WAIT_VMCNT(2 * OPS);  // this tile's K and V have landed
+        __builtin_amdgcn_sched_barrier(0);  // nothing that reads them moves above the wait
+        f32x4 sacc;
+        if (BIF && stage_remote) {
+            // u of key n: (j - jb) - (f(j) - f(jb)), f(j) - f(jb) = floor((r0 + j - jb) / G)
+            const int32_t dl = max(j0 + n - jb, 0);
+            int32_t fd = (int32_t)((float)(r0 + dl) * invG);
+            if ((fd + 1) * G <= r0 + dl) ++fd;
+            if (fd * G > r0 + dl) --fd;
+            const int32_t uu = min(max(dl - fd, 0), kStageB - 1);
+            sacc = scores_remote(kcur, uu);
+        } else {
+            sacc = scores_local(kcur);
+        }
+        process(j0, sacc, scur);
+    };
+
+    for (int32_t js = kbeg; js < kend; js += kStageB) {
+        stage_remote = BIF && bif && js <= rem_last;
+        jb = max(js, 0);
+        const int32_t fjb = remap(jb, G);
+        r0 = jb - fjb * G;
+        if (stage_remote || !q_local) {
+            rotate_q(stage_remote ? (int64_t)fp - fjb + jb : (int64_t)p);
+            q_local = !stage_remote;
+        }
+        // tiles js, js + 16, js + 32 sit in (kA, slot0), (kB, slot1), (kC,
+        // slot2); tiles past kend are fully masked
+        step(js, kA, slot0, kC, slot2);
+        step(js + kTile, kB, slot1, kA, slot0);
+        step(js + 2 * kTile, kC, slot2, kB, slot1);
+    }
+
+    // ---- partial (m, l, unnormalised O) of this chunk ----
+    float l_tot = l_part + __shfl_xor(l_part, 16);
+    l_tot += __shfl_xor(l_tot, 32);
+    if (c == 0 && n < grp) {
+        pm[2 * (pbase + n)] = m_run;
+        pm[2 * (pbase + n) + 1] = l_tot;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        if (4 * c + i < grp) {
+#pragma unroll
+            for (int bd = 0; bd < NDB; ++bd) po[(pbase + 4 * c + i) * D + 16 * bd + n] = O[bd][i];
+        }
+}
+
+// Merge of the chunk partials in one pass: o = sum 2^(m_c - M) O_c /
+// sum 2^(m_c - M) l_c, lse = (M + log2 sum ...) ln 2 -- the LogSumExp
+// combination of [TW] §四.  Workgroup (head, sequence, 32-wide slice of d),
+// 256 threads = 32 chunk groups x 8 quads of d; each thread folds its chunks
+// with a running max, then the 32 groups are folded through LDS.  A sequence
+// with no keys gets o = 0 and lse = -inf.
 template <typename TOUT>
 __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
-    __shared__ float red[256];
-    __shared__ float accs[8][33];
+    constexpr int NG = 32;
+    __shared__ float sm[NG][8], sl[NG][8];
+    __shared__ f32x4 so[NG][8];
     const int head = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
-    const int x = 32 * blockIdx.z + (tid & 31), grp8 = tid >> 5;
+    const int g = tid >> 3, q4 = tid & 7;
+    const int x0 = 32 * blockIdx.z + 4 * q4;
     const float* pm = (const float*)((const char*)a.ws + a.lay.part_ml);
     const float* po = (const float*)((const char*)a.ws + a.lay.part_o);
-    const int64_t base = (int64_t)b * a.lay.n_splits * a.Hq + head;
     const int ns = a.lay.n_splits;
-    float M = -INFINITY;
-    for (int sp = tid; sp < ns; sp += 256) M = fmaxf(M, pm[2 * (base + (int64_t)sp * a.Hq)]);
-    red[tid] = M;
-    __syncthreads();
-    for (int o = 128; o > 0; o >>= 1) {
-        if (tid < o) red[tid] = fmaxf(red[tid], red[tid + o]);
-        __syncthreads();
-    }
-    M = red[0];
-    __syncthreads();
-    float ls = 0.0f;
-    for (int sp = tid; sp < ns; sp += 256) {
-        const int64_t idx = base + (int64_t)sp * a.Hq;
-        ls += __builtin_amdgcn_exp2f(pm[2 * idx] - M) * pm[2 * idx + 1];
-    }
-    red[tid] = ls;
-    float acc = 0.0f;
-#pragma unroll 4
-    for (int sp = grp8; sp < ns; sp += 8) {
-        const int64_t idx = base + (int64_t)sp * a.Hq;
-        acc += __builtin_amdgcn_exp2f(pm[2 * idx] - M) * po[idx * a.d + x];
-    }
-    accs[grp8][tid & 31] = acc;
-    __syncthreads();
-    for (int o = 128; o > 0; o >>= 1) {
-        if (tid < o) red[tid] += red[tid + o];
-        __syncthreads();
-    }
-    const float Lsum = red[0];
-    if (grp8 == 0) {
-        float tot = 0.0f;
+    const int64_t base = (int64_t)b * ns * a.Hq + head;
+    float M = -INFINITY, Ls = 0.0f;
+    f32x4 acc = {};
+    for (int s0 = g; s0 < ns; s0 += NG * 4) {
+        float2 ml[4];
+        f32x4 ov[4];
 #pragma unroll
-        for (int q = 0; q < 8; ++q) tot += accs[q][tid & 31];
-        ((TOUT*)a.o)[((int64_t)b * a.Hq + head) * a.d + x] = (TOUT)(tot / Lsum);
-        if (x == 0) a.lse[(int64_t)b * a.Hq + head] = (M + log2f(Lsum)) * kLn2;
+        for (int k = 0; k < 4; ++k) {
+            const int sp = s0 + NG * k;
+            if (sp < ns) {
+                const int64_t idx = base + (int64_t)sp * a.Hq;
+                ml[k] = *(const float2*)(pm + 2 * idx);
+                ov[k] = *(const f32x4*)(po + idx * a.d + x0);
+            } else {
+                ml[k] = make_float2(-INFINITY, 0.0f);
+                ov[k] = f32x4{};
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            if (ml[k].x == -INFINITY) continue;
+            if (ml[k].x > M) {
+                const float sc = __builtin_amdgcn_exp2f(M - ml[k].x);  // 0 when M = -inf
+                Ls *= sc;
+                acc *= sc;
+                M = ml[k].x;
+            }
+            const float w = __builtin_amdgcn_exp2f(ml[k].x - M);
+            Ls += w * ml[k].y;
+            acc += w * ov[k];
+        }
+    }
+    sm[g][q4] = M;
+    sl[g][q4] = Ls;
+    so[g][q4] = acc;
+    __syncthreads();
+    if (g == 0) {
+        float Mt = -INFINITY;
+#pragma unroll 8
+        for (int k = 0; k < NG; ++k) Mt = fmaxf(Mt, sm[k][q4]);
+        float Lt = 0.0f;
+        f32x4 At = {};
+        if (Mt != -INFINITY) {
+#pragma unroll 8
+            for (int k = 0; k < NG; ++k) {
+                if (sm[k][q4] == -INFINITY) continue;
+                const float w = __builtin_amdgcn_exp2f(sm[k][q4] - Mt);
+                Lt += w * sl[k][q4];
+                At += w * so[k][q4];
+            }
+        }
+        const bool empty = !(Lt > 0.0f);
+        TOUT* o = (TOUT*)a.o + ((int64_t)b * a.Hq + head) * a.d + x0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[i] = (TOUT)(empty ? 0.0f : At[i] / Lt);
+        if (blockIdx.z == 0 && q4 == 0)
+            a.lse[(int64_t)b * a.Hq + head] = empty ? -INFINITY : (Mt + log2f(Lt)) * kLn2;
     }
 }
 
 template <int D, typename TIN, int GQ>
 static hipError_t launch_decode_g(const DecodeArgs& a, hipStream_t s) {
-    const int nw = a.Hkv < 8 ? a.Hkv : 8;
+    const int wmax = sizeof(TIN) == 2 ? kWavesB : kDecodeWaves;
+    const int nw = a.Hkv < wmax ? a.Hkv : wmax;
     const dim3 grid(a.lay.n_splits, (a.Hkv + nw - 1) / nw, a.B);
     LaunchScope scope(a.bifocal ? "decode_split" : "decode_split_plain", s);
-    if (a.bifocal)
-        hipLaunchKernelGGL((decode_split_kernel<D, TIN, true, GQ>), grid, dim3(64 * nw), 0, s, a);
-    else
-        hipLaunchKernelGGL((decode_split_kernel<D, TIN, false, GQ>), grid, dim3(64 * nw), 0, s, a);
+    if constexpr (sizeof(TIN) == 2) {
+        if (a.bifocal)
+            hipLaunchKernelGGL((decode_split_bf16_kernel<D, true, GQ>), grid, dim3(64 * nw), 0, s, a);
+        else
+            hipLaunchKernelGGL((decode_split_bf16_kernel<D, false, GQ>), grid, dim3(64 * nw), 0, s, a);
+    } else {
+        if (a.bifocal)
+            hipLaunchKernelGGL((decode_split_kernel<D, TIN, true, GQ>), grid, dim3(64 * nw), 0, s, a);
+        else
+            hipLaunchKernelGGL((decode_split_kernel<D, TIN, false, GQ>), grid, dim3(64 * nw), 0, s, a);
+    }
     return hipGetLastError();
 }
 

@@ -33,7 +33,8 @@ struct DecodeLayout {
     int32_t chunk;
     size_t part_o, part_ml, total;
 };
-DecodeLayout decode_layout(int32_t batch, int32_t max_seqlen_k, int32_t Hq, int32_t Hkv, int32_t d);
+DecodeLayout decode_layout(int32_t batch, int32_t max_seqlen_k, int32_t Hq, int32_t Hkv, int32_t d,
+                           int dtype);
 
 RopeFreq make_rope_freq(double base, int d);
 
