@@ -132,7 +132,7 @@ DecodeLayout decode_layout(int32_t B, int32_t max_seqlen_k, int32_t Hq, int32_t 
     // fp32: 4-wave workgroups (two per compute unit), 64-position stages
     const bool b16 = dtype == JL_DTYPE_BF16;
     const int wmax = b16 ? 8 : 4;
-    const int stage = b16 ? 48 : 64;
+    const int stage = b16 ? kDecodeStageB : 64;
     const int nw = Hkv < wmax ? Hkv : wmax;  // waves (kv heads) per decode workgroup
     const int64_t groups = (Hkv + nw - 1) / nw;
     // JL_DECODE_WGS overrides the workgroup target for tuning
@@ -146,6 +146,7 @@ DecodeLayout decode_layout(int32_t B, int32_t max_seqlen_k, int32_t Hq, int32_t 
     if (want < 1) want = 1;
     int64_t chunk = (span + want - 1) / want;
     chunk = (chunk + stage - 1) / stage * stage;
+    if (b16 && chunk > (int64_t)kDecodeMaxStagesB * stage) chunk = (int64_t)kDecodeMaxStagesB * stage;
     L.chunk = (int32_t)chunk;
     L.n_splits = (int32_t)((span + chunk - 1) / chunk);
     size_t off = 0;

@@ -31,7 +31,7 @@ constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kStage = 64;  // key positions per angle-table stage
 constexpr int kTile = 16;   // keys per wave step
 constexpr int kDecodeWaves = 4;  // fp32 kernel: waves (kv heads) per workgroup
-constexpr int kStageB = 48;      // bf16 kernel: positions per stage (three tiles)
+constexpr int kStageB = kDecodeStageB;  // bf16 kernel: positions per stage (three tiles)
 constexpr int kWavesB = 8;       // bf16 kernel: waves (kv heads) per workgroup
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -43,12 +43,11 @@ __device__ __forceinline__ f32x4 mfma16k16(s16x4 a, s16x4 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
 }
 
-// s_waitcnt vmcnt(n) (n < 64), other counters untouched
-#define JL_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(0x0F70 | ((n) & 15) | (((n) >> 4) << 14))
 
 __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
+
 
 template <typename TIN>
 struct Vec8;
@@ -450,13 +449,14 @@ void decode_split_kernel(DecodeArgs a) {
         }
 }
 
-// bf16 decode.  Same scoring as above; P V runs on MFMA and V never enters
-// registers: each wave streams its V tiles into a 3-slot LDS ring with
-// global->LDS DMA, and the transposing LDS read ds_read_b64_tr_b16 hands every
+// bf16 decode.  Same scoring as above; P V runs on MFMA.  Each wave stages
+// its V tile in LDS and the transposing read ds_read_b64_tr_b16 hands every
 // lane its B operand (4 keys x 1 d per 16-d block) directly.  The
 // probabilities are already in the A operand layout (lane (n, c) holds keys
 // 4c..4c+3 of query column n), rounded to bf16; the row sums use the same
-// rounded values.  K tiles stay two ahead in registers.
+// rounded values.  K and V tiles stay two ahead in registers.  All loads are
+// unconditional (indices clamped to valid rows), so the memory stream has no
+// branches and the compiler's waits stay exact.
 template <int D, bool BIF, int GQ>
 __global__ __launch_bounds__(512) void decode_split_bf16_kernel(DecodeArgs a) {
     constexpr int HALF = D / 2;
@@ -466,17 +466,16 @@ __global__ __launch_bounds__(512) void decode_split_bf16_kernel(DecodeArgs a) {
     constexpr int TSTR = HALF + 2;       // LDS row stride of the angle table (float2)
     constexpr int ROWB = D * 2;          // bytes of one key row of V
     constexpr int CPR = ROWB / 16;       // 16-byte chunks per row
-    constexpr int RPI = 64 / CPR;        // rows per DMA instruction
-    constexpr int NI = kTile / RPI;      // DMA instructions per tile
-    constexpr int GSTR = RPI * ROWB + 32;  // bytes per instruction group (+32 spreads LDS banks)
-    constexpr int SLOT = NI * GSTR;      // bytes of one wave's V tile
+    constexpr int RPI = 64 / CPR;        // rows per 64-lane load
+    constexpr int NI = kTile / RPI;      // V loads per lane per tile
+    constexpr int VRS = ROWB + 32;       // LDS row stride of a V tile (+32 spreads banks)
+    constexpr int SLOT = kTile * VRS;    // bytes of one wave's V tile
     constexpr int NDB = D / 16;          // 16-wide d blocks of O
-    constexpr int OPS = NST + NI;        // memory instructions per tile
     __shared__ float2 tab[BIF ? kStageB * TSTR : 1];  // R(-u theta_t): (cos, sin)
-    __shared__ double revs[HALF];                     // theta_t / 2 pi
-    __shared__ __align__(16) char vs0[kWavesB * SLOT];
-    __shared__ __align__(16) char vs1[kWavesB * SLOT];
-    __shared__ __align__(16) char vs2[kWavesB * SLOT];
+    // query angles: row st < kDecodeMaxStagesB holds R(f(p) - f(jb) + jb) of
+    // stage st of this chunk (remote stages), the last row R(p)
+    __shared__ float2 qtab[(kDecodeMaxStagesB + 1) * HALF];
+    __shared__ __align__(16) char vs[kWavesB * SLOT];  // per wave: the V tile in use
 
     const int nw = blockDim.x >> 6;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
@@ -524,9 +523,7 @@ __global__ __launch_bounds__(512) void decode_split_bf16_kernel(DecodeArgs a) {
     const bf16* kc = (const bf16*)a.kc + (int64_t)b * a.S_max * a.Hkv * D + (int64_t)kvh_c * D;
     const bf16* vc = (const bf16*)a.vc + (int64_t)b * a.S_max * a.Hkv * D + (int64_t)kvh_c * D;
     const int64_t rstride = (int64_t)a.Hkv * D;
-    char* const slot0 = vs0 + wave * SLOT;
-    char* const slot1 = vs1 + wave * SLOT;
-    char* const slot2 = vs2 + wave * SLOT;
+    char* const slot = vs + wave * SLOT;
 
     const int32_t klo = max(kbeg, 0), khi = kend - 1;
     // K of key j0 + n into registers (keys outside the chunk read a row
@@ -537,31 +534,49 @@ __global__ __launch_bounds__(512) void decode_split_bf16_kernel(DecodeArgs a) {
         for (int s = 0; s < NST; ++s)
             kd[s] = *reinterpret_cast<const bf16x8*>(kc + (int64_t)kj * rstride + 32 * s + 8 * c);
     };
-    // V rows of a tile into a slot: instruction r moves keys r + NI q
-    // (q = lane / CPR) to slot + r * GSTR + q * ROWB (same clamping)
-    auto dma_v = [&](int32_t j0, char* slot) __attribute__((always_inline)) {
+    // V tiles are staged in registers two tiles ahead (load r of a lane
+    // reads 16 bytes of key RPI r + lane / CPR, so one load instruction
+    // covers whole rows) and written to the wave's LDS slot, rows VRS bytes
+    // apart, right before use
+    auto load_vr = [&](int32_t j0, bf16x8* vd) __attribute__((always_inline)) {
         const int q = lane / CPR, ch = lane % CPR;
-        // a rolled loop: one DMA instruction per call site keeps the
-        // compiler's LDS-DMA dependency tracking exact
-#pragma unroll 1
+#pragma unroll
         for (int r = 0; r < NI; ++r) {
-            const int32_t key = min(max(j0 + r + NI * q, klo), khi);
-            __builtin_amdgcn_global_load_lds((const void*)(vc + (int64_t)key * rstride + 8 * ch),
-                                             (void*)(slot + r * GSTR), 16, 0, 0);
+            const int32_t key = min(max(j0 + RPI * r + q, klo), khi);
+            vd[r] = *reinterpret_cast<const bf16x8*>(vc + (int64_t)key * rstride + 8 * ch);
         }
     };
+    auto store_vr = [&](const bf16x8* vsrc, char* dst) __attribute__((always_inline)) {
+        const int q = lane / CPR, ch = lane % CPR;
+#pragma unroll
+        for (int r = 0; r < NI; ++r)
+            *reinterpret_cast<bf16x8*>(dst + (RPI * r + q) * VRS + 16 * ch) = vsrc[r];
+    };
+    bf16x8 vA[NI], vB[NI], vC[NI];
 
     bf16x8 kA[NST], kB[NST], kC[NST];
     load_k(kbeg, kA);
-    dma_v(kbeg, slot0);
+    load_vr(kbeg, vA);
     load_k(kbeg + kTile, kB);
-    dma_v(kbeg + kTile, slot1);
+    load_vr(kbeg + kTile, vB);
 
-    // ---- theta_t / 2 pi and the small-angle table, once per workgroup (the
-    // only barrier) ----
+    // ---- angle tables, once per workgroup (the only barrier): the query
+    // rows and the small key angles -u theta_t ----
+    constexpr int QLOC = kDecodeMaxStagesB;  // row of R(p)
     {
         const double rv = rope_rev(a.tab, threadIdx.x % HALF);  // blockDim is a multiple of HALF
-        if (threadIdx.x < HALF) revs[threadIdx.x] = rv;
+        const int nst = min((kend - kbeg + kStageB - 1) / kStageB, (int32_t)kDecodeMaxStagesB);
+        for (int x = threadIdx.x; x < (nst + 1) * HALF; x += blockDim.x) {
+            const int st = x / HALF;
+            int64_t pos = p;
+            if (st < nst) {
+                const int32_t jbs = max(kbeg + kStageB * st, 0);
+                pos = (int64_t)fp - remap(jbs, G) + jbs;
+            }
+            float cs, sn;
+            rope_cs_hw(pos, rv, cs, sn);
+            qtab[(st < nst ? st : QLOC) * HALF + x % HALF] = make_float2(cs, sn);
+        }
         if (BIF && bif) {
             for (int x = threadIdx.x; x < kStageB * HALF; x += blockDim.x) {
                 float cs, sn;
@@ -587,17 +602,16 @@ __global__ __launch_bounds__(512) void decode_split_bf16_kernel(DecodeArgs a) {
     }
     bf16x8 Q[NST];
     bf16x8 Qlo[PACK ? 1 : NST];
-    auto rotate_q = [&](int64_t pos) __attribute__((always_inline)) {
+    auto rotate_q = [&](int row) __attribute__((always_inline)) {
+        const float2* qt = qtab + row * HALF + 8 * c;
 #pragma unroll
         for (int s = 0; s < NH; ++s)
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
-                const int t = 32 * s + 8 * c + u;
-                float cs, sn;
-                rope_cs_hw(pos, revs[t], cs, sn);
+                const float2 cs = qt[32 * s + u];
                 const float x0 = (float)qraw[s][u], x1 = (float)qraw[s + NH][u];
-                const float y0 = (x0 * cs - x1 * sn) * qscale;
-                const float y1 = (x1 * cs + x0 * sn) * qscale;
+                const float y0 = (x0 * cs.x - x1 * cs.y) * qscale;
+                const float y1 = (x1 * cs.x + x0 * cs.y) * qscale;
                 const bf16 h0 = (bf16)y0, h1 = (bf16)y1;
                 const bf16 l0 = (bf16)(y0 - (float)h0), l1 = (bf16)(y1 - (float)h1);
                 if constexpr (PACK) {
@@ -669,7 +683,7 @@ __global__ __launch_bounds__(512) void decode_split_bf16_kernel(DecodeArgs a) {
     // the lane's transposing-read address in a slot: it supplies the 4 d of
     // key 4c + n/4 starting at d = 4 (n % 4) of each 16-d block
     const int vkey = 4 * c + (n >> 2);
-    const int voff = (vkey % NI) * GSTR + (vkey / NI) * ROWB + (n & 3) * 8;
+    const int voff = vkey * VRS + (n & 3) * 8;
 
     auto process = [&](int32_t j0, const f32x4& sacc, const char* slot) __attribute__((always_inline)) {
         const bool col = n < GQ;  // lanes of packed lo parts carry no scores
@@ -716,13 +730,13 @@ __global__ __launch_bounds__(512) void decode_split_bf16_kernel(DecodeArgs a) {
     const float invG = 1.0f / (float)G;
     int32_t jb = 0, r0 = 0;  // angle base of the stage (>= 0) and jb mod G
     bool stage_remote = false;
-    // one tile: issue the loads two tiles ahead, wait for this tile's, score, P V
-    auto step = [&](int32_t j0, const bf16x8* kcur, const char* scur, bf16x8* knext, char* snext)
-        __attribute__((always_inline)) {
+    // one tile: issue the loads two tiles ahead, stage this tile's V in LDS,
+    // score, P V
+    auto step = [&](int32_t j0, const bf16x8* kcur, const bf16x8* vcur, bf16x8* knext,
+                    bf16x8* vnext) __attribute__((always_inline)) {
         load_k(j0 + 2 * kTile, knext);
-        dma_v(j0 + 2 * kTile, snext);
-        JL_WAIT_VMCNT(2 * OPS);  // this tile's K and V have landed
-        __builtin_amdgcn_sched_barrier(0);  // nothing that reads them moves above the wait
+        load_vr(j0 + 2 * kTile, vnext);
+        store_vr(vcur, slot);  // the same wave writes then reads: LDS keeps its order
         f32x4 sacc;
         if (BIF && stage_remote) {
             // u of key n: (j - jb) - (f(j) - f(jb)), f(j) - f(jb) = floor((r0 + j - jb) / G)
@@ -735,7 +749,7 @@ __global__ __launch_bounds__(512) void decode_split_bf16_kernel(DecodeArgs a) {
         } else {
             sacc = scores_local(kcur);
         }
-        process(j0, sacc, scur);
+        process(j0, sacc, slot);
     };
 
     for (int32_t js = kbeg; js < kend; js += kStageB) {
@@ -744,14 +758,14 @@ __global__ __launch_bounds__(512) void decode_split_bf16_kernel(DecodeArgs a) {
         const int32_t fjb = remap(jb, G);
         r0 = jb - fjb * G;
         if (stage_remote || !q_local) {
-            rotate_q(stage_remote ? (int64_t)fp - fjb + jb : (int64_t)p);
+            rotate_q(stage_remote ? (js - kbeg) / kStageB : QLOC);
             q_local = !stage_remote;
         }
-        // tiles js, js + 16, js + 32 sit in (kA, slot0), (kB, slot1), (kC,
-        // slot2); tiles past kend are fully masked
-        step(js, kA, slot0, kC, slot2);
-        step(js + kTile, kB, slot1, kA, slot0);
-        step(js + 2 * kTile, kC, slot2, kB, slot1);
+        // tiles js, js + 16, js + 32 sit in (kA, vA), (kB, vB), (kC, vC);
+        // tiles past kend are fully masked
+        step(js, kA, vA, kC, vC);
+        step(js + kTile, kB, vB, kA, vA);
+        step(js + 2 * kTile, kC, vC, kB, vB);
     }
 
     // ---- partial (m, l, unnormalised O) of this chunk ----
@@ -773,7 +787,8 @@ __global__ __launch_bounds__(512) void decode_split_bf16_kernel(DecodeArgs a) {
 // sum 2^(m_c - M) l_c, lse = (M + log2 sum ...) ln 2 -- the LogSumExp
 // combination of [TW] §四.  Workgroup (head, sequence, 32-wide slice of d),
 // 256 threads = 32 chunk groups x 8 quads of d; each thread folds its chunks
-// with a running max, then the 32 groups are folded through LDS.  A sequence
+// (loaded together) against their common max, then the 32 groups are folded
+// through LDS.  A sequence
 // with no keys gets o = 0 and lse = -inf.
 template <typename TOUT>
 __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
@@ -787,32 +802,34 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
     const float* po = (const float*)((const char*)a.ws + a.lay.part_o);
     const int ns = a.lay.n_splits;
     const int64_t base = (int64_t)b * ns * a.Hq + head;
+    // every load of a thread is issued before any is used (one memory round
+    // trip for up to 8 chunks per thread, more chunks loop)
     float M = -INFINITY, Ls = 0.0f;
     f32x4 acc = {};
-    for (int s0 = g; s0 < ns; s0 += NG * 4) {
-        float2 ml[4];
-        f32x4 ov[4];
+    for (int s0 = g; s0 < ns; s0 += NG * 8) {
+        float2 ml[8];
+        f32x4 ov[8];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const int sp = s0 + NG * k;
-            if (sp < ns) {
-                const int64_t idx = base + (int64_t)sp * a.Hq;
-                ml[k] = *(const float2*)(pm + 2 * idx);
-                ov[k] = *(const f32x4*)(po + idx * a.d + x0);
-            } else {
-                ml[k] = make_float2(-INFINITY, 0.0f);
-                ov[k] = f32x4{};
-            }
+        for (int k = 0; k < 8; ++k) {
+            const int sp = min(s0 + NG * k, ns - 1);
+            const int64_t idx = base + (int64_t)sp * a.Hq;
+            ml[k] = *(const float2*)(pm + 2 * idx);
+            ov[k] = *(const f32x4*)(po + idx * a.d + x0);
+        }
+        float mk = -INFINITY;
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+            if (s0 + NG * k < ns) mk = fmaxf(mk, ml[k].x);
+        if (mk == -INFINITY) continue;
+        if (mk > M) {
+            const float sc = __builtin_amdgcn_exp2f(M - mk);  // 0 when M = -inf
+            Ls *= sc;
+            acc *= sc;
+            M = mk;
         }
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            if (ml[k].x == -INFINITY) continue;
-            if (ml[k].x > M) {
-                const float sc = __builtin_amdgcn_exp2f(M - ml[k].x);  // 0 when M = -inf
-                Ls *= sc;
-                acc *= sc;
-                M = ml[k].x;
-            }
+        for (int k = 0; k < 8; ++k) {
+            if (s0 + NG * k >= ns || ml[k].x == -INFINITY) continue;
             const float w = __builtin_amdgcn_exp2f(ml[k].x - M);
             Ls += w * ml[k].y;
             acc += w * ov[k];

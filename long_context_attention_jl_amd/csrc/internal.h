@@ -28,6 +28,11 @@ struct PrefillLayout {
 };
 PrefillLayout prefill_layout(int64_t T, int32_t n_seqs, int32_t Hkv, int32_t d, int dtype);
 
+// bf16 decode: positions per stage and the most stages one chunk may hold
+// (the kernel keeps one query-angle row per stage in LDS)
+constexpr int kDecodeStageB = 48;
+constexpr int kDecodeMaxStagesB = 32;
+
 struct DecodeLayout {
     int32_t n_splits;
     int32_t chunk;
