@@ -26,8 +26,10 @@
 //   laid out by the pre-pass so each lane reads its 8 keys as one 16-byte
 //   vector).  Tiles of 64 keys are double-buffered in LDS and filled by
 //   global->LDS DMA while the previous tile is processed.
-// Queries are rotated at entry (fp64-reduced angles) and scaled by
-// softmax_scale * log2(e) so the softmax runs on exp2.
+// Queries are rotated at entry (fp64-reduced angles, hardware sin/cos) and
+// scaled by softmax_scale * log2(e) so the softmax runs on exp2.  Score
+// accumulators start at -m_c (m_c: the running max, or 0 before a row has
+// one), so the exponentials need no subtraction unless the max is raised.
 //
 // Operand precision: rounding a key is a random error per key and averages
 // out over the softmax, but rounding a query is a fixed error per row whose
@@ -151,7 +153,7 @@ void prefill_bf16_kernel(PrefillArgs a, int rb_first, int n_rb) {
                     x1 = (float)qp[t + HALF];
                 }
                 float c, sn;
-                rope_cs(remapped ? remap(row, G) : row, rv, c, sn);
+                rope_cs_hw(remapped ? remap(row, G) : row, rv, c, sn);
                 const float y0 = (x0 * c - x1 * sn) * qscale, y1 = (x1 * c + x0 * sn) * qscale;
                 qimg[r * C::KSTR + t] = lo ? (f16)(y0 - (float)(f16)y0) : (f16)y0;
                 qimg[r * C::KSTR + t + HALF] = lo ? (f16)(y1 - (float)(f16)y1) : (f16)y1;
@@ -198,6 +200,7 @@ void prefill_bf16_kernel(PrefillArgs a, int rb_first, int n_rb) {
     // m starts at a finite floor so rows that have not met a key of the
     // current phase yet give exp2(-inf - m) = 0, never NaN.
     float m_run = -1e30f, l_run = 0.0f;
+    float m_c = 0.0f;  // what the score accumulators start from (negated)
     f32x16 O[C::ND];
 #pragma unroll
     for (int db = 0; db < C::ND; ++db) O[db] = f32x16{};
@@ -221,7 +224,9 @@ void prefill_bf16_kernel(PrefillArgs a, int rb_first, int n_rb) {
                 vv[u][db] = *reinterpret_cast<const f16x8*>(vb + 32 * db * C::VSTR + 16 * u);
         // all operand reads of the block are in flight before its MFMA chain
         __builtin_amdgcn_sched_barrier(0);
-        f32x16 Sb = {};
+        f32x16 Sb;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) Sb[i] = -m_c;
 #pragma unroll
         for (int st = 0; st < C::NS; ++st) {
             Sb = mfma32h(kv[st], Qc[st], Sb);
@@ -240,15 +245,21 @@ void prefill_bf16_kernel(PrefillArgs a, int rb_first, int n_rb) {
                 if (!keep) Sb[i] = -INFINITY;
             }
         }
+        // Sb holds s - m_c; while m_c == m_run (always, once a row has a
+        // finite max) p = exp2(Sb) directly
         float mx = -INFINITY;
 #pragma unroll
         for (int i = 0; i < 16; ++i) mx = fmaxf(mx, Sb[i]);
-        mx = max_other_half(mx);
+        mx = max_other_half(mx) + m_c;
         const bool raise = mx > m_run + 8.0f;
         if (__any(raise)) {
             const float m_new = raise ? mx : m_run;
             const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+            const float d = m_new - m_c;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) Sb[i] -= d;
             m_run = m_new;
+            m_c = m_new > -1e29f ? m_new : 0.0f;
             l_run *= alpha;
 #pragma unroll
             for (int db = 0; db < C::ND; ++db)
@@ -257,7 +268,7 @@ void prefill_bf16_kernel(PrefillArgs a, int rb_first, int n_rb) {
         }
         f16x8 Pb[2];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) Pb[i >> 3][i & 7] = (f16)__builtin_amdgcn_exp2f(Sb[i] - m_run);
+        for (int i = 0; i < 16; ++i) Pb[i >> 3][i & 7] = (f16)__builtin_amdgcn_exp2f(Sb[i]);
 #pragma unroll
         for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
