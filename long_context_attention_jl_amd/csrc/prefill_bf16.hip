@@ -201,6 +201,7 @@ void prefill_bf16_kernel(PrefillArgs a, int rb_first, int n_rb) {
     // current phase yet give exp2(-inf - m) = 0, never NaN.
     float m_run = -1e30f, l_run = 0.0f;
     float m_c = 0.0f;  // what the score accumulators start from (negated)
+    f32x16 negm = {};  // -m_c in every element: the C operand of a block's first MFMA
     f32x16 O[C::ND];
 #pragma unroll
     for (int db = 0; db < C::ND; ++db) O[db] = f32x16{};
@@ -224,9 +225,7 @@ void prefill_bf16_kernel(PrefillArgs a, int rb_first, int n_rb) {
                 vv[u][db] = *reinterpret_cast<const f16x8*>(vb + 32 * db * C::VSTR + 16 * u);
         // all operand reads of the block are in flight before its MFMA chain
         __builtin_amdgcn_sched_barrier(0);
-        f32x16 Sb;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) Sb[i] = -m_c;
+        f32x16 Sb = negm;
 #pragma unroll
         for (int st = 0; st < C::NS; ++st) {
             Sb = mfma32h(kv[st], Qc[st], Sb);
@@ -260,6 +259,8 @@ void prefill_bf16_kernel(PrefillArgs a, int rb_first, int n_rb) {
             for (int i = 0; i < 16; ++i) Sb[i] -= d;
             m_run = m_new;
             m_c = m_new > -1e29f ? m_new : 0.0f;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) negm[i] = -m_c;
             l_run *= alpha;
 #pragma unroll
             for (int db = 0; db < C::ND; ++db)
