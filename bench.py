@@ -77,6 +77,7 @@ def main():
     ap.add_argument("--decode-iters", type=int, default=200)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-three-call", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0,
                     help="only run a plain device copy of this many bytes (counter calibration)")
     args = ap.parse_args()
@@ -168,6 +169,9 @@ def main():
     }
     del o, lse
 
+    if not args.no_three_call:
+        out["three_call"] = bench_three_call(jl, torch, case, ms_per_step)
+
     if not args.no_decode:
         out["decode"] = bench_decode(jl, inputs, torch, args.decode_iters)
 
@@ -175,6 +179,28 @@ def main():
         out["cpu_baseline"] = cpu_baseline(case)
 
     print(json.dumps(out), flush=True)
+
+
+def bench_three_call(jl, torch, case, fused_ms):
+    """The pages' unfused form on the same layer: three attention calls (B every
+    pair remapped, A local standard, C local remapped) plus the LogSumExp merge,
+    timed once warm.  Context for the pages' fused-versus-unfused comparison."""
+    p = case.params
+    T, Hq, d = case.q.shape
+    Hkv = case.k.shape[1]
+    q, k, v = case.q.cuda(), case.k.cuda(), case.v.cuda()
+    ws = torch.empty(jl.prefill_three_call_workspace_bytes(T, 1, Hq, Hkv, d), dtype=torch.uint8,
+                     device="cuda")
+    kw = dict(w_pretrained=p.w_pretrained, w_local=p.w_local, rope_base=p.rope_base,
+              softmax_scale=p.softmax_scale, workspace=ws)
+    jl.bifocal_prefill_three_call(q, k, v, **kw)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    jl.bifocal_prefill_three_call(q, k, v, **kw)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3
+    return {"ms_per_step": round(ms, 3), "tokens_per_s": round(T / (ms / 1e3), 1),
+            "fused_speedup": round(ms / fused_ms, 3)}
 
 
 def bench_decode(jl, inputs, torch, iters):

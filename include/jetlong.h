@@ -133,6 +133,31 @@ jl_status jl_bifocal_prefill(void* o, float* lse, const void* q, const void* k, 
                              const jl_params* params, jl_dtype dtype, void* k_rot_out,
                              void* workspace, size_t workspace_bytes, void* stream);
 
+/* Bytes of device workspace jl_bifocal_prefill_three_call needs (bf16 only). */
+jl_status jl_bifocal_prefill_three_call_workspace(int64_t T, int32_t n_seqs, int32_t Hq,
+                                                  int32_t Hkv, int32_t d, jl_dtype dtype,
+                                                  size_t* bytes);
+
+/*
+ * The pages' unfused form of the same prefill ([TW] §四, [BT] §3.2): three
+ * separate attention calls,
+ *     B: every causal pair under remapped RoPE,
+ *     A: the local pairs (i - j < w_local) under standard RoPE,
+ *     C: the local pairs under remapped RoPE,
+ * combined as Z = e^lse_B - e^lse_C + e^lse_A and
+ * o = (e^lse_B o_B - e^lse_C o_C + e^lse_A o_A) / Z (the remote mass
+ * e^lse_B - e^lse_C clamped at 0).  Up to rounding this equals
+ * jl_bifocal_prefill; it exists to compare the two forms on the device.
+ * Arguments as for jl_bifocal_prefill (no k_rot_out); params->bifocal must
+ * be 1; dtype must be JL_DTYPE_BF16 (else JL_ERR_UNSUPPORTED).  The three
+ * calls' outputs live in the workspace.
+ */
+jl_status jl_bifocal_prefill_three_call(void* o, float* lse, const void* q, const void* k,
+                                        const void* v, const int32_t* cu_seqlens, int32_t n_seqs,
+                                        int64_t T, int32_t max_seqlen, int32_t Hq, int32_t Hkv,
+                                        int32_t d, const jl_params* params, jl_dtype dtype,
+                                        void* workspace, size_t workspace_bytes, void* stream);
+
 /* Bytes of device workspace jl_bifocal_decode needs for these sizes. */
 jl_status jl_bifocal_decode_workspace(int32_t batch, int32_t max_seqlen_k, int32_t Hq,
                                       int32_t Hkv, int32_t d, jl_dtype dtype, size_t* bytes);

@@ -313,6 +313,106 @@ jl_status jl_bifocal_prefill(void* o, float* lse, const void* q, const void* k, 
     return finish(s, "jl_bifocal_prefill");
 }
 
+// Unfused form: scratch for the three calls' outputs after the prefill workspace.
+struct ThreeCallLayout {
+    size_t oA, oB, oC, lA, lB, lC, total;
+};
+static ThreeCallLayout three_call_layout(const PrefillLayout& pl, int64_t T, int32_t Hq, int32_t d) {
+    ThreeCallLayout L{};
+    const size_t ob = align256((size_t)T * Hq * d * 2), lb = align256((size_t)Hq * T * 4);
+    size_t off = align256(pl.total);
+    L.oA = off; off += ob;
+    L.oB = off; off += ob;
+    L.oC = off; off += ob;
+    L.lA = off; off += lb;
+    L.lB = off; off += lb;
+    L.lC = off; off += lb;
+    L.total = off;
+    return L;
+}
+
+jl_status jl_bifocal_prefill_three_call_workspace(int64_t T, int32_t n_seqs, int32_t Hq, int32_t Hkv,
+                                                  int32_t d, jl_dtype dtype, size_t* bytes) {
+    if (!bytes) return fail(JL_ERR_INVALID_ARGUMENT, "bytes is NULL");
+    if (T < 1 || n_seqs < 1) return fail(JL_ERR_INVALID_ARGUMENT, "T and n_seqs must be >= 1");
+    jl_status st = check_heads(Hq, Hkv);
+    if (st != JL_OK) return st;
+    st = check_dtype_d(dtype, d);
+    if (st != JL_OK) return st;
+    if (dtype != JL_DTYPE_BF16) return fail(JL_ERR_UNSUPPORTED, "the unfused form is bf16 only");
+    *bytes = three_call_layout(prefill_layout(T, n_seqs, Hkv, d, dtype), T, Hq, d).total;
+    g_err.clear();
+    return JL_OK;
+}
+
+jl_status jl_bifocal_prefill_three_call(void* o, float* lse, const void* q, const void* k,
+                                        const void* v, const int32_t* cu_seqlens, int32_t n_seqs,
+                                        int64_t T, int32_t max_seqlen, int32_t Hq, int32_t Hkv,
+                                        int32_t d, const jl_params* params, jl_dtype dtype,
+                                        void* workspace, size_t workspace_bytes, void* stream) {
+    if (!o || !lse || !q || !k || !v || !workspace)
+        return fail(JL_ERR_INVALID_ARGUMENT, "null pointer argument");
+    jl_status st = check_params(params);
+    if (st != JL_OK) return st;
+    if (!params->bifocal) return fail(JL_ERR_INVALID_ARGUMENT, "the unfused form needs bifocal = 1");
+    if (T < 1) return fail(JL_ERR_INVALID_ARGUMENT, "T must be >= 1");
+    if (n_seqs < 1) return fail(JL_ERR_INVALID_ARGUMENT, "n_seqs must be >= 1");
+    if (!cu_seqlens && n_seqs != 1)
+        return fail(JL_ERR_INVALID_ARGUMENT, "cu_seqlens == NULL requires n_seqs == 1");
+    if (max_seqlen < 1 || max_seqlen > T)
+        return fail(JL_ERR_INVALID_ARGUMENT, "max_seqlen must be in [1, T]");
+    if (!cu_seqlens && max_seqlen != T)
+        return fail(JL_ERR_INVALID_ARGUMENT, "a single sequence needs max_seqlen == T");
+    if ((int64_t)n_seqs > T) return fail(JL_ERR_INVALID_ARGUMENT, "n_seqs > T");
+    if (n_seqs > 65535) return fail(JL_ERR_UNSUPPORTED, "n_seqs above 65535");
+    if ((int64_t)max_seqlen > 65535LL * kBM)
+        return fail(JL_ERR_UNSUPPORTED, "max_seqlen above 65535 * 256");
+    st = check_heads(Hq, Hkv);
+    if (st != JL_OK) return st;
+    st = check_dtype_d(dtype, d);
+    if (st != JL_OK) return st;
+    if (dtype != JL_DTYPE_BF16) return fail(JL_ERR_UNSUPPORTED, "the unfused form is bf16 only");
+    if (T + (int64_t)n_seqs * kBN >= 2147483647LL)
+        return fail(JL_ERR_UNSUPPORTED, "T + 64 * n_seqs must stay below 2^31");
+    if ((unsigned long long)T > 2147483647ULL) return fail(JL_ERR_UNSUPPORTED, "T above 2^31 - 1");
+    if (o == q || o == k || o == v || (void*)lse == q)
+        return fail(JL_ERR_INVALID_ARGUMENT, "outputs must not alias inputs");
+    if ((uintptr_t)workspace & 255) return fail(JL_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
+    const PrefillLayout lay = prefill_layout(T, n_seqs, Hkv, d, dtype);
+    const ThreeCallLayout tl = three_call_layout(lay, T, Hq, d);
+    if (workspace_bytes < tl.total)
+        return fail(JL_ERR_WORKSPACE_TOO_SMALL,
+                    "workspace needs " + std::to_string(tl.total) + " bytes");
+
+    char* ws = (char*)workspace;
+    PrefillArgs a{};
+    a.q = q; a.k = k; a.v = v; a.k_rot_out = nullptr; a.ws = workspace; a.lay = lay;
+    a.n_seqs = n_seqs; a.Hq = Hq; a.Hkv = Hkv; a.d = d; a.max_seqlen = max_seqlen; a.T = T;
+    a.w_local = params->w_local; a.bifocal = 1;
+    a.softmax_scale = params->softmax_scale;
+    a.tab = make_rope_freq(params->rope_base, d);
+
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e = launch_plan((int32_t*)(ws + lay.plan), cu_seqlens, n_seqs, T, max_seqlen,
+                               params->w_pretrained, s);
+    if (e != hipSuccess) return hip_fail(e, "plan launch");
+    e = launch_kv_prepass(a, dtype, s);
+    if (e != hipSuccess) return hip_fail(e, "key/value pre-pass launch");
+    const size_t oofs[3] = {tl.oB, tl.oA, tl.oC}, lofs[3] = {tl.lB, tl.lA, tl.lC};
+    for (int c = 0; c < 3; ++c) {  // modes 1 (B), 2 (A), 3 (C)
+        a.mode = c + 1;
+        a.o = ws + oofs[c];
+        a.lse = (float*)(ws + lofs[c]);
+        e = launch_prefill_bf16(a, s);
+        if (e != hipSuccess) return hip_fail(e, "prefill launch");
+    }
+    e = launch_three_call_merge(ws + tl.oA, ws + tl.oB, ws + tl.oC, (const float*)(ws + tl.lA),
+                                (const float*)(ws + tl.lB), (const float*)(ws + tl.lC), o, lse, T,
+                                Hq, d, s);
+    if (e != hipSuccess) return hip_fail(e, "merge launch");
+    return finish(s, "jl_bifocal_prefill_three_call");
+}
+
 jl_status jl_bifocal_decode_workspace(int32_t batch, int32_t max_seqlen_k, int32_t Hq,
                                       int32_t Hkv, int32_t d, jl_dtype dtype, size_t* bytes) {
     if (!bytes) return fail(JL_ERR_INVALID_ARGUMENT, "bytes is NULL");

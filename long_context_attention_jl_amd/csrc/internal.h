@@ -64,9 +64,14 @@ struct PrefillArgs {
     int32_t w_local, bifocal;
     float softmax_scale;
     RopeFreq tab;
+    int32_t mode;  // 0 bifocal; unfused calls: 1 all pairs remapped, 2 local standard, 3 local remapped
 };
 
 hipError_t launch_kv_prepass(const PrefillArgs& a, int dtype, hipStream_t s);
+// O = the LogSumExp combination of the three unfused calls B + A - C
+hipError_t launch_three_call_merge(const void* oA, const void* oB, const void* oC, const float* lA,
+                                   const float* lB, const float* lC, void* o, float* lse,
+                                   int64_t T, int32_t Hq, int32_t d, hipStream_t s);
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t s);
 hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t s);
 

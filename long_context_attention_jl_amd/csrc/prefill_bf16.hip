@@ -108,7 +108,18 @@ void prefill_bf16_kernel(PrefillArgs a, int rb_first, int n_rb) {
     if (row0 >= len) return;
     if (!PRECISE && row0 < kPreciseRows) return;
     const int32_t row_end = min(row0 + kBM, len);
-    const bool bif = a.bifocal && G > 1;
+    // Which pairs and which RoPE.  Mode 0 is the bifocal softmax (remote
+    // pairs remapped, local pairs standard).  Modes 1-3 are the three
+    // separate attention calls of the pages' unfused form ([TW] §四): 1 every
+    // causal pair under remapped RoPE (B), 2 the local pairs under standard
+    // RoPE (A), 3 the local pairs under remapped RoPE (C).
+    const bool have_kr = a.bifocal && G > 1;  // the pre-pass wrote remapped key tiles
+    const int mode = a.mode;
+    const bool bif = mode == 0 ? have_kr : true;  // the remote/local band split is on
+    const int32_t wl = mode == 1 ? 0 : a.w_local;
+    const bool do_remote = mode == 0 ? bif : mode == 1;
+    const bool do_local = mode != 1;
+    const bool local_remapped = mode == 3;
     const int g = head / (a.Hq / a.Hkv);
     const int32_t wr0 = row0 + wave * kWaveRows;
     const int32_t wr_end = min(wr0 + kWaveRows, len);
@@ -121,9 +132,9 @@ void prefill_bf16_kernel(PrefillArgs a, int rb_first, int n_rb) {
     const int ntiles = (row_end + kBN - 1) / kBN;
     int r_end = 0, s_begin = 0;
     if (bif) {
-        const int32_t jr = row_end - 1 - a.w_local;
+        const int32_t jr = row_end - 1 - wl;
         r_end = jr >= 0 ? jr / kBN + 1 : 0;
-        s_begin = a.w_local == 0 ? ntiles : max(0, row0 - a.w_local + 1) / kBN;
+        s_begin = wl == 0 ? ntiles : max(0, row0 - wl + 1) / kBN;
     }
 
     // ---- rotated, scaled queries as MFMA B operands ----
@@ -189,10 +200,13 @@ void prefill_bf16_kernel(PrefillArgs a, int rb_first, int n_rb) {
             __builtin_amdgcn_global_load_lds((const void*)(src + (int64_t)(c0 + lane) * 8),
                                              (void*)(dst + c0 * 8), 16, 0, 0);
     };
-    auto load_tile = [&](int tau, bool remote_phase, bf16* base)  __attribute__((always_inline)) {
-        dma((remote_phase ? KRg : KSg) + (int64_t)tau * C::KSLOT, base, C::KSLOT);
+    // key tiles of the phase's RoPE (remapped tiles equal the standard ones
+    // when G = 1, and the pre-pass then writes only those)
+    auto load_tile = [&](int tau, bool remapped, bf16* base)  __attribute__((always_inline)) {
+        const bool kr = remapped && have_kr;
+        dma((kr ? KRg : KSg) + (int64_t)tau * C::KSLOT, base, C::KSLOT);
         if constexpr (PRECISE)
-            dma((remote_phase ? KRlg : KSlg) + (int64_t)tau * C::KSLOT, base + C::KSLOT, C::KSLOT);
+            dma((kr ? KRlg : KSlg) + (int64_t)tau * C::KSLOT, base + C::KSLOT, C::KSLOT);
         dma(VTg + (int64_t)tau * C::VSLOT, base + C::NK * C::KSLOT, C::VSLOT);
     };
 
@@ -240,7 +254,7 @@ void prefill_bf16_kernel(PrefillArgs a, int rb_first, int n_rb) {
             for (int i = 0; i < 16; ++i) {
                 const int32_t key = jb + (i >> 2) * 8 + 4 * hh + (i & 3);
                 const int32_t dist = myrow - key;
-                const bool keep = dist >= 0 && (!bif || ((dist >= a.w_local) == remote_phase));
+                const bool keep = dist >= 0 && (!bif || ((dist >= wl) == remote_phase));
                 if (!keep) Sb[i] = -INFINITY;
             }
         }
@@ -288,48 +302,52 @@ void prefill_bf16_kernel(PrefillArgs a, int rb_first, int n_rb) {
 #pragma unroll
         for (int b = 0; b < 2; ++b) {
             const int32_t jb = tau * kBN + 32 * b;
-            const uint32_t cls = tile_class32(wr0, wr_end, jb, jb + 32, a.w_local, bif);
+            const uint32_t cls = tile_class32(wr0, wr_end, jb, jb + 32, wl, bif);
             if (cls & want) do_block(base, b, cls != want, remote_phase, jb);
         }
     };
 
     // ---- one phase: tiles [t0, t1), unrolled by two so each step names its
     // LDS buffers statically ----
-    auto step = [&](int tau, int t1, bool remote_phase, const bf16* cur, bf16* nxt)
+    auto step = [&](int tau, int t1, bool remote_phase, bool remapped, const bf16* cur, bf16* nxt)
         __attribute__((always_inline)) {
         const bool more = tau + 1 < t1;
         // the other buffer was last read in the previous step, which every
         // wave finished before the barrier that ended it
-        if (more) load_tile(tau + 1, remote_phase, nxt);
+        if (more) load_tile(tau + 1, remapped, nxt);
         if (wave_active) compute(tau, cur, remote_phase);
         if (more) {
             __builtin_amdgcn_s_waitcnt(0);  // this wave's DMA writes have landed
             __syncthreads();
         }
     };
-    auto run_phase = [&](int t0, int t1, bool remote_phase) __attribute__((always_inline)) {
-        load_tile(t0, remote_phase, lds0);
+    // remote_phase selects the band (pairs with i - j >= wl, or < wl);
+    // remapped selects the RoPE of the key tiles
+    auto run_phase = [&](int t0, int t1, bool remote_phase, bool remapped) __attribute__((always_inline)) {
+        load_tile(t0, remapped, lds0);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         for (int tau = t0; tau < t1; tau += 2) {
-            step(tau, t1, remote_phase, lds0, lds1);
-            if (tau + 1 < t1) step(tau + 1, t1, remote_phase, lds1, lds0);
+            step(tau, t1, remote_phase, remapped, lds0, lds1);
+            if (tau + 1 < t1) step(tau + 1, t1, remote_phase, remapped, lds1, lds0);
         }
     };
 
-    if (r_end > 0) {
+    if (do_remote && r_end > 0) {
         stage_q(true);
-        run_phase(0, r_end, true);
+        run_phase(0, r_end, true, true);
     }
-    if (s_begin < ntiles) {
-        stage_q(false);  // begins with a barrier: no wave still reads a buffer
-        run_phase(s_begin, ntiles, false);
+    if (do_local && s_begin < ntiles) {
+        stage_q(local_remapped);  // begins with a barrier: no wave still reads a buffer
+        run_phase(s_begin, ntiles, false, local_remapped);
     }
 
     // ---- epilogue: O = O^T / l, LSE = ln(sum exp(score)) ----
     if (!wave_active || !row_valid) return;
     l_run += __shfl_xor(l_run, 32);
-    const float inv = 1.0f / l_run;
+    // a row with no key of the call (the local calls with w_local = 0): o = 0, lse = -inf
+    const bool none = !(l_run > 0.0f);
+    const float inv = none ? 0.0f : 1.0f / l_run;
     bf16* op = (bf16*)a.o + ((int64_t)(start + myrow) * a.Hq + head) * D;
 #pragma unroll
     for (int db = 0; db < C::ND; ++db)
@@ -340,7 +358,7 @@ void prefill_bf16_kernel(PrefillArgs a, int rb_first, int n_rb) {
             for (int r = 0; r < 4; ++r) w[r] = (bf16)(O[db][4 * g4 + r] * inv);
             *reinterpret_cast<bf16x4*>(op + 32 * db + 8 * g4 + 4 * hh) = w;
         }
-    if (hh == 0) a.lse[(int64_t)head * a.T + start + myrow] = (m_run + log2f(l_run)) * kLn2;
+    if (hh == 0) a.lse[(int64_t)head * a.T + start + myrow] = none ? -INFINITY : (m_run + log2f(l_run)) * kLn2;
 }
 
 template <int D, bool PRECISE>
@@ -366,6 +384,47 @@ hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t s) {
     err = launch_one<64, true>(a, 0, n_prec, s, "prefill_bf16_precise");
     if (err != hipSuccess) return err;
     return launch_one<64, false>(a, precise_rb, total_rb - precise_rb, s, "prefill_bf16");
+}
+
+// LogSumExp combination of the pages' three unfused calls ([TW] §四, [BT]
+// §3.2): with B every causal pair under remapped RoPE, A the local pairs under
+// standard RoPE and C the local pairs under remapped RoPE,
+//   Z = e^lse_B - e^lse_C + e^lse_A,  o = (e^lse_B o_B - e^lse_C o_C + e^lse_A o_A) / Z.
+// B and C hold the same local pairs, so the remote mass e^lse_B - e^lse_C is
+// computed relative to e^lse_B and clamped at 0 (rows with no remote key give
+// 0 up to rounding); a clamped remote part contributes nothing.  One wave per
+// (token, head); lse is the natural log, lse_B is finite for every row (its
+// own key is always in B).
+__global__ __launch_bounds__(256) void three_call_merge_kernel(
+    const bf16* __restrict__ oA, const bf16* __restrict__ oB, const bf16* __restrict__ oC,
+    const float* __restrict__ lA, const float* __restrict__ lB, const float* __restrict__ lC,
+    bf16* __restrict__ o, float* __restrict__ lse, int64_t T, int Hq, int d) {
+    const int64_t tok = blockIdx.x;
+    const int head = blockIdx.y * 4 + (int)(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (head >= Hq) return;
+    const int64_t li = (int64_t)head * T + tok;
+    const float la = lA[li], lb = lB[li], lc = lC[li];
+    const float rem = fmaxf(0.0f, 1.0f - expf(lc - lb));  // remote mass / e^lse_B
+    const float loc = expf(la - lb);                      // local mass / e^lse_B
+    const float z = rem + loc;
+    const float wB = rem > 0.0f ? 1.0f / z : 0.0f;
+    const float wC = rem > 0.0f ? expf(lc - lb) / z : 0.0f;
+    const float wA = loc / z;
+    const int64_t base = (tok * Hq + head) * d;
+    for (int x = lane; x < d; x += 64)
+        o[base + x] = (bf16)(wB * (float)oB[base + x] - wC * (float)oC[base + x] + wA * (float)oA[base + x]);
+    if (lane == 0) lse[li] = lb + logf(z);
+}
+
+hipError_t launch_three_call_merge(const void* oA, const void* oB, const void* oC, const float* lA,
+                                   const float* lB, const float* lC, void* o, float* lse,
+                                   int64_t T, int32_t Hq, int32_t d, hipStream_t s) {
+    LaunchScope scope("three_call_merge", s);
+    hipLaunchKernelGGL(three_call_merge_kernel, dim3((unsigned)T, (unsigned)((Hq + 3) / 4)), dim3(256), 0, s,
+                       (const bf16*)oA, (const bf16*)oB, (const bf16*)oC, lA, lB, lC, (bf16*)o, lse,
+                       T, (int)Hq, (int)d);
+    return hipGetLastError();
 }
 
 }  // namespace jl

@@ -74,6 +74,14 @@ def lib() -> ctypes.CDLL:
         L.jl_bifocal_prefill.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i64, _i32, _i32, _i32,
                                          _i32, ctypes.POINTER(jl_params), ctypes.c_int, _vp, _vp,
                                          ctypes.c_size_t, _vp]
+        L.jl_bifocal_prefill_three_call_workspace.restype = ctypes.c_int
+        L.jl_bifocal_prefill_three_call_workspace.argtypes = [_i64, _i32, _i32, _i32, _i32,
+                                                              ctypes.c_int,
+                                                              ctypes.POINTER(ctypes.c_size_t)]
+        L.jl_bifocal_prefill_three_call.restype = ctypes.c_int
+        L.jl_bifocal_prefill_three_call.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i64, _i32,
+                                                    _i32, _i32, _i32, ctypes.POINTER(jl_params),
+                                                    ctypes.c_int, _vp, ctypes.c_size_t, _vp]
         L.jl_bifocal_decode_workspace.restype = ctypes.c_int
         L.jl_bifocal_decode_workspace.argtypes = [_i32, _i32, _i32, _i32, _i32, ctypes.c_int,
                                                   ctypes.POINTER(ctypes.c_size_t)]
@@ -161,6 +169,57 @@ def _workspace(nbytes: int, device, ws: Optional[torch.Tensor]) -> torch.Tensor:
     return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
 
 
+def _varlen(cu_seqlens, max_seqlen, T: int, dev):
+    """(cu_seqlens device tensor or None, n_seqs, max_seqlen)."""
+    if cu_seqlens is None:
+        return None, 1, (T if max_seqlen is None else max_seqlen)
+    if isinstance(cu_seqlens, torch.Tensor):
+        cu_t = cu_seqlens.to(device=dev, dtype=torch.int32).contiguous()
+        if max_seqlen is None:
+            max_seqlen = int((cu_t[1:] - cu_t[:-1]).max().item())
+    else:
+        cu_list = [int(x) for x in cu_seqlens]
+        cu_t = torch.tensor(cu_list, dtype=torch.int32, device=dev)
+        if max_seqlen is None:
+            max_seqlen = max(b - a for a, b in zip(cu_list[:-1], cu_list[1:]))
+    return cu_t, cu_t.numel() - 1, max_seqlen
+
+
+def prefill_three_call_workspace_bytes(T: int, n_seqs: int, Hq: int, Hkv: int, d: int) -> int:
+    n = ctypes.c_size_t()
+    _check(lib().jl_bifocal_prefill_three_call_workspace(T, n_seqs, Hq, Hkv, d, JL_DTYPE_BF16,
+                                                         ctypes.byref(n)),
+           "jl_bifocal_prefill_three_call_workspace")
+    return n.value
+
+
+def bifocal_prefill_three_call(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *,
+                               w_pretrained: int, w_local: int, rope_base: float,
+                               softmax_scale: float,
+                               cu_seqlens: Union[None, Sequence[int], torch.Tensor] = None,
+                               max_seqlen: Optional[int] = None,
+                               workspace: Optional[torch.Tensor] = None,
+                               out: Optional[torch.Tensor] = None,
+                               lse_out: Optional[torch.Tensor] = None
+                               ) -> Tuple[torch.Tensor, torch.Tensor]:
+    """The pages' unfused form ([TW] §四): three attention calls B, A, C merged in
+    LogSumExp space.  bf16 only.  Returns (o [T, Hq, d], lse [Hq, T] float32)."""
+    T, Hq, d = q.shape
+    Hkv = k.shape[1]
+    dev = q.device
+    cu_t, n_seqs, max_seqlen = _varlen(cu_seqlens, max_seqlen, T, dev)
+    o = out if out is not None else torch.empty_like(q)
+    lse = lse_out if lse_out is not None else torch.empty((Hq, T), dtype=torch.float32, device=dev)
+    ws = _workspace(prefill_three_call_workspace_bytes(T, n_seqs, Hq, Hkv, d), dev, workspace)
+    p = _params(w_pretrained, w_local, rope_base, softmax_scale, True)
+    _check(lib().jl_bifocal_prefill_three_call(
+        _dev(o, "o"), _dev(lse, "lse"), _dev(q, "q"), _dev(k, "k"), _dev(v, "v"),
+        None if cu_t is None else _dev(cu_t, "cu_seqlens"), n_seqs, T, int(max_seqlen), Hq, Hkv,
+        d, ctypes.byref(p), _dtype(q), _dev(ws, "workspace"), ws.numel() * ws.element_size(),
+        _stream()), "jl_bifocal_prefill_three_call")
+    return o, lse
+
+
 def bifocal_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, w_pretrained: int,
                     w_local: int, rope_base: float, softmax_scale: float, bifocal: bool = True,
                     cu_seqlens: Union[None, Sequence[int], torch.Tensor] = None,
@@ -172,21 +231,7 @@ def bifocal_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, w_pret
     T, Hq, d = q.shape
     Hkv = k.shape[1]
     dev = q.device
-    if cu_seqlens is None:
-        cu_t, n_seqs = None, 1
-        if max_seqlen is None:
-            max_seqlen = T
-    else:
-        if isinstance(cu_seqlens, torch.Tensor):
-            cu_t = cu_seqlens.to(device=dev, dtype=torch.int32).contiguous()
-            if max_seqlen is None:
-                max_seqlen = int((cu_t[1:] - cu_t[:-1]).max().item())
-        else:
-            cu_list = [int(x) for x in cu_seqlens]
-            cu_t = torch.tensor(cu_list, dtype=torch.int32, device=dev)
-            if max_seqlen is None:
-                max_seqlen = max(b - a for a, b in zip(cu_list[:-1], cu_list[1:]))
-        n_seqs = cu_t.numel() - 1
+    cu_t, n_seqs, max_seqlen = _varlen(cu_seqlens, max_seqlen, T, dev)
     o = out if out is not None else torch.empty_like(q)
     lse = lse_out if lse_out is not None else torch.empty((Hq, T), dtype=torch.float32, device=dev)
     nbytes = prefill_workspace_bytes(T, n_seqs, Hq, Hkv, d, q.dtype)

@@ -91,6 +91,40 @@ def test_prefill_validation(kw, status):
     assert jlb.lib().jl_last_error()
 
 
+def _three_call(**kw):
+    a = dict(o=FAKE, lse=FAKE * 2, q=FAKE * 3, k=FAKE * 4, v=FAKE * 5, cu=None, n_seqs=1, T=1024,
+             max_seqlen=1024, Hq=32, Hkv=8, d=128, params=_params(), dtype=1,
+             ws=FAKE * 8, ws_bytes=1 << 40, stream=None)
+    a.update(kw)
+    p = a["params"]
+    return jlb.lib().jl_bifocal_prefill_three_call(
+        a["o"], a["lse"], a["q"], a["k"], a["v"], a["cu"], a["n_seqs"], a["T"], a["max_seqlen"],
+        a["Hq"], a["Hkv"], a["d"], None if p is None else ctypes.byref(p), a["dtype"],
+        a["ws"], a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(o=None), 1), (dict(ws=None), 1), (dict(params=None), 1), (dict(T=0), 1),
+    (dict(n_seqs=2), 1), (dict(max_seqlen=2000), 1), (dict(Hq=30), 1), (dict(d=96), 2),
+    (dict(dtype=0), 2), (dict(params=_params(bifocal=0)), 1), (dict(ws_bytes=1000), 3),
+    (dict(ws=FAKE * 8 + 4), 1), (dict(o=FAKE * 3), 1),
+])
+def test_three_call_validation(kw, status):
+    assert _three_call(**kw) == status
+    assert jlb.lib().jl_last_error()
+
+
+def test_three_call_workspace_query():
+    n = ctypes.c_size_t()
+    m = ctypes.c_size_t()
+    L = jlb.lib()
+    assert L.jl_bifocal_prefill_three_call_workspace(4096, 1, 32, 8, 128, 1, ctypes.byref(n)) == 0
+    assert L.jl_bifocal_prefill_workspace(4096, 1, 32, 8, 128, 1, ctypes.byref(m)) == 0
+    # the three calls' bf16 outputs and fp32 LSEs come on top of the prefill workspace
+    assert n.value >= m.value + 3 * (4096 * 32 * 128 * 2 + 32 * 4096 * 4)
+    assert L.jl_bifocal_prefill_three_call_workspace(4096, 1, 32, 8, 128, 0, ctypes.byref(n)) == 2
+
+
 def test_prefill_workspace_query():
     n = ctypes.c_size_t()
     L = jlb.lib()

@@ -1,0 +1,90 @@
+"""GPU parity of the pages' unfused form (jl_bifocal_prefill_three_call):
+three attention calls B (every pair, remapped RoPE), A (local pairs, standard)
+and C (local pairs, remapped) merged in LogSumExp space must equal the direct
+bifocal definition computed by the fp64 oracle, within the bf16 bars, and
+match the fused kernel."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from long_context_attention_jl_amd import inputs
+from long_context_attention_jl_amd import jetlong as jl
+from long_context_attention_jl_amd.inputs import Params
+
+from _parity import check_prefill, oracle_prefill_rows, sample_rows, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _three(q, k, v, params, cu=None):
+    return jl.bifocal_prefill_three_call(q.cuda(), k.cuda(), v.cuda(),
+                                         w_pretrained=params.w_pretrained, w_local=params.w_local,
+                                         rope_base=params.rope_base,
+                                         softmax_scale=params.softmax_scale, cu_seqlens=cu)
+
+
+@pytest.mark.parametrize("T,Hq,Hkv,d,w_pre,w_local", [
+    (700, 4, 2, 128, 200, 64),      # G = 4, several tiles, ragged tail
+    (3000, 4, 4, 64, 1000, 500),    # G = 3, d = 64
+    (2600, 8, 2, 128, 600, 2048),   # G = 5, rows below and above w_local
+])
+def test_three_call_small_full(T, Hq, Hkv, d, w_pre, w_local):
+    p = Params(w_pre, w_local, 1e4, 1.0 / math.sqrt(d))
+    q, k, v = inputs.prefill_inputs(T, Hq, Hkv, d, seed=T + d)
+    say("three-call T=%d Hq=%d Hkv=%d d=%d w_pre=%d w_local=%d" % (T, Hq, Hkv, d, w_pre, w_local))
+    o, lse = _three(q, k, v, p)
+    torch.cuda.synchronize()
+    rows = list(range(T))
+    o_ref, lse_ref = oracle_prefill_rows(q, k, v, p, rows)
+    check_prefill(o, lse, o_ref, lse_ref, rows, torch.bfloat16, "three-call T=%d" % T)
+    # the fused kernel and the unfused form agree with each other as closely
+    o_f, lse_f = jl.bifocal_prefill(q.cuda(), k.cuda(), v.cuda(), w_pretrained=w_pre,
+                                    w_local=w_local, rope_base=1e4, softmax_scale=p.softmax_scale)
+    torch.cuda.synchronize()
+    dO = (o_f.float() - o.float()).abs().max().item()
+    dL = (lse_f - lse).abs().max().item()
+    say("fused vs three-call: max|dO|=%.3g max|dLSE|=%.3g" % (dO, dL))
+    assert dO <= 2e-2 and dL <= 1e-3
+
+
+@pytest.mark.parametrize("label,params", [
+    ("w_local0", Params(300, 0, 1e4, 0.125)),        # A and C empty: B alone
+    ("w_local_all", Params(300, 5000, 1e4, 0.125)),  # B == C: A alone (plain RoPE)
+    ("G1", Params(5000, 100, 1e4, 0.125)),           # L <= w_pretrained: all standard
+])
+def test_three_call_degenerate(label, params):
+    T, Hq, Hkv, d = 1300, 4, 2, 64
+    q, k, v = inputs.prefill_inputs(T, Hq, Hkv, d, seed=11)
+    say("three-call degenerate", label)
+    o, lse = _three(q, k, v, params)
+    torch.cuda.synchronize()
+    rows = list(range(T))
+    o_ref, lse_ref = oracle_prefill_rows(q, k, v, params, rows)
+    check_prefill(o, lse, o_ref, lse_ref, rows, torch.bfloat16, "three-call " + label)
+
+
+def test_three_call_varlen_small():
+    cu = [0, 300, 301, 1500, 2200]
+    p = Params(400, 128, 1e4, 1.0 / math.sqrt(128))
+    q, k, v = inputs.prefill_inputs(cu[-1], 4, 2, 128, seed=21)
+    say("three-call varlen", cu)
+    o, lse = _three(q, k, v, p, cu=cu)
+    torch.cuda.synchronize()
+    rows = list(range(cu[-1]))
+    o_ref, lse_ref = oracle_prefill_rows(q, k, v, p, rows, cu=cu)
+    check_prefill(o, lse, o_ref, lse_ref, rows, torch.bfloat16, "three-call varlen")
+
+
+def test_three_call_qwen3_8b_131072_sampled():
+    """The 128K layer (G = 4) in the benchmark's shape: sampled rows against the
+    oracle."""
+    c = inputs.qwen3_8b_128k()
+    p = c.params
+    say("three-call", c.name)
+    o, lse = _three(c.q, c.k, c.v, p)
+    torch.cuda.synchronize()
+    rows = sample_rows(c.T, p.w_local, 4, n_strided=24)
+    o_ref, lse_ref = oracle_prefill_rows(c.q, c.k, c.v, p, rows)
+    check_prefill(o, lse, o_ref, lse_ref, rows, torch.bfloat16, "three-call " + c.name)
