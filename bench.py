@@ -234,12 +234,41 @@ def bench_decode(jl, inputs, torch, iters):
         torch.cuda.synchronize()
         return ev0.elapsed_time(ev1) * 1e3 / n  # microseconds per token
 
+    # Paged form of the same caches: each copy viewed as a pool of pages,
+    # named by a shuffled block table (timing only; the rows' order is moot).
+    pools = {}
+    for page in (16, 64):
+        n_pages = S_max // page
+        bt = torch.randperm(n_pages, generator=torch.Generator().manual_seed(page))
+        pools[page] = (bt.to(torch.int32).view(1, n_pages).cuda(),
+                       [(kc.view(n_pages, page, Hkv, d), vc.view(n_pages, page, Hkv, d))
+                        for kc, vc in copies])
+
+    def run_paged(page, n):
+        bt, pool = pools[page]
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        ev0.record()
+        for i in range(n):
+            kp, vp = pool[i % 4]
+            jl.bifocal_decode_paged(q, kp, vp, bt, sl, max_seqlen_k=L,
+                                    w_pretrained=p.w_pretrained, w_local=p.w_local,
+                                    rope_base=p.rope_base, softmax_scale=p.softmax_scale,
+                                    workspace=ws, out=o, lse_out=lse)
+        ev1.record()
+        torch.cuda.synchronize()
+        return ev0.elapsed_time(ev1) * 1e3 / n
+
     run(True, 10)
     run(False, 10)
-    tb, tp = [], []
+    for page in pools:
+        run_paged(page, 10)
+    tb, tp, tpg = [], [], {page: [] for page in pools}
     for _ in range(4):
         tb.append(run(True, iters // 4))
         tp.append(run(False, iters // 4))
+        for page in pools:
+            tpg[page].append(run_paged(page, iters // 4))
     jl.profile_enable(True)
     run(True, 20)
     prof = jl.profile_read()
@@ -259,6 +288,7 @@ def bench_decode(jl, inputs, torch, iters):
         "split_kernel_us": round(split_us, 2),
         "split_kernel_GBps": round(nbytes / (split_us * 1e-6) / 1e9, 1),
         "split_kernel_traffic": _profiled_traffic("traffic_decode_split_L131072.md"),
+        "paged_us_per_token": {"page_%d" % page: round(min(t), 2) for page, t in tpg.items()},
         "kernels": {n: {"launches": c2, "avg_us": round(ms * 1e3 / max(c2, 1), 2)}
                     for n, (c2, ms) in sorted(prof.items())},
     }

@@ -187,6 +187,25 @@ jl_status jl_bifocal_decode(void* o, float* lse, const void* q, const void* k_ca
                             size_t workspace_bytes, void* stream);
 
 /*
+ * jl_bifocal_decode on a paged KV cache (the layout serving systems keep):
+ * k_pages, v_pages are pools of n_pages pages, each [page_size][Hkv][d] bf16
+ * holding standard-RoPE keys (values) at their original positions; key j of
+ * sequence b sits in page block_table[b * bt_stride + j / page_size], row
+ * j % page_size.  Same scores, outputs and workspace size
+ * (jl_bifocal_decode_workspace) as jl_bifocal_decode; the pool is read-only.
+ *   block_table  device int32 [batch][bt_stride]; bt_stride * page_size >= max_seqlen_k.
+ *   page_size    a power of two in [16, 65536].
+ * Page numbers outside [0, n_pages) are clamped into the pool (the result is
+ * then unspecified, but nothing is read outside it).  bf16 only.
+ */
+jl_status jl_bifocal_decode_paged(void* o, float* lse, const void* q, const void* k_pages,
+                                  const void* v_pages, const int32_t* block_table,
+                                  const int32_t* seqlens_k, int32_t batch, int32_t max_seqlen_k,
+                                  int32_t page_size, int64_t n_pages, int32_t bt_stride, int32_t Hq,
+                                  int32_t Hkv, int32_t d, const jl_params* params, jl_dtype dtype,
+                                  void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Test export: runs the kernels' own device index functions for a sequence of
  * length L (1 <= L) and writes
  *   G_out     device int32 [1]    G(L)

@@ -467,6 +467,56 @@ jl_status jl_bifocal_decode(void* o, float* lse, const void* q, const void* k_ca
     return finish(s, "jl_bifocal_decode");
 }
 
+jl_status jl_bifocal_decode_paged(void* o, float* lse, const void* q, const void* k_pages,
+                                  const void* v_pages, const int32_t* block_table,
+                                  const int32_t* seqlens_k, int32_t batch, int32_t max_seqlen_k,
+                                  int32_t page_size, int64_t n_pages, int32_t bt_stride, int32_t Hq,
+                                  int32_t Hkv, int32_t d, const jl_params* params, jl_dtype dtype,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
+    if (!o || !lse || !q || !k_pages || !v_pages || !block_table || !seqlens_k || !workspace)
+        return fail(JL_ERR_INVALID_ARGUMENT, "null pointer argument");
+    jl_status st = check_params(params);
+    if (st != JL_OK) return st;
+    if (batch < 1 || max_seqlen_k < 1)
+        return fail(JL_ERR_INVALID_ARGUMENT, "batch and max_seqlen_k must be >= 1");
+    if (batch > 65535) return fail(JL_ERR_UNSUPPORTED, "batch above 65535");
+    if (page_size < 16 || page_size > 65536 || (page_size & (page_size - 1)))
+        return fail(JL_ERR_INVALID_ARGUMENT, "page_size must be a power of two in [16, 65536]");
+    if (n_pages < 1) return fail(JL_ERR_INVALID_ARGUMENT, "n_pages must be >= 1");
+    if ((int64_t)bt_stride * page_size < max_seqlen_k)
+        return fail(JL_ERR_INVALID_ARGUMENT, "bt_stride * page_size < max_seqlen_k");
+    st = check_heads(Hq, Hkv);
+    if (st != JL_OK) return st;
+    if (Hq / Hkv > 16) return fail(JL_ERR_UNSUPPORTED, "decode supports Hq / Hkv <= 16");
+    st = check_dtype_d(dtype, d);
+    if (st != JL_OK) return st;
+    if (dtype != JL_DTYPE_BF16) return fail(JL_ERR_UNSUPPORTED, "paged decode is bf16 only");
+    if (n_pages > (1LL << 40) / ((int64_t)page_size * Hkv * d))
+        return fail(JL_ERR_INVALID_ARGUMENT, "page pool too large");
+    if (o == q || o == k_pages || o == v_pages)
+        return fail(JL_ERR_INVALID_ARGUMENT, "outputs must not alias inputs");
+    if ((uintptr_t)workspace & 255) return fail(JL_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
+    const DecodeLayout lay = decode_layout(batch, max_seqlen_k, Hq, Hkv, d, dtype);
+    if (workspace_bytes < lay.total)
+        return fail(JL_ERR_WORKSPACE_TOO_SMALL,
+                    "workspace needs " + std::to_string(lay.total) + " bytes");
+    DecodeArgs a{};
+    a.q = q; a.kc = k_pages; a.vc = v_pages; a.o = o; a.lse = lse; a.seqlens = seqlens_k;
+    a.ws = workspace; a.lay = lay;
+    a.B = batch; a.max_seqlen_k = max_seqlen_k; a.Hq = Hq; a.Hkv = Hkv; a.d = d; a.S_max = 0;
+    a.w_pretrained = params->w_pretrained; a.w_local = params->w_local;
+    a.bifocal = params->bifocal; a.softmax_scale = params->softmax_scale;
+    a.tab = make_rope_freq(params->rope_base, d);
+    a.block_table = block_table;
+    int shift = 0;
+    while ((1 << shift) < page_size) ++shift;
+    a.page_shift = shift; a.bt_stride = bt_stride; a.n_pages = n_pages;
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e = launch_decode(a, dtype, s);
+    if (e != hipSuccess) return hip_fail(e, "decode launch");
+    return finish(s, "jl_bifocal_decode_paged");
+}
+
 jl_status jl_debug_index_math(int64_t L, int32_t w_pretrained, int32_t w_local, int32_t bifocal,
                               int32_t bm, int32_t bn, int32_t* G_out, int32_t* f_out,
                               uint8_t* band_out, uint8_t* tile_out, void* stream) {

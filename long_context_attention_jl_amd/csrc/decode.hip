@@ -457,7 +457,10 @@ void decode_split_kernel(DecodeArgs a) {
 // rounded values.  K and V tiles stay two ahead in registers.  All loads are
 // unconditional (indices clamped to valid rows), so the memory stream has no
 // branches and the compiler's waits stay exact.
-template <int D, bool BIF, int GQ>
+// PAGED: the cache is a pool of pages of 2^page_shift rows addressed through
+// a per-sequence block table (each workgroup copies its chunk's page numbers
+// to LDS, clamped to the pool, so a bad table entry cannot read outside it).
+template <int D, bool BIF, int GQ, bool PAGED>
 __global__ __launch_bounds__(512) void decode_split_bf16_kernel(DecodeArgs a) {
     constexpr int HALF = D / 2;
     constexpr int NST = D / 32;          // k-steps of the QK^T product
@@ -476,6 +479,7 @@ __global__ __launch_bounds__(512) void decode_split_bf16_kernel(DecodeArgs a) {
     // stage st of this chunk (remote stages), the last row R(p)
     __shared__ float2 qtab[(kDecodeMaxStagesB + 1) * HALF];
     __shared__ __align__(16) char vs[kWavesB * SLOT];  // per wave: the V tile in use
+    __shared__ int32_t ptab[PAGED ? kDecodeMaxPages : 1];  // page numbers of this chunk
 
     const int nw = blockDim.x >> 6;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
@@ -520,19 +524,37 @@ __global__ __launch_bounds__(512) void decode_split_bf16_kernel(DecodeArgs a) {
     // every load below is unconditional (branch-free memory stream, exact
     // waits): indices are clamped to valid rows, masked keys weigh 0
     const int kvh_c = min(kvh, a.Hkv - 1);
-    const bf16* kc = (const bf16*)a.kc + (int64_t)b * a.S_max * a.Hkv * D + (int64_t)kvh_c * D;
-    const bf16* vc = (const bf16*)a.vc + (int64_t)b * a.S_max * a.Hkv * D + (int64_t)kvh_c * D;
+    const int64_t boff = PAGED ? 0 : (int64_t)b * a.S_max * a.Hkv * D;
+    const bf16* kc = (const bf16*)a.kc + boff + (int64_t)kvh_c * D;
+    const bf16* vc = (const bf16*)a.vc + boff + (int64_t)kvh_c * D;
     const int64_t rstride = (int64_t)a.Hkv * D;
     char* const slot = vs + wave * SLOT;
 
     const int32_t klo = max(kbeg, 0), khi = kend - 1;
+    // cache row of key j (j in [klo, khi])
+    const int32_t pg0 = PAGED ? (klo >> a.page_shift) : 0;
+    if constexpr (PAGED) {
+        const int32_t npg = (khi >> a.page_shift) - pg0 + 1;
+        const int32_t* bt = a.block_table + (int64_t)b * a.bt_stride;
+        for (int x = threadIdx.x; x < npg; x += blockDim.x)
+            ptab[x] = (int32_t)min(max((int64_t)bt[pg0 + x], (int64_t)0), a.n_pages - 1);
+        __syncthreads();
+    }
+    auto row_of = [&](int32_t j) __attribute__((always_inline)) -> int64_t {
+        if constexpr (PAGED) {
+            return ((int64_t)ptab[(j >> a.page_shift) - pg0] << a.page_shift) |
+                   (j & ((1 << a.page_shift) - 1));
+        } else {
+            return j;
+        }
+    };
     // K of key j0 + n into registers (keys outside the chunk read a row
     // inside it; their scores are masked)
     auto load_k = [&](int32_t j0, bf16x8* kd) __attribute__((always_inline)) {
         const int32_t kj = min(max(j0 + n, klo), khi);
 #pragma unroll
         for (int s = 0; s < NST; ++s)
-            kd[s] = *reinterpret_cast<const bf16x8*>(kc + (int64_t)kj * rstride + 32 * s + 8 * c);
+            kd[s] = *reinterpret_cast<const bf16x8*>(kc + row_of(kj) * rstride + 32 * s + 8 * c);
     };
     // V tiles are staged in registers two tiles ahead (load r of a lane
     // reads 16 bytes of key RPI r + lane / CPR, so one load instruction
@@ -543,7 +565,7 @@ __global__ __launch_bounds__(512) void decode_split_bf16_kernel(DecodeArgs a) {
 #pragma unroll
         for (int r = 0; r < NI; ++r) {
             const int32_t key = min(max(j0 + RPI * r + q, klo), khi);
-            vd[r] = *reinterpret_cast<const bf16x8*>(vc + (int64_t)key * rstride + 8 * ch);
+            vd[r] = *reinterpret_cast<const bf16x8*>(vc + row_of(key) * rstride + 8 * ch);
         }
     };
     auto store_vr = [&](const bf16x8* vsrc, char* dst) __attribute__((always_inline)) {
@@ -870,10 +892,16 @@ static hipError_t launch_decode_g(const DecodeArgs& a, hipStream_t s) {
     const dim3 grid(a.lay.n_splits, (a.Hkv + nw - 1) / nw, a.B);
     LaunchScope scope(a.bifocal ? "decode_split" : "decode_split_plain", s);
     if constexpr (sizeof(TIN) == 2) {
-        if (a.bifocal)
-            hipLaunchKernelGGL((decode_split_bf16_kernel<D, true, GQ>), grid, dim3(64 * nw), 0, s, a);
-        else
-            hipLaunchKernelGGL((decode_split_bf16_kernel<D, false, GQ>), grid, dim3(64 * nw), 0, s, a);
+        if (a.block_table) {
+            if (a.bifocal)
+                hipLaunchKernelGGL((decode_split_bf16_kernel<D, true, GQ, true>), grid, dim3(64 * nw), 0, s, a);
+            else
+                hipLaunchKernelGGL((decode_split_bf16_kernel<D, false, GQ, true>), grid, dim3(64 * nw), 0, s, a);
+        } else if (a.bifocal) {
+            hipLaunchKernelGGL((decode_split_bf16_kernel<D, true, GQ, false>), grid, dim3(64 * nw), 0, s, a);
+        } else {
+            hipLaunchKernelGGL((decode_split_bf16_kernel<D, false, GQ, false>), grid, dim3(64 * nw), 0, s, a);
+        }
     } else {
         if (a.bifocal)
             hipLaunchKernelGGL((decode_split_kernel<D, TIN, true, GQ>), grid, dim3(64 * nw), 0, s, a);

@@ -32,6 +32,9 @@ PrefillLayout prefill_layout(int64_t T, int32_t n_seqs, int32_t Hkv, int32_t d, 
 // (the kernel keeps one query-angle row per stage in LDS)
 constexpr int kDecodeStageB = 48;
 constexpr int kDecodeMaxStagesB = 32;
+// a chunk spans at most 32 * 48 + 47 positions: with pages of >= 16 rows, at
+// most this many pages
+constexpr int kDecodeMaxPages = (kDecodeMaxStagesB * kDecodeStageB + kDecodeStageB - 1) / 16 + 2;
 
 struct DecodeLayout {
     int32_t n_splits;
@@ -89,6 +92,11 @@ struct DecodeArgs {
     int32_t w_pretrained, w_local, bifocal;
     float softmax_scale;
     RopeFreq tab;
+    // paged cache (block_table != nullptr): key j of sequence b sits in row
+    // block_table[b * bt_stride + j / 2^page_shift] * 2^page_shift + j % 2^page_shift
+    const int32_t* block_table;
+    int32_t page_shift, bt_stride;
+    int64_t n_pages;
 };
 hipError_t launch_decode(const DecodeArgs& a, int dtype, hipStream_t s);
 

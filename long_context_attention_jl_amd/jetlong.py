@@ -89,6 +89,11 @@ def lib() -> ctypes.CDLL:
         L.jl_bifocal_decode.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i64, _i32, _i32,
                                         _i32, ctypes.POINTER(jl_params), ctypes.c_int, _vp,
                                         ctypes.c_size_t, _vp]
+        L.jl_bifocal_decode_paged.restype = ctypes.c_int
+        L.jl_bifocal_decode_paged.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32,
+                                              _i64, _i32, _i32, _i32, _i32,
+                                              ctypes.POINTER(jl_params), ctypes.c_int, _vp,
+                                              ctypes.c_size_t, _vp]
         L.jl_debug_index_math.restype = ctypes.c_int
         L.jl_debug_index_math.argtypes = [_i64, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp]
         L.jl_profile_enable.restype = ctypes.c_int
@@ -283,6 +288,48 @@ def bifocal_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor
         _dev(v_cache, "v_cache"), _dev(sl, "seqlens_k"), B, int(max_seqlen_k), S_max, Hq, Hkv, d,
         ctypes.byref(p), _dtype(q), _dev(ws, "workspace"), ws.numel() * ws.element_size(),
         _stream()), "jl_bifocal_decode")
+    return o, lse
+
+
+def _seqlens(seqlens_k, max_seqlen_k, dev):
+    if isinstance(seqlens_k, torch.Tensor):
+        sl = seqlens_k.to(device=dev, dtype=torch.int32).contiguous()
+        if max_seqlen_k is None:
+            max_seqlen_k = int(sl.max().item())
+    else:
+        lens = [int(x) for x in seqlens_k]
+        sl = torch.tensor(lens, dtype=torch.int32, device=dev)
+        if max_seqlen_k is None:
+            max_seqlen_k = max(lens)
+    return sl, int(max_seqlen_k)
+
+
+def bifocal_decode_paged(q: torch.Tensor, k_pages: torch.Tensor, v_pages: torch.Tensor,
+                         block_table: torch.Tensor, seqlens_k: Union[Sequence[int], torch.Tensor],
+                         *, w_pretrained: int, w_local: int, rope_base: float,
+                         softmax_scale: float, bifocal: bool = True,
+                         max_seqlen_k: Optional[int] = None,
+                         workspace: Optional[torch.Tensor] = None,
+                         out: Optional[torch.Tensor] = None,
+                         lse_out: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Bifocal decode on a paged cache: k_pages / v_pages [n_pages, page_size, Hkv, d]
+    bf16, block_table [B, bt_stride] int32 (page of key j: block_table[b, j // page_size]).
+    Returns (o [B, Hq, d], lse [B, Hq])."""
+    B, Hq, d = q.shape
+    n_pages, page_size, Hkv = k_pages.shape[0], k_pages.shape[1], k_pages.shape[2]
+    dev = q.device
+    sl, max_seqlen_k = _seqlens(seqlens_k, max_seqlen_k, dev)
+    bt = block_table.to(device=dev, dtype=torch.int32).contiguous()
+    o = out if out is not None else torch.empty_like(q)
+    lse = lse_out if lse_out is not None else torch.empty((B, Hq), dtype=torch.float32, device=dev)
+    ws = _workspace(decode_workspace_bytes(B, max_seqlen_k, Hq, Hkv, d, q.dtype), dev, workspace)
+    p = _params(w_pretrained, w_local, rope_base, softmax_scale, bifocal)
+    _check(lib().jl_bifocal_decode_paged(
+        _dev(o, "o"), _dev(lse, "lse"), _dev(q, "q"), _dev(k_pages, "k_pages"),
+        _dev(v_pages, "v_pages"), _dev(bt, "block_table"), _dev(sl, "seqlens_k"), B, max_seqlen_k,
+        page_size, n_pages, bt.shape[1], Hq, Hkv, d, ctypes.byref(p), _dtype(q),
+        _dev(ws, "workspace"), ws.numel() * ws.element_size(), _stream()),
+        "jl_bifocal_decode_paged")
     return o, lse
 
 

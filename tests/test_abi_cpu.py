@@ -186,3 +186,26 @@ def test_binding_fails_loudly_without_library(monkeypatch):
     monkeypatch.setattr(jlb, "LIB_PATH", "/nonexistent/libjetlong.so")
     with pytest.raises(RuntimeError):
         jlb.lib()
+
+
+def _paged(**kw):
+    a = dict(o=FAKE, lse=FAKE * 2, q=FAKE * 3, kp=FAKE * 4, vp=FAKE * 5, bt=FAKE * 6, sl=FAKE * 7,
+             B=2, max_len=4096, page=64, n_pages=200, bt_stride=64, Hq=32, Hkv=8, d=128,
+             params=_params(), dtype=1, ws=FAKE * 8, ws_bytes=1 << 40, stream=None)
+    a.update(kw)
+    p = a["params"]
+    return jlb.lib().jl_bifocal_decode_paged(
+        a["o"], a["lse"], a["q"], a["kp"], a["vp"], a["bt"], a["sl"], a["B"], a["max_len"],
+        a["page"], a["n_pages"], a["bt_stride"], a["Hq"], a["Hkv"], a["d"],
+        None if p is None else ctypes.byref(p), a["dtype"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(bt=None), 1), (dict(kp=None), 1), (dict(B=0), 1), (dict(page=48), 1), (dict(page=8), 1),
+    (dict(n_pages=0), 1), (dict(bt_stride=63), 1), (dict(Hq=30), 1), (dict(Hq=32, Hkv=1), 2),
+    (dict(dtype=0), 2), (dict(d=96), 2), (dict(ws_bytes=100), 3), (dict(ws=FAKE * 8 + 4), 1),
+    (dict(o=FAKE * 3), 1), (dict(params=_params(w_pretrained=0)), 1),
+])
+def test_paged_decode_validation(kw, status):
+    assert _paged(**kw) == status
+    assert jlb.lib().jl_last_error()
