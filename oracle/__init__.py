@@ -74,6 +74,13 @@ def _load():
                                    ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                    ctypes.c_int64, ctypes.c_int64, ctypes.c_double,
                                    ctypes.c_double, ctypes.c_int, ctypes.c_int]
+        lib.jlo_prefill_chunk.restype = ctypes.c_int
+        lib.jlo_prefill_chunk.argtypes = [_f64p, _f64p, _vp, _vp, _vp, ctypes.c_int, _i64p, _i64p,
+                                          ctypes.c_int, ctypes.c_int64, ctypes.c_int64,
+                                          ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                          ctypes.c_int64, ctypes.c_int64, ctypes.c_double,
+                                          ctypes.c_double, ctypes.c_int, _i64p, ctypes.c_int64,
+                                          ctypes.c_int]
         _lib = lib
     return _lib
 
@@ -221,4 +228,41 @@ def decode(q, k_cache, v_cache, seqlens, *, w_pretrained, w_local, rope_base, so
                             int(n_threads))
     if rc != 0:
         raise ValueError("oracle decode rejected its arguments")
+    return o, lse
+
+
+def prefill_chunk(q, k_cache, v_cache, seqlens, *, w_pretrained, w_local, rope_base,
+                  softmax_scale, bifocal=True, cu_seqlens_q=None, rows=None, n_threads=0):
+    """A prefill chunk against a cache ([TW] §三, [BT] §3.1, §3.3).
+
+    q [Tq, Hq, d] raw: the newest C_b positions L_b - C_b .. L_b - 1 of each
+    sequence b, packed by ``cu_seqlens_q`` (None: one sequence, C = Tq);
+    k_cache/v_cache [B, S_max, Hkv, d] hold the L_b = seqlens[b] keys of the
+    sequence (standard-RoPE keys at their original positions, the chunk's own
+    keys included).  G = G(L_b).  Returns (o [R, Hq, d], lse [R, Hq]) in fp64
+    for the R selected rows of q (all when ``rows`` is None).
+    """
+    qa, dt = _host(q)
+    ka, dk = _host(k_cache)
+    va, dv = _host(v_cache)
+    assert dt == dk == dv
+    Tq, Hq, d = qa.shape
+    B, S_max, Hkv = ka.shape[0], ka.shape[1], ka.shape[2]
+    cu = _cu(cu_seqlens_q, Tq)
+    assert len(cu) == B + 1, "one chunk per cache row"
+    sl = np.ascontiguousarray(np.asarray(seqlens, dtype=np.int64).reshape(B))
+    if rows is None:
+        R, rp = Tq, None
+    else:
+        ra = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+        R, rp = len(ra), _ptr(ra, _i64p)
+    o = np.empty((R, Hq, d), dtype=np.float64)
+    lse = np.empty((R, Hq), dtype=np.float64)
+    rc = _load().jlo_prefill_chunk(_ptr(o, _f64p), _ptr(lse, _f64p), _ptr(qa), _ptr(ka),
+                                   _ptr(va), dt, _ptr(cu, _i64p), _ptr(sl, _i64p), B, Tq, S_max,
+                                   Hq, Hkv, d, int(w_pretrained), int(w_local), float(rope_base),
+                                   float(softmax_scale), int(bool(bifocal)), rp, R,
+                                   int(n_threads))
+    if rc != 0:
+        raise ValueError("oracle chunked prefill rejected its arguments")
     return o, lse

@@ -400,3 +400,90 @@ int jlo_decode(double* o, double* lse, const void* q, const void* kc, const void
         }
     return 0;
 }
+
+/*
+ * Chunked prefill against a cache ([TW] §三 and [BT] §3.3 for the cache and
+ * its correction rotation, [BT] §3.1 for G).  Sequence b holds L_b =
+ * seqlens[b] keys in kc/vc; kc rows hold R(j) k_j (standard RoPE at the
+ * original index).  Its newest C_b = cu_q[b + 1] - cu_q[b] positions,
+ * L_b - C_b .. L_b - 1, are the queries q[cu_q[b] .. cu_q[b + 1]) (raw).  G is
+ * G(L_b), the length the call sees.  A query at position p scores every key
+ * j <= p: local keys against R(p) q, remote keys turned by R(f(j) - j) against
+ * R(f(p)) q.  Decode is the case C_b = 1.  The turned keys of a sequence do
+ * not depend on the query, so they are formed once per sequence.
+ * q [Tq][Hq][d]; kc, vc [B][S_max][Hkv][d]; rows as in jlo_prefill (indices
+ * into q); returns -1 on inconsistent arguments.
+ */
+int jlo_prefill_chunk(double* o_sel, double* lse_sel, const void* q, const void* kc,
+                      const void* vc, int dtype, const int64_t* cu_q, const int64_t* seqlens,
+                      int B, int64_t Tq, int64_t S_max, int Hq, int Hkv, int d,
+                      int64_t w_pretrained, int64_t w_local, double base, double scale,
+                      int bifocal, const int64_t* rows, int64_t n_rows, int n_threads) {
+    if (Hkv <= 0 || Hq % Hkv != 0 || d <= 0 || d % 2 || w_pretrained < 1 || w_local < 0) return -1;
+    if (cu_q[0] != 0 || cu_q[B] != Tq) return -1;
+    for (int b = 0; b < B; ++b) {
+        const int64_t C = cu_q[b + 1] - cu_q[b];
+        if (C < 0 || C > seqlens[b] || seqlens[b] > S_max) return -1;
+    }
+#ifdef _OPENMP
+    if (n_threads > 0) omp_set_num_threads(n_threads);
+#else
+    (void)n_threads;
+#endif
+    if (!rows) n_rows = Tq;
+    const int grp = Hq / Hkv;
+    for (int b = 0; b < B; ++b) {
+        const int64_t L = seqlens[b], C = cu_q[b + 1] - cu_q[b], qstart = cu_q[b];
+        int64_t cnt = 0;
+        for (int64_t a = 0; a < n_rows; ++a) {
+            const int64_t r = rows ? rows[a] : a;
+            cnt += (r >= qstart && r < qstart + C);
+        }
+        if (cnt == 0) continue;
+        const int64_t G = jlo_group_size(L, w_pretrained);
+        /* kS[g][j] = cache row j as stored, kR[g][j] = R(f(j) - j) cache row j */
+        double* kS = (double*)malloc(sizeof(double) * (size_t)(Hkv * L * d));
+        double* kR = (double*)malloc(sizeof(double) * (size_t)(Hkv * L * d));
+#pragma omp parallel for schedule(static)
+        for (int64_t j = 0; j < L; ++j)
+            for (int g = 0; g < Hkv; ++g) {
+                double* ks = kS + ((int64_t)g * L + j) * d;
+                widen(ks, kc, dtype, (((int64_t)b * S_max + j) * Hkv + g) * d, d);
+                rotate(kR + ((int64_t)g * L + j) * d, ks, (double)(jlo_remap(j, G) - j), d, base);
+            }
+#pragma omp parallel
+        {
+            double* qr = (double*)malloc(sizeof(double) * (size_t)d);
+            double* qS = (double*)malloc(sizeof(double) * (size_t)d);
+            double* qR = (double*)malloc(sizeof(double) * (size_t)d);
+            double* sc = (double*)malloc(sizeof(double) * (size_t)L);
+#pragma omp for collapse(2) schedule(dynamic, 1)
+            for (int64_t a = 0; a < n_rows; ++a)
+                for (int h = 0; h < Hq; ++h) {
+                    const int64_t r = rows ? rows[a] : a;
+                    if (r < qstart || r >= qstart + C) continue;
+                    const int64_t p = L - C + (r - qstart);
+                    const int g = h / grp;
+                    widen(qr, q, dtype, (r * Hq + h) * (int64_t)d, d);
+                    rotate(qS, qr, (double)p, d, base);
+                    rotate(qR, qr, (double)jlo_remap(p, G), d, base);
+                    for (int64_t j = 0; j <= p; ++j) {
+                        const int local = jlo_band(p, j, w_local, bifocal) == 1;
+                        const double* kj = (local ? kS : kR) + ((int64_t)g * L + j) * d;
+                        sc[j] = scale * dot(local ? qS : qR, kj, d);
+                    }
+                    vsrc vs = {vc, dtype, (int64_t)b * S_max, (int64_t)Hkv * d, (int64_t)g * d,
+                               NULL};
+                    softmax_pv(o_sel + (a * Hq + h) * (int64_t)d, lse_sel + a * Hq + h, sc, p + 1,
+                               &vs, d);
+                }
+            free(qr);
+            free(qS);
+            free(qR);
+            free(sc);
+        }
+        free(kS);
+        free(kR);
+    }
+    return 0;
+}

@@ -354,3 +354,68 @@ def test_bf16_inputs_widen_exactly():
     o2, l2 = oracle.prefill(q.double(), k.double(), v.double(), **kw)
     np.testing.assert_array_equal(o1, o2)
     np.testing.assert_array_equal(l1, l2)
+
+
+def test_chunk_equals_prefill_rows():
+    """A prefill chunk over a cache of standard-RoPE keys ([TW] §三, [BT] §3.3)
+    equals the prefill definition ([BT] §3.2) at the chunk's rows of the whole
+    sequence of length L (G = G(L)), for every L across the G switch
+    (w_pretrained = 8: G goes 1 -> 2 at L = 9, 2 -> 3 at L = 17) and several
+    chunk sizes, with and without the bifocal split."""
+    rng = np.random.default_rng(23)
+    S, Hq, Hkv, d, base, scale = 26, 4, 2, 16, 1e4, 0.4
+    q_all = rng.standard_normal((S, Hq, d))
+    k = rng.standard_normal((S, Hkv, d))
+    v = rng.standard_normal((S, Hkv, d))
+    cache_k = oracle.rope(k, np.arange(S), base)  # R(j) k_j, fp64
+    for bifocal in (True, False):
+        kw = dict(w_pretrained=8, w_local=3, rope_base=base, softmax_scale=scale,
+                  bifocal=bifocal)
+        for L in range(1, S + 1):
+            for C in sorted({1, 2, (L + 1) // 2, L}):
+                if C > L:
+                    continue
+                o_c, l_c = oracle.prefill_chunk(q_all[L - C:L], cache_k[None], v[None], [L], **kw)
+                o_p, l_p = oracle.prefill(q_all[:L], k[:L], v[:L], rows=range(L - C, L), **kw)
+                np.testing.assert_allclose(o_c, o_p, rtol=0, atol=1e-11)
+                np.testing.assert_allclose(l_c, l_p, rtol=0, atol=1e-11)
+
+
+def test_chunk_of_one_is_decode():
+    rng = np.random.default_rng(29)
+    B, S, Hq, Hkv, d = 2, 40, 4, 2, 8
+    q = rng.standard_normal((B, Hq, d))
+    kc = rng.standard_normal((B, S, Hkv, d))
+    vc = rng.standard_normal((B, S, Hkv, d))
+    lens = [40, 17]
+    kw = dict(w_pretrained=9, w_local=4, rope_base=1e4, softmax_scale=0.5)
+    o_d, l_d = oracle.decode(q, kc, vc, lens, **kw)
+    o_c, l_c = oracle.prefill_chunk(q, kc, vc, lens, cu_seqlens_q=[0, 1, 2], **kw)
+    np.testing.assert_allclose(o_c, o_d, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(l_c, l_d, rtol=0, atol=1e-12)
+
+
+def test_chunk_batch_is_per_sequence():
+    """Packed chunks (one of them empty): each sequence gets its own G, its own
+    positions and its own cache row; selecting rows changes nothing."""
+    rng = np.random.default_rng(31)
+    B, S, Hq, Hkv, d = 3, 30, 2, 1, 8
+    kc = rng.standard_normal((B, S, Hkv, d))
+    vc = rng.standard_normal((B, S, Hkv, d))
+    lens, chunks = [30, 11, 19], [7, 0, 19]
+    cu = np.cumsum([0] + chunks)
+    q = rng.standard_normal((int(cu[-1]), Hq, d))
+    kw = dict(w_pretrained=6, w_local=3, rope_base=1e4, softmax_scale=0.5)
+    o, lse = oracle.prefill_chunk(q, kc, vc, lens, cu_seqlens_q=cu, **kw)
+    for b in range(B):
+        a, e = cu[b], cu[b + 1]
+        if a == e:
+            continue
+        o1, l1 = oracle.prefill_chunk(q[a:e], kc[b:b + 1], vc[b:b + 1], [lens[b]], **kw)
+        np.testing.assert_array_equal(o[a:e], o1)
+        np.testing.assert_array_equal(lse[a:e], l1)
+    o_s, l_s = oracle.prefill_chunk(q, kc, vc, lens, cu_seqlens_q=cu, rows=[25, 0, 9], **kw)
+    np.testing.assert_array_equal(o_s, o[[25, 0, 9]])
+    np.testing.assert_array_equal(l_s, lse[[25, 0, 9]])
+    with pytest.raises(ValueError):
+        oracle.prefill_chunk(q, kc, vc, [30, 11, 18], cu_seqlens_q=cu, **kw)  # chunk > length
