@@ -78,6 +78,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-three-call", action="store_true")
+    ap.add_argument("--no-chunk", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0,
                     help="only run a plain device copy of this many bytes (counter calibration)")
     args = ap.parse_args()
@@ -172,6 +173,9 @@ def main():
     if not args.no_three_call:
         out["three_call"] = bench_three_call(jl, torch, case, ms_per_step)
 
+    if not args.no_chunk:
+        out["chunk"] = bench_chunk(jl, inputs, torch)
+
     if not args.no_decode:
         out["decode"] = bench_decode(jl, inputs, torch, args.decode_iters)
 
@@ -201,6 +205,63 @@ def bench_three_call(jl, torch, case, fused_ms):
     ms = (time.perf_counter() - t0) * 1e3
     return {"ms_per_step": round(ms, 3), "tokens_per_s": round(T / (ms / 1e3), 1),
             "fused_speedup": round(ms / fused_ms, 3)}
+
+
+def bench_chunk(jl, inputs, torch, iters=10):
+    """Chunked prefill: 4096 new rows appended to a 126976-key cache (L = 131072,
+    G = 4), flat and on 64-row pages under a shuffled block table.  Algorithmic
+    flops count 4 d Hq per causal pair of the chunk's rows."""
+    c = inputs.chunk_128k()
+    p = c.params
+    C, Hq, d = c.q.shape
+    S_max, Hkv = c.k_cache.shape[1], c.k_cache.shape[2]
+    L = c.seqlens[0]
+    q, kc, vc = c.q.cuda(), c.k_cache.cuda(), c.v_cache.cuda()
+    sl = torch.tensor(c.seqlens, dtype=torch.int32, device="cuda")
+    ws = torch.empty(jl.prefill_chunk_workspace_bytes(1, L, Hq, Hkv, d), dtype=torch.uint8,
+                     device="cuda")
+    o = torch.empty_like(q)
+    lse = torch.empty((Hq, C), dtype=torch.float32, device="cuda")
+    page = 64
+    n_pages = S_max // page
+    bt = torch.randperm(n_pages, generator=torch.Generator().manual_seed(page))
+    bt = bt.to(torch.int32).view(1, n_pages).cuda()
+    kp, vp = kc.view(n_pages, page, Hkv, d), vc.view(n_pages, page, Hkv, d)
+    kw = dict(w_pretrained=p.w_pretrained, w_local=p.w_local, rope_base=p.rope_base,
+              softmax_scale=p.softmax_scale, max_seqlen_k=L, workspace=ws, out=o, lse_out=lse)
+
+    def run(paged, n):
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        ev0.record()
+        for _ in range(n):
+            if paged:
+                jl.bifocal_prefill_chunk_paged(q, kp, vp, bt, sl, **kw)
+            else:
+                jl.bifocal_prefill_chunk(q, kc, vc, sl, **kw)
+        ev1.record()
+        torch.cuda.synchronize()
+        return ev0.elapsed_time(ev1) / n
+
+    run(False, 2)
+    run(True, 2)
+    t_flat = min(run(False, iters // 2) for _ in range(2))
+    t_paged = min(run(True, iters // 2) for _ in range(2))
+    jl.profile_enable(True)
+    run(False, 4)
+    prof = jl.profile_read()
+    jl.profile_enable(False)
+    q0 = L - C
+    flops = 4.0 * d * Hq * ((L * (L + 1) - q0 * (q0 + 1)) // 2)
+    return {
+        "workload": "chunk of 4096 rows on a 131072-key sequence (Hq=32, Hkv=8, d=128, G=4)",
+        "ms": round(t_flat, 3),
+        "tflops": round(flops / (t_flat * 1e-3) / 1e12, 1),
+        "frac_of_bf16_peak": round(flops / (t_flat * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "paged64_ms": round(t_paged, 3),
+        "kernels": {n: {"launches": c2, "avg_ms": round(ms / max(c2, 1), 4)}
+                    for n, (c2, ms) in sorted(prof.items())},
+    }
 
 
 def bench_decode(jl, inputs, torch, iters):

@@ -205,6 +205,65 @@ jl_status jl_bifocal_decode_paged(void* o, float* lse, const void* q, const void
                                   int32_t Hkv, int32_t d, const jl_params* params, jl_dtype dtype,
                                   void* workspace, size_t workspace_bytes, void* stream);
 
+/* Bytes of device workspace the chunk calls below need for batch sequences
+ * of at most max_seqlen_k keys (bf16 only). */
+jl_status jl_bifocal_prefill_chunk_workspace(int32_t batch, int32_t max_seqlen_k, int32_t Hq,
+                                             int32_t Hkv, int32_t d, jl_dtype dtype,
+                                             size_t* bytes);
+
+/*
+ * Chunked prefill ([TW] §三 and [BT] §3.3 for the cache, [BT] §3.1 for G): a
+ * chunk of new tokens per sequence attends causally to every key of its
+ * sequence held in a KV cache of standard-RoPE keys (the chunk's own keys,
+ * appended by the caller, included).  Sequence b has L_b = seqlens_k[b] keys
+ * and C_b = cu_seqlens_q[b + 1] - cu_seqlens_q[b] new query rows at positions
+ * L_b - C_b .. L_b - 1, with G = G(L_b), the length the call sees: each row
+ * gets exactly what jl_bifocal_prefill gives that row of the whole sequence
+ * of length L_b.  A query at position p scores key j <= p as
+ *     local  (p - j <  w_local): s = scale * <R(p) q, k_cache[j]>
+ *     remote (p - j >= w_local): s = scale * <R(f(p)) q, R(f(j) - j) k_cache[j]>
+ * and the cache is never rewritten (jl_bifocal_decode is the case C_b = 1).
+ *   o             [Tq][Hq][d] bf16 (written); lse float32 [Hq][Tq] (written).
+ *   q             raw (un-rotated) queries [Tq][Hq][d], the chunks packed.
+ *   cu_seqlens_q  device int32 [batch + 1], 0 = cu[0] <= ... <= cu[batch] = Tq;
+ *                 NULL for one chunk (batch == 1, max_seqlen_q == Tq).
+ *                 A sequence may have C_b = 0 (nothing is computed for it).
+ *   max_seqlen_q  host int, >= every C_b.
+ *   k_cache, v_cache  [batch][S_max][Hkv][d] bf16, read-only.
+ *   seqlens_k     device int32 [batch], C_b <= L_b <= max_seqlen_k <= S_max.
+ *   workspace     at least jl_bifocal_prefill_chunk_workspace() bytes.
+ * If the device arrays break their contract nothing is read or written
+ * outside the buffers and o, lse are left unwritten.  bf16 only; d in
+ * {64, 128}; rotated q and k must stay below 65504 in magnitude (fp16 MFMA
+ * operands).
+ */
+jl_status jl_bifocal_prefill_chunk(void* o, float* lse, const void* q,
+                                   const int32_t* cu_seqlens_q, int64_t Tq, int32_t max_seqlen_q,
+                                   const void* k_cache, const void* v_cache,
+                                   const int32_t* seqlens_k, int32_t batch,
+                                   int32_t max_seqlen_k, int64_t S_max, int32_t Hq, int32_t Hkv,
+                                   int32_t d, const jl_params* params, jl_dtype dtype,
+                                   void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * jl_bifocal_prefill_chunk on a paged KV cache: pools k_pages, v_pages of
+ * n_pages pages [page_size][Hkv][d] bf16; key j of sequence b sits in page
+ * block_table[b * bt_stride + j / page_size], row j % page_size (page_size a
+ * power of two in [16, 65536], bt_stride * page_size >= max_seqlen_k).  Page
+ * numbers outside [0, n_pages) are clamped into the pool.  Same results and
+ * workspace as the flat form.
+ */
+jl_status jl_bifocal_prefill_chunk_paged(void* o, float* lse, const void* q,
+                                         const int32_t* cu_seqlens_q, int64_t Tq,
+                                         int32_t max_seqlen_q, const void* k_pages,
+                                         const void* v_pages, const int32_t* block_table,
+                                         const int32_t* seqlens_k, int32_t batch,
+                                         int32_t max_seqlen_k, int32_t page_size,
+                                         int64_t n_pages, int32_t bt_stride, int32_t Hq,
+                                         int32_t Hkv, int32_t d, const jl_params* params,
+                                         jl_dtype dtype, void* workspace,
+                                         size_t workspace_bytes, void* stream);
+
 /*
  * Test export: runs the kernels' own device index functions for a sequence of
  * length L (1 <= L) and writes

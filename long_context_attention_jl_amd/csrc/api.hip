@@ -517,6 +517,131 @@ jl_status jl_bifocal_decode_paged(void* o, float* lse, const void* q, const void
     return finish(s, "jl_bifocal_decode_paged");
 }
 
+// ---------------------------------------------------------------------------
+// Chunked prefill against a cache: the prefill workspace for batch sequences
+// of up to max_seqlen_k keys each.
+static jl_status chunk_sizes_ok(int32_t batch, int32_t max_seqlen_k) {
+    if (batch < 1 || max_seqlen_k < 1)
+        return fail(JL_ERR_INVALID_ARGUMENT, "batch and max_seqlen_k must be >= 1");
+    if (batch > 65535) return fail(JL_ERR_UNSUPPORTED, "batch above 65535");
+    if ((int64_t)batch * max_seqlen_k + (int64_t)batch * kBN >= 2147483647LL)
+        return fail(JL_ERR_UNSUPPORTED, "batch * (max_seqlen_k + 64) must stay below 2^31");
+    return JL_OK;
+}
+
+jl_status jl_bifocal_prefill_chunk_workspace(int32_t batch, int32_t max_seqlen_k, int32_t Hq,
+                                             int32_t Hkv, int32_t d, jl_dtype dtype,
+                                             size_t* bytes) {
+    if (!bytes) return fail(JL_ERR_INVALID_ARGUMENT, "bytes is NULL");
+    jl_status st = chunk_sizes_ok(batch, max_seqlen_k);
+    if (st != JL_OK) return st;
+    st = check_heads(Hq, Hkv);
+    if (st != JL_OK) return st;
+    st = check_dtype_d(dtype, d);
+    if (st != JL_OK) return st;
+    if (dtype != JL_DTYPE_BF16) return fail(JL_ERR_UNSUPPORTED, "chunked prefill is bf16 only");
+    *bytes = prefill_layout((int64_t)batch * max_seqlen_k, batch, Hkv, d, dtype).total;
+    g_err.clear();
+    return JL_OK;
+}
+
+// Shared checks and launches of the flat and paged chunk calls.
+static jl_status chunk_call(PrefillArgs& a, const int32_t* cu_seqlens_q,
+                            const int32_t* seqlens_k, const jl_params* params, jl_dtype dtype,
+                            void* workspace, size_t workspace_bytes, void* stream,
+                            const char* where) {
+    if (!a.o || !a.lse || !a.q || !a.k || !a.v || !seqlens_k || !workspace)
+        return fail(JL_ERR_INVALID_ARGUMENT, "null pointer argument");
+    jl_status st = check_params(params);
+    if (st != JL_OK) return st;
+    st = chunk_sizes_ok(a.n_seqs, a.max_seqlen_k);
+    if (st != JL_OK) return st;
+    if (a.T < 1) return fail(JL_ERR_INVALID_ARGUMENT, "Tq must be >= 1");
+    if (!cu_seqlens_q && a.n_seqs != 1)
+        return fail(JL_ERR_INVALID_ARGUMENT, "cu_seqlens_q == NULL requires batch == 1");
+    if (a.max_seqlen < 1 || a.max_seqlen > a.T || a.max_seqlen > a.max_seqlen_k)
+        return fail(JL_ERR_INVALID_ARGUMENT, "max_seqlen_q must be in [1, min(Tq, max_seqlen_k)]");
+    if (!cu_seqlens_q && a.max_seqlen != a.T)
+        return fail(JL_ERR_INVALID_ARGUMENT, "a single chunk needs max_seqlen_q == Tq");
+    if (a.T >= 2147483647LL) return fail(JL_ERR_UNSUPPORTED, "Tq must stay below 2^31");
+    st = check_heads(a.Hq, a.Hkv);
+    if (st != JL_OK) return st;
+    st = check_dtype_d(dtype, a.d);
+    if (st != JL_OK) return st;
+    if (dtype != JL_DTYPE_BF16) return fail(JL_ERR_UNSUPPORTED, "chunked prefill is bf16 only");
+    if (a.o == a.q || a.o == a.k || a.o == a.v || (const void*)a.lse == a.q)
+        return fail(JL_ERR_INVALID_ARGUMENT, "outputs must not alias inputs");
+    if ((uintptr_t)workspace & 255) return fail(JL_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
+    const PrefillLayout lay =
+        prefill_layout((int64_t)a.n_seqs * a.max_seqlen_k, a.n_seqs, a.Hkv, a.d, dtype);
+    if (workspace_bytes < lay.total)
+        return fail(JL_ERR_WORKSPACE_TOO_SMALL,
+                    "workspace needs " + std::to_string(lay.total) + " bytes");
+    a.ws = workspace;
+    a.lay = lay;
+    a.chunked = 1;
+    a.w_local = params->w_local; a.bifocal = params->bifocal;
+    a.softmax_scale = params->softmax_scale;
+    a.tab = make_rope_freq(params->rope_base, a.d);
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e = launch_plan_chunk((int32_t*)((char*)workspace + lay.plan), cu_seqlens_q,
+                                     seqlens_k, a.n_seqs, a.T, a.max_seqlen, a.max_seqlen_k,
+                                     params->w_pretrained, s);
+    if (e != hipSuccess) return hip_fail(e, "plan launch");
+    e = launch_kv_prepass(a, dtype, s);
+    if (e != hipSuccess) return hip_fail(e, "key/value pre-pass launch");
+    e = launch_prefill_bf16(a, s);
+    if (e != hipSuccess) return hip_fail(e, "prefill launch");
+    return finish(s, where);
+}
+
+jl_status jl_bifocal_prefill_chunk(void* o, float* lse, const void* q,
+                                   const int32_t* cu_seqlens_q, int64_t Tq, int32_t max_seqlen_q,
+                                   const void* k_cache, const void* v_cache,
+                                   const int32_t* seqlens_k, int32_t batch,
+                                   int32_t max_seqlen_k, int64_t S_max, int32_t Hq, int32_t Hkv,
+                                   int32_t d, const jl_params* params, jl_dtype dtype,
+                                   void* workspace, size_t workspace_bytes, void* stream) {
+    if (S_max < max_seqlen_k || S_max < 1)
+        return fail(JL_ERR_INVALID_ARGUMENT, "S_max must be >= max_seqlen_k");
+    PrefillArgs a{};
+    a.q = q; a.k = k_cache; a.v = v_cache; a.o = o; a.lse = lse;
+    a.n_seqs = batch; a.Hq = Hq; a.Hkv = Hkv; a.d = d; a.max_seqlen = max_seqlen_q; a.T = Tq;
+    a.max_seqlen_k = max_seqlen_k; a.S_max = S_max;
+    return chunk_call(a, cu_seqlens_q, seqlens_k, params, dtype, workspace, workspace_bytes,
+                      stream, "jl_bifocal_prefill_chunk");
+}
+
+jl_status jl_bifocal_prefill_chunk_paged(void* o, float* lse, const void* q,
+                                         const int32_t* cu_seqlens_q, int64_t Tq,
+                                         int32_t max_seqlen_q, const void* k_pages,
+                                         const void* v_pages, const int32_t* block_table,
+                                         const int32_t* seqlens_k, int32_t batch,
+                                         int32_t max_seqlen_k, int32_t page_size,
+                                         int64_t n_pages, int32_t bt_stride, int32_t Hq,
+                                         int32_t Hkv, int32_t d, const jl_params* params,
+                                         jl_dtype dtype, void* workspace,
+                                         size_t workspace_bytes, void* stream) {
+    if (!block_table) return fail(JL_ERR_INVALID_ARGUMENT, "null pointer argument");
+    if (page_size < 16 || page_size > 65536 || (page_size & (page_size - 1)))
+        return fail(JL_ERR_INVALID_ARGUMENT, "page_size must be a power of two in [16, 65536]");
+    if (n_pages < 1) return fail(JL_ERR_INVALID_ARGUMENT, "n_pages must be >= 1");
+    if ((int64_t)bt_stride * page_size < max_seqlen_k)
+        return fail(JL_ERR_INVALID_ARGUMENT, "bt_stride * page_size < max_seqlen_k");
+    if (Hkv >= 1 && d >= 1 && n_pages > (1LL << 40) / ((int64_t)page_size * Hkv * d))
+        return fail(JL_ERR_INVALID_ARGUMENT, "page pool too large");
+    PrefillArgs a{};
+    a.q = q; a.k = k_pages; a.v = v_pages; a.o = o; a.lse = lse;
+    a.n_seqs = batch; a.Hq = Hq; a.Hkv = Hkv; a.d = d; a.max_seqlen = max_seqlen_q; a.T = Tq;
+    a.max_seqlen_k = max_seqlen_k; a.S_max = 0;
+    a.block_table = block_table;
+    int shift = 0;
+    while ((1 << shift) < page_size) ++shift;
+    a.page_shift = shift; a.bt_stride = bt_stride; a.n_pages = (int32_t)n_pages;
+    return chunk_call(a, cu_seqlens_q, seqlens_k, params, dtype, workspace, workspace_bytes,
+                      stream, "jl_bifocal_prefill_chunk_paged");
+}
+
 jl_status jl_debug_index_math(int64_t L, int32_t w_pretrained, int32_t w_local, int32_t bifocal,
                               int32_t bm, int32_t bn, int32_t* G_out, int32_t* f_out,
                               uint8_t* band_out, uint8_t* tile_out, void* stream) {

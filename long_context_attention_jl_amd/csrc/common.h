@@ -31,7 +31,7 @@ constexpr int kBM = kWaveRows * kWaves;  // 256 query rows per workgroup
 // path: those rows see few keys, so the LSE inherits the rounding of a single
 // score almost undiluted.  Keys they read are < kPreciseRows as well.
 constexpr int kPreciseRows = 2048;
-constexpr int kPlanFields = 8;      // int32 fields per sequence in the plan
+constexpr int kPlanFields = 9;      // int32 fields per sequence in the plan
 
 // Key and value tiles are stored in the workspace exactly as they sit in LDS
 // (rows padded by 8 halves against bank conflicts), so the prefill kernel
@@ -43,14 +43,16 @@ __host__ __device__ constexpr int vtile_elems(int d) { return d * kVStr; }
 
 // Plan fields (per sequence s, written by the plan kernel).
 enum PlanField {
-    kPlanStart = 0,   // cu_seqlens[s]
-    kPlanLen = 1,     // L_s
+    kPlanStart = 0,   // token of the sequence's first query row (cu_seqlens[s])
+    kPlanLen = 1,     // L_s: keys of the sequence
     kPlanG = 2,       // G(L_s)
     kPlanPadOff = 3,  // first row of the sequence in the padded key layout (multiple of kBN)
     kPlanLoOff = 4,   // first row in the padded "lo" layout (multiple of kBN)
     kPlanTile0 = 5,   // kPlanPadOff / kBN
     kPlanLoTile0 = 6, // kPlanLoOff / kBN
-    kPlanBad = 7      // nonzero in entry n_seqs if cu_seqlens broke its contract
+    kPlanBad = 7,     // nonzero in entry n_seqs if cu_seqlens broke its contract
+    kPlanQ0 = 8       // position of the first query row: 0, or L_s - C_s for a chunk of
+                      // C_s new rows appended to a cache
 };
 
 // ---------------------------------------------------------------------------

@@ -68,8 +68,22 @@ struct PrefillArgs {
     float softmax_scale;
     RopeFreq tab;
     int32_t mode;  // 0 bifocal; unfused calls: 1 all pairs remapped, 2 local standard, 3 local remapped
+    // A chunk against a cache (chunked != 0): the queries are each sequence's
+    // newest rows, keys and values are read from the cache, whose keys already
+    // carry standard RoPE.  Flat cache: sequence s owns rows [s * S_max, ...);
+    // paged cache (block_table != nullptr): key j of sequence s sits in row
+    // block_table[s * bt_stride + j / 2^page_shift] * 2^page_shift + j % 2^page_shift.
+    int32_t chunked, max_seqlen_k;
+    int64_t S_max;
+    const int32_t* block_table;
+    int32_t page_shift, bt_stride, n_pages;
 };
 
+// Plan of a chunk call: per sequence b, C_b = cu_q[b + 1] - cu_q[b] query rows
+// at positions seqlens_k[b] - C_b .. seqlens_k[b] - 1.
+hipError_t launch_plan_chunk(int32_t* plan, const int32_t* cu_q, const int32_t* seqlens_k,
+                             int32_t B, int64_t Tq, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                             int32_t w_pretrained, hipStream_t s);
 hipError_t launch_kv_prepass(const PrefillArgs& a, int dtype, hipStream_t s);
 // O = the LogSumExp combination of the three unfused calls B + A - C
 hipError_t launch_three_call_merge(const void* oA, const void* oB, const void* oC, const float* lA,

@@ -104,9 +104,16 @@ void prefill_bf16_kernel(PrefillArgs a, int rb_first, int n_rb) {
     const int32_t* plan = (const int32_t*)((const char*)a.ws + a.lay.plan);
     const int32_t* e = plan + s * kPlanFields;
     const int32_t start = e[kPlanStart], len = e[kPlanLen], G = e[kPlanG];
-    const int32_t row0 = rb * kBM;
+    // Query rows are positions [q0, len): q0 = 0 for a whole sequence, or the
+    // first new row of a chunk appended to a cache.  Row blocks are aligned
+    // to multiples of 256 positions, so the split-precision rows (< 2048)
+    // never share a block with the others; position `row` is token
+    // qbase + row of q, o and lse.
+    const int32_t q0 = e[kPlanQ0];
+    const int64_t qbase = (int64_t)start - q0;
+    const int32_t row0 = (q0 / kBM + rb) * kBM;
     if (row0 >= len) return;
-    if (!PRECISE && row0 < kPreciseRows) return;
+    if (PRECISE != (row0 < kPreciseRows)) return;
     const int32_t row_end = min(row0 + kBM, len);
     // Which pairs and which RoPE.  Mode 0 is the bifocal softmax (remote
     // pairs remapped, local pairs standard).  Modes 1-3 are the three
@@ -123,9 +130,10 @@ void prefill_bf16_kernel(PrefillArgs a, int rb_first, int n_rb) {
     const int g = head / (a.Hq / a.Hkv);
     const int32_t wr0 = row0 + wave * kWaveRows;
     const int32_t wr_end = min(wr0 + kWaveRows, len);
-    const bool wave_active = wr0 < wr_end;
+    const int32_t wlo = max(wr0, q0);  // the wave's first query row
+    const bool wave_active = wlo < wr_end;
     const int32_t myrow = wr0 + qr;
-    const bool row_valid = myrow < len;
+    const bool row_valid = myrow >= q0 && myrow < len;
 
     // ---- the two phases as tile ranges of this workgroup ----
     // remote pairs need key j <= i - w_local; local pairs j > i - w_local.
@@ -134,7 +142,7 @@ void prefill_bf16_kernel(PrefillArgs a, int rb_first, int n_rb) {
     if (bif) {
         const int32_t jr = row_end - 1 - wl;
         r_end = jr >= 0 ? jr / kBN + 1 : 0;
-        s_begin = wl == 0 ? ntiles : max(0, row0 - wl + 1) / kBN;
+        s_begin = wl == 0 ? ntiles : max(0, max(row0, q0) - wl + 1) / kBN;
     }
 
     // ---- rotated, scaled queries as MFMA B operands ----
@@ -158,8 +166,8 @@ void prefill_bf16_kernel(PrefillArgs a, int rb_first, int n_rb) {
             for (int r = tid / HALF; r < C::QROWS; r += 512 / HALF) {
                 const int32_t row = row0 + half_rows * C::QROWS + r;
                 float x0 = 0.0f, x1 = 0.0f;
-                if (row < len) {
-                    const bf16* qp = qg + (int64_t)(start + row) * a.Hq * D;
+                if (row >= q0 && row < len) {
+                    const bf16* qp = qg + (qbase + row) * a.Hq * D;
                     x0 = (float)qp[t];
                     x1 = (float)qp[t + HALF];
                 }
@@ -302,7 +310,7 @@ void prefill_bf16_kernel(PrefillArgs a, int rb_first, int n_rb) {
 #pragma unroll
         for (int b = 0; b < 2; ++b) {
             const int32_t jb = tau * kBN + 32 * b;
-            const uint32_t cls = tile_class32(wr0, wr_end, jb, jb + 32, wl, bif);
+            const uint32_t cls = tile_class32(wlo, wr_end, jb, jb + 32, wl, bif);
             if (cls & want) do_block(base, b, cls != want, remote_phase, jb);
         }
     };
@@ -348,7 +356,7 @@ void prefill_bf16_kernel(PrefillArgs a, int rb_first, int n_rb) {
     // a row with no key of the call (the local calls with w_local = 0): o = 0, lse = -inf
     const bool none = !(l_run > 0.0f);
     const float inv = none ? 0.0f : 1.0f / l_run;
-    bf16* op = (bf16*)a.o + ((int64_t)(start + myrow) * a.Hq + head) * D;
+    bf16* op = (bf16*)a.o + ((qbase + myrow) * a.Hq + head) * D;
 #pragma unroll
     for (int db = 0; db < C::ND; ++db)
 #pragma unroll
@@ -358,7 +366,7 @@ void prefill_bf16_kernel(PrefillArgs a, int rb_first, int n_rb) {
             for (int r = 0; r < 4; ++r) w[r] = (bf16)(O[db][4 * g4 + r] * inv);
             *reinterpret_cast<bf16x4*>(op + 32 * db + 8 * g4 + 4 * hh) = w;
         }
-    if (hh == 0) a.lse[(int64_t)head * a.T + start + myrow] = none ? -INFINITY : (m_run + log2f(l_run)) * kLn2;
+    if (hh == 0) a.lse[(int64_t)head * a.T + qbase + myrow] = none ? -INFINITY : (m_run + log2f(l_run)) * kLn2;
 }
 
 template <int D, bool PRECISE>
@@ -372,18 +380,29 @@ static hipError_t launch_one(const PrefillArgs& a, int rb_first, int n_rb, hipSt
 }
 
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t s) {
-    const int total_rb = (a.max_seqlen + kBM - 1) / kBM;
     const int precise_rb = kPreciseRows / kBM;
+    int total_rb, main_first;
+    if (a.chunked) {
+        // row blocks counted from the block holding a chunk's first row: a
+        // chunk of at most max_seqlen rows touches at most this many
+        total_rb = (a.max_seqlen + kBM - 1) / kBM + 1;
+        const int key_rb = (a.max_seqlen_k + kBM - 1) / kBM;
+        total_rb = total_rb < key_rb ? total_rb : key_rb;
+        main_first = 0;
+    } else {
+        total_rb = (a.max_seqlen + kBM - 1) / kBM;
+        main_first = precise_rb;
+    }
     const int n_prec = total_rb < precise_rb ? total_rb : precise_rb;
     hipError_t err;
     if (a.d == 128) {
         err = launch_one<128, true>(a, 0, n_prec, s, "prefill_bf16_precise");
         if (err != hipSuccess) return err;
-        return launch_one<128, false>(a, precise_rb, total_rb - precise_rb, s, "prefill_bf16");
+        return launch_one<128, false>(a, main_first, total_rb - main_first, s, "prefill_bf16");
     }
     err = launch_one<64, true>(a, 0, n_prec, s, "prefill_bf16_precise");
     if (err != hipSuccess) return err;
-    return launch_one<64, false>(a, precise_rb, total_rb - precise_rb, s, "prefill_bf16");
+    return launch_one<64, false>(a, main_first, total_rb - main_first, s, "prefill_bf16");
 }
 
 // LogSumExp combination of the pages' three unfused calls ([TW] §四, [BT]

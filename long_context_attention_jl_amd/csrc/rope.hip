@@ -79,6 +79,7 @@ __global__ void plan_kernel(int32_t* __restrict__ plan, const int32_t* __restric
         e[kPlanTile0] = (int32_t)(pad / kBN);
         e[kPlanLoTile0] = (int32_t)(lo / kBN);
         e[kPlanBad] = 0;
+        e[kPlanQ0] = 0;
         pad += (len + kBN - 1) / kBN * kBN;
         const int32_t nlo = len < kPreciseRows ? len : kPreciseRows;
         lo += (nlo + kBN - 1) / kBN * kBN;
@@ -92,6 +93,7 @@ __global__ void plan_kernel(int32_t* __restrict__ plan, const int32_t* __restric
     e[kPlanTile0] = (int32_t)(pad / kBN);
     e[kPlanLoTile0] = (int32_t)(lo / kBN);
     e[kPlanBad] = bad ? 1 : 0;
+    e[kPlanQ0] = 0;
 }
 
 hipError_t launch_plan(int32_t* plan, const int32_t* cu, int32_t n_seqs, int64_t T,
@@ -99,6 +101,65 @@ hipError_t launch_plan(int32_t* plan, const int32_t* cu, int32_t n_seqs, int64_t
     LaunchScope scope("plan", s);
     hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(64), 0, s, plan, cu, n_seqs, T, max_seqlen,
                        w_pretrained);
+    return hipGetLastError();
+}
+
+// Plan of a chunk call ([TW] §三: new rows appended to a cache of
+// standard-RoPE keys).  Sequence b has L_b = seqlens_k[b] keys in the cache,
+// its own C_b = cu_q[b + 1] - cu_q[b] new rows among them, and one G from L_b
+// ([BT] §3.1).  Its key tiles cover [0, L_b); its query rows are positions
+// [L_b - C_b, L_b).  A sequence with no new row gets length 0 (no work).  If
+// the device arrays break their contract (cu_q not starting at 0 or ending at
+// Tq, C_b outside [0, max_seqlen_q], L_b outside [C_b, max_seqlen_k]) every
+// length is 0 and the bad flag is raised.
+__global__ void plan_chunk_kernel(int32_t* __restrict__ plan, const int32_t* __restrict__ cu_q,
+                                  const int32_t* __restrict__ seqlens_k, int32_t B, int64_t Tq,
+                                  int32_t max_seqlen_q, int32_t max_seqlen_k,
+                                  int32_t w_pretrained) {
+    if (threadIdx.x != 0 || blockIdx.x != 0) return;
+    bool bad = cu_q && (cu_q[0] != 0 || (int64_t)cu_q[B] != Tq);
+    for (int b = 0; b < B && !bad; ++b) {
+        const int64_t C = cu_q ? (int64_t)cu_q[b + 1] - cu_q[b] : Tq;
+        const int32_t L = seqlens_k[b];
+        if (C < 0 || C > max_seqlen_q || L < C || L > max_seqlen_k) bad = true;
+    }
+    int64_t pad = 0, lo = 0;
+    for (int b = 0; b < B; ++b) {
+        int32_t* e = plan + b * kPlanFields;
+        const int32_t start = cu_q ? cu_q[b] : 0;
+        const int32_t C = cu_q ? cu_q[b + 1] - cu_q[b] : (int32_t)Tq;
+        const int32_t len = (bad || C == 0) ? 0 : seqlens_k[b];
+        e[kPlanStart] = bad ? 0 : start;
+        e[kPlanLen] = len;
+        e[kPlanG] = (int32_t)group_size(len, w_pretrained);
+        e[kPlanPadOff] = (int32_t)pad;
+        e[kPlanLoOff] = (int32_t)lo;
+        e[kPlanTile0] = (int32_t)(pad / kBN);
+        e[kPlanLoTile0] = (int32_t)(lo / kBN);
+        e[kPlanBad] = 0;
+        e[kPlanQ0] = len - (len ? C : 0);
+        pad += (len + kBN - 1) / kBN * kBN;
+        const int32_t nlo = len < kPreciseRows ? len : kPreciseRows;
+        lo += (nlo + kBN - 1) / kBN * kBN;
+    }
+    int32_t* e = plan + B * kPlanFields;
+    e[kPlanStart] = (int32_t)Tq;
+    e[kPlanLen] = 0;
+    e[kPlanG] = 1;
+    e[kPlanPadOff] = (int32_t)pad;
+    e[kPlanLoOff] = (int32_t)lo;
+    e[kPlanTile0] = (int32_t)(pad / kBN);
+    e[kPlanLoTile0] = (int32_t)(lo / kBN);
+    e[kPlanBad] = bad ? 1 : 0;
+    e[kPlanQ0] = 0;
+}
+
+hipError_t launch_plan_chunk(int32_t* plan, const int32_t* cu_q, const int32_t* seqlens_k,
+                             int32_t B, int64_t Tq, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                             int32_t w_pretrained, hipStream_t s) {
+    LaunchScope scope("plan", s);
+    hipLaunchKernelGGL(plan_chunk_kernel, dim3(1), dim3(64), 0, s, plan, cu_q, seqlens_k, B, Tq,
+                       max_seqlen_q, max_seqlen_k, w_pretrained);
     return hipGetLastError();
 }
 
@@ -129,6 +190,8 @@ __host__ __device__ constexpr int vt_perm16(int p) {
 // looping over kv heads so each (position, pair) angle is computed once):
 //   KS[g][row]  = R(n) k_n            (standard RoPE, [TW] §二), fp16
 //   KR[g][row]  = R(f(n)) k_n         (remapped RoPE, [BT] §3.1; only if G > 1), fp16
+// In a chunk call the source rows are cache rows c_n = R(n) k_n, so
+// KS = c_n and KR = R(f(n) - n) c_n (the correction rotation of [BT] §3.3).
 //   KS_lo/KR_lo = f16(x - f16(x))     for n < kPreciseRows (split precision)
 //   VT[g][tile][d][key']              V tile transposed to fp16, keys in vt_perm16 order
 //   k_rot_out[tok][g] = KS row        (optional, the caller's cache layout)
@@ -138,6 +201,7 @@ __global__ __launch_bounds__(256) void kv_prepass_bf16_kernel(PrefillArgs a) {
     constexpr int HALF = D / 2;
     constexpr int TPC = D / 8;  // pairs per thread: 4 threads per key row
     __shared__ bf16 vs[kBN * (D + 2)];
+    __shared__ int64_t vrow[kBN];
 
     const int32_t* plan = (const int32_t*)((char*)a.ws + a.lay.plan);
     f16* KS = (f16*)((char*)a.ws + a.lay.ks);
@@ -156,20 +220,30 @@ __global__ __launch_bounds__(256) void kv_prepass_bf16_kernel(PrefillArgs a) {
     const int32_t start = e[kPlanStart], len = e[kPlanLen], G = e[kPlanG];
     const bool bif = a.bifocal && G > 1;
     const int32_t n0 = (tile - e[kPlanTile0]) * kBN;  // first position of the tile
+    const bool cache = a.chunked != 0;
+    // source row of position nn < len: the packed input, or the cache
+    auto src_row = [&](int32_t nn) -> int64_t {
+        if (!cache) return (int64_t)start + nn;
+        if (!a.block_table) return (int64_t)s * a.S_max + nn;
+        int32_t pg = a.block_table[(int64_t)s * a.bt_stride + (nn >> a.page_shift)];
+        pg = pg < 0 ? 0 : (pg >= a.n_pages ? a.n_pages - 1 : pg);
+        return ((int64_t)pg << a.page_shift) | (nn & ((1 << a.page_shift) - 1));
+    };
 
     // ---- keys: thread (r, c) rotates pairs [c*TPC, (c+1)*TPC) of row r ----
     const int r = threadIdx.x / 4, c = threadIdx.x % 4;
     const int32_t n = n0 + r;
     const bool valid = n < len;
     const bool lo_row = n < kPreciseRows;
+    const int64_t krow = valid ? src_row(n) : 0;
     float cs[TPC], sn[TPC], cr[TPC], sr[TPC];
     if (valid) {
         const int32_t fn = remap(n, G);
 #pragma unroll
         for (int u = 0; u < TPC; ++u) {
             const double rv = rope_rev(a.tab, c * TPC + u);
-            rope_cs(n, rv, cs[u], sn[u]);
-            if (bif) rope_cs(fn, rv, cr[u], sr[u]);
+            rope_cs(cache ? 0 : n, rv, cs[u], sn[u]);
+            if (bif) rope_cs(cache ? fn - n : fn, rv, cr[u], sr[u]);
         }
     }
     for (int g = 0; g < a.Hkv; ++g) {
@@ -177,7 +251,7 @@ __global__ __launch_bounds__(256) void kv_prepass_bf16_kernel(PrefillArgs a) {
         f16 ls0[TPC], ls1[TPC], lr0[TPC], lr1[TPC];
         bf16 kb0[TPC], kb1[TPC];
         if (valid) {
-            const bf16* src = k + ((int64_t)(start + n) * a.Hkv + g) * D + c * TPC;
+            const bf16* src = k + (krow * a.Hkv + g) * D + c * TPC;
 #pragma unroll
             for (int u = 0; u < TPC; ++u) {
                 const float x0 = (float)src[u], x1 = (float)src[u + HALF];
@@ -249,13 +323,16 @@ __global__ __launch_bounds__(256) void kv_prepass_bf16_kernel(PrefillArgs a) {
     }
 
     // ---- values: transpose each head's [kBN][D] tile through LDS ----
+    // (source rows of the tile's positions shared through LDS; the first
+    // barrier of the loop publishes them)
+    if (c == 0) vrow[r] = krow;
     for (int g = 0; g < a.Hkv; ++g) {
         __syncthreads();
         for (int idx = threadIdx.x; idx < kBN * D; idx += 256) {
             const int rr = idx / D, dd = idx % D;
             const int32_t nn = n0 + rr;
             vs[rr * (D + 2) + dd] =
-                nn < len ? v[((int64_t)(start + nn) * a.Hkv + g) * D + dd] : (bf16)0.0f;
+                nn < len ? v[(vrow[rr] * a.Hkv + g) * D + dd] : (bf16)0.0f;
         }
         __syncthreads();
         f16* dst = VT + ((int64_t)g * (a.lay.T_pad / kBN) + tile) * vtile_elems(D);

@@ -154,3 +154,35 @@ def decode_16step_cache():
     lens = [32761 + s for s in range(16)]
     queries = [decode_query(1, 32, 128, seed=4 + 100 * (s + 1)) for s in range(16)]
     return queries, k, v, lens, DECODE_PARAMS
+
+
+@dataclasses.dataclass
+class ChunkCase:
+    name: str
+    q: torch.Tensor  # [Tq, Hq, d] raw: the chunks' new rows, packed
+    k_cache: torch.Tensor  # [B, S_max, Hkv, d] standard-RoPE keys (the chunks' own included)
+    v_cache: torch.Tensor  # [B, S_max, Hkv, d]
+    seqlens: List[int]  # L_b: keys of sequence b; its chunk is positions L_b - C_b .. L_b - 1
+    cu_q: Optional[List[int]]  # chunk offsets in q (None: one chunk)
+    params: Params
+
+
+def chunk_inputs(chunks: List[int], seqlens: List[int], S_max: int, Hq: int, Hkv: int, d: int,
+                 *, seed: int, dtype=torch.bfloat16):
+    """Packed chunk queries [sum(chunks), Hq, d] and caches [B, S_max, Hkv, d]."""
+    g = torch.Generator("cpu").manual_seed(seed)
+    q = _randn(g, (sum(chunks), Hq, d), 1.0, dtype)
+    k = _randn(g, (len(seqlens), S_max, Hkv, d), 1.0, dtype)
+    v = _randn(g, (len(seqlens), S_max, Hkv, d), 1.0, dtype)
+    cu = [0]
+    for c in chunks:
+        cu.append(cu[-1] + c)
+    return q, k, v, cu
+
+
+def chunk_128k() -> ChunkCase:
+    """A chunk of 4096 new rows (32 q heads, 8 kv heads, d=128) appended to a
+    cache of 126976 keys: the chunk is positions 126976 .. 131071 of a sequence
+    of L = 131072 (G = 4), w_local 2048."""
+    q, k, v, _ = chunk_inputs([4096], [131072], 131072, 32, 8, 128, seed=6)
+    return ChunkCase("chunk4096_L131072", q, k, v, [131072], None, DECODE_PARAMS)

@@ -94,6 +94,20 @@ def lib() -> ctypes.CDLL:
                                               _i64, _i32, _i32, _i32, _i32,
                                               ctypes.POINTER(jl_params), ctypes.c_int, _vp,
                                               ctypes.c_size_t, _vp]
+        L.jl_bifocal_prefill_chunk_workspace.restype = ctypes.c_int
+        L.jl_bifocal_prefill_chunk_workspace.argtypes = [_i32, _i32, _i32, _i32, _i32,
+                                                         ctypes.c_int,
+                                                         ctypes.POINTER(ctypes.c_size_t)]
+        L.jl_bifocal_prefill_chunk.restype = ctypes.c_int
+        L.jl_bifocal_prefill_chunk.argtypes = [_vp, _vp, _vp, _vp, _i64, _i32, _vp, _vp, _vp,
+                                               _i32, _i32, _i64, _i32, _i32, _i32,
+                                               ctypes.POINTER(jl_params), ctypes.c_int, _vp,
+                                               ctypes.c_size_t, _vp]
+        L.jl_bifocal_prefill_chunk_paged.restype = ctypes.c_int
+        L.jl_bifocal_prefill_chunk_paged.argtypes = [_vp, _vp, _vp, _vp, _i64, _i32, _vp, _vp,
+                                                     _vp, _vp, _i32, _i32, _i32, _i64, _i32,
+                                                     _i32, _i32, _i32, ctypes.POINTER(jl_params),
+                                                     ctypes.c_int, _vp, ctypes.c_size_t, _vp]
         L.jl_debug_index_math.restype = ctypes.c_int
         L.jl_debug_index_math.argtypes = [_i64, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp]
         L.jl_profile_enable.restype = ctypes.c_int
@@ -330,6 +344,85 @@ def bifocal_decode_paged(q: torch.Tensor, k_pages: torch.Tensor, v_pages: torch.
         page_size, n_pages, bt.shape[1], Hq, Hkv, d, ctypes.byref(p), _dtype(q),
         _dev(ws, "workspace"), ws.numel() * ws.element_size(), _stream()),
         "jl_bifocal_decode_paged")
+    return o, lse
+
+
+def prefill_chunk_workspace_bytes(B: int, max_seqlen_k: int, Hq: int, Hkv: int, d: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().jl_bifocal_prefill_chunk_workspace(B, max_seqlen_k, Hq, Hkv, d, 1,
+                                                    ctypes.byref(n)),
+           "jl_bifocal_prefill_chunk_workspace")
+    return n.value
+
+
+def _chunk_common(q, seqlens_k, cu_seqlens_q, max_seqlen_q, max_seqlen_k, dev, out, lse_out):
+    Tq, Hq, d = q.shape
+    cu, B, max_q = _varlen(cu_seqlens_q, max_seqlen_q, Tq, dev)
+    sl, max_k = _seqlens(seqlens_k, max_seqlen_k, dev)
+    if sl.numel() != B:
+        raise ValueError("seqlens_k needs one entry per chunk")
+    o = out if out is not None else torch.empty_like(q)
+    lse = lse_out if lse_out is not None else torch.empty((Hq, Tq), dtype=torch.float32,
+                                                          device=dev)
+    return cu, B, max(int(max_q), 1), sl, max_k, o, lse
+
+
+def bifocal_prefill_chunk(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                          seqlens_k: Union[Sequence[int], torch.Tensor], *, w_pretrained: int,
+                          w_local: int, rope_base: float, softmax_scale: float,
+                          bifocal: bool = True, cu_seqlens_q=None,
+                          max_seqlen_q: Optional[int] = None,
+                          max_seqlen_k: Optional[int] = None,
+                          workspace: Optional[torch.Tensor] = None,
+                          out: Optional[torch.Tensor] = None,
+                          lse_out: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Chunked prefill ([TW] §三, [BT] §3.1, §3.3): q [Tq, Hq, d] raw, the new
+    rows of each sequence packed by cu_seqlens_q (None: one chunk); caches
+    [B, S_max, Hkv, d] bf16 of standard-RoPE keys holding seqlens_k[b] keys,
+    the chunk's own included.  Returns (o [Tq, Hq, d], lse [Hq, Tq])."""
+    dev = q.device
+    Hq, d = q.shape[1], q.shape[2]
+    S_max, Hkv = k_cache.shape[1], k_cache.shape[2]
+    cu, B, max_q, sl, max_k, o, lse = _chunk_common(q, seqlens_k, cu_seqlens_q, max_seqlen_q,
+                                                    max_seqlen_k, dev, out, lse_out)
+    ws = _workspace(prefill_chunk_workspace_bytes(B, max_k, Hq, Hkv, d), dev, workspace)
+    p = _params(w_pretrained, w_local, rope_base, softmax_scale, bifocal)
+    _check(lib().jl_bifocal_prefill_chunk(
+        _dev(o, "o"), _dev(lse, "lse"), _dev(q, "q"), None if cu is None else _dev(cu, "cu"),
+        q.shape[0], max_q, _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+        _dev(sl, "seqlens_k"), B, max_k, S_max, Hq, Hkv, d, ctypes.byref(p), _dtype(q),
+        _dev(ws, "workspace"), ws.numel() * ws.element_size(), _stream()),
+        "jl_bifocal_prefill_chunk")
+    return o, lse
+
+
+def bifocal_prefill_chunk_paged(q: torch.Tensor, k_pages: torch.Tensor, v_pages: torch.Tensor,
+                                block_table: torch.Tensor,
+                                seqlens_k: Union[Sequence[int], torch.Tensor], *,
+                                w_pretrained: int, w_local: int, rope_base: float,
+                                softmax_scale: float, bifocal: bool = True, cu_seqlens_q=None,
+                                max_seqlen_q: Optional[int] = None,
+                                max_seqlen_k: Optional[int] = None,
+                                workspace: Optional[torch.Tensor] = None,
+                                out: Optional[torch.Tensor] = None,
+                                lse_out: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """bifocal_prefill_chunk on a paged cache: k_pages / v_pages
+    [n_pages, page_size, Hkv, d] bf16, block_table [B, bt_stride] int32."""
+    dev = q.device
+    Hq, d = q.shape[1], q.shape[2]
+    n_pages, page_size, Hkv = k_pages.shape[0], k_pages.shape[1], k_pages.shape[2]
+    cu, B, max_q, sl, max_k, o, lse = _chunk_common(q, seqlens_k, cu_seqlens_q, max_seqlen_q,
+                                                    max_seqlen_k, dev, out, lse_out)
+    bt = block_table.to(device=dev, dtype=torch.int32).contiguous()
+    ws = _workspace(prefill_chunk_workspace_bytes(B, max_k, Hq, Hkv, d), dev, workspace)
+    p = _params(w_pretrained, w_local, rope_base, softmax_scale, bifocal)
+    _check(lib().jl_bifocal_prefill_chunk_paged(
+        _dev(o, "o"), _dev(lse, "lse"), _dev(q, "q"), None if cu is None else _dev(cu, "cu"),
+        q.shape[0], max_q, _dev(k_pages, "k_pages"), _dev(v_pages, "v_pages"),
+        _dev(bt, "block_table"), _dev(sl, "seqlens_k"), B, max_k, page_size, n_pages,
+        bt.shape[1], Hq, Hkv, d, ctypes.byref(p), _dtype(q), _dev(ws, "workspace"),
+        ws.numel() * ws.element_size(), _stream()),
+        "jl_bifocal_prefill_chunk_paged")
     return o, lse
 
 

@@ -209,3 +209,65 @@ def _paged(**kw):
 def test_paged_decode_validation(kw, status):
     assert _paged(**kw) == status
     assert jlb.lib().jl_last_error()
+
+
+def _chunk(paged=False, **kw):
+    a = dict(o=FAKE, lse=FAKE * 2, q=FAKE * 3, cu=FAKE * 4, Tq=512, max_q=512, kc=FAKE * 5,
+             vc=FAKE * 6, bt=FAKE * 9, sl=FAKE * 7, B=2, max_k=4096, S_max=4096, page=64,
+             n_pages=200, bt_stride=64, Hq=32, Hkv=8, d=128, params=_params(), dtype=1,
+             ws=FAKE * 8, ws_bytes=1 << 40, stream=None)
+    a.update(kw)
+    p = a["params"]
+    pp = None if p is None else ctypes.byref(p)
+    L = jlb.lib()
+    if paged:
+        return L.jl_bifocal_prefill_chunk_paged(
+            a["o"], a["lse"], a["q"], a["cu"], a["Tq"], a["max_q"], a["kc"], a["vc"], a["bt"],
+            a["sl"], a["B"], a["max_k"], a["page"], a["n_pages"], a["bt_stride"], a["Hq"],
+            a["Hkv"], a["d"], pp, a["dtype"], a["ws"], a["ws_bytes"], a["stream"])
+    return L.jl_bifocal_prefill_chunk(
+        a["o"], a["lse"], a["q"], a["cu"], a["Tq"], a["max_q"], a["kc"], a["vc"], a["sl"], a["B"],
+        a["max_k"], a["S_max"], a["Hq"], a["Hkv"], a["d"], pp, a["dtype"], a["ws"],
+        a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("paged", [False, True])
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), 1), (dict(sl=None), 1), (dict(kc=None), 1), (dict(params=None), 1),
+    (dict(B=0), 1), (dict(B=70000), 2), (dict(Tq=0), 1), (dict(max_q=0), 1),
+    (dict(max_q=513), 1), (dict(max_q=5000, Tq=6000), 1), (dict(cu=None), 1),
+    (dict(cu=None, B=1, max_q=100), 1), (dict(max_k=0), 1), (dict(B=600, max_k=4000000, S_max=4000000, bt_stride=70000), 2),
+    (dict(Hq=30), 1), (dict(Hq=32, Hkv=64), 1), (dict(dtype=0), 2), (dict(d=96), 2),
+    (dict(o=FAKE * 3), 1), (dict(ws=FAKE * 8 + 4), 1), (dict(ws_bytes=100), 3),
+    (dict(params=_params(w_pretrained=0)), 1),
+])
+def test_chunk_validation(paged, kw, status):
+    assert _chunk(paged, **kw) == status
+    assert jlb.lib().jl_last_error()
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(S_max=4095), 1), (dict(S_max=0, max_k=1), 1),
+])
+def test_chunk_flat_validation(kw, status):
+    assert _chunk(False, **kw) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(bt=None), 1), (dict(page=48), 1), (dict(page=8), 1), (dict(n_pages=0), 1),
+    (dict(bt_stride=63), 1), (dict(n_pages=1 << 40), 1),
+])
+def test_chunk_paged_validation(kw, status):
+    assert _chunk(True, **kw) == status
+
+
+def test_chunk_workspace_query():
+    n = ctypes.c_size_t(0)
+    L = jlb.lib()
+    assert L.jl_bifocal_prefill_chunk_workspace(1, 131072, 32, 8, 128, 1, ctypes.byref(n)) == 0
+    n1 = n.value
+    assert L.jl_bifocal_prefill_workspace(131072, 1, 32, 8, 128, 1, ctypes.byref(n)) == 0
+    assert n1 == n.value  # one sequence of 128K keys: the prefill workspace
+    assert L.jl_bifocal_prefill_chunk_workspace(1, 131072, 32, 8, 128, 0, ctypes.byref(n)) == 2
+    assert L.jl_bifocal_prefill_chunk_workspace(0, 10, 32, 8, 128, 1, ctypes.byref(n)) == 1
+    assert L.jl_bifocal_prefill_chunk_workspace(1, 10, 32, 8, 128, 1, None) == 1
