@@ -81,6 +81,16 @@ def _load():
                                           ctypes.c_int64, ctypes.c_int64, ctypes.c_double,
                                           ctypes.c_double, ctypes.c_int, _i64p, ctypes.c_int64,
                                           ctypes.c_int]
+        lib.jlo_e4m3_value.restype = ctypes.c_double
+        lib.jlo_e4m3_value.argtypes = [ctypes.c_uint8]
+        lib.jlo_e4m3_encode.restype = ctypes.c_uint8
+        lib.jlo_e4m3_encode.argtypes = [ctypes.c_double]
+        lib.jlo_e4m3_dequant.restype = None
+        lib.jlo_e4m3_dequant.argtypes = [_f64p, _vp, _vp, ctypes.c_int64, ctypes.c_int,
+                                         ctypes.c_int]
+        lib.jlo_e4m3_quant.restype = None
+        lib.jlo_e4m3_quant.argtypes = [_vp, _vp, ctypes.c_int, _vp, ctypes.c_int64, ctypes.c_int,
+                                       ctypes.c_int]
         _lib = lib
     return _lib
 
@@ -266,3 +276,60 @@ def prefill_chunk(q, k_cache, v_cache, seqlens, *, w_pretrained, w_local, rope_b
     if rc != 0:
         raise ValueError("oracle chunked prefill rejected its arguments")
     return o, lse
+
+
+# ---- fp8 (OCP E4M3) KV cache ------------------------------------------------
+
+def e4m3_value(code: int) -> float:
+    """Value of one OCP E4M3 code (bias 7, subnormals, S.1111.111 = NaN)."""
+    return float(_load().jlo_e4m3_value(int(code)))
+
+
+def e4m3_encode(x: float) -> int:
+    """Nearest E4M3 code, ties to even, saturating at +-448."""
+    return int(_load().jlo_e4m3_encode(float(x)))
+
+
+def _codes(a):
+    try:
+        import torch
+
+        if isinstance(a, torch.Tensor):
+            a = a.detach().cpu().contiguous().view(torch.uint8).numpy()
+    except ImportError:  # pragma: no cover
+        pass
+    a = np.ascontiguousarray(a)
+    assert a.dtype == np.uint8, "fp8 caches are passed as their uint8 codes"
+    return a
+
+
+def e4m3_dequant(codes, scale) -> np.ndarray:
+    """fp64 values scale[h] * E4M3(code) of a [..., H, d] cache."""
+    c = _codes(codes)
+    H, d = c.shape[-2], c.shape[-1]
+    sc = np.ascontiguousarray(np.asarray(scale, dtype=np.float32).reshape(H))
+    out = np.empty(c.shape, dtype=np.float64)
+    _load().jlo_e4m3_dequant(_ptr(out, _f64p), _ptr(c), _ptr(sc), c.size // (H * d), H, d)
+    return out
+
+
+def e4m3_quant(x, scale) -> np.ndarray:
+    """E4M3 codes of x / scale[h] for a [..., H, d] cache (fp32 quotient, RNE,
+    saturating); returns uint8 of x's shape."""
+    xa, dt = _host(x)
+    H, d = xa.shape[-2], xa.shape[-1]
+    sc = np.ascontiguousarray(np.asarray(scale, dtype=np.float32).reshape(H))
+    out = np.empty(xa.shape, dtype=np.uint8)
+    _load().jlo_e4m3_quant(_ptr(out), _ptr(xa), dt, _ptr(sc), xa.size // (H * d), H, d)
+    return out
+
+
+def decode_fp8(q, k_codes, v_codes, k_scale, v_scale, seqlens, **kw):
+    """Bifocal decode ([TW] §三, [BT] §3.3) on an fp8 cache: the keys and values
+    are scale[h] * E4M3(code); the rest is ``decode`` on those fp64 values."""
+    kc = e4m3_dequant(k_codes, k_scale)
+    vc = e4m3_dequant(v_codes, v_scale)
+    qa, _ = _host(q)
+    if qa.dtype == np.uint16:  # bf16 bits -> fp64, exact
+        qa = (qa.astype(np.uint32) << 16).view(np.float32)
+    return decode(qa.astype(np.float64), kc, vc, seqlens, **kw)

@@ -487,3 +487,58 @@ int jlo_prefill_chunk(double* o_sel, double* lse_sel, const void* q, const void*
     }
     return 0;
 }
+
+/*
+ * fp8 KV cache (a cache format beside the pages' method: the correction
+ * rotation is applied to the dequantized keys, so the method is unchanged).
+ * Format: OCP 8-bit floating point (OFP8), E4M3: 1 sign bit, 4 exponent bits
+ * with bias 7, 3 mantissa bits; exponent 0 holds subnormals m * 2^-9; there
+ * are no infinities; S.1111.111 is NaN, so the largest finite value is
+ * S.1111.110 = 448.
+ */
+double jlo_e4m3_value(uint8_t c) {
+    const int s = c >> 7, e = (c >> 3) & 15, m = c & 7;
+    if (e == 15 && m == 7) return NAN;
+    const double mag = e == 0 ? ldexp((double)m, -9) : ldexp(1.0 + m / 8.0, e - 7);
+    return s ? -mag : mag;
+}
+
+/* Nearest E4M3 code to x: ties go to the even code (the one whose mantissa
+ * ends in 0), magnitudes beyond 448 saturate to +-448, NaN gives S.1111.111.
+ * Found by comparing |x| with every finite non-negative code. */
+uint8_t jlo_e4m3_encode(double x) {
+    const uint8_t sign = signbit(x) ? 0x80 : 0x00;
+    if (isnan(x)) return sign | 0x7F;
+    const double a = fabs(x);
+    if (a >= 448.0) return sign | 0x7E;
+    int best = 0;
+    double bd = a;  /* distance to code 0 */
+    for (int c = 1; c <= 0x7E; ++c) {
+        const double dd = fabs(jlo_e4m3_value((uint8_t)c) - a);
+        if (dd < bd || (dd == bd && (c & 1) == 0)) {
+            best = c;
+            bd = dd;
+        }
+    }
+    return sign | (uint8_t)best;
+}
+
+/* out[i] = scale[(i / d) % H] * value(code[i]) for a [N][H][d] cache (exact in fp64). */
+void jlo_e4m3_dequant(double* out, const uint8_t* code, const float* scale, int64_t N, int H,
+                      int d) {
+    for (int64_t i = 0; i < N * H * d; ++i)
+        out[i] = (double)scale[(i / d) % H] * jlo_e4m3_value(code[i]);
+}
+
+/* Quantization of a [N][H][d] cache with one scale per head:
+ * code = E4M3(x / scale[h]).  The quotient is formed in fp32 (a correctly
+ * rounded float division), the precision the device kernel divides in, so
+ * that both sides round the same number to a code. */
+void jlo_e4m3_quant(uint8_t* code, const void* x, int dtype, const float* scale, int64_t N, int H,
+                    int d) {
+    for (int64_t i = 0; i < N * H * d; ++i) {
+        const float xi = (float)load_elem(x, dtype, i);
+        const float qi = xi / scale[(i / d) % H];
+        code[i] = jlo_e4m3_encode((double)qi);
+    }
+}

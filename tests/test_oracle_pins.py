@@ -419,3 +419,85 @@ def test_chunk_batch_is_per_sequence():
     np.testing.assert_array_equal(l_s, lse[[25, 0, 9]])
     with pytest.raises(ValueError):
         oracle.prefill_chunk(q, kc, vc, [30, 11, 18], cu_seqlens_q=cu, **kw)  # chunk > length
+
+
+def _hex_rows(name):
+    rows = []
+    for line in open(os.path.join(os.path.dirname(__file__), "golden", name), encoding="utf-8"):
+        line = line.strip()
+        if line and not line.startswith("#"):
+            a, b, *_ = line.split()
+            rows.append((a, b))
+    return rows
+
+
+@pytest.mark.parametrize("code,value", _hex_rows("fp8_e4m3.txt"))
+def test_e4m3_values_golden(code, value):
+    got = oracle.e4m3_value(int(code, 16))
+    if value == "nan":
+        assert np.isnan(got)
+    else:
+        assert got == float(value) and np.signbit(got) == value.startswith("-")
+
+
+@pytest.mark.parametrize("x,code", _hex_rows("fp8_e4m3_rounding.txt"))
+def test_e4m3_rounding_golden(x, code):
+    assert oracle.e4m3_encode(float(x)) == int(code, 16)
+
+
+def test_e4m3_against_torch_float8():
+    """Every code's value, and round-to-nearest-even of in-range reals, agree
+    with torch's float8_e4m3fn conversions (an independent implementation of
+    the same OCP format)."""
+    import torch
+
+    ref = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).double().numpy()
+    got = np.array([oracle.e4m3_value(c) for c in range(256)])
+    fin = np.isfinite(ref)
+    assert np.array_equal(np.isnan(got), ~fin)
+    np.testing.assert_array_equal(got[fin], ref[fin])
+    rng = np.random.default_rng(5)
+    x = np.concatenate([rng.standard_normal(3000) * 40, rng.standard_normal(1000) * 0.01,
+                        (ref[fin][:-1] + ref[fin][1:]) / 2])
+    x = np.clip(x, -448, 448).astype(np.float32)
+    t = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    mine = np.array([oracle.e4m3_encode(float(v)) for v in x], dtype=np.uint8)
+    np.testing.assert_array_equal(mine, t)
+
+
+def test_e4m3_quant_dequant_roundtrip():
+    """Codes survive dequantize -> quantize with the same scale exactly
+    (scale a power of two, so value * scale / scale is exact), and the
+    quantizer picks the code nearest to x / scale."""
+    rng = np.random.default_rng(7)
+    codes = rng.integers(0, 256, size=(5, 3, 8), dtype=np.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 0x11  # no NaN codes
+    scale = np.array([0.25, 1.0, 8.0], dtype=np.float32)
+    vals = oracle.e4m3_dequant(codes, scale)
+    again = oracle.e4m3_quant(vals.astype(np.float32), scale)
+    zero = (codes & 0x7F) == 0
+    np.testing.assert_array_equal(again[~zero], codes[~zero])
+    x = rng.standard_normal((4, 3, 8)).astype(np.float32) * 30
+    q = oracle.e4m3_quant(x, scale)
+    back = oracle.e4m3_dequant(q, scale)
+    allv = np.array([oracle.e4m3_value(c) for c in range(0x7F)])
+    for idx in np.ndindex(x.shape):
+        t = min(abs(float(x[idx]) / scale[idx[1]]), 448.0)
+        assert abs(abs(back[idx]) / scale[idx[1]] - t) <= np.abs(allv - t).min() + 1e-12
+
+
+def test_decode_fp8_is_decode_of_dequantized_cache():
+    """fp8 decode = decode on scale * E4M3(code), the scale per kv head."""
+    rng = np.random.default_rng(11)
+    B, S, Hq, Hkv, d = 2, 30, 4, 2, 8
+    q = rng.standard_normal((B, Hq, d))
+    k8 = rng.integers(0, 0x7E, size=(B, S, Hkv, d), dtype=np.uint8)
+    v8 = rng.integers(0x80, 0xFE, size=(B, S, Hkv, d), dtype=np.uint8)
+    ks, vs = np.array([0.01, 0.02], np.float32), np.array([0.5, 0.25], np.float32)
+    kw = dict(w_pretrained=7, w_local=3, rope_base=1e4, softmax_scale=0.5)
+    o, lse = oracle.decode_fp8(q, k8, v8, ks, vs, [30, 12], **kw)
+    kd = np.vectorize(oracle.e4m3_value)(k8) * ks[None, None, :, None]
+    vd = np.vectorize(oracle.e4m3_value)(v8) * vs[None, None, :, None]
+    o2, l2 = oracle.decode(q, kd, vd, [30, 12], **kw)
+    np.testing.assert_array_equal(o, o2)
+    np.testing.assert_array_equal(lse, l2)
