@@ -320,16 +320,40 @@ def bench_decode(jl, inputs, torch, iters):
         torch.cuda.synchronize()
         return ev0.elapsed_time(ev1) * 1e3 / n
 
+    # fp8 (E4M3) form of the same workload: four copies of the quantized cache
+    _, k8, v8, ks, vs, _, _ = inputs.decode_fp8_128k()
+    copies8 = [(k8.cuda(), v8.cuda()) for _ in range(4)]
+    ks, vs = ks.cuda(), vs.cuda()
+
+    def run_fp8(bifocal, n):
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        ev0.record()
+        for i in range(n):
+            kc8, vc8 = copies8[i % 4]
+            jl.bifocal_decode_fp8(q, kc8, vc8, ks, vs, sl, max_seqlen_k=L,
+                                  w_pretrained=p.w_pretrained, w_local=p.w_local,
+                                  rope_base=p.rope_base, softmax_scale=p.softmax_scale,
+                                  bifocal=bifocal, workspace=ws, out=o, lse_out=lse)
+        ev1.record()
+        torch.cuda.synchronize()
+        return ev0.elapsed_time(ev1) * 1e3 / n
+
     run(True, 10)
     run(False, 10)
+    run_fp8(True, 10)
+    run_fp8(False, 10)
     for page in pools:
         run_paged(page, 10)
     tb, tp, tpg = [], [], {page: [] for page in pools}
+    t8b, t8p = [], []
     for _ in range(4):
         tb.append(run(True, iters // 4))
         tp.append(run(False, iters // 4))
         for page in pools:
             tpg[page].append(run_paged(page, iters // 4))
+        t8b.append(run_fp8(True, iters // 4))
+        t8p.append(run_fp8(False, iters // 4))
     jl.profile_enable(True)
     run(True, 20)
     prof = jl.profile_read()
@@ -350,6 +374,10 @@ def bench_decode(jl, inputs, torch, iters):
         "split_kernel_GBps": round(nbytes / (split_us * 1e-6) / 1e9, 1),
         "split_kernel_traffic": _profiled_traffic("traffic_decode_split_L131072.md"),
         "paged_us_per_token": {"page_%d" % page: round(min(t), 2) for page, t in tpg.items()},
+        "fp8": {"us_per_token": round(min(t8b), 2), "plain_us_per_token": round(min(t8p), 2),
+                "overhead_pct": round(100.0 * (min(t8b) - min(t8p)) / min(t8p), 2),
+                "kv_bytes_per_step": nbytes // 2,
+                "achieved_GBps": round(nbytes / 2 / (min(t8b) * 1e-6) / 1e9, 1)},
         "kernels": {n: {"launches": c2, "avg_us": round(ms * 1e3 / max(c2, 1), 2)}
                     for n, (c2, ms) in sorted(prof.items())},
     }

@@ -205,6 +205,51 @@ jl_status jl_bifocal_decode_paged(void* o, float* lse, const void* q, const void
                                   int32_t Hkv, int32_t d, const jl_params* params, jl_dtype dtype,
                                   void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * jl_bifocal_decode on an fp8 KV cache, for decode bandwidth: k_cache and
+ * v_cache hold OCP E4M3 codes (1 byte per element, the OCP 8-bit floating
+ * point format: bias 7, subnormals, no infinities), and element (b, j, h, x)
+ * stands for k_scale[h] * E4M3(code) (v_scale[h] for values).  The scores,
+ * the correction rotation ([TW] §三, [BT] §3.3) and the outputs are those
+ * of jl_bifocal_decode on these dequantized values: the rotation is applied
+ * after dequantization, so the cache format leaves the method unchanged.
+ * Codes widen exactly to bf16; the key scale is folded into the query and
+ * the value scale into the output.
+ *   q, o          bf16 [B][Hq][d]; lse float32 [B][Hq].
+ *   k_cache, v_cache  uint8 [B][S_max][Hkv][d] E4M3 codes, read-only.
+ *   k_scale, v_scale  device float32 [Hkv].
+ *   workspace     jl_bifocal_decode_workspace(..., JL_DTYPE_BF16) bytes.
+ * NaN codes (S.1111.111) are the caller's to avoid (jl_kv_quantize_fp8
+ * writes them only for NaN input).  d in {64, 128}, Hq / Hkv <= 16.
+ */
+jl_status jl_bifocal_decode_fp8(void* o, float* lse, const void* q, const void* k_cache,
+                                const void* v_cache, const float* k_scale, const float* v_scale,
+                                const int32_t* seqlens_k, int32_t batch, int32_t max_seqlen_k,
+                                int64_t S_max, int32_t Hq, int32_t Hkv, int32_t d,
+                                const jl_params* params, void* workspace, size_t workspace_bytes,
+                                void* stream);
+
+/* jl_bifocal_decode_fp8 on a paged pool of E4M3 pages [n_pages][page_size][Hkv][d],
+ * addressed as in jl_bifocal_decode_paged. */
+jl_status jl_bifocal_decode_fp8_paged(void* o, float* lse, const void* q, const void* k_pages,
+                                      const void* v_pages, const float* k_scale,
+                                      const float* v_scale, const int32_t* block_table,
+                                      const int32_t* seqlens_k, int32_t batch,
+                                      int32_t max_seqlen_k, int32_t page_size, int64_t n_pages,
+                                      int32_t bt_stride, int32_t Hq, int32_t Hkv, int32_t d,
+                                      const jl_params* params, void* workspace,
+                                      size_t workspace_bytes, void* stream);
+
+/*
+ * Writes fp8 cache rows: out[t][h][x] = E4M3(x[t][h][x] / scale[h]) with the
+ * quotient a correctly rounded fp32 division, rounded to the nearest code
+ * (ties to the even code) and saturated to +-448; NaN input gives a NaN code.
+ *   x      bf16 [ntok][H][d], 16-byte aligned;  out uint8 [ntok][H][d], 8-byte aligned.
+ *   scale  device float32 [H] (> 0).  d a multiple of 8.
+ */
+jl_status jl_kv_quantize_fp8(void* out, const void* x, const float* scale, int64_t ntok,
+                             int32_t H, int32_t d, void* stream);
+
 /* Bytes of device workspace the chunk calls below need for batch sequences
  * of at most max_seqlen_k keys (bf16 only). */
 jl_status jl_bifocal_prefill_chunk_workspace(int32_t batch, int32_t max_seqlen_k, int32_t Hq,

@@ -427,44 +427,96 @@ jl_status jl_bifocal_decode_workspace(int32_t batch, int32_t max_seqlen_k, int32
     return JL_OK;
 }
 
+// Shared body of the four decode entry points: flat or paged cache, bf16
+// (or f32) or fp8 codes.  Every check runs on the host before any launch.
+struct DecodeCall {
+    void* o;
+    float* lse;
+    const void* q;
+    const void* kc;
+    const void* vc;
+    const int32_t* seqlens_k;
+    int32_t batch, max_seqlen_k;
+    int64_t S_max;  // flat cache
+    const int32_t* block_table;  // paged cache (else nullptr)
+    int32_t page_size;
+    int64_t n_pages;
+    int32_t bt_stride;
+    int32_t fp8;
+    const float* k_scale;
+    const float* v_scale;
+    int32_t Hq, Hkv, d;
+};
+
+static jl_status decode_impl(const DecodeCall& c, const jl_params* params, jl_dtype dtype,
+                             void* workspace, size_t workspace_bytes, void* stream,
+                             const char* where) {
+    if (!c.o || !c.lse || !c.q || !c.kc || !c.vc || !c.seqlens_k || !workspace)
+        return fail(JL_ERR_INVALID_ARGUMENT, "null pointer argument");
+    jl_status st = check_params(params);
+    if (st != JL_OK) return st;
+    if (c.batch < 1 || c.max_seqlen_k < 1)
+        return fail(JL_ERR_INVALID_ARGUMENT, "batch and max_seqlen_k must be >= 1");
+    if (c.batch > 65535) return fail(JL_ERR_UNSUPPORTED, "batch above 65535");
+    const bool paged = c.block_table != nullptr;
+    if (paged) {
+        if (c.page_size < 16 || c.page_size > 65536 || (c.page_size & (c.page_size - 1)))
+            return fail(JL_ERR_INVALID_ARGUMENT, "page_size must be a power of two in [16, 65536]");
+        if (c.n_pages < 1) return fail(JL_ERR_INVALID_ARGUMENT, "n_pages must be >= 1");
+        if ((int64_t)c.bt_stride * c.page_size < c.max_seqlen_k)
+            return fail(JL_ERR_INVALID_ARGUMENT, "bt_stride * page_size < max_seqlen_k");
+    } else if (c.S_max < c.max_seqlen_k) {
+        return fail(JL_ERR_INVALID_ARGUMENT, "S_max < max_seqlen_k");
+    }
+    st = check_heads(c.Hq, c.Hkv);
+    if (st != JL_OK) return st;
+    if (c.Hq / c.Hkv > 16) return fail(JL_ERR_UNSUPPORTED, "decode supports Hq / Hkv <= 16");
+    st = check_dtype_d(dtype, c.d);
+    if (st != JL_OK) return st;
+    if ((paged || c.fp8) && dtype != JL_DTYPE_BF16)
+        return fail(JL_ERR_UNSUPPORTED, "paged and fp8 decode take bf16 queries");
+    if (paged) {
+        if (c.n_pages > (1LL << 40) / ((int64_t)c.page_size * c.Hkv * c.d))
+            return fail(JL_ERR_INVALID_ARGUMENT, "page pool too large");
+    } else if (c.S_max > (1LL << 40) / ((int64_t)c.batch * c.Hkv * c.d)) {
+        return fail(JL_ERR_INVALID_ARGUMENT, "cache too large");
+    }
+    if (c.o == c.q || c.o == c.kc || c.o == c.vc)
+        return fail(JL_ERR_INVALID_ARGUMENT, "outputs must not alias inputs");
+    if ((uintptr_t)workspace & 255) return fail(JL_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
+    const DecodeLayout lay = decode_layout(c.batch, c.max_seqlen_k, c.Hq, c.Hkv, c.d, dtype);
+    if (workspace_bytes < lay.total)
+        return fail(JL_ERR_WORKSPACE_TOO_SMALL,
+                    "workspace needs " + std::to_string(lay.total) + " bytes");
+    DecodeArgs a{};
+    a.q = c.q; a.kc = c.kc; a.vc = c.vc; a.o = c.o; a.lse = c.lse; a.seqlens = c.seqlens_k;
+    a.ws = workspace; a.lay = lay;
+    a.B = c.batch; a.max_seqlen_k = c.max_seqlen_k; a.Hq = c.Hq; a.Hkv = c.Hkv; a.d = c.d;
+    a.S_max = paged ? 0 : c.S_max;
+    a.w_pretrained = params->w_pretrained; a.w_local = params->w_local;
+    a.bifocal = params->bifocal; a.softmax_scale = params->softmax_scale;
+    a.tab = make_rope_freq(params->rope_base, c.d);
+    if (paged) {
+        a.block_table = c.block_table;
+        int shift = 0;
+        while ((1 << shift) < c.page_size) ++shift;
+        a.page_shift = shift; a.bt_stride = c.bt_stride; a.n_pages = c.n_pages;
+    }
+    a.fp8 = c.fp8; a.k_scale = c.k_scale; a.v_scale = c.v_scale;
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e = launch_decode(a, dtype, s);
+    if (e != hipSuccess) return hip_fail(e, "decode launch");
+    return finish(s, where);
+}
+
 jl_status jl_bifocal_decode(void* o, float* lse, const void* q, const void* k_cache,
                             const void* v_cache, const int32_t* seqlens_k, int32_t batch,
                             int32_t max_seqlen_k, int64_t S_max, int32_t Hq, int32_t Hkv,
                             int32_t d, const jl_params* params, jl_dtype dtype, void* workspace,
                             size_t workspace_bytes, void* stream) {
-    if (!o || !lse || !q || !k_cache || !v_cache || !seqlens_k || !workspace)
-        return fail(JL_ERR_INVALID_ARGUMENT, "null pointer argument");
-    jl_status st = check_params(params);
-    if (st != JL_OK) return st;
-    if (batch < 1 || max_seqlen_k < 1)
-        return fail(JL_ERR_INVALID_ARGUMENT, "batch and max_seqlen_k must be >= 1");
-    if (S_max < max_seqlen_k) return fail(JL_ERR_INVALID_ARGUMENT, "S_max < max_seqlen_k");
-    if (batch > 65535) return fail(JL_ERR_UNSUPPORTED, "batch above 65535");
-    st = check_heads(Hq, Hkv);
-    if (st != JL_OK) return st;
-    if (Hq / Hkv > 16) return fail(JL_ERR_UNSUPPORTED, "decode supports Hq / Hkv <= 16");
-    st = check_dtype_d(dtype, d);
-    if (st != JL_OK) return st;
-    if (S_max > (1LL << 40) / ((int64_t)batch * Hkv * d))
-        return fail(JL_ERR_INVALID_ARGUMENT, "cache too large");
-    if (o == q || o == k_cache || o == v_cache)
-        return fail(JL_ERR_INVALID_ARGUMENT, "outputs must not alias inputs");
-    if ((uintptr_t)workspace & 255) return fail(JL_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
-    const DecodeLayout lay = decode_layout(batch, max_seqlen_k, Hq, Hkv, d, dtype);
-    if (workspace_bytes < lay.total)
-        return fail(JL_ERR_WORKSPACE_TOO_SMALL,
-                    "workspace needs " + std::to_string(lay.total) + " bytes");
-    DecodeArgs a{};
-    a.q = q; a.kc = k_cache; a.vc = v_cache; a.o = o; a.lse = lse; a.seqlens = seqlens_k;
-    a.ws = workspace; a.lay = lay;
-    a.B = batch; a.max_seqlen_k = max_seqlen_k; a.Hq = Hq; a.Hkv = Hkv; a.d = d; a.S_max = S_max;
-    a.w_pretrained = params->w_pretrained; a.w_local = params->w_local;
-    a.bifocal = params->bifocal; a.softmax_scale = params->softmax_scale;
-    a.tab = make_rope_freq(params->rope_base, d);
-    hipStream_t s = (hipStream_t)stream;
-    hipError_t e = launch_decode(a, dtype, s);
-    if (e != hipSuccess) return hip_fail(e, "decode launch");
-    return finish(s, "jl_bifocal_decode");
+    DecodeCall c{o, lse, q, k_cache, v_cache, seqlens_k, batch, max_seqlen_k, S_max,
+                 nullptr, 0, 0, 0, 0, nullptr, nullptr, Hq, Hkv, d};
+    return decode_impl(c, params, dtype, workspace, workspace_bytes, stream, "jl_bifocal_decode");
 }
 
 jl_status jl_bifocal_decode_paged(void* o, float* lse, const void* q, const void* k_pages,
@@ -473,48 +525,55 @@ jl_status jl_bifocal_decode_paged(void* o, float* lse, const void* q, const void
                                   int32_t page_size, int64_t n_pages, int32_t bt_stride, int32_t Hq,
                                   int32_t Hkv, int32_t d, const jl_params* params, jl_dtype dtype,
                                   void* workspace, size_t workspace_bytes, void* stream) {
-    if (!o || !lse || !q || !k_pages || !v_pages || !block_table || !seqlens_k || !workspace)
+    if (!block_table) return fail(JL_ERR_INVALID_ARGUMENT, "null pointer argument");
+    DecodeCall c{o, lse, q, k_pages, v_pages, seqlens_k, batch, max_seqlen_k, 0,
+                 block_table, page_size, n_pages, bt_stride, 0, nullptr, nullptr, Hq, Hkv, d};
+    return decode_impl(c, params, dtype, workspace, workspace_bytes, stream,
+                       "jl_bifocal_decode_paged");
+}
+
+jl_status jl_bifocal_decode_fp8(void* o, float* lse, const void* q, const void* k_cache,
+                                const void* v_cache, const float* k_scale, const float* v_scale,
+                                const int32_t* seqlens_k, int32_t batch, int32_t max_seqlen_k,
+                                int64_t S_max, int32_t Hq, int32_t Hkv, int32_t d,
+                                const jl_params* params, void* workspace, size_t workspace_bytes,
+                                void* stream) {
+    if (!k_scale || !v_scale) return fail(JL_ERR_INVALID_ARGUMENT, "null pointer argument");
+    DecodeCall c{o, lse, q, k_cache, v_cache, seqlens_k, batch, max_seqlen_k, S_max,
+                 nullptr, 0, 0, 0, 1, k_scale, v_scale, Hq, Hkv, d};
+    return decode_impl(c, params, JL_DTYPE_BF16, workspace, workspace_bytes, stream,
+                       "jl_bifocal_decode_fp8");
+}
+
+jl_status jl_bifocal_decode_fp8_paged(void* o, float* lse, const void* q, const void* k_pages,
+                                      const void* v_pages, const float* k_scale,
+                                      const float* v_scale, const int32_t* block_table,
+                                      const int32_t* seqlens_k, int32_t batch,
+                                      int32_t max_seqlen_k, int32_t page_size, int64_t n_pages,
+                                      int32_t bt_stride, int32_t Hq, int32_t Hkv, int32_t d,
+                                      const jl_params* params, void* workspace,
+                                      size_t workspace_bytes, void* stream) {
+    if (!k_scale || !v_scale || !block_table)
         return fail(JL_ERR_INVALID_ARGUMENT, "null pointer argument");
-    jl_status st = check_params(params);
-    if (st != JL_OK) return st;
-    if (batch < 1 || max_seqlen_k < 1)
-        return fail(JL_ERR_INVALID_ARGUMENT, "batch and max_seqlen_k must be >= 1");
-    if (batch > 65535) return fail(JL_ERR_UNSUPPORTED, "batch above 65535");
-    if (page_size < 16 || page_size > 65536 || (page_size & (page_size - 1)))
-        return fail(JL_ERR_INVALID_ARGUMENT, "page_size must be a power of two in [16, 65536]");
-    if (n_pages < 1) return fail(JL_ERR_INVALID_ARGUMENT, "n_pages must be >= 1");
-    if ((int64_t)bt_stride * page_size < max_seqlen_k)
-        return fail(JL_ERR_INVALID_ARGUMENT, "bt_stride * page_size < max_seqlen_k");
-    st = check_heads(Hq, Hkv);
-    if (st != JL_OK) return st;
-    if (Hq / Hkv > 16) return fail(JL_ERR_UNSUPPORTED, "decode supports Hq / Hkv <= 16");
-    st = check_dtype_d(dtype, d);
-    if (st != JL_OK) return st;
-    if (dtype != JL_DTYPE_BF16) return fail(JL_ERR_UNSUPPORTED, "paged decode is bf16 only");
-    if (n_pages > (1LL << 40) / ((int64_t)page_size * Hkv * d))
-        return fail(JL_ERR_INVALID_ARGUMENT, "page pool too large");
-    if (o == q || o == k_pages || o == v_pages)
-        return fail(JL_ERR_INVALID_ARGUMENT, "outputs must not alias inputs");
-    if ((uintptr_t)workspace & 255) return fail(JL_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
-    const DecodeLayout lay = decode_layout(batch, max_seqlen_k, Hq, Hkv, d, dtype);
-    if (workspace_bytes < lay.total)
-        return fail(JL_ERR_WORKSPACE_TOO_SMALL,
-                    "workspace needs " + std::to_string(lay.total) + " bytes");
-    DecodeArgs a{};
-    a.q = q; a.kc = k_pages; a.vc = v_pages; a.o = o; a.lse = lse; a.seqlens = seqlens_k;
-    a.ws = workspace; a.lay = lay;
-    a.B = batch; a.max_seqlen_k = max_seqlen_k; a.Hq = Hq; a.Hkv = Hkv; a.d = d; a.S_max = 0;
-    a.w_pretrained = params->w_pretrained; a.w_local = params->w_local;
-    a.bifocal = params->bifocal; a.softmax_scale = params->softmax_scale;
-    a.tab = make_rope_freq(params->rope_base, d);
-    a.block_table = block_table;
-    int shift = 0;
-    while ((1 << shift) < page_size) ++shift;
-    a.page_shift = shift; a.bt_stride = bt_stride; a.n_pages = n_pages;
+    DecodeCall c{o, lse, q, k_pages, v_pages, seqlens_k, batch, max_seqlen_k, 0,
+                 block_table, page_size, n_pages, bt_stride, 1, k_scale, v_scale, Hq, Hkv, d};
+    return decode_impl(c, params, JL_DTYPE_BF16, workspace, workspace_bytes, stream,
+                       "jl_bifocal_decode_fp8_paged");
+}
+
+jl_status jl_kv_quantize_fp8(void* out, const void* x, const float* scale, int64_t ntok,
+                             int32_t H, int32_t d, void* stream) {
+    if (!out || !x || !scale) return fail(JL_ERR_INVALID_ARGUMENT, "null pointer argument");
+    if (ntok < 1 || H < 1) return fail(JL_ERR_INVALID_ARGUMENT, "ntok and H must be >= 1");
+    if (d < 8 || d % 8) return fail(JL_ERR_INVALID_ARGUMENT, "d must be a positive multiple of 8");
+    if (ntok > (1LL << 40) / ((int64_t)H * d)) return fail(JL_ERR_INVALID_ARGUMENT, "too many elements");
+    if (((uintptr_t)out & 7) || ((uintptr_t)x & 15))
+        return fail(JL_ERR_INVALID_ARGUMENT, "out must be 8-byte and x 16-byte aligned");
+    if (out == x) return fail(JL_ERR_INVALID_ARGUMENT, "outputs must not alias inputs");
     hipStream_t s = (hipStream_t)stream;
-    hipError_t e = launch_decode(a, dtype, s);
-    if (e != hipSuccess) return hip_fail(e, "decode launch");
-    return finish(s, "jl_bifocal_decode_paged");
+    hipError_t e = launch_e4m3_quant((uint8_t*)out, x, scale, ntok, H, d, s);
+    if (e != hipSuccess) return hip_fail(e, "quantize launch");
+    return finish(s, "jl_kv_quantize_fp8");
 }
 
 // ---------------------------------------------------------------------------

@@ -449,6 +449,36 @@ void decode_split_kernel(DecodeArgs a) {
         }
 }
 
+// OCP E4M3 codes (4 per 32-bit word, little-endian) widened exactly; the
+// hardware conversion v_cvt_pk_f32_fp8 reads E4M3 in this format on gfx950.
+__device__ __forceinline__ void e4m3x8_to_f32(uint32_t w0, uint32_t w1, float* f) {
+    const float2v a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w0, false);
+    const float2v b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w0, true);
+    const float2v c = __builtin_amdgcn_cvt_pk_f32_fp8((int)w1, false);
+    const float2v d = __builtin_amdgcn_cvt_pk_f32_fp8((int)w1, true);
+    f[0] = a[0]; f[1] = a[1]; f[2] = b[0]; f[3] = b[1];
+    f[4] = c[0]; f[5] = c[1]; f[6] = d[0]; f[7] = d[1];
+}
+// the same as fp16 (an E4M3 value has 4 significant bits and an exponent in
+// [-9, 8]: fp16 holds it exactly)
+__device__ __forceinline__ f16x8 e4m3x8_to_f16(uint32_t w0, uint32_t w1) {
+    float f[8];
+    e4m3x8_to_f32(w0, w1, f);
+    f16x8 r;
+#pragma unroll
+    for (int x = 0; x < 8; ++x) r[x] = (f16)f[x];
+    return r;
+}
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ f32x4 mfma16(f16x8 a, f16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+// P V product on fp16 operands (bits passed as shorts, as the LDS read gives them)
+__device__ __forceinline__ f32x4 mfma16k16h(s16x4 a, s16x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, a),
+                                                 __builtin_bit_cast(f16x4, b), c, 0, 0, 0);
+}
+
 // bf16 decode.  Same scoring as above; P V runs on MFMA.  Each wave stages
 // its V tile in LDS and the transposing read ds_read_b64_tr_b16 hands every
 // lane its B operand (4 keys x 1 d per 16-d block) directly.  The
@@ -460,18 +490,31 @@ void decode_split_kernel(DecodeArgs a) {
 // PAGED: the cache is a pool of pages of 2^page_shift rows addressed through
 // a per-sequence block table (each workgroup copies its chunk's page numbers
 // to LDS, clamped to the pool, so a bad table entry cannot read outside it).
-template <int D, bool BIF, int GQ, bool PAGED>
+// FP8: the cache holds OCP E4M3 codes with one scale per kv head.  With half
+// the bytes per key the remote keys' rotation would bound the kernel, so this
+// path runs on fp16 operands: codes widen exactly to fp16 (local keys, the V
+// tile in LDS) or f32 (remote keys, rotated and rounded once to fp16, 11
+// significant bits, where the bf16 path needs a hi + lo pair); the query is
+// an fp16 hi + lo pair, P is fp16.  The key scale multiplies the finished
+// scores and the value scale the partial output.
+template <int D, bool BIF, int GQ, bool PAGED, bool FP8>
 __global__ __launch_bounds__(512) void decode_split_bf16_kernel(DecodeArgs a) {
+    using TC = typename std::conditional<FP8, uint8_t, bf16>::type;  // cache element
+    using KRAW = typename std::conditional<FP8, u32x2, bf16x8>::type;  // 8 key elements
+    using VRAW = typename std::conditional<FP8, u32x4, bf16x8>::type;  // 16 bytes of a V row
+    using OT = typename std::conditional<FP8, f16, bf16>::type;         // MFMA operand element
+    using OV = typename std::conditional<FP8, f16x8, bf16x8>::type;     // 8 MFMA operands
     constexpr int HALF = D / 2;
     constexpr int NST = D / 32;          // k-steps of the QK^T product
     constexpr int NH = NST / 2;          // k-steps per RoPE half
     constexpr bool PACK = GQ <= 8;       // hi and lo query parts in one operand
     constexpr int TSTR = HALF + 2;       // LDS row stride of the angle table (float2)
-    constexpr int ROWB = D * 2;          // bytes of one key row of V
+    constexpr int ROWB = D * (int)sizeof(TC);  // bytes of one cache row of V
+    constexpr int VEL = 16 / (int)sizeof(TC);  // V elements per 16-byte load
     constexpr int CPR = ROWB / 16;       // 16-byte chunks per row
     constexpr int RPI = 64 / CPR;        // rows per 64-lane load
     constexpr int NI = kTile / RPI;      // V loads per lane per tile
-    constexpr int VRS = ROWB + 32;       // LDS row stride of a V tile (+32 spreads banks)
+    constexpr int VRS = D * 2 + 32;      // LDS row stride of a bf16 V tile (+32 spreads banks)
     constexpr int SLOT = kTile * VRS;    // bytes of one wave's V tile
     constexpr int NDB = D / 16;          // 16-wide d blocks of O
     __shared__ float2 tab[BIF ? kStageB * TSTR : 1];  // R(-u theta_t): (cos, sin)
@@ -525,8 +568,8 @@ __global__ __launch_bounds__(512) void decode_split_bf16_kernel(DecodeArgs a) {
     // waits): indices are clamped to valid rows, masked keys weigh 0
     const int kvh_c = min(kvh, a.Hkv - 1);
     const int64_t boff = PAGED ? 0 : (int64_t)b * a.S_max * a.Hkv * D;
-    const bf16* kc = (const bf16*)a.kc + boff + (int64_t)kvh_c * D;
-    const bf16* vc = (const bf16*)a.vc + boff + (int64_t)kvh_c * D;
+    const TC* kc = (const TC*)a.kc + boff + (int64_t)kvh_c * D;
+    const TC* vc = (const TC*)a.vc + boff + (int64_t)kvh_c * D;
     const int64_t rstride = (int64_t)a.Hkv * D;
     char* const slot = vs + wave * SLOT;
 
@@ -550,33 +593,45 @@ __global__ __launch_bounds__(512) void decode_split_bf16_kernel(DecodeArgs a) {
     };
     // K of key j0 + n into registers (keys outside the chunk read a row
     // inside it; their scores are masked)
-    auto load_k = [&](int32_t j0, bf16x8* kd) __attribute__((always_inline)) {
+    auto load_k = [&](int32_t j0, KRAW* kd) __attribute__((always_inline)) {
         const int32_t kj = min(max(j0 + n, klo), khi);
 #pragma unroll
         for (int s = 0; s < NST; ++s)
-            kd[s] = *reinterpret_cast<const bf16x8*>(kc + row_of(kj) * rstride + 32 * s + 8 * c);
+            kd[s] = *reinterpret_cast<const KRAW*>(kc + row_of(kj) * rstride + 32 * s + 8 * c);
     };
     // V tiles are staged in registers two tiles ahead (load r of a lane
     // reads 16 bytes of key RPI r + lane / CPR, so one load instruction
     // covers whole rows) and written to the wave's LDS slot, rows VRS bytes
     // apart, right before use
-    auto load_vr = [&](int32_t j0, bf16x8* vd) __attribute__((always_inline)) {
+    auto load_vr = [&](int32_t j0, VRAW* vd) __attribute__((always_inline)) {
         const int q = lane / CPR, ch = lane % CPR;
 #pragma unroll
         for (int r = 0; r < NI; ++r) {
             const int32_t key = min(max(j0 + RPI * r + q, klo), khi);
-            vd[r] = *reinterpret_cast<const bf16x8*>(vc + row_of(key) * rstride + 8 * ch);
+            vd[r] = *reinterpret_cast<const VRAW*>(vc + row_of(key) * rstride + VEL * ch);
         }
     };
-    auto store_vr = [&](const bf16x8* vsrc, char* dst) __attribute__((always_inline)) {
+    auto store_vr = [&](const VRAW* vsrc, char* dst) __attribute__((always_inline)) {
         const int q = lane / CPR, ch = lane % CPR;
 #pragma unroll
-        for (int r = 0; r < NI; ++r)
-            *reinterpret_cast<bf16x8*>(dst + (RPI * r + q) * VRS + 16 * ch) = vsrc[r];
+        for (int r = 0; r < NI; ++r) {
+            char* row = dst + (RPI * r + q) * VRS + 2 * VEL * ch;
+            if constexpr (FP8) {
+                *reinterpret_cast<f16x8*>(row) = e4m3x8_to_f16(vsrc[r][0], vsrc[r][1]);
+                *reinterpret_cast<f16x8*>(row + 16) = e4m3x8_to_f16(vsrc[r][2], vsrc[r][3]);
+            } else {
+                *reinterpret_cast<bf16x8*>(row) = vsrc[r];
+            }
+        }
     };
-    bf16x8 vA[NI], vB[NI], vC[NI];
+    // the 8 key elements of a k-step as MFMA operands (exact for E4M3 codes)
+    auto kop = [&](const KRAW& kr) __attribute__((always_inline)) -> OV {
+        if constexpr (FP8) return e4m3x8_to_f16(kr[0], kr[1]);
+        else return kr;
+    };
+    VRAW vA[NI], vB[NI], vC[NI];
 
-    bf16x8 kA[NST], kB[NST], kC[NST];
+    KRAW kA[NST], kB[NST], kC[NST];
     load_k(kbeg, kA);
     load_vr(kbeg, vA);
     load_k(kbeg + kTile, kB);
@@ -612,6 +667,7 @@ __global__ __launch_bounds__(512) void decode_split_bf16_kernel(DecodeArgs a) {
 
     // ---- query (as in the generic kernel) ----
     const float qscale = a.softmax_scale * kLog2e;
+    const float kscale = FP8 && a.k_scale ? a.k_scale[kvh_c] : 1.0f;
     const int hq = PACK ? (n & (GQ - 1)) : n;
     const bool qlo = PACK && n >= GQ;
     bf16x8 qraw[NST];
@@ -622,8 +678,8 @@ __global__ __launch_bounds__(512) void decode_split_bf16_kernel(DecodeArgs a) {
         for (int s = 0; s < NST; ++s)
             qraw[s] = qok ? *reinterpret_cast<const bf16x8*>(qp + 32 * s) : bf16x8{};
     }
-    bf16x8 Q[NST];
-    bf16x8 Qlo[PACK ? 1 : NST];
+    OV Q[NST];
+    OV Qlo[PACK ? 1 : NST];
     auto rotate_q = [&](int row) __attribute__((always_inline)) {
         const float2* qt = qtab + row * HALF + 8 * c;
 #pragma unroll
@@ -634,8 +690,8 @@ __global__ __launch_bounds__(512) void decode_split_bf16_kernel(DecodeArgs a) {
                 const float x0 = (float)qraw[s][u], x1 = (float)qraw[s + NH][u];
                 const float y0 = (x0 * cs.x - x1 * cs.y) * qscale;
                 const float y1 = (x1 * cs.x + x0 * cs.y) * qscale;
-                const bf16 h0 = (bf16)y0, h1 = (bf16)y1;
-                const bf16 l0 = (bf16)(y0 - (float)h0), l1 = (bf16)(y1 - (float)h1);
+                const OT h0 = (OT)y0, h1 = (OT)y1;
+                const OT l0 = (OT)(y0 - (float)h0), l1 = (OT)(y1 - (float)h1);
                 if constexpr (PACK) {
                     Q[s][u] = qlo ? l0 : h0;
                     Q[s + NH][u] = qlo ? l1 : h1;
@@ -654,42 +710,72 @@ __global__ __launch_bounds__(512) void decode_split_bf16_kernel(DecodeArgs a) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) acc[i] += __shfl_xor(acc[i], GQ);
         }
+        if constexpr (FP8) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[i] *= kscale;
+        }
         return acc;
     };
-    auto scores_local = [&](const bf16x8* kcur) __attribute__((always_inline)) -> f32x4 {
+    auto scores_local = [&](const KRAW* kcur) __attribute__((always_inline)) -> f32x4 {
         f32x4 acc = {};
 #pragma unroll
         for (int s = 0; s < NST; ++s) {
-            acc = mfma16(kcur[s], Q[s], acc);
-            if constexpr (!PACK) acc = mfma16(kcur[s], Qlo[s], acc);
+            const OV kb = kop(kcur[s]);
+            acc = mfma16(kb, Q[s], acc);
+            if constexpr (!PACK) acc = mfma16(kb, Qlo[s], acc);
         }
         return finish(acc);
     };
-    auto scores_remote = [&](const bf16x8* kcur, int32_t u) __attribute__((always_inline)) -> f32x4 {
+    auto scores_remote = [&](const KRAW* kcur, int32_t u) __attribute__((always_inline)) -> f32x4 {
         f32x4 acc = {};
         const float2* tp = tab + u * TSTR + 8 * c;
 #pragma unroll
         for (int s = 0; s < NH; ++s) {
-            bf16x8 h0, l0, h1, l1;
+            float kf0[8], kf1[8];
+            if constexpr (FP8) {
+                e4m3x8_to_f32(kcur[s][0], kcur[s][1], kf0);
+                e4m3x8_to_f32(kcur[s + NH][0], kcur[s + NH][1], kf1);
+            } else {
 #pragma unroll
-            for (int x = 0; x < 8; ++x) {
-                const float2 cs = tp[32 * s + x];
-                const float k0 = (float)kcur[s][x];
-                const float k1 = (float)kcur[s + NH][x];
-                const float y0 = k0 * cs.x - k1 * cs.y;
-                const float y1 = k1 * cs.x + k0 * cs.y;
-                h0[x] = (bf16)y0;
-                l0[x] = (bf16)(y0 - (float)h0[x]);
-                h1[x] = (bf16)y1;
-                l1[x] = (bf16)(y1 - (float)h1[x]);
+                for (int x = 0; x < 8; ++x) {
+                    kf0[x] = (float)kcur[s][x];
+                    kf1[x] = (float)kcur[s + NH][x];
+                }
             }
-            acc = mfma16(h0, Q[s], acc);
-            acc = mfma16(l0, Q[s], acc);
-            acc = mfma16(h1, Q[s + NH], acc);
-            acc = mfma16(l1, Q[s + NH], acc);
-            if constexpr (!PACK) {
-                acc = mfma16(h0, Qlo[s], acc);
-                acc = mfma16(h1, Qlo[s + NH], acc);
+            if constexpr (FP8) {
+                f16x8 h0, h1;
+#pragma unroll
+                for (int x = 0; x < 8; ++x) {
+                    const float2 cs = tp[32 * s + x];
+                    h0[x] = (f16)(kf0[x] * cs.x - kf1[x] * cs.y);
+                    h1[x] = (f16)(kf1[x] * cs.x + kf0[x] * cs.y);
+                }
+                acc = mfma16(h0, Q[s], acc);
+                acc = mfma16(h1, Q[s + NH], acc);
+                if constexpr (!PACK) {
+                    acc = mfma16(h0, Qlo[s], acc);
+                    acc = mfma16(h1, Qlo[s + NH], acc);
+                }
+            } else {
+                bf16x8 h0, l0, h1, l1;
+#pragma unroll
+                for (int x = 0; x < 8; ++x) {
+                    const float2 cs = tp[32 * s + x];
+                    const float y0 = kf0[x] * cs.x - kf1[x] * cs.y;
+                    const float y1 = kf1[x] * cs.x + kf0[x] * cs.y;
+                    h0[x] = (bf16)y0;
+                    l0[x] = (bf16)(y0 - (float)h0[x]);
+                    h1[x] = (bf16)y1;
+                    l1[x] = (bf16)(y1 - (float)h1[x]);
+                }
+                acc = mfma16(h0, Q[s], acc);
+                acc = mfma16(l0, Q[s], acc);
+                acc = mfma16(h1, Q[s + NH], acc);
+                acc = mfma16(l1, Q[s + NH], acc);
+                if constexpr (!PACK) {
+                    acc = mfma16(h0, Qlo[s], acc);
+                    acc = mfma16(h1, Qlo[s + NH], acc);
+                }
             }
         }
         return finish(acc);
@@ -728,7 +814,7 @@ __global__ __launch_bounds__(512) void decode_split_bf16_kernel(DecodeArgs a) {
         float ps = 0.0f;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const bf16 pb = (bf16)__builtin_amdgcn_exp2f(sc[i] - m_run);
+            const OT pb = (OT)__builtin_amdgcn_exp2f(sc[i] - m_run);
             ps += (float)pb;
             pa[i] = __builtin_bit_cast(short, pb);
         }
@@ -745,7 +831,7 @@ __global__ __launch_bounds__(512) void decode_split_bf16_kernel(DecodeArgs a) {
 #pragma unroll
         for (int bd = 0; bd < NDB; ++bd) {
             const s16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(slot + voff + 32 * bd));
-            O[bd] = mfma16k16(pa, vb, O[bd]);
+            O[bd] = FP8 ? mfma16k16h(pa, vb, O[bd]) : mfma16k16(pa, vb, O[bd]);
         }
     };
 
@@ -754,8 +840,8 @@ __global__ __launch_bounds__(512) void decode_split_bf16_kernel(DecodeArgs a) {
     bool stage_remote = false;
     // one tile: issue the loads two tiles ahead, stage this tile's V in LDS,
     // score, P V
-    auto step = [&](int32_t j0, const bf16x8* kcur, const bf16x8* vcur, bf16x8* knext,
-                    bf16x8* vnext) __attribute__((always_inline)) {
+    auto step = [&](int32_t j0, const KRAW* kcur, const VRAW* vcur, KRAW* knext,
+                    VRAW* vnext) __attribute__((always_inline)) {
         load_k(j0 + 2 * kTile, knext);
         load_vr(j0 + 2 * kTile, vnext);
         store_vr(vcur, slot);  // the same wave writes then reads: LDS keeps its order
@@ -797,11 +883,13 @@ __global__ __launch_bounds__(512) void decode_split_bf16_kernel(DecodeArgs a) {
         pm[2 * (pbase + n)] = m_run;
         pm[2 * (pbase + n) + 1] = l_tot;
     }
+    const float vscale = FP8 && a.v_scale ? a.v_scale[kvh_c] : 1.0f;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
         if (4 * c + i < grp) {
 #pragma unroll
-            for (int bd = 0; bd < NDB; ++bd) po[(pbase + 4 * c + i) * D + 16 * bd + n] = O[bd][i];
+            for (int bd = 0; bd < NDB; ++bd)
+                po[(pbase + 4 * c + i) * D + 16 * bd + n] = FP8 ? O[bd][i] * vscale : O[bd][i];
         }
 }
 
@@ -892,15 +980,18 @@ static hipError_t launch_decode_g(const DecodeArgs& a, hipStream_t s) {
     const dim3 grid(a.lay.n_splits, (a.Hkv + nw - 1) / nw, a.B);
     LaunchScope scope(a.bifocal ? "decode_split" : "decode_split_plain", s);
     if constexpr (sizeof(TIN) == 2) {
-        if (a.block_table) {
-            if (a.bifocal)
-                hipLaunchKernelGGL((decode_split_bf16_kernel<D, true, GQ, true>), grid, dim3(64 * nw), 0, s, a);
-            else
-                hipLaunchKernelGGL((decode_split_bf16_kernel<D, false, GQ, true>), grid, dim3(64 * nw), 0, s, a);
-        } else if (a.bifocal) {
-            hipLaunchKernelGGL((decode_split_bf16_kernel<D, true, GQ, false>), grid, dim3(64 * nw), 0, s, a);
-        } else {
-            hipLaunchKernelGGL((decode_split_bf16_kernel<D, false, GQ, false>), grid, dim3(64 * nw), 0, s, a);
+        // (bifocal, paged, fp8) -> one instantiation each
+        const int sel = (a.bifocal ? 4 : 0) | (a.block_table ? 2 : 0) | (a.fp8 ? 1 : 0);
+        const dim3 blk(64 * nw);
+        switch (sel) {
+            case 0: hipLaunchKernelGGL((decode_split_bf16_kernel<D, false, GQ, false, false>), grid, blk, 0, s, a); break;
+            case 1: hipLaunchKernelGGL((decode_split_bf16_kernel<D, false, GQ, false, true>), grid, blk, 0, s, a); break;
+            case 2: hipLaunchKernelGGL((decode_split_bf16_kernel<D, false, GQ, true, false>), grid, blk, 0, s, a); break;
+            case 3: hipLaunchKernelGGL((decode_split_bf16_kernel<D, false, GQ, true, true>), grid, blk, 0, s, a); break;
+            case 4: hipLaunchKernelGGL((decode_split_bf16_kernel<D, true, GQ, false, false>), grid, blk, 0, s, a); break;
+            case 5: hipLaunchKernelGGL((decode_split_bf16_kernel<D, true, GQ, false, true>), grid, blk, 0, s, a); break;
+            case 6: hipLaunchKernelGGL((decode_split_bf16_kernel<D, true, GQ, true, false>), grid, blk, 0, s, a); break;
+            default: hipLaunchKernelGGL((decode_split_bf16_kernel<D, true, GQ, true, true>), grid, blk, 0, s, a); break;
         }
     } else {
         if (a.bifocal)
@@ -921,6 +1012,45 @@ static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t s) {
     if (err != hipSuccess) return err;
     LaunchScope scope("decode_merge", s);
     hipLaunchKernelGGL(decode_merge_kernel<TIN>, dim3(a.Hq, a.B, D / 32), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// fp8 cache writer: one thread per 8 elements of a row (d / 8 threads per
+// (token, head)); the quotient x / scale is a correctly rounded fp32
+// division, clamped to +-448 and rounded to nearest even by
+// v_cvt_pk_fp8_f32.  NaN stays NaN.
+__global__ __launch_bounds__(256) void e4m3_quant_kernel(uint8_t* __restrict__ out,
+                                                         const bf16* __restrict__ x,
+                                                         const float* __restrict__ scale,
+                                                         int64_t n8, int32_t H, int32_t d) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n8) return;
+    const int h = (int)((i * 8 / d) % H);
+    const float sc = scale[h];
+    const bf16x8 v = *reinterpret_cast<const bf16x8*>(x + 8 * i);
+    uint32_t w[2];
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+        float q[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const float y = (float)v[4 * half + u] / sc;
+            q[u] = y != y ? y : __builtin_amdgcn_fmed3f(y, 448.0f, -448.0f);
+        }
+        int pk = __builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], 0, false);
+        pk = __builtin_amdgcn_cvt_pk_fp8_f32(q[2], q[3], pk, true);
+        w[half] = (uint32_t)pk;
+    }
+    *reinterpret_cast<u32x2*>(out + 8 * i) = u32x2{w[0], w[1]};
+}
+
+hipError_t launch_e4m3_quant(uint8_t* out, const void* x, const float* scale, int64_t ntok,
+                             int32_t H, int32_t d, hipStream_t s) {
+    const int64_t n8 = ntok * H * (d / 8);
+    LaunchScope scope("e4m3_quant", s);
+    hipLaunchKernelGGL(e4m3_quant_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, s,
+                       out, (const bf16*)x, scale, n8, H, d);
     return hipGetLastError();
 }
 

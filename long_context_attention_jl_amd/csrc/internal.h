@@ -84,6 +84,10 @@ struct PrefillArgs {
 hipError_t launch_plan_chunk(int32_t* plan, const int32_t* cu_q, const int32_t* seqlens_k,
                              int32_t B, int64_t Tq, int32_t max_seqlen_q, int32_t max_seqlen_k,
                              int32_t w_pretrained, hipStream_t s);
+// out[t][h][:] = E4M3(x[t][h][:] / scale[h]) (fp32 quotient, round to nearest
+// even, saturating at +-448); x bf16 [ntok][H][d]
+hipError_t launch_e4m3_quant(uint8_t* out, const void* x, const float* scale, int64_t ntok,
+                             int32_t H, int32_t d, hipStream_t s);
 hipError_t launch_kv_prepass(const PrefillArgs& a, int dtype, hipStream_t s);
 // O = the LogSumExp combination of the three unfused calls B + A - C
 hipError_t launch_three_call_merge(const void* oA, const void* oB, const void* oC, const float* lA,
@@ -111,6 +115,11 @@ struct DecodeArgs {
     const int32_t* block_table;
     int32_t page_shift, bt_stride;
     int64_t n_pages;
+    // fp8 cache (fp8 != 0): OCP E4M3 codes, element = scale[kv head] * code
+    // (k_scale / v_scale device float32 [Hkv], or nullptr for 1)
+    int32_t fp8;
+    const float* k_scale;
+    const float* v_scale;
 };
 hipError_t launch_decode(const DecodeArgs& a, int dtype, hipStream_t s);
 

@@ -186,3 +186,30 @@ def chunk_128k() -> ChunkCase:
     of L = 131072 (G = 4), w_local 2048."""
     q, k, v, _ = chunk_inputs([4096], [131072], 131072, 32, 8, 128, seed=6)
     return ChunkCase("chunk4096_L131072", q, k, v, [131072], None, DECODE_PARAMS)
+
+
+def to_e4m3(x: torch.Tensor):
+    """Stores a [..., H, d] cache block as OCP E4M3 codes with one scale per head
+    (scale = max |x| of the head / 448, so every value is in range), using
+    torch's own float8_e4m3fn conversion.  Returns (uint8 codes, float32 scales)."""
+    xf = x.float()
+    H = xf.shape[-2]
+    amax = xf.abs().transpose(0, -2).reshape(H, -1).amax(dim=1)
+    scale = torch.where(amax > 0, amax / 448.0, torch.ones_like(amax))
+    codes = (xf / scale.view(H, 1)).to(torch.float8_e4m3fn).view(torch.uint8)
+    return codes, scale
+
+
+def decode_fp8_inputs(B: int, S_max: int, Hq: int, Hkv: int, d: int, *, seed: int):
+    """bf16 queries and an fp8 cache: the bf16 caches of ``decode_inputs``
+    stored as E4M3 codes with per-kv-head scales."""
+    q, k, v = decode_inputs(B, S_max, Hq, Hkv, d, seed=seed)
+    k8, ks = to_e4m3(k)
+    v8, vs = to_e4m3(v)
+    return q, k8, v8, ks, vs
+
+
+def decode_fp8_128k():
+    """The 128K decode workload (L = 131072, G = 4) on an fp8 cache."""
+    q, k8, v8, ks, vs = decode_fp8_inputs(1, 131072, 32, 8, 128, seed=4)
+    return q, k8, v8, ks, vs, [131072], DECODE_PARAMS

@@ -108,6 +108,17 @@ def lib() -> ctypes.CDLL:
                                                      _vp, _vp, _i32, _i32, _i32, _i64, _i32,
                                                      _i32, _i32, _i32, ctypes.POINTER(jl_params),
                                                      ctypes.c_int, _vp, ctypes.c_size_t, _vp]
+        L.jl_bifocal_decode_fp8.restype = ctypes.c_int
+        L.jl_bifocal_decode_fp8.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32,
+                                            _i64, _i32, _i32, _i32, ctypes.POINTER(jl_params),
+                                            _vp, ctypes.c_size_t, _vp]
+        L.jl_bifocal_decode_fp8_paged.restype = ctypes.c_int
+        L.jl_bifocal_decode_fp8_paged.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                                  _i32, _i32, _i32, _i64, _i32, _i32, _i32, _i32,
+                                                  ctypes.POINTER(jl_params), _vp,
+                                                  ctypes.c_size_t, _vp]
+        L.jl_kv_quantize_fp8.restype = ctypes.c_int
+        L.jl_kv_quantize_fp8.argtypes = [_vp, _vp, _vp, _i64, _i32, _i32, _vp]
         L.jl_debug_index_math.restype = ctypes.c_int
         L.jl_debug_index_math.argtypes = [_i64, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp]
         L.jl_profile_enable.restype = ctypes.c_int
@@ -423,6 +434,69 @@ def bifocal_prefill_chunk_paged(q: torch.Tensor, k_pages: torch.Tensor, v_pages:
         bt.shape[1], Hq, Hkv, d, ctypes.byref(p), _dtype(q), _dev(ws, "workspace"),
         ws.numel() * ws.element_size(), _stream()),
         "jl_bifocal_prefill_chunk_paged")
+    return o, lse
+
+
+def _u8(t: torch.Tensor, name: str) -> int:
+    if t.dtype not in (torch.uint8, torch.float8_e4m3fn):
+        raise ValueError("%s must hold E4M3 codes (uint8 or float8_e4m3fn)" % name)
+    return _dev(t, name)
+
+
+def _scale(x, H: int, dev) -> torch.Tensor:
+    if isinstance(x, torch.Tensor):
+        return x.to(device=dev, dtype=torch.float32).contiguous().reshape(H)
+    return torch.tensor([float(v) for v in x], dtype=torch.float32, device=dev).reshape(H)
+
+
+def kv_quantize_fp8(x: torch.Tensor, scale, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """E4M3 codes (uint8) of x / scale[h] for a bf16 cache block x [..., H, d]."""
+    H, d = x.shape[-2], x.shape[-1]
+    sc = _scale(scale, H, x.device)
+    o = out if out is not None else torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    _check(lib().jl_kv_quantize_fp8(_u8(o, "out"), _dev(x, "x"), _dev(sc, "scale"),
+                                    x.numel() // (H * d), H, d, _stream()),
+           "jl_kv_quantize_fp8")
+    return o
+
+
+def bifocal_decode_fp8(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, k_scale,
+                       v_scale, seqlens_k: Union[Sequence[int], torch.Tensor], *,
+                       w_pretrained: int, w_local: int, rope_base: float, softmax_scale: float,
+                       bifocal: bool = True, max_seqlen_k: Optional[int] = None,
+                       block_table: Optional[torch.Tensor] = None,
+                       workspace: Optional[torch.Tensor] = None,
+                       out: Optional[torch.Tensor] = None,
+                       lse_out: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Bifocal decode on an fp8 (E4M3) cache with per-kv-head scales.  Flat
+    caches [B, S_max, Hkv, d]; with ``block_table`` page pools
+    [n_pages, page_size, Hkv, d].  Returns (o [B, Hq, d], lse [B, Hq])."""
+    B, Hq, d = q.shape
+    dev = q.device
+    Hkv = k_cache.shape[2]
+    sl, max_seqlen_k = _seqlens(seqlens_k, max_seqlen_k, dev)
+    ks, vs = _scale(k_scale, Hkv, dev), _scale(v_scale, Hkv, dev)
+    o = out if out is not None else torch.empty_like(q)
+    lse = lse_out if lse_out is not None else torch.empty((B, Hq), dtype=torch.float32, device=dev)
+    ws = _workspace(decode_workspace_bytes(B, max_seqlen_k, Hq, Hkv, d, torch.bfloat16), dev,
+                    workspace)
+    p = _params(w_pretrained, w_local, rope_base, softmax_scale, bifocal)
+    if block_table is None:
+        _check(lib().jl_bifocal_decode_fp8(
+            _dev(o, "o"), _dev(lse, "lse"), _dev(q, "q"), _u8(k_cache, "k_cache"),
+            _u8(v_cache, "v_cache"), _dev(ks, "k_scale"), _dev(vs, "v_scale"),
+            _dev(sl, "seqlens_k"), B, max_seqlen_k, k_cache.shape[1], Hq, Hkv, d,
+            ctypes.byref(p), _dev(ws, "workspace"), ws.numel() * ws.element_size(), _stream()),
+            "jl_bifocal_decode_fp8")
+    else:
+        bt = block_table.to(device=dev, dtype=torch.int32).contiguous()
+        _check(lib().jl_bifocal_decode_fp8_paged(
+            _dev(o, "o"), _dev(lse, "lse"), _dev(q, "q"), _u8(k_cache, "k_pages"),
+            _u8(v_cache, "v_pages"), _dev(ks, "k_scale"), _dev(vs, "v_scale"),
+            _dev(bt, "block_table"), _dev(sl, "seqlens_k"), B, max_seqlen_k, k_cache.shape[1],
+            k_cache.shape[0], bt.shape[1], Hq, Hkv, d, ctypes.byref(p), _dev(ws, "workspace"),
+            ws.numel() * ws.element_size(), _stream()),
+            "jl_bifocal_decode_fp8_paged")
     return o, lse
 
 

@@ -271,3 +271,60 @@ def test_chunk_workspace_query():
     assert L.jl_bifocal_prefill_chunk_workspace(1, 131072, 32, 8, 128, 0, ctypes.byref(n)) == 2
     assert L.jl_bifocal_prefill_chunk_workspace(0, 10, 32, 8, 128, 1, ctypes.byref(n)) == 1
     assert L.jl_bifocal_prefill_chunk_workspace(1, 10, 32, 8, 128, 1, None) == 1
+
+
+def _fp8(paged=False, **kw):
+    a = dict(o=FAKE, lse=FAKE * 2, q=FAKE * 3, kc=FAKE * 4, vc=FAKE * 5, ks=FAKE * 9,
+             vs=FAKE * 10, bt=FAKE * 6, sl=FAKE * 7, B=2, max_len=4096, S_max=4096, page=64,
+             n_pages=200, bt_stride=64, Hq=32, Hkv=8, d=128, params=_params(), ws=FAKE * 8,
+             ws_bytes=1 << 40, stream=None)
+    a.update(kw)
+    p = a["params"]
+    pp = None if p is None else ctypes.byref(p)
+    L = jlb.lib()
+    if paged:
+        return L.jl_bifocal_decode_fp8_paged(
+            a["o"], a["lse"], a["q"], a["kc"], a["vc"], a["ks"], a["vs"], a["bt"], a["sl"],
+            a["B"], a["max_len"], a["page"], a["n_pages"], a["bt_stride"], a["Hq"], a["Hkv"],
+            a["d"], pp, a["ws"], a["ws_bytes"], a["stream"])
+    return L.jl_bifocal_decode_fp8(
+        a["o"], a["lse"], a["q"], a["kc"], a["vc"], a["ks"], a["vs"], a["sl"], a["B"],
+        a["max_len"], a["S_max"], a["Hq"], a["Hkv"], a["d"], pp, a["ws"], a["ws_bytes"],
+        a["stream"])
+
+
+@pytest.mark.parametrize("paged", [False, True])
+@pytest.mark.parametrize("kw,status", [
+    (dict(ks=None), 1), (dict(vs=None), 1), (dict(kc=None), 1), (dict(sl=None), 1),
+    (dict(params=None), 1), (dict(B=0), 1), (dict(B=70000), 2), (dict(max_len=0), 1),
+    (dict(Hq=30), 1), (dict(Hq=32, Hkv=1), 2), (dict(d=96), 2), (dict(ws_bytes=100), 3),
+    (dict(ws=FAKE * 8 + 4), 1), (dict(o=FAKE * 3), 1),
+])
+def test_fp8_decode_validation(paged, kw, status):
+    assert _fp8(paged, **kw) == status
+    assert jlb.lib().jl_last_error()
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(bt=None), 1), (dict(page=48), 1), (dict(n_pages=0), 1), (dict(bt_stride=63), 1),
+])
+def test_fp8_paged_decode_validation(kw, status):
+    assert _fp8(True, **kw) == status
+
+
+def test_fp8_decode_workspace_is_the_bf16_one():
+    """The fp8 decode call accepts exactly the bf16 decode workspace size."""
+    n = ctypes.c_size_t(0)
+    assert jlb.lib().jl_bifocal_decode_workspace(2, 4096, 32, 8, 128, 1, ctypes.byref(n)) == 0
+    assert _fp8(ws_bytes=n.value - 1) == 3
+
+
+@pytest.mark.parametrize("args,status", [
+    ((None, FAKE, FAKE * 2, 10, 8, 128), 1), ((FAKE, None, FAKE * 2, 10, 8, 128), 1),
+    ((FAKE, FAKE * 3, None, 10, 8, 128), 1), ((FAKE, FAKE * 3, FAKE * 2, 0, 8, 128), 1),
+    ((FAKE, FAKE * 3, FAKE * 2, 10, 0, 128), 1), ((FAKE, FAKE * 3, FAKE * 2, 10, 8, 100), 1),
+    ((FAKE + 4, FAKE * 3, FAKE * 2, 10, 8, 128), 1), ((FAKE, FAKE * 3 + 8, FAKE * 2, 10, 8, 128), 1),
+    ((FAKE, FAKE, FAKE * 2, 10, 8, 128), 1),
+])
+def test_kv_quantize_validation(args, status):
+    assert jlb.lib().jl_kv_quantize_fp8(*args, None) == status
