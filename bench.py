@@ -168,6 +168,17 @@ def main():
                      "traffic": _profiled_traffic("traffic_prefill_bf16_qwen3_L131072.md"),
                      "algorithmic_flops_per_launch": main_flops},
     }
+    # the same prefill with the bifocal logic off (every pair under standard
+    # RoPE): the overhead baseline, timed warm after the timed region
+    t_plain = []
+    for _ in range(2):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        jl.bifocal_prefill(q, k, v, bifocal=False, **kw)
+        torch.cuda.synchronize()
+        t_plain.append((time.perf_counter() - t0) * 1e3)
+    out["prefill_plain_ms"] = round(min(t_plain), 3)
+    out["prefill_bifocal_over_plain"] = round(ms_per_step / min(t_plain), 4)
     del o, lse
 
     if not args.no_three_call:
@@ -362,8 +373,58 @@ def bench_decode(jl, inputs, torch, iters):
     nbytes = 2 * L * Hkv * d * 2
     split_cnt, split_ms = prof.get("decode_split", (1, float("nan")))
     split_us = split_ms * 1e3 / max(split_cnt, 1)
+    # the 16-step run: a cache filled to 32760 plus one appended token per
+    # step (L = 32761 .. 32776, G switches 1 -> 2 after step 8); four copies
+    # of the 134 MB cache rotate so no step is served from the last-level cache
+    queries, kc16, vc16, lens16, p16 = inputs.decode_16step_cache()
+    copies16 = [(kc16.cuda(), vc16.cuda()) for _ in range(4)]
+    ws16 = torch.empty(jl.decode_workspace_bytes(1, max(lens16), Hq, Hkv, d, q.dtype),
+                       dtype=torch.uint8, device="cuda")
+
+    def run16(qs, L16, bifocal, n):
+        sl16 = torch.tensor([L16], dtype=torch.int32, device="cuda")
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        ev0.record()
+        for i in range(n):
+            kc_, vc_ = copies16[i % 4]
+            jl.bifocal_decode(qs, kc_, vc_, sl16, max_seqlen_k=L16, w_pretrained=p16.w_pretrained,
+                              w_local=p16.w_local, rope_base=p16.rope_base,
+                              softmax_scale=p16.softmax_scale, bifocal=bifocal, workspace=ws16,
+                              out=o, lse_out=lse)
+        ev1.record()
+        torch.cuda.synchronize()
+        return ev0.elapsed_time(ev1) * 1e3 / n
+
+    s16 = {"L": [], "us": [], "plain_us": [], "overhead_pct": []}
+    for qs, L16 in zip(queries, lens16):
+        qs = qs.cuda()
+        run16(qs, L16, True, 4)
+        tb16 = min(run16(qs, L16, True, 20) for _ in range(3))
+        tp16 = min(run16(qs, L16, False, 20) for _ in range(3))
+        s16["L"].append(L16)
+        s16["us"].append(round(tb16, 2))
+        s16["plain_us"].append(round(tp16, 2))
+        s16["overhead_pct"].append(round(100.0 * (tb16 - tp16) / tp16, 2))
+
+    # streaming reference: a 1 GiB device-to-device copy (bytes read + written)
+    src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for _ in range(10):
+        dst.copy_(src)
+    ev1.record()
+    torch.cuda.synchronize()
+    copy_gbps = 2 * src.numel() * 10 / (ev0.elapsed_time(ev1) * 1e-3) / 1e9
+    del src, dst
+
     return {
         "workload": "decode_L131072 (Hq=32, Hkv=8, d=128, G=4, w_local=2048, batch 1)",
+        "steps16": s16,
+        "stream_copy_GBps": round(copy_gbps, 1),
         "us_per_token": round(t_bif, 2),
         "plain_us_per_token": round(t_plain, 2),
         "overhead_pct": round(100.0 * (t_bif - t_plain) / t_plain, 2),
