@@ -79,6 +79,8 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-three-call", action="store_true")
     ap.add_argument("--no-chunk", action="store_true")
+    ap.add_argument("--no-decode-extras", action="store_true",
+                    help="decode: time only the flat bf16 cache (no paged, fp8 or 16-step runs)")
     ap.add_argument("--copy-calibration", type=int, default=0,
                     help="only run a plain device copy of this many bytes (counter calibration)")
     args = ap.parse_args()
@@ -188,7 +190,8 @@ def main():
         out["chunk"] = bench_chunk(jl, inputs, torch)
 
     if not args.no_decode:
-        out["decode"] = bench_decode(jl, inputs, torch, args.decode_iters)
+        out["decode"] = bench_decode(jl, inputs, torch, args.decode_iters,
+                                     extras=not args.no_decode_extras)
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(case)
@@ -275,7 +278,7 @@ def bench_chunk(jl, inputs, torch, iters=10):
     }
 
 
-def bench_decode(jl, inputs, torch, iters):
+def bench_decode(jl, inputs, torch, iters, extras=True):
     """Decode at L = 131072 (G = 4): bifocal vs the same kernel with the bifocal
     logic compiled out.  Four cache copies (2.1 GB) rotate so no iteration is
     served from the 256 MB last-level cache."""
@@ -309,7 +312,7 @@ def bench_decode(jl, inputs, torch, iters):
     # Paged form of the same caches: each copy viewed as a pool of pages,
     # named by a shuffled block table (timing only; the rows' order is moot).
     pools = {}
-    for page in (16, 64):
+    for page in ((16, 64) if extras else ()):
         n_pages = S_max // page
         bt = torch.randperm(n_pages, generator=torch.Generator().manual_seed(page))
         pools[page] = (bt.to(torch.int32).view(1, n_pages).cuda(),
@@ -332,9 +335,10 @@ def bench_decode(jl, inputs, torch, iters):
         return ev0.elapsed_time(ev1) * 1e3 / n
 
     # fp8 (E4M3) form of the same workload: four copies of the quantized cache
-    _, k8, v8, ks, vs, _, _ = inputs.decode_fp8_128k()
-    copies8 = [(k8.cuda(), v8.cuda()) for _ in range(4)]
-    ks, vs = ks.cuda(), vs.cuda()
+    if extras:
+        _, k8, v8, ks, vs, _, _ = inputs.decode_fp8_128k()
+        copies8 = [(k8.cuda(), v8.cuda()) for _ in range(4)]
+        ks, vs = ks.cuda(), vs.cuda()
 
     def run_fp8(bifocal, n):
         ev0 = torch.cuda.Event(enable_timing=True)
@@ -352,8 +356,9 @@ def bench_decode(jl, inputs, torch, iters):
 
     run(True, 10)
     run(False, 10)
-    run_fp8(True, 10)
-    run_fp8(False, 10)
+    if extras:
+        run_fp8(True, 10)
+        run_fp8(False, 10)
     for page in pools:
         run_paged(page, 10)
     tb, tp, tpg = [], [], {page: [] for page in pools}
@@ -363,8 +368,9 @@ def bench_decode(jl, inputs, torch, iters):
         tp.append(run(False, iters // 4))
         for page in pools:
             tpg[page].append(run_paged(page, iters // 4))
-        t8b.append(run_fp8(True, iters // 4))
-        t8p.append(run_fp8(False, iters // 4))
+        if extras:
+            t8b.append(run_fp8(True, iters // 4))
+            t8p.append(run_fp8(False, iters // 4))
     jl.profile_enable(True)
     run(True, 20)
     prof = jl.profile_read()
@@ -376,6 +382,28 @@ def bench_decode(jl, inputs, torch, iters):
     # the 16-step run: a cache filled to 32760 plus one appended token per
     # step (L = 32761 .. 32776, G switches 1 -> 2 after step 8); four copies
     # of the 134 MB cache rotate so no step is served from the last-level cache
+    res = {
+        "workload": "decode_L131072 (Hq=32, Hkv=8, d=128, G=4, w_local=2048, batch 1)",
+        "us_per_token": round(t_bif, 2),
+        "plain_us_per_token": round(t_plain, 2),
+        "overhead_pct": round(100.0 * (t_bif - t_plain) / t_plain, 2),
+        "kv_bytes_per_step": nbytes,
+        "achieved_GBps": round(nbytes / (t_bif * 1e-6) / 1e9, 1),
+        "hbm_frac": round(nbytes / (t_bif * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4),
+        "split_kernel_us": round(split_us, 2),
+        "split_kernel_GBps": round(nbytes / (split_us * 1e-6) / 1e9, 1),
+        "split_kernel_traffic": _profiled_traffic("traffic_decode_split_L131072.md"),
+        "kernels": {n: {"launches": c2, "avg_us": round(ms * 1e3 / max(c2, 1), 2)}
+                    for n, (c2, ms) in sorted(prof.items())},
+    }
+    if not extras:
+        return res
+    res["paged_us_per_token"] = {"page_%d" % page: round(min(t), 2) for page, t in tpg.items()}
+    res["fp8"] = {"us_per_token": round(min(t8b), 2), "plain_us_per_token": round(min(t8p), 2),
+                  "overhead_pct": round(100.0 * (min(t8b) - min(t8p)) / min(t8p), 2),
+                  "kv_bytes_per_step": nbytes // 2,
+                  "achieved_GBps": round(nbytes / 2 / (min(t8b) * 1e-6) / 1e9, 1)}
+
     queries, kc16, vc16, lens16, p16 = inputs.decode_16step_cache()
     copies16 = [(kc16.cuda(), vc16.cuda()) for _ in range(4)]
     ws16 = torch.empty(jl.decode_workspace_bytes(1, max(lens16), Hq, Hkv, d, q.dtype),
@@ -421,27 +449,9 @@ def bench_decode(jl, inputs, torch, iters):
     copy_gbps = 2 * src.numel() * 10 / (ev0.elapsed_time(ev1) * 1e-3) / 1e9
     del src, dst
 
-    return {
-        "workload": "decode_L131072 (Hq=32, Hkv=8, d=128, G=4, w_local=2048, batch 1)",
-        "steps16": s16,
-        "stream_copy_GBps": round(copy_gbps, 1),
-        "us_per_token": round(t_bif, 2),
-        "plain_us_per_token": round(t_plain, 2),
-        "overhead_pct": round(100.0 * (t_bif - t_plain) / t_plain, 2),
-        "kv_bytes_per_step": nbytes,
-        "achieved_GBps": round(nbytes / (t_bif * 1e-6) / 1e9, 1),
-        "hbm_frac": round(nbytes / (t_bif * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4),
-        "split_kernel_us": round(split_us, 2),
-        "split_kernel_GBps": round(nbytes / (split_us * 1e-6) / 1e9, 1),
-        "split_kernel_traffic": _profiled_traffic("traffic_decode_split_L131072.md"),
-        "paged_us_per_token": {"page_%d" % page: round(min(t), 2) for page, t in tpg.items()},
-        "fp8": {"us_per_token": round(min(t8b), 2), "plain_us_per_token": round(min(t8p), 2),
-                "overhead_pct": round(100.0 * (min(t8b) - min(t8p)) / min(t8p), 2),
-                "kv_bytes_per_step": nbytes // 2,
-                "achieved_GBps": round(nbytes / 2 / (min(t8b) * 1e-6) / 1e9, 1)},
-        "kernels": {n: {"launches": c2, "avg_us": round(ms * 1e3 / max(c2, 1), 2)}
-                    for n, (c2, ms) in sorted(prof.items())},
-    }
+    res["steps16"] = s16
+    res["stream_copy_GBps"] = round(copy_gbps, 1)
+    return res
 
 
 def cpu_baseline(case):
