@@ -238,14 +238,7 @@ void prefill_bf16_kernel(PrefillArgs a, int rb_first, int n_rb) {
         f16x8 kv[C::NS];
 #pragma unroll
         for (int st = 0; st < C::NS; ++st) kv[st] = *reinterpret_cast<const f16x8*>(kp + 16 * st);
-        const bf16* vb = base + C::NK * C::KSLOT + qr * C::VSTR + 32 * b + 8 * hh;
-        f16x8 vv[2][C::ND];
-#pragma unroll
-        for (int u = 0; u < 2; ++u)
-#pragma unroll
-            for (int db = 0; db < C::ND; ++db)
-                vv[u][db] = *reinterpret_cast<const f16x8*>(vb + 32 * db * C::VSTR + 16 * u);
-        // all operand reads of the block are in flight before its MFMA chain
+        // the K operands are in flight before the score chain starts
         __builtin_amdgcn_sched_barrier(0);
         f32x16 Sb = negm;
 #pragma unroll
@@ -257,6 +250,15 @@ void prefill_bf16_kernel(PrefillArgs a, int rb_first, int n_rb) {
                 Sb = mfma32h(kl, Qc[st], Sb);
             }
         }
+        // the V operands are read while the score chain and the softmax run
+        const bf16* vb = base + C::NK * C::KSLOT + qr * C::VSTR + 32 * b + 8 * hh;
+        f16x8 vv[2][C::ND];
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int db = 0; db < C::ND; ++db)
+                vv[u][db] = *reinterpret_cast<const f16x8*>(vb + 32 * db * C::VSTR + 16 * u);
+        __builtin_amdgcn_sched_barrier(0);
         if (masked) {
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
