@@ -140,7 +140,7 @@ def remap(x: int, G: int) -> int:
 
 def band(i: int, j: int, w_local: int, bifocal: bool = True) -> int:
     """0 masked (j > i), 1 local (0 <= i-j < w_local), 2 remote.  [TW] §二, [BT] §3.3."""
-    return int(_load().jlo_band(int(i), int(j), int(w_local), int(bool(bifocal))))
+    return int(_load().jlo_band(int(i), int(j), int(w_local), _mode(bifocal)))
 
 
 def rope(x, positions, rope_base: float) -> np.ndarray:
@@ -151,6 +151,15 @@ def rope(x, positions, rope_base: float) -> np.ndarray:
     out = np.empty((T, H, d), dtype=np.float64)
     _load().jlo_rope(_ptr(out, _f64p), _ptr(xa), dt, _ptr(pos, _i64p), T, H, d, float(rope_base))
     return out
+
+
+def _mode(bifocal) -> int:
+    """0 plain RoPE, 1 the method (integer grouping), 2 continuous interpolation
+    in the remote window; booleans map to 0 and 1."""
+    m = int(bifocal)
+    if m not in (0, 1, 2):
+        raise ValueError("bifocal must be 0, 1 or 2")
+    return m
 
 
 def _cu(cu_seqlens, T):
@@ -184,7 +193,7 @@ def prefill(q, k, v, *, w_pretrained, w_local, rope_base, softmax_scale, bifocal
     rc = _load().jlo_prefill(_ptr(o, _f64p), _ptr(lse, _f64p), _ptr(qa), _ptr(ka), _ptr(va), dt,
                              _ptr(cu, _i64p), len(cu) - 1, T, Hq, Hkv, d, int(w_pretrained),
                              int(w_local), float(rope_base), float(softmax_scale),
-                             int(bool(bifocal)), rp, R, int(n_threads))
+                             _mode(bifocal), rp, R, int(n_threads))
     if rc != 0:
         raise ValueError("oracle prefill rejected its arguments")
     return o, lse
@@ -234,7 +243,7 @@ def decode(q, k_cache, v_cache, seqlens, *, w_pretrained, w_local, rope_base, so
     lse = np.empty((B, Hq), dtype=np.float64)
     rc = _load().jlo_decode(_ptr(o, _f64p), _ptr(lse, _f64p), _ptr(qa), _ptr(ka), _ptr(va), dt,
                             _ptr(sl, _i64p), B, S_max, Hq, Hkv, d, int(w_pretrained), int(w_local),
-                            float(rope_base), float(softmax_scale), int(bool(bifocal)),
+                            float(rope_base), float(softmax_scale), _mode(bifocal),
                             int(n_threads))
     if rc != 0:
         raise ValueError("oracle decode rejected its arguments")
@@ -271,7 +280,7 @@ def prefill_chunk(q, k_cache, v_cache, seqlens, *, w_pretrained, w_local, rope_b
     rc = _load().jlo_prefill_chunk(_ptr(o, _f64p), _ptr(lse, _f64p), _ptr(qa), _ptr(ka),
                                    _ptr(va), dt, _ptr(cu, _i64p), _ptr(sl, _i64p), B, Tq, S_max,
                                    Hq, Hkv, d, int(w_pretrained), int(w_local), float(rope_base),
-                                   float(softmax_scale), int(bool(bifocal)), rp, R,
+                                   float(softmax_scale), _mode(bifocal), rp, R,
                                    int(n_threads))
     if rc != 0:
         raise ValueError("oracle chunked prefill rejected its arguments")

@@ -152,9 +152,22 @@ static int find_seq(const int64_t* cu, int n_seqs, int64_t r) {
     return -1;
 }
 
-/* Per-sequence rotated keys: kS[g][n] = R(n) k_n, kR[g][n] = R(f(n)) k_n. */
+/*
+ * Remote position of x in a sequence of length L.
+ *   bifocal == 1 (the method): f(x) = floor(x / G), G = G(L)  ([BT] §3.1).
+ *   bifocal == 2: the continuous-interpolation alternative the pages compare
+ *   the integer grouping against ([BT] §4.4, [TW] §八), read as x / s with the
+ *   real scale s = max(1, L / w_pretrained), so remote angles may fall between
+ *   the integer positions of pretraining.
+ */
+static double remote_pos(int64_t x, int64_t L, int64_t w, int mode) {
+    if (mode == 2) return L > w ? (double)(x * w) / (double)L : (double)x;
+    return (double)jlo_remap(x, jlo_group_size(L, w));
+}
+
+/* Per-sequence rotated keys: kS[g][n] = R(n) k_n, kR[g][n] = R(remote_pos(n)) k_n. */
 static void rotate_keys(double* kS, double* kR, const void* k, int dtype, int64_t start, int64_t L,
-                        int Hkv, int d, int64_t G, double base) {
+                        int Hkv, int d, int64_t w, int mode, double base) {
 #pragma omp parallel
     {
         double* tmp = (double*)malloc(sizeof(double) * (size_t)d);
@@ -164,7 +177,7 @@ static void rotate_keys(double* kS, double* kR, const void* k, int dtype, int64_
                 widen(tmp, k, dtype, ((start + n) * Hkv + g) * (int64_t)d, d);
                 int64_t dst = ((int64_t)g * L + n) * d;
                 rotate(kS + dst, tmp, (double)n, d, base);
-                rotate(kR + dst, tmp, (double)jlo_remap(n, G), d, base);
+                rotate(kR + dst, tmp, remote_pos(n, L, w, mode), d, base);
             }
         free(tmp);
     }
@@ -186,7 +199,9 @@ int jlo_prefill(double* o_sel, double* lse_sel, const void* q, const void* k, co
                 int dtype, const int64_t* cu, int n_seqs, int64_t T, int Hq, int Hkv, int d,
                 int64_t w_pretrained, int64_t w_local, double base, double scale, int bifocal,
                 const int64_t* rows, int64_t n_rows, int n_threads) {
-    if (Hkv <= 0 || Hq % Hkv != 0 || d <= 0 || d % 2 || w_pretrained < 1 || w_local < 0) return -1;
+    if (Hkv <= 0 || Hq % Hkv != 0 || d <= 0 || d % 2 || w_pretrained < 1 || w_local < 0 ||
+        bifocal < 0 || bifocal > 2)
+        return -1;
     if (cu[0] != 0 || cu[n_seqs] != T) return -1;
 #ifdef _OPENMP
     if (n_threads > 0) omp_set_num_threads(n_threads);
@@ -203,10 +218,9 @@ int jlo_prefill(double* o_sel, double* lse_sel, const void* q, const void* k, co
             cnt += (r >= start && r < start + L);
         }
         if (cnt == 0) continue;
-        const int64_t G = jlo_group_size(L, w_pretrained);
         double* kS = (double*)malloc(sizeof(double) * (size_t)(Hkv * L * d));
         double* kR = (double*)malloc(sizeof(double) * (size_t)(Hkv * L * d));
-        rotate_keys(kS, kR, k, dtype, start, L, Hkv, d, G, base);
+        rotate_keys(kS, kR, k, dtype, start, L, Hkv, d, w_pretrained, bifocal, base);
 #pragma omp parallel
         {
             double* qr = (double*)malloc(sizeof(double) * (size_t)d);
@@ -222,7 +236,7 @@ int jlo_prefill(double* o_sel, double* lse_sel, const void* q, const void* k, co
                     const int g = h / grp;
                     widen(qr, q, dtype, (r * Hq + h) * (int64_t)d, d);
                     rotate(qS, qr, (double)i, d, base);
-                    rotate(qR, qr, (double)jlo_remap(i, G), d, base);
+                    rotate(qR, qr, remote_pos(i, L, w_pretrained, bifocal), d, base);
                     for (int64_t j = 0; j <= i; ++j) {
                         const double* kj;
                         const double* qi;
@@ -356,7 +370,9 @@ int jlo_decode(double* o, double* lse, const void* q, const void* kc, const void
                const int64_t* seqlens, int B, int64_t S_max, int Hq, int Hkv, int d,
                int64_t w_pretrained, int64_t w_local, double base, double scale, int bifocal,
                int n_threads) {
-    if (Hkv <= 0 || Hq % Hkv != 0 || d <= 0 || d % 2 || w_pretrained < 1 || w_local < 0) return -1;
+    if (Hkv <= 0 || Hq % Hkv != 0 || d <= 0 || d % 2 || w_pretrained < 1 || w_local < 0 ||
+        bifocal < 0 || bifocal > 2)
+        return -1;
     for (int b = 0; b < B; ++b)
         if (seqlens[b] < 1 || seqlens[b] > S_max) return -1;
 #ifdef _OPENMP
@@ -369,8 +385,7 @@ int jlo_decode(double* o, double* lse, const void* q, const void* kc, const void
     for (int b = 0; b < B; ++b)
         for (int h = 0; h < Hq; ++h) {
             const int64_t L = seqlens[b], p = L - 1;
-            const int64_t G = jlo_group_size(L, w_pretrained);
-            const int g = h / grp;
+                const int g = h / grp;
             double* qr = (double*)malloc(sizeof(double) * (size_t)d);
             double* qS = (double*)malloc(sizeof(double) * (size_t)d);
             double* qR = (double*)malloc(sizeof(double) * (size_t)d);
@@ -379,13 +394,13 @@ int jlo_decode(double* o, double* lse, const void* q, const void* kc, const void
             double* sc = (double*)malloc(sizeof(double) * (size_t)L);
             widen(qr, q, dtype, ((int64_t)b * Hq + h) * d, d);
             rotate(qS, qr, (double)p, d, base);
-            rotate(qR, qr, (double)jlo_remap(p, G), d, base);
+            rotate(qR, qr, remote_pos(p, L, w_pretrained, bifocal), d, base);
             for (int64_t j = 0; j < L; ++j) {
                 widen(kj, kc, dtype, (((int64_t)b * S_max + j) * Hkv + g) * d, d);
                 if (jlo_band(p, j, w_local, bifocal) == 1) {
                     sc[j] = scale * dot(qS, kj, d);
                 } else {
-                    rotate(kc2, kj, (double)(jlo_remap(j, G) - j), d, base);
+                    rotate(kc2, kj, remote_pos(j, L, w_pretrained, bifocal) - (double)j, d, base);
                     sc[j] = scale * dot(qR, kc2, d);
                 }
             }
@@ -419,7 +434,9 @@ int jlo_prefill_chunk(double* o_sel, double* lse_sel, const void* q, const void*
                       int B, int64_t Tq, int64_t S_max, int Hq, int Hkv, int d,
                       int64_t w_pretrained, int64_t w_local, double base, double scale,
                       int bifocal, const int64_t* rows, int64_t n_rows, int n_threads) {
-    if (Hkv <= 0 || Hq % Hkv != 0 || d <= 0 || d % 2 || w_pretrained < 1 || w_local < 0) return -1;
+    if (Hkv <= 0 || Hq % Hkv != 0 || d <= 0 || d % 2 || w_pretrained < 1 || w_local < 0 ||
+        bifocal < 0 || bifocal > 2)
+        return -1;
     if (cu_q[0] != 0 || cu_q[B] != Tq) return -1;
     for (int b = 0; b < B; ++b) {
         const int64_t C = cu_q[b + 1] - cu_q[b];
@@ -440,7 +457,6 @@ int jlo_prefill_chunk(double* o_sel, double* lse_sel, const void* q, const void*
             cnt += (r >= qstart && r < qstart + C);
         }
         if (cnt == 0) continue;
-        const int64_t G = jlo_group_size(L, w_pretrained);
         /* kS[g][j] = cache row j as stored, kR[g][j] = R(f(j) - j) cache row j */
         double* kS = (double*)malloc(sizeof(double) * (size_t)(Hkv * L * d));
         double* kR = (double*)malloc(sizeof(double) * (size_t)(Hkv * L * d));
@@ -449,7 +465,8 @@ int jlo_prefill_chunk(double* o_sel, double* lse_sel, const void* q, const void*
             for (int g = 0; g < Hkv; ++g) {
                 double* ks = kS + ((int64_t)g * L + j) * d;
                 widen(ks, kc, dtype, (((int64_t)b * S_max + j) * Hkv + g) * d, d);
-                rotate(kR + ((int64_t)g * L + j) * d, ks, (double)(jlo_remap(j, G) - j), d, base);
+                rotate(kR + ((int64_t)g * L + j) * d, ks,
+                       remote_pos(j, L, w_pretrained, bifocal) - (double)j, d, base);
             }
 #pragma omp parallel
         {
@@ -466,7 +483,7 @@ int jlo_prefill_chunk(double* o_sel, double* lse_sel, const void* q, const void*
                     const int g = h / grp;
                     widen(qr, q, dtype, (r * Hq + h) * (int64_t)d, d);
                     rotate(qS, qr, (double)p, d, base);
-                    rotate(qR, qr, (double)jlo_remap(p, G), d, base);
+                    rotate(qR, qr, remote_pos(p, L, w_pretrained, bifocal), d, base);
                     for (int64_t j = 0; j <= p; ++j) {
                         const int local = jlo_band(p, j, w_local, bifocal) == 1;
                         const double* kj = (local ? kS : kR) + ((int64_t)g * L + j) * d;

@@ -239,7 +239,7 @@ def test_zero_query_closed_form():
         np.testing.assert_allclose(lse[:, h], np.log(np.arange(1, T + 1)), atol=1e-13)
 
 
-def _probe(i, jstar, L, w_pre, w_local, kappa, d=2):
+def _probe(i, jstar, L, w_pre, w_local, kappa, d=2, bifocal=1):
     """Boundary probe: q_i = e_0, key j* = kappa e_0, all other keys 0.  Pair 0
     has theta_0 = 1, so the score of j* is kappa cos(distance) with the
     distance i - j* (standard) or f(i) - f(j*) (remapped); every other score is
@@ -250,7 +250,7 @@ def _probe(i, jstar, L, w_pre, w_local, kappa, d=2):
     k[jstar, 0, 0] = kappa
     v = np.zeros((L, 1, d))
     _, lse = oracle.prefill(q, k, v, w_pretrained=w_pre, w_local=w_local, rope_base=1e4,
-                            softmax_scale=1.0, rows=[i])
+                            softmax_scale=1.0, rows=[i], bifocal=bifocal)
     return lse[0, 0]
 
 
@@ -501,3 +501,75 @@ def test_decode_fp8_is_decode_of_dequantized_cache():
     o2, l2 = oracle.decode(q, kd, vd, [30, 12], **kw)
     np.testing.assert_array_equal(o, o2)
     np.testing.assert_array_equal(lse, l2)
+
+
+
+# ---- continuous interpolation in the remote window (bifocal = 2) ----------
+
+def test_interp_probe_closed_form():
+    """[BT] §4.4 / [TW] §八 variant: a remote pair's angle is (i - j) / s with the
+    real scale s = L / w_pretrained (the probe of the boundary test, read off the
+    LSE); local pairs keep i - j.  L / w = 2.6 is not an integer, so the angles
+    differ from the integer grouping's f(i) - f(j) (G = 3)."""
+    L, w_pre, w_local, kappa = 52, 20, 5, 3.0
+    s = L / w_pre
+    checked = 0
+    for i in range(w_local, L):
+        for jstar in (0, i // 2, i - w_local, i - w_local + 1, i - 1):
+            if jstar < 0 or jstar > i:
+                continue
+            remote = i - jstar >= w_local
+            dist = (i - jstar) / s if remote else i - jstar
+            want = math.log(i + math.exp(kappa * math.cos(dist)))
+            got = _probe(i, jstar, L, w_pre, w_local, kappa, bifocal=2)
+            assert abs(got - want) < 1e-12, (i, jstar)
+            checked += 1
+    assert checked >= 150
+
+
+def test_interp_equals_grouping_on_multiples_of_an_integer_scale():
+    """When L / w_pretrained is an integer G, x / s = floor(x / G) at multiples
+    of G: for a query and a key both at multiples of G the two variants give the
+    same remote angle, elsewhere (in general) not."""
+    L, w_pre, w_local, kappa = 60, 20, 4, 3.0
+    G = oracle.group_size(L, w_pre)
+    assert G * w_pre == L
+    same = diff = 0
+    for i in range(w_local, L):
+        for jstar in range(0, i - w_local + 1):
+            a = _probe(i, jstar, L, w_pre, w_local, kappa, bifocal=2)
+            b = _probe(i, jstar, L, w_pre, w_local, kappa, bifocal=1)
+            if i % G == 0 and jstar % G == 0:
+                assert abs(a - b) < 1e-12
+                same += 1
+            elif abs(a - b) > 1e-6:
+                diff += 1
+    assert same >= 20 and diff >= 100
+
+
+@pytest.mark.parametrize("L", [10, 20, 21, 33, 47])
+def test_interp_short_sequences_and_decode_chunk_paths(L):
+    """bifocal = 2: L <= w_pretrained is plain attention (s = 1); decode (the
+    correction rotation R(j / s - j) of cache keys) and the chunk form equal the
+    prefill definition on the same keys, across s = 1 .. 2.35."""
+    rng = np.random.default_rng(L)
+    Hq, Hkv, d, base, scale, w_pre, w_local = 4, 2, 16, 1e4, 0.4, 20, 4
+    q = rng.standard_normal((L, Hq, d))
+    k = rng.standard_normal((L, Hkv, d))
+    v = rng.standard_normal((L, Hkv, d))
+    kw = dict(w_pretrained=w_pre, w_local=w_local, rope_base=base, softmax_scale=scale)
+    o2, l2 = oracle.prefill(q, k, v, bifocal=2, **kw)
+    if L <= w_pre:
+        o0, l0 = oracle.prefill(q, k, v, bifocal=0, **kw)
+        np.testing.assert_allclose(o2, o0, rtol=0, atol=1e-12)
+        np.testing.assert_allclose(l2, l0, rtol=0, atol=1e-12)
+    cache = oracle.rope(k, np.arange(L), base)
+    od, ld = oracle.decode(q[L - 1:L], cache[None], v[None], [L], bifocal=2, **kw)
+    np.testing.assert_allclose(od[0], o2[L - 1], rtol=0, atol=1e-11)
+    np.testing.assert_allclose(ld[0], l2[L - 1], rtol=0, atol=1e-11)
+    C = (L + 1) // 2
+    oc, lc = oracle.prefill_chunk(q[L - C:], cache[None], v[None], [L], bifocal=2, **kw)
+    np.testing.assert_allclose(oc, o2[L - C:], rtol=0, atol=1e-11)
+    np.testing.assert_allclose(lc, l2[L - C:], rtol=0, atol=1e-11)
+    with pytest.raises(ValueError):
+        oracle.prefill(q, k, v, bifocal=3, **kw)
