@@ -181,6 +181,15 @@ def main():
         t_plain.append((time.perf_counter() - t0) * 1e3)
     out["prefill_plain_ms"] = round(min(t_plain), 3)
     out["prefill_bifocal_over_plain"] = round(ms_per_step / min(t_plain), 4)
+    # the remote-window variant with continuous interpolation (bifocal = 2)
+    t_interp = []
+    for _ in range(2):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        jl.bifocal_prefill(q, k, v, bifocal=2, **kw)
+        torch.cuda.synchronize()
+        t_interp.append((time.perf_counter() - t0) * 1e3)
+    out["prefill_interp_ms"] = round(min(t_interp), 3)
     del o, lse
 
     if not args.no_three_call:
@@ -357,18 +366,20 @@ def bench_decode(jl, inputs, torch, iters, extras=True):
     run(True, 10)
     run(False, 10)
     if extras:
+        run(2, 10)
         run_fp8(True, 10)
         run_fp8(False, 10)
     for page in pools:
         run_paged(page, 10)
     tb, tp, tpg = [], [], {page: [] for page in pools}
-    t8b, t8p = [], []
+    t8b, t8p, t2 = [], [], []
     for _ in range(4):
         tb.append(run(True, iters // 4))
         tp.append(run(False, iters // 4))
         for page in pools:
             tpg[page].append(run_paged(page, iters // 4))
         if extras:
+            t2.append(run(2, iters // 4))
             t8b.append(run_fp8(True, iters // 4))
             t8p.append(run_fp8(False, iters // 4))
     jl.profile_enable(True)
@@ -398,6 +409,7 @@ def bench_decode(jl, inputs, torch, iters, extras=True):
     }
     if not extras:
         return res
+    res["interp_us_per_token"] = round(min(t2), 2)
     res["paged_us_per_token"] = {"page_%d" % page: round(min(t), 2) for page, t in tpg.items()}
     res["fp8"] = {"us_per_token": round(min(t8b), 2), "plain_us_per_token": round(min(t8p), 2),
                   "overhead_pct": round(100.0 * (min(t8b) - min(t8p)) / min(t8p), 2),

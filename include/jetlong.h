@@ -63,7 +63,12 @@ typedef struct {
     int32_t w_local;       /* >= 0: local window size in tokens ([TW] §二; 2048 there)     */
     double rope_base;      /* > 0: theta_t = rope_base^(-2t/d)                             */
     float softmax_scale;   /* > 0 and finite                                               */
-    int32_t bifocal;       /* 1: Jet-Long; 0: plain RoPE causal attention (same kernels)   */
+    int32_t bifocal;       /* 1: Jet-Long; 0: plain RoPE causal attention (same kernels);  */
+                           /* 2: the remote-window variant the pages compare against     */
+                           /*    ([BT] §4.4, [TW] §八): continuous interpolation, remote  */
+                           /*    position x / s with the real s = max(1, L / w_pretrained) */
+                           /*    in place of floor(x / G).  bf16 prefill, chunked prefill */
+                           /*    and decode only (JL_ERR_UNSUPPORTED elsewhere)           */
 } jl_params;
 
 /* JL_ABI_VERSION of the built library. */

@@ -187,8 +187,8 @@ static jl_status check_params(const jl_params* p) {
         return fail(JL_ERR_INVALID_ARGUMENT, "rope_base must be finite and > 0");
     if (!(p->softmax_scale > 0.0f) || !isfinite(p->softmax_scale))
         return fail(JL_ERR_INVALID_ARGUMENT, "softmax_scale must be finite and > 0");
-    if (p->bifocal != 0 && p->bifocal != 1)
-        return fail(JL_ERR_INVALID_ARGUMENT, "bifocal must be 0 or 1");
+    if (p->bifocal < 0 || p->bifocal > 2)
+        return fail(JL_ERR_INVALID_ARGUMENT, "bifocal must be 0, 1 or 2");
     return JL_OK;
 }
 
@@ -301,6 +301,9 @@ jl_status jl_bifocal_prefill(void* o, float* lse, const void* q, const void* k, 
     a.w_local = params->w_local; a.bifocal = params->bifocal;
     a.softmax_scale = params->softmax_scale;
     a.tab = make_rope_freq(params->rope_base, d);
+    a.w_pretrained = params->w_pretrained;
+    if (params->bifocal == 2 && dtype != JL_DTYPE_BF16)
+        return fail(JL_ERR_UNSUPPORTED, "continuous interpolation (bifocal = 2) is bf16 only");
 
     hipStream_t s = (hipStream_t)stream;
     hipError_t e = launch_plan((int32_t*)((char*)workspace + lay.plan), cu_seqlens, n_seqs, T,
@@ -354,7 +357,7 @@ jl_status jl_bifocal_prefill_three_call(void* o, float* lse, const void* q, cons
         return fail(JL_ERR_INVALID_ARGUMENT, "null pointer argument");
     jl_status st = check_params(params);
     if (st != JL_OK) return st;
-    if (!params->bifocal) return fail(JL_ERR_INVALID_ARGUMENT, "the unfused form needs bifocal = 1");
+    if (params->bifocal != 1) return fail(JL_ERR_INVALID_ARGUMENT, "the unfused form needs bifocal = 1");
     if (T < 1) return fail(JL_ERR_INVALID_ARGUMENT, "T must be >= 1");
     if (n_seqs < 1) return fail(JL_ERR_INVALID_ARGUMENT, "n_seqs must be >= 1");
     if (!cu_seqlens && n_seqs != 1)
@@ -473,8 +476,9 @@ static jl_status decode_impl(const DecodeCall& c, const jl_params* params, jl_dt
     if (c.Hq / c.Hkv > 16) return fail(JL_ERR_UNSUPPORTED, "decode supports Hq / Hkv <= 16");
     st = check_dtype_d(dtype, c.d);
     if (st != JL_OK) return st;
-    if ((paged || c.fp8) && dtype != JL_DTYPE_BF16)
-        return fail(JL_ERR_UNSUPPORTED, "paged and fp8 decode take bf16 queries");
+    if ((paged || c.fp8 || params->bifocal == 2) && dtype != JL_DTYPE_BF16)
+        return fail(JL_ERR_UNSUPPORTED,
+                    "paged, fp8 and continuous-interpolation decode take bf16 queries");
     if (paged) {
         if (c.n_pages > (1LL << 40) / ((int64_t)c.page_size * c.Hkv * c.d))
             return fail(JL_ERR_INVALID_ARGUMENT, "page pool too large");
@@ -642,6 +646,7 @@ static jl_status chunk_call(PrefillArgs& a, const int32_t* cu_seqlens_q,
     a.w_local = params->w_local; a.bifocal = params->bifocal;
     a.softmax_scale = params->softmax_scale;
     a.tab = make_rope_freq(params->rope_base, a.d);
+    a.w_pretrained = params->w_pretrained;
     hipStream_t s = (hipStream_t)stream;
     hipError_t e = launch_plan_chunk((int32_t*)((char*)workspace + lay.plan), cu_seqlens_q,
                                      seqlens_k, a.n_seqs, a.T, a.max_seqlen, a.max_seqlen_k,

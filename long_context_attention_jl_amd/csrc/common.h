@@ -131,6 +131,15 @@ __device__ __forceinline__ void rope_cs(int64_t p, double rev_t, float& c, float
     sincosf(a, &s, &c);
 }
 
+// Angle given directly in revolutions (any real position times theta_t / 2pi),
+// reduced in fp64, through the hardware sine and cosine.
+__device__ __forceinline__ void rope_cs_rev(double x, float& c, float& s) {
+    x -= rint(x);
+    const float r = (float)x;
+    s = __builtin_amdgcn_sinf(r);
+    c = __builtin_amdgcn_cosf(r);
+}
+
 // Same angle through the hardware sine and cosine (v_sin_f32 / v_cos_f32 take
 // their argument in revolutions); used where many angles are needed per key.
 __device__ __forceinline__ void rope_cs_hw(int64_t p, double rev_t, float& c, float& s) {

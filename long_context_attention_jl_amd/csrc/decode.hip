@@ -539,6 +539,11 @@ __global__ __launch_bounds__(512) void decode_split_bf16_kernel(DecodeArgs a) {
     const bool bif = BIF && G > 1;
     const int32_t fp = remap(p, G);
     const int32_t rem_last = p - a.w_local;  // keys j <= rem_last are remote (if bif)
+    // continuous-interpolation variant (bifocal 2): remote positions x / s,
+    // s = L / w_pretrained; within a stage the key correction is then
+    // -(j - jb)(1 - 1/s) and the table is indexed by j - jb
+    const bool interp = BIF && a.bifocal == 2;
+    const double rsc = interp ? (double)a.w_pretrained / (double)max(L, 1) : 1.0;
     // chunks start at z0 + split * chunk, z0 in (-kStageB, 0], so that the
     // first local key starts a stage; positions below 0 are masked
     int32_t z0 = 0;
@@ -645,19 +650,25 @@ __global__ __launch_bounds__(512) void decode_split_bf16_kernel(DecodeArgs a) {
         const int nst = min((kend - kbeg + kStageB - 1) / kStageB, (int32_t)kDecodeMaxStagesB);
         for (int x = threadIdx.x; x < (nst + 1) * HALF; x += blockDim.x) {
             const int st = x / HALF;
-            int64_t pos = p;
+            float cs, sn;
             if (st < nst) {
                 const int32_t jbs = max(kbeg + kStageB * st, 0);
-                pos = (int64_t)fp - remap(jbs, G) + jbs;
+                if (interp)  // R(p / s - jb / s + jb)
+                    rope_cs_rev(((double)(p - jbs) * rsc + (double)jbs) * rv, cs, sn);
+                else
+                    rope_cs_hw((int64_t)fp - remap(jbs, G) + jbs, rv, cs, sn);
+            } else {
+                rope_cs_hw(p, rv, cs, sn);
             }
-            float cs, sn;
-            rope_cs_hw(pos, rv, cs, sn);
             qtab[(st < nst ? st : QLOC) * HALF + x % HALF] = make_float2(cs, sn);
         }
         if (BIF && bif) {
             for (int x = threadIdx.x; x < kStageB * HALF; x += blockDim.x) {
                 float cs, sn;
-                rope_cs_hw(-(int64_t)(x / HALF), rv, cs, sn);
+                if (interp)  // key delta positions past the stage base: R(-delta (1 - 1/s))
+                    rope_cs_rev(-(double)(x / HALF) * (1.0 - rsc) * rv, cs, sn);
+                else
+                    rope_cs_hw(-(int64_t)(x / HALF), rv, cs, sn);
                 tab[(x / HALF) * TSTR + x % HALF] = make_float2(cs, sn);
             }
         }
@@ -852,7 +863,7 @@ __global__ __launch_bounds__(512) void decode_split_bf16_kernel(DecodeArgs a) {
             int32_t fd = (int32_t)((float)(r0 + dl) * invG);
             if ((fd + 1) * G <= r0 + dl) ++fd;
             if (fd * G > r0 + dl) --fd;
-            const int32_t uu = min(max(dl - fd, 0), kStageB - 1);
+            const int32_t uu = interp ? min(dl, kStageB - 1) : min(max(dl - fd, 0), kStageB - 1);
             sacc = scores_remote(kcur, uu);
         } else {
             sacc = scores_local(kcur);

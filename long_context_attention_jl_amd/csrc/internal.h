@@ -64,10 +64,11 @@ struct PrefillArgs {
     PrefillLayout lay;
     int32_t n_seqs, Hq, Hkv, d, max_seqlen;
     int64_t T;
-    int32_t w_local, bifocal;
+    int32_t w_local, bifocal;  // bifocal: 0 plain, 1 integer grouping, 2 continuous interpolation
     float softmax_scale;
     RopeFreq tab;
-    int32_t mode;  // 0 bifocal; unfused calls: 1 all pairs remapped, 2 local standard, 3 local remapped
+    int32_t mode;
+    int32_t w_pretrained;  // for the continuous scale s = L / w_pretrained (bifocal 2)  // 0 bifocal; unfused calls: 1 all pairs remapped, 2 local standard, 3 local remapped
     // A chunk against a cache (chunked != 0): the queries are each sequence's
     // newest rows, keys and values are read from the cache, whose keys already
     // carry standard RoPE.  Flat cache: sequence s owns rows [s * S_max, ...);

@@ -128,6 +128,10 @@ void prefill_bf16_kernel(PrefillArgs a, int rb_first, int n_rb) {
     const bool do_local = mode != 1;
     const bool local_remapped = mode == 3;
     const int g = head / (a.Hq / a.Hkv);
+    // remote queries of the continuous-interpolation variant (bifocal 2) sit at
+    // row / s, s = len / w_pretrained
+    const bool interp = a.bifocal == 2;
+    const double rsc = interp ? (double)a.w_pretrained / (double)len : 1.0;
     const int32_t wr0 = row0 + wave * kWaveRows;
     const int32_t wr_end = min(wr0 + kWaveRows, len);
     const int32_t wlo = max(wr0, q0);  // the wave's first query row
@@ -172,7 +176,8 @@ void prefill_bf16_kernel(PrefillArgs a, int rb_first, int n_rb) {
                     x1 = (float)qp[t + HALF];
                 }
                 float c, sn;
-                rope_cs_hw(remapped ? remap(row, G) : row, rv, c, sn);
+                if (remapped && interp) rope_cs_hw(row, rv * rsc, c, sn);
+                else rope_cs_hw(remapped ? remap(row, G) : row, rv, c, sn);
                 const float y0 = (x0 * c - x1 * sn) * qscale, y1 = (x1 * c + x0 * sn) * qscale;
                 qimg[r * C::KSTR + t] = lo ? (f16)(y0 - (float)(f16)y0) : (f16)y0;
                 qimg[r * C::KSTR + t + HALF] = lo ? (f16)(y1 - (float)(f16)y1) : (f16)y1;

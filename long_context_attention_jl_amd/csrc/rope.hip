@@ -237,13 +237,20 @@ __global__ __launch_bounds__(256) void kv_prepass_bf16_kernel(PrefillArgs a) {
     const bool lo_row = n < kPreciseRows;
     const int64_t krow = valid ? src_row(n) : 0;
     float cs[TPC], sn[TPC], cr[TPC], sr[TPC];
+    // remote position: f(n) = floor(n / G), or n / s with s = len / w_pretrained
+    // for the continuous-interpolation variant (bifocal 2)
+    const bool interp = a.bifocal == 2;
+    const double rsc = interp ? (double)a.w_pretrained / (double)len : 1.0;
     if (valid) {
         const int32_t fn = remap(n, G);
 #pragma unroll
         for (int u = 0; u < TPC; ++u) {
             const double rv = rope_rev(a.tab, c * TPC + u);
             rope_cs(cache ? 0 : n, rv, cs[u], sn[u]);
-            if (bif) rope_cs(cache ? fn - n : fn, rv, cr[u], sr[u]);
+            if (bif) {
+                if (interp) rope_cs(n, rv * (cache ? rsc - 1.0 : rsc), cr[u], sr[u]);
+                else rope_cs(cache ? fn - n : fn, rv, cr[u], sr[u]);
+            }
         }
     }
     for (int g = 0; g < a.Hkv; ++g) {

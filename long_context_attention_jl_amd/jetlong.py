@@ -157,8 +157,10 @@ def _stream() -> int:
 
 
 def _params(w_pretrained, w_local, rope_base, softmax_scale, bifocal) -> jl_params:
+    """bifocal: False / 0 plain RoPE, True / 1 the method (integer grouping in the
+    remote window), 2 continuous interpolation in the remote window."""
     return jl_params(int(w_pretrained), int(w_local), float(rope_base), float(softmax_scale),
-                     1 if bifocal else 0)
+                     int(bifocal))
 
 
 def abi_version() -> int:
@@ -251,7 +253,7 @@ def bifocal_prefill_three_call(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor
 
 
 def bifocal_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, w_pretrained: int,
-                    w_local: int, rope_base: float, softmax_scale: float, bifocal: bool = True,
+                    w_local: int, rope_base: float, softmax_scale: float, bifocal: Union[bool, int] = True,
                     cu_seqlens: Union[None, Sequence[int], torch.Tensor] = None,
                     max_seqlen: Optional[int] = None, k_rot_out: Optional[torch.Tensor] = None,
                     workspace: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
@@ -285,7 +287,7 @@ def decode_workspace_bytes(B: int, max_seqlen_k: int, Hq: int, Hkv: int, d: int,
 
 def bifocal_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                    seqlens_k: Union[Sequence[int], torch.Tensor], *, w_pretrained: int,
-                   w_local: int, rope_base: float, softmax_scale: float, bifocal: bool = True,
+                   w_local: int, rope_base: float, softmax_scale: float, bifocal: Union[bool, int] = True,
                    max_seqlen_k: Optional[int] = None, workspace: Optional[torch.Tensor] = None,
                    out: Optional[torch.Tensor] = None,
                    lse_out: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
@@ -332,7 +334,7 @@ def _seqlens(seqlens_k, max_seqlen_k, dev):
 def bifocal_decode_paged(q: torch.Tensor, k_pages: torch.Tensor, v_pages: torch.Tensor,
                          block_table: torch.Tensor, seqlens_k: Union[Sequence[int], torch.Tensor],
                          *, w_pretrained: int, w_local: int, rope_base: float,
-                         softmax_scale: float, bifocal: bool = True,
+                         softmax_scale: float, bifocal: Union[bool, int] = True,
                          max_seqlen_k: Optional[int] = None,
                          workspace: Optional[torch.Tensor] = None,
                          out: Optional[torch.Tensor] = None,
@@ -381,7 +383,7 @@ def _chunk_common(q, seqlens_k, cu_seqlens_q, max_seqlen_q, max_seqlen_k, dev, o
 def bifocal_prefill_chunk(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                           seqlens_k: Union[Sequence[int], torch.Tensor], *, w_pretrained: int,
                           w_local: int, rope_base: float, softmax_scale: float,
-                          bifocal: bool = True, cu_seqlens_q=None,
+                          bifocal: Union[bool, int] = True, cu_seqlens_q=None,
                           max_seqlen_q: Optional[int] = None,
                           max_seqlen_k: Optional[int] = None,
                           workspace: Optional[torch.Tensor] = None,
@@ -411,7 +413,7 @@ def bifocal_prefill_chunk_paged(q: torch.Tensor, k_pages: torch.Tensor, v_pages:
                                 block_table: torch.Tensor,
                                 seqlens_k: Union[Sequence[int], torch.Tensor], *,
                                 w_pretrained: int, w_local: int, rope_base: float,
-                                softmax_scale: float, bifocal: bool = True, cu_seqlens_q=None,
+                                softmax_scale: float, bifocal: Union[bool, int] = True, cu_seqlens_q=None,
                                 max_seqlen_q: Optional[int] = None,
                                 max_seqlen_k: Optional[int] = None,
                                 workspace: Optional[torch.Tensor] = None,
@@ -463,7 +465,7 @@ def kv_quantize_fp8(x: torch.Tensor, scale, out: Optional[torch.Tensor] = None) 
 def bifocal_decode_fp8(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, k_scale,
                        v_scale, seqlens_k: Union[Sequence[int], torch.Tensor], *,
                        w_pretrained: int, w_local: int, rope_base: float, softmax_scale: float,
-                       bifocal: bool = True, max_seqlen_k: Optional[int] = None,
+                       bifocal: Union[bool, int] = True, max_seqlen_k: Optional[int] = None,
                        block_table: Optional[torch.Tensor] = None,
                        workspace: Optional[torch.Tensor] = None,
                        out: Optional[torch.Tensor] = None,

@@ -82,7 +82,8 @@ def _prefill(**kw):
     (dict(d=96), 2), (dict(d=65), 1), (dict(dtype=7), 2),
     (dict(params=_params(w_pretrained=0)), 1), (dict(params=_params(w_local=-1)), 1),
     (dict(params=_params(rope_base=0.0)), 1), (dict(params=_params(softmax_scale=0.0)), 1),
-    (dict(params=_params(softmax_scale=float("inf"))), 1), (dict(params=_params(bifocal=2)), 1),
+    (dict(params=_params(softmax_scale=float("inf"))), 1), (dict(params=_params(bifocal=3)), 1),
+    (dict(params=_params(bifocal=-1)), 1), (dict(params=_params(bifocal=2), dtype=0), 2),
     (dict(ws_bytes=1000), 3), (dict(ws=FAKE * 8 + 4), 1), (dict(o=FAKE * 3), 1),
     (dict(krot=FAKE * 4), 1), (dict(cu=FAKE * 9, n_seqs=70000, T=1 << 20, max_seqlen=1024), 2),
 ])
@@ -106,7 +107,8 @@ def _three_call(**kw):
 @pytest.mark.parametrize("kw,status", [
     (dict(o=None), 1), (dict(ws=None), 1), (dict(params=None), 1), (dict(T=0), 1),
     (dict(n_seqs=2), 1), (dict(max_seqlen=2000), 1), (dict(Hq=30), 1), (dict(d=96), 2),
-    (dict(dtype=0), 2), (dict(params=_params(bifocal=0)), 1), (dict(ws_bytes=1000), 3),
+    (dict(dtype=0), 2), (dict(params=_params(bifocal=0)), 1), (dict(params=_params(bifocal=2)), 1),
+    (dict(ws_bytes=1000), 3),
     (dict(ws=FAKE * 8 + 4), 1), (dict(o=FAKE * 3), 1),
 ])
 def test_three_call_validation(kw, status):
@@ -155,7 +157,8 @@ def _decode(**kw):
     (dict(max_L=0), 1), (dict(S_max=100), 1), (dict(Hq=33), 1), (dict(Hq=34, Hkv=2), 2),
     (dict(d=32), 2), (dict(dtype=3), 2), (dict(params=_params(w_local=-5)), 1),
     (dict(ws_bytes=16), 3), (dict(ws=FAKE * 8 + 128), 1), (dict(o=FAKE * 4), 1),
-    (dict(B=70000), 2),
+    (dict(B=70000), 2), (dict(params=_params(bifocal=2), dtype=0), 2),
+    (dict(params=_params(bifocal=5)), 1),
 ])
 def test_decode_validation(kw, status):
     assert _decode(**kw) == status
