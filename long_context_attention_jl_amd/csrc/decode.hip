@@ -637,6 +637,20 @@ __global__ __launch_bounds__(512) void decode_split_bf16_kernel(DecodeArgs a) {
     VRAW vA[NI], vB[NI], vC[NI];
 
     KRAW kA[NST], kB[NST], kC[NST];
+    // query first (unconditional loads from a clamped head; other lanes zeroed)
+    const int hq = PACK ? (n & (GQ - 1)) : n;
+    const bool qlo = PACK && n >= GQ;
+    bf16x8 qraw[NST];
+    {
+        const bool qok = hq < grp && (!PACK || n < 2 * GQ);
+        const int hq_c = min(hq, grp - 1);
+        const bf16* qp = (const bf16*)a.q + ((int64_t)b * a.Hq + kvh_c * grp + hq_c) * D + 8 * c;
+#pragma unroll
+        for (int s = 0; s < NST; ++s) {
+            const bf16x8 x = *reinterpret_cast<const bf16x8*>(qp + 32 * s);
+            qraw[s] = qok ? x : bf16x8{};
+        }
+    }
     load_k(kbeg, kA);
     load_vr(kbeg, vA);
     load_k(kbeg + kTile, kB);
@@ -679,16 +693,6 @@ __global__ __launch_bounds__(512) void decode_split_bf16_kernel(DecodeArgs a) {
     // ---- query (as in the generic kernel) ----
     const float qscale = a.softmax_scale * kLog2e;
     const float kscale = FP8 && a.k_scale ? a.k_scale[kvh_c] : 1.0f;
-    const int hq = PACK ? (n & (GQ - 1)) : n;
-    const bool qlo = PACK && n >= GQ;
-    bf16x8 qraw[NST];
-    {
-        const bool qok = hq < grp && (!PACK || n < 2 * GQ);
-        const bf16* qp = (const bf16*)a.q + ((int64_t)b * a.Hq + kvh * grp + hq) * D + 8 * c;
-#pragma unroll
-        for (int s = 0; s < NST; ++s)
-            qraw[s] = qok ? *reinterpret_cast<const bf16x8*>(qp + 32 * s) : bf16x8{};
-    }
     OV Q[NST];
     OV Qlo[PACK ? 1 : NST];
     auto rotate_q = [&](int row) __attribute__((always_inline)) {
