@@ -314,10 +314,16 @@ void prefill_bf16_kernel(PrefillArgs a, int rb_first, int n_rb) {
 
     auto compute = [&](int tau, const bf16* base, bool remote_phase)  __attribute__((always_inline)) {
         const uint32_t want = (bif && remote_phase) ? kHasRemote : kHasLocal;
+        // most tiles hold only pairs of the phase for every row of the wave
+        // (no band edge, no diagonal): skip the per-block classification
+        const int32_t jl = tau * kBN + kBN - 1;  // the tile's last key
+        const bool pure = (bif && remote_phase)
+                              ? jl <= wlo - wl
+                              : (jl <= wlo && (!bif || (wr_end - 1) - tau * kBN < wl));
 #pragma unroll
         for (int b = 0; b < 2; ++b) {
             const int32_t jb = tau * kBN + 32 * b;
-            const uint32_t cls = tile_class32(wlo, wr_end, jb, jb + 32, wl, bif);
+            const uint32_t cls = pure ? want : tile_class32(wlo, wr_end, jb, jb + 32, wl, bif);
             if (cls & want) do_block(base, b, cls != want, remote_phase, jb);
         }
     };
