@@ -241,7 +241,7 @@ def bench_chunk(jl, inputs, torch, iters=10):
     L = c.seqlens[0]
     q, kc, vc = c.q.cuda(), c.k_cache.cuda(), c.v_cache.cuda()
     sl = torch.tensor(c.seqlens, dtype=torch.int32, device="cuda")
-    ws = torch.empty(jl.prefill_chunk_workspace_bytes(1, L, Hq, Hkv, d), dtype=torch.uint8,
+    ws = torch.empty(jl.prefill_chunk_workspace_bytes(C, 1, L, Hq, Hkv, d), dtype=torch.uint8,
                      device="cuda")
     o = torch.empty_like(q)
     lse = torch.empty((Hq, C), dtype=torch.float32, device="cuda")
@@ -274,6 +274,21 @@ def bench_chunk(jl, inputs, torch, iters=10):
     run(False, 4)
     prof = jl.profile_read()
     jl.profile_enable(False)
+    # a 1024-row chunk on the same cache: a small grid, keys split in shares
+    q1k = q[:1024].contiguous()
+    ws1k = torch.empty(jl.prefill_chunk_workspace_bytes(1024, 1, L, Hq, Hkv, d),
+                       dtype=torch.uint8, device="cuda")
+    kw1k = dict(kw, workspace=ws1k, out=None, lse_out=None)
+    jl.bifocal_prefill_chunk(q1k, kc, vc, sl, **kw1k)
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for _ in range(5):
+        jl.bifocal_prefill_chunk(q1k, kc, vc, sl, **kw1k)
+    ev1.record()
+    torch.cuda.synchronize()
+    t_1k = ev0.elapsed_time(ev1) / 5
     q0 = L - C
     flops = 4.0 * d * Hq * ((L * (L + 1) - q0 * (q0 + 1)) // 2)
     return {
@@ -282,6 +297,7 @@ def bench_chunk(jl, inputs, torch, iters=10):
         "tflops": round(flops / (t_flat * 1e-3) / 1e12, 1),
         "frac_of_bf16_peak": round(flops / (t_flat * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
         "paged64_ms": round(t_paged, 3),
+        "chunk1024_ms": round(t_1k, 3),
         "kernels": {n: {"launches": c2, "avg_ms": round(ms / max(c2, 1), 4)}
                     for n, (c2, ms) in sorted(prof.items())},
     }

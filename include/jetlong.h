@@ -255,10 +255,13 @@ jl_status jl_bifocal_decode_fp8_paged(void* o, float* lse, const void* q, const 
 jl_status jl_kv_quantize_fp8(void* out, const void* x, const float* scale, int64_t ntok,
                              int32_t H, int32_t d, void* stream);
 
-/* Bytes of device workspace the chunk calls below need for batch sequences
- * of at most max_seqlen_k keys (bf16 only). */
-jl_status jl_bifocal_prefill_chunk_workspace(int32_t batch, int32_t max_seqlen_k, int32_t Hq,
-                                             int32_t Hkv, int32_t d, jl_dtype dtype,
+/* Bytes of device workspace the chunk calls below need for Tq query rows in
+ * batch sequences of at most max_seqlen_k keys (bf16 only).  Besides the
+ * key tiles it holds fp32 partials for calls whose grid is small (a 4096-row
+ * chunk of 32 heads, for example): those split each row block's keys in up
+ * to four shares and merge the shares in LogSumExp space. */
+jl_status jl_bifocal_prefill_chunk_workspace(int64_t Tq, int32_t batch, int32_t max_seqlen_k,
+                                             int32_t Hq, int32_t Hkv, int32_t d, jl_dtype dtype,
                                              size_t* bytes);
 
 /*

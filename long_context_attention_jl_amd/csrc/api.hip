@@ -592,10 +592,44 @@ static jl_status chunk_sizes_ok(int32_t batch, int32_t max_seqlen_k) {
     return JL_OK;
 }
 
-jl_status jl_bifocal_prefill_chunk_workspace(int32_t batch, int32_t max_seqlen_k, int32_t Hq,
-                                             int32_t Hkv, int32_t d, jl_dtype dtype,
+// Workspace of a chunk call: the prefill layout for the cache keys, then the
+// key-split partials.  A call whose main-rows grid holds fewer than
+// kChunkTargetWgs workgroups (two per compute unit) splits each row block's key tiles in up to
+// kChunkMaxSplit shares; the partials are sized for the most shares Tq
+// query rows can need (every row block holds at most 256 of them).
+constexpr int kChunkTargetWgs = 512;  // two workgroups per compute unit
+constexpr int kChunkMaxSplit = 4;
+static int chunk_split_bound(int64_t wgs) {
+    if (wgs < 1) wgs = 1;
+    const int64_t k = (kChunkTargetWgs + wgs - 1) / wgs;
+    return (int)(k < 1 ? 1 : (k > kChunkMaxSplit ? kChunkMaxSplit : k));
+}
+struct ChunkLayout {
+    PrefillLayout pl;
+    int kmax;
+    size_t part_o, part_ml, total;
+};
+static ChunkLayout chunk_layout(int64_t Tq, int32_t batch, int32_t max_seqlen_k, int32_t Hq,
+                                int32_t Hkv, int32_t d) {
+    ChunkLayout L{};
+    L.pl = prefill_layout((int64_t)batch * max_seqlen_k, batch, Hkv, d, JL_DTYPE_BF16);
+    L.kmax = chunk_split_bound((int64_t)Hq * ((Tq + kBM - 1) / kBM));
+    size_t off = align256(L.pl.total);
+    if (L.kmax > 1) {
+        L.part_o = off;
+        off = align256(off + (size_t)L.kmax * Tq * Hq * d * sizeof(float));
+        L.part_ml = off;
+        off = align256(off + (size_t)L.kmax * Hq * Tq * 2 * sizeof(float));
+    }
+    L.total = off;
+    return L;
+}
+
+jl_status jl_bifocal_prefill_chunk_workspace(int64_t Tq, int32_t batch, int32_t max_seqlen_k,
+                                             int32_t Hq, int32_t Hkv, int32_t d, jl_dtype dtype,
                                              size_t* bytes) {
     if (!bytes) return fail(JL_ERR_INVALID_ARGUMENT, "bytes is NULL");
+    if (Tq < 1 || Tq >= 2147483647LL) return fail(JL_ERR_INVALID_ARGUMENT, "Tq must be in [1, 2^31)");
     jl_status st = chunk_sizes_ok(batch, max_seqlen_k);
     if (st != JL_OK) return st;
     st = check_heads(Hq, Hkv);
@@ -603,7 +637,7 @@ jl_status jl_bifocal_prefill_chunk_workspace(int32_t batch, int32_t max_seqlen_k
     st = check_dtype_d(dtype, d);
     if (st != JL_OK) return st;
     if (dtype != JL_DTYPE_BF16) return fail(JL_ERR_UNSUPPORTED, "chunked prefill is bf16 only");
-    *bytes = prefill_layout((int64_t)batch * max_seqlen_k, batch, Hkv, d, dtype).total;
+    *bytes = chunk_layout(Tq, batch, max_seqlen_k, Hq, Hkv, d).total;
     g_err.clear();
     return JL_OK;
 }
@@ -635,14 +669,26 @@ static jl_status chunk_call(PrefillArgs& a, const int32_t* cu_seqlens_q,
     if (a.o == a.q || a.o == a.k || a.o == a.v || (const void*)a.lse == a.q)
         return fail(JL_ERR_INVALID_ARGUMENT, "outputs must not alias inputs");
     if ((uintptr_t)workspace & 255) return fail(JL_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
-    const PrefillLayout lay =
-        prefill_layout((int64_t)a.n_seqs * a.max_seqlen_k, a.n_seqs, a.Hkv, a.d, dtype);
-    if (workspace_bytes < lay.total)
+    const ChunkLayout cl = chunk_layout(a.T, a.n_seqs, a.max_seqlen_k, a.Hq, a.Hkv, a.d);
+    const PrefillLayout& lay = cl.pl;
+    if (workspace_bytes < cl.total)
         return fail(JL_ERR_WORKSPACE_TOO_SMALL,
-                    "workspace needs " + std::to_string(lay.total) + " bytes");
+                    "workspace needs " + std::to_string(cl.total) + " bytes");
     a.ws = workspace;
     a.lay = lay;
     a.chunked = 1;
+    // key split of the main rows: the launcher's row-block count per sequence
+    {
+        int64_t rb = (a.max_seqlen + kBM - 1) / kBM + 1;
+        const int64_t key_rb = (a.max_seqlen_k + kBM - 1) / kBM;
+        rb = rb < key_rb ? rb : key_rb;
+        int k = chunk_split_bound((int64_t)a.Hq * a.n_seqs * rb);
+        a.ksplit = k < cl.kmax ? k : cl.kmax;
+        if (a.ksplit > 1) {
+            a.part_o = (float*)((char*)workspace + cl.part_o);
+            a.part_ml = (float2*)((char*)workspace + cl.part_ml);
+        }
+    }
     a.w_local = params->w_local; a.bifocal = params->bifocal;
     a.softmax_scale = params->softmax_scale;
     a.tab = make_rope_freq(params->rope_base, a.d);
@@ -656,6 +702,10 @@ static jl_status chunk_call(PrefillArgs& a, const int32_t* cu_seqlens_q,
     if (e != hipSuccess) return hip_fail(e, "key/value pre-pass launch");
     e = launch_prefill_bf16(a, s);
     if (e != hipSuccess) return hip_fail(e, "prefill launch");
+    if (a.ksplit > 1) {
+        e = launch_chunk_merge(a, s);
+        if (e != hipSuccess) return hip_fail(e, "chunk merge launch");
+    }
     return finish(s, where);
 }
 

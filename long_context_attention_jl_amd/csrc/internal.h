@@ -68,7 +68,14 @@ struct PrefillArgs {
     float softmax_scale;
     RopeFreq tab;
     int32_t mode;
-    int32_t w_pretrained;  // for the continuous scale s = L / w_pretrained (bifocal 2)  // 0 bifocal; unfused calls: 1 all pairs remapped, 2 local standard, 3 local remapped
+    int32_t w_pretrained;  // for the continuous scale s = L / w_pretrained (bifocal 2)
+    // Key split of a chunk call (ksplit > 1): the main-rows kernel runs each
+    // row block as ksplit workgroups over equal shares of its key tiles and
+    // writes partials (unnormalised O in fp32 [ksplit][T][Hq][D], and
+    // (m in log2 units, l) [ksplit][Hq][T]) that a merge kernel combines.
+    int32_t ksplit;
+    float* part_o;
+    float2* part_ml;  // 0 bifocal; unfused calls: 1 all pairs remapped, 2 local standard, 3 local remapped
     // A chunk against a cache (chunked != 0): the queries are each sequence's
     // newest rows, keys and values are read from the cache, whose keys already
     // carry standard RoPE.  Flat cache: sequence s owns rows [s * S_max, ...);
@@ -95,6 +102,9 @@ hipError_t launch_three_call_merge(const void* oA, const void* oB, const void* o
                                    const float* lB, const float* lC, void* o, float* lse,
                                    int64_t T, int32_t Hq, int32_t d, hipStream_t s);
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t s);
+// combines the key-split partials of the main rows (positions >= 2048) of a
+// chunk call into o and lse
+hipError_t launch_chunk_merge(const PrefillArgs& a, hipStream_t s);
 hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t s);
 
 struct DecodeArgs {

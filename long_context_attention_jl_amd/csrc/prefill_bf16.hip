@@ -100,7 +100,10 @@ void prefill_bf16_kernel(PrefillArgs a, int rb_first, int n_rb) {
     int head = blockIdx.x;
     if ((a.Hq & 7) == 0) head = (blockIdx.x & 7) * (a.Hq >> 3) + (blockIdx.x >> 3);
     const int s = blockIdx.y;
-    const int rb = rb_first + (n_rb - 1 - (int)blockIdx.z);  // longest rows first
+    // key split (main rows of a chunk call): grid z = row block x split
+    const int nsp = (!PRECISE && a.ksplit > 1) ? a.ksplit : 1;
+    const int rb = rb_first + (n_rb - 1 - (int)blockIdx.z / nsp);  // longest rows first
+    const int ks = (int)blockIdx.z % nsp;
     const int32_t* plan = (const int32_t*)((const char*)a.ws + a.lay.plan);
     const int32_t* e = plan + s * kPlanFields;
     const int32_t start = e[kPlanStart], len = e[kPlanLen], G = e[kPlanG];
@@ -147,6 +150,18 @@ void prefill_bf16_kernel(PrefillArgs a, int rb_first, int n_rb) {
         const int32_t jr = row_end - 1 - wl;
         r_end = jr >= 0 ? jr / kBN + 1 : 0;
         s_begin = wl == 0 ? ntiles : max(0, max(row0, q0) - wl + 1) / kBN;
+    }
+    // this workgroup's share of the phases' tiles (all of them without a key
+    // split; with one, an equal slice of the remote tiles followed by the
+    // local ones)
+    int r_lo = 0, r_hi = do_remote ? r_end : 0, l_lo = s_begin, l_hi = do_local ? ntiles : s_begin;
+    if (nsp > 1) {
+        const int nrem = r_hi, nloc = max(l_hi - s_begin, 0), ntot = nrem + nloc;
+        const int a0 = (int)((int64_t)ntot * ks / nsp), a1 = (int)((int64_t)ntot * (ks + 1) / nsp);
+        r_lo = min(a0, nrem);
+        r_hi = min(a1, nrem);
+        l_lo = s_begin + max(a0 - nrem, 0);
+        l_hi = s_begin + max(a1 - nrem, 0);
     }
 
     // ---- rotated, scaled queries as MFMA B operands ----
@@ -354,13 +369,32 @@ void prefill_bf16_kernel(PrefillArgs a, int rb_first, int n_rb) {
         }
     };
 
-    if (do_remote && r_end > 0) {
+    if (r_hi > r_lo) {
         stage_q(true);
-        run_phase(0, r_end, true, true);
+        run_phase(r_lo, r_hi, true, true);
     }
-    if (do_local && s_begin < ntiles) {
+    if (l_hi > l_lo) {
         stage_q(local_remapped);  // begins with a barrier: no wave still reads a buffer
-        run_phase(s_begin, ntiles, false, local_remapped);
+        run_phase(l_lo, l_hi, false, local_remapped);
+    }
+
+    if (nsp > 1) {
+        // partial of this key share: unnormalised O^T and (m, l), relative to m
+        if (!wave_active || !row_valid) return;
+        const float l_tot = l_run + __shfl_xor(l_run, 32);
+        const int64_t tok = qbase + myrow;
+        float* po = a.part_o + (((int64_t)ks * a.T + tok) * a.Hq + head) * D;
+#pragma unroll
+        for (int db = 0; db < C::ND; ++db)
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+                const f32x4 w = {O[db][4 * g4], O[db][4 * g4 + 1], O[db][4 * g4 + 2], O[db][4 * g4 + 3]};
+                *reinterpret_cast<f32x4*>(po + 32 * db + 8 * g4 + 4 * hh) = w;
+            }
+        if (hh == 0)
+            a.part_ml[((int64_t)ks * a.Hq + head) * a.T + tok] =
+                make_float2(l_tot > 0.0f ? m_run : -INFINITY, l_tot);
+        return;
     }
 
     // ---- epilogue: O = O^T / l, LSE = ln(sum exp(score)) ----
@@ -387,8 +421,9 @@ static hipError_t launch_one(const PrefillArgs& a, int rb_first, int n_rb, hipSt
                              const char* name) {
     if (n_rb <= 0) return hipSuccess;
     LaunchScope scope(name, s);
-    hipLaunchKernelGGL((prefill_bf16_kernel<D, PRECISE>), dim3(a.Hq, a.n_seqs, n_rb), dim3(512),
-                       0, s, a, rb_first, n_rb);
+    const int nsp = (!PRECISE && a.ksplit > 1) ? a.ksplit : 1;
+    hipLaunchKernelGGL((prefill_bf16_kernel<D, PRECISE>), dim3(a.Hq, a.n_seqs, n_rb * nsp),
+                       dim3(512), 0, s, a, rb_first, n_rb);
     return hipGetLastError();
 }
 
@@ -416,6 +451,63 @@ hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t s) {
     err = launch_one<64, true>(a, 0, n_prec, s, "prefill_bf16_precise");
     if (err != hipSuccess) return err;
     return launch_one<64, false>(a, main_first, total_rb - main_first, s, "prefill_bf16");
+}
+
+// Key-split partials of a chunk call, combined in LogSumExp space
+// ([TW] §四's merge of partial attentions): with m_k in log2 units,
+//   Z = sum_k 2^(m_k - M) l_k,  o = sum_k 2^(m_k - M) O_k / Z,
+//   lse = (M + log2 Z) ln 2,  M = max_k m_k.
+// One wave per (token, head).  A token is looked up in the plan (its
+// sequence and position); rows of a block below the split-precision bound
+// were written directly by that kernel and are skipped, as are tokens of
+// no sequence (a broken plan has every length 0).
+__global__ __launch_bounds__(256) void chunk_merge_kernel(PrefillArgs a) {
+    const int64_t tok = blockIdx.x;
+    const int head = blockIdx.y * 4 + (int)(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (head >= a.Hq) return;
+    const int32_t* plan = (const int32_t*)((const char*)a.ws + a.lay.plan);
+    int lo = 0, hi = a.n_seqs - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) / 2;
+        if (plan[mid * kPlanFields + kPlanStart] <= tok) lo = mid;
+        else hi = mid - 1;
+    }
+    const int32_t* e = plan + lo * kPlanFields;
+    const int32_t len = e[kPlanLen], q0 = e[kPlanQ0];
+    if (len <= 0 || tok < e[kPlanStart] || tok >= (int64_t)e[kPlanStart] + (len - q0)) return;
+    const int32_t pos = q0 + (int32_t)(tok - e[kPlanStart]);
+    if (pos - pos % kBM < kPreciseRows) return;
+    const int K = a.ksplit;
+    float M = -INFINITY;
+    for (int k = 0; k < K; ++k) M = fmaxf(M, a.part_ml[((int64_t)k * a.Hq + head) * a.T + tok].x);
+    float Z = 0.0f;
+    float w[8];
+    for (int k = 0; k < K; ++k) {
+        const float2 ml = a.part_ml[((int64_t)k * a.Hq + head) * a.T + tok];
+        w[k] = (M == -INFINITY || ml.x == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(ml.x - M) * ml.y;
+        w[k] = ml.y > 0.0f ? w[k] : 0.0f;
+        Z += w[k];
+    }
+    const bool none = !(Z > 0.0f);
+    bf16* o = (bf16*)a.o + (tok * a.Hq + head) * (int64_t)a.d;
+    for (int x = lane; x < a.d; x += 64) {
+        float acc = 0.0f;
+        for (int k = 0; k < K; ++k) {
+            const float2 ml = a.part_ml[((int64_t)k * a.Hq + head) * a.T + tok];
+            const float wk = (none || ml.y <= 0.0f) ? 0.0f : __builtin_amdgcn_exp2f(ml.x - M);
+            acc += wk * a.part_o[(((int64_t)k * a.T + tok) * a.Hq + head) * a.d + x];
+        }
+        o[x] = (bf16)(none ? 0.0f : acc / Z);
+    }
+    if (lane == 0) a.lse[(int64_t)head * a.T + tok] = none ? -INFINITY : (M + log2f(Z)) * kLn2;
+}
+
+hipError_t launch_chunk_merge(const PrefillArgs& a, hipStream_t s) {
+    LaunchScope scope("chunk_merge", s);
+    hipLaunchKernelGGL(chunk_merge_kernel, dim3((unsigned)a.T, (unsigned)((a.Hq + 3) / 4)),
+                       dim3(256), 0, s, a);
+    return hipGetLastError();
 }
 
 // LogSumExp combination of the pages' three unfused calls ([TW] §四, [BT]

@@ -95,7 +95,7 @@ def lib() -> ctypes.CDLL:
                                               ctypes.POINTER(jl_params), ctypes.c_int, _vp,
                                               ctypes.c_size_t, _vp]
         L.jl_bifocal_prefill_chunk_workspace.restype = ctypes.c_int
-        L.jl_bifocal_prefill_chunk_workspace.argtypes = [_i32, _i32, _i32, _i32, _i32,
+        L.jl_bifocal_prefill_chunk_workspace.argtypes = [_i64, _i32, _i32, _i32, _i32, _i32,
                                                          ctypes.c_int,
                                                          ctypes.POINTER(ctypes.c_size_t)]
         L.jl_bifocal_prefill_chunk.restype = ctypes.c_int
@@ -360,9 +360,10 @@ def bifocal_decode_paged(q: torch.Tensor, k_pages: torch.Tensor, v_pages: torch.
     return o, lse
 
 
-def prefill_chunk_workspace_bytes(B: int, max_seqlen_k: int, Hq: int, Hkv: int, d: int) -> int:
+def prefill_chunk_workspace_bytes(Tq: int, B: int, max_seqlen_k: int, Hq: int, Hkv: int,
+                                  d: int) -> int:
     n = ctypes.c_size_t(0)
-    _check(lib().jl_bifocal_prefill_chunk_workspace(B, max_seqlen_k, Hq, Hkv, d, 1,
+    _check(lib().jl_bifocal_prefill_chunk_workspace(Tq, B, max_seqlen_k, Hq, Hkv, d, 1,
                                                     ctypes.byref(n)),
            "jl_bifocal_prefill_chunk_workspace")
     return n.value
@@ -398,7 +399,8 @@ def bifocal_prefill_chunk(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch
     S_max, Hkv = k_cache.shape[1], k_cache.shape[2]
     cu, B, max_q, sl, max_k, o, lse = _chunk_common(q, seqlens_k, cu_seqlens_q, max_seqlen_q,
                                                     max_seqlen_k, dev, out, lse_out)
-    ws = _workspace(prefill_chunk_workspace_bytes(B, max_k, Hq, Hkv, d), dev, workspace)
+    ws = _workspace(prefill_chunk_workspace_bytes(q.shape[0], B, max_k, Hq, Hkv, d), dev,
+                    workspace)
     p = _params(w_pretrained, w_local, rope_base, softmax_scale, bifocal)
     _check(lib().jl_bifocal_prefill_chunk(
         _dev(o, "o"), _dev(lse, "lse"), _dev(q, "q"), None if cu is None else _dev(cu, "cu"),
@@ -427,7 +429,8 @@ def bifocal_prefill_chunk_paged(q: torch.Tensor, k_pages: torch.Tensor, v_pages:
     cu, B, max_q, sl, max_k, o, lse = _chunk_common(q, seqlens_k, cu_seqlens_q, max_seqlen_q,
                                                     max_seqlen_k, dev, out, lse_out)
     bt = block_table.to(device=dev, dtype=torch.int32).contiguous()
-    ws = _workspace(prefill_chunk_workspace_bytes(B, max_k, Hq, Hkv, d), dev, workspace)
+    ws = _workspace(prefill_chunk_workspace_bytes(q.shape[0], B, max_k, Hq, Hkv, d), dev,
+                    workspace)
     p = _params(w_pretrained, w_local, rope_base, softmax_scale, bifocal)
     _check(lib().jl_bifocal_prefill_chunk_paged(
         _dev(o, "o"), _dev(lse, "lse"), _dev(q, "q"), None if cu is None else _dev(cu, "cu"),

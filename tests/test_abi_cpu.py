@@ -265,15 +265,29 @@ def test_chunk_paged_validation(kw, status):
 
 
 def test_chunk_workspace_query():
+    """A large chunk needs the prefill workspace of its keys; a grid of fewer than
+    two workgroups per compute unit adds the key-split partials: up to 4 shares
+    x Tq x Hq x (d + 2) fp32."""
     n = ctypes.c_size_t(0)
     L = jlb.lib()
-    assert L.jl_bifocal_prefill_chunk_workspace(1, 131072, 32, 8, 128, 1, ctypes.byref(n)) == 0
-    n1 = n.value
     assert L.jl_bifocal_prefill_workspace(131072, 1, 32, 8, 128, 1, ctypes.byref(n)) == 0
-    assert n1 == n.value  # one sequence of 128K keys: the prefill workspace
-    assert L.jl_bifocal_prefill_chunk_workspace(1, 131072, 32, 8, 128, 0, ctypes.byref(n)) == 2
-    assert L.jl_bifocal_prefill_chunk_workspace(0, 10, 32, 8, 128, 1, ctypes.byref(n)) == 1
-    assert L.jl_bifocal_prefill_chunk_workspace(1, 10, 32, 8, 128, 1, None) == 1
+    base = n.value
+    # 32768 rows of 32 heads: 4096 row blocks >= 1024 workgroups, no split
+    assert L.jl_bifocal_prefill_chunk_workspace(32768, 1, 131072, 32, 8, 128, 1, ctypes.byref(n)) == 0
+    assert n.value == base
+    # 4096 rows: 512 row-block workgroups, two per compute unit: no split
+    assert L.jl_bifocal_prefill_chunk_workspace(4096, 1, 131072, 32, 8, 128, 1, ctypes.byref(n)) == 0
+    assert n.value == base
+    # 1024 rows: 128 workgroups -> up to 4 shares
+    assert L.jl_bifocal_prefill_chunk_workspace(1024, 1, 131072, 32, 8, 128, 1, ctypes.byref(n)) == 0
+    assert base + 4 * 1024 * 32 * 130 * 4 <= n.value < base + 4 * 1024 * 32 * 130 * 4 + 1024
+    # one row: capped at 4 shares
+    assert L.jl_bifocal_prefill_chunk_workspace(1, 1, 131072, 32, 8, 128, 1, ctypes.byref(n)) == 0
+    assert base + 4 * 32 * 130 * 4 <= n.value < base + 4 * 32 * 130 * 4 + 1024
+    assert L.jl_bifocal_prefill_chunk_workspace(1, 1, 131072, 32, 8, 128, 0, ctypes.byref(n)) == 2
+    assert L.jl_bifocal_prefill_chunk_workspace(1, 0, 10, 32, 8, 128, 1, ctypes.byref(n)) == 1
+    assert L.jl_bifocal_prefill_chunk_workspace(0, 1, 10, 32, 8, 128, 1, ctypes.byref(n)) == 1
+    assert L.jl_bifocal_prefill_chunk_workspace(1, 1, 10, 32, 8, 128, 1, None) == 1
 
 
 def _fp8(paged=False, **kw):

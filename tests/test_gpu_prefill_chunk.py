@@ -149,3 +149,15 @@ def test_chunk_invalid_device_lengths_write_nothing():
                              max_seqlen_q=300, max_seqlen_k=700, out=o, lse_out=lse, **_kw(p))
     torch.cuda.synchronize()
     assert bool((o == 7.0).all()) and bool((lse == 7.0).all())
+
+
+def test_chunk_1024_rows_key_split_128k():
+    """1024 new rows on a 131072-key sequence: 128 row-block workgroups, so each
+    row block's keys are split in four shares merged in LogSumExp space."""
+    q, kc, vc, _ = inputs.chunk_inputs([1024], [131072], 131072, 32, 8, 128, seed=66)
+    p = inputs.DECODE_PARAMS
+    say("chunk 1024 rows on 131072 keys (key split)")
+    o, lse = _gpu(q, kc, vc, [131072], None, p)
+    rows = [0, 1, 255, 256, 511, 700, 1022, 1023]
+    o_ref, lse_ref = _oracle(q, kc, vc, [131072], None, p, rows=rows)
+    check_prefill(o, lse, o_ref, lse_ref, rows, torch.bfloat16, "chunk1024 split")
