@@ -199,8 +199,7 @@ __host__ __device__ constexpr int vt_perm16(int p) {
 template <int D>
 __global__ __launch_bounds__(256) void kv_prepass_bf16_kernel(PrefillArgs a) {
     constexpr int HALF = D / 2;
-    constexpr int TPC = D / 8;  // pairs per thread: 4 threads per key row
-    __shared__ bf16 vs[kBN * (D + 2)];
+    __shared__ __align__(16) bf16 vs[kBN * (D + 8)];
     __shared__ int64_t vrow[kBN];
 
     const int32_t* plan = (const int32_t*)((char*)a.ws + a.lay.plan);
@@ -230,38 +229,51 @@ __global__ __launch_bounds__(256) void kv_prepass_bf16_kernel(PrefillArgs a) {
         return ((int64_t)pg << a.page_shift) | (nn & ((1 << a.page_shift) - 1));
     };
 
-    // ---- keys: thread (r, c) rotates pairs [c*TPC, (c+1)*TPC) of row r ----
-    const int r = threadIdx.x / 4, c = threadIdx.x % 4;
-    const int32_t n = n0 + r;
-    const bool valid = n < len;
-    const bool lo_row = n < kPreciseRows;
-    const int64_t krow = valid ? src_row(n) : 0;
-    float cs[TPC], sn[TPC], cr[TPC], sr[TPC];
+    // ---- keys: thread (r, c) rotates pairs [8c, 8c + 8) of row r: one
+    // 16-byte vector in each RoPE half (tile rows are 16-byte aligned:
+    // kstr(D) * 2 = 16 * 17); 256 / (D / 16) rows per pass ----
+    constexpr int TPR = D / 16;          // threads per key row
+    constexpr int RPP = 256 / TPR;       // rows per pass
     // remote position: f(n) = floor(n / G), or n / s with s = len / w_pretrained
     // for the continuous-interpolation variant (bifocal 2)
     const bool interp = a.bifocal == 2;
     const double rsc = interp ? (double)a.w_pretrained / (double)len : 1.0;
-    if (valid) {
-        const int32_t fn = remap(n, G);
-#pragma unroll
-        for (int u = 0; u < TPC; ++u) {
-            const double rv = rope_rev(a.tab, c * TPC + u);
-            rope_cs(cache ? 0 : n, rv, cs[u], sn[u]);
-            if (bif) {
-                if (interp) rope_cs(n, rv * (cache ? rsc - 1.0 : rsc), cr[u], sr[u]);
-                else rope_cs(cache ? fn - n : fn, rv, cr[u], sr[u]);
-            }
-        }
-    }
-    for (int g = 0; g < a.Hkv; ++g) {
-        f16 ys0[TPC], ys1[TPC], yr0[TPC], yr1[TPC];
-        f16 ls0[TPC], ls1[TPC], lr0[TPC], lr1[TPC];
-        bf16 kb0[TPC], kb1[TPC];
+    for (int pass = 0; pass < kBN / RPP; ++pass) {
+        const int r = pass * RPP + (int)threadIdx.x / TPR, c = (int)threadIdx.x % TPR;
+        const int32_t n = n0 + r;
+        const bool valid = n < len;
+        const bool lo_row = n < kPreciseRows;
+        const int64_t krow = valid ? src_row(n) : 0;
+        if (c == 0) vrow[r] = krow;  // published by the first barrier of the value loop
+        float cs[8], sn[8], cr[8], sr[8];
         if (valid) {
-            const bf16* src = k + (krow * a.Hkv + g) * D + c * TPC;
+            const int32_t fn = remap(n, G);
 #pragma unroll
-            for (int u = 0; u < TPC; ++u) {
-                const float x0 = (float)src[u], x1 = (float)src[u + HALF];
+            for (int u = 0; u < 8; ++u) {
+                const double rv = rope_rev(a.tab, 8 * c + u);
+                rope_cs(cache ? 0 : n, rv, cs[u], sn[u]);
+                if (bif) {
+                    if (interp) rope_cs(n, rv * (cache ? rsc - 1.0 : rsc), cr[u], sr[u]);
+                    else rope_cs(cache ? fn - n : fn, rv, cr[u], sr[u]);
+                }
+            }
+        } else {
+            // pad rows (n >= len): zero angles on zero data give zero tiles
+#pragma unroll
+            for (int u = 0; u < 8; ++u) cs[u] = sn[u] = cr[u] = sr[u] = 0.0f;
+        }
+        for (int g = 0; g < a.Hkv; ++g) {
+            bf16x8 xa = bf16x8{}, xb = bf16x8{};
+            if (valid) {
+                const bf16* src = k + (krow * a.Hkv + g) * D + 8 * c;
+                xa = *reinterpret_cast<const bf16x8*>(src);
+                xb = *reinterpret_cast<const bf16x8*>(src + HALF);
+            }
+            f16x8 ys0, ys1, yr0, yr1, ls0, ls1, lr0, lr1;
+            bf16x8 kb0, kb1;
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const float x0 = (float)xa[u], x1 = (float)xb[u];
                 const float s0 = x0 * cs[u] - x1 * sn[u];
                 const float s1 = x1 * cs[u] + x0 * sn[u];
                 ys0[u] = (f16)s0;
@@ -279,74 +291,61 @@ __global__ __launch_bounds__(256) void kv_prepass_bf16_kernel(PrefillArgs a) {
                     lr1[u] = (f16)(r1 - (float)yr1[u]);
                 }
             }
-        } else {
-#pragma unroll
-            for (int u = 0; u < TPC; ++u) {
-                ys0[u] = ys1[u] = yr0[u] = yr1[u] = (f16)0.0f;
-                ls0[u] = ls1[u] = lr0[u] = lr1[u] = (f16)0.0f;
-                kb0[u] = kb1[u] = (bf16)0.0f;
-            }
-        }
-        // tile image: row r of tile `tile`, stride kstr(D)
-        const int64_t drow = ((int64_t)g * (a.lay.T_pad / kBN) + tile) * ktile_elems(D) +
-                             (int64_t)r * kstr(D) + c * TPC;
-#pragma unroll
-        for (int u = 0; u < TPC; ++u) {
-            KS[drow + u] = ys0[u];
-            KS[drow + u + HALF] = ys1[u];
-        }
-        if (bif) {
-#pragma unroll
-            for (int u = 0; u < TPC; ++u) {
-                KR[drow + u] = yr0[u];
-                KR[drow + u + HALF] = yr1[u];
-            }
-        }
-        if (lo_row) {
-            const int64_t lrow =
-                ((int64_t)g * (a.lay.lo_pad / kBN) + e[kPlanLoTile0] + n / kBN) * ktile_elems(D) +
-                (int64_t)(n % kBN) * kstr(D) + c * TPC;
-#pragma unroll
-            for (int u = 0; u < TPC; ++u) {
-                KSlo[lrow + u] = ls0[u];
-                KSlo[lrow + u + HALF] = ls1[u];
-            }
+            // tile image: row r of tile `tile`, stride kstr(D)
+            const int64_t drow = ((int64_t)g * (a.lay.T_pad / kBN) + tile) * ktile_elems(D) +
+                                 (int64_t)r * kstr(D) + 8 * c;
+            *reinterpret_cast<f16x8*>(KS + drow) = ys0;
+            *reinterpret_cast<f16x8*>(KS + drow + HALF) = ys1;
             if (bif) {
-#pragma unroll
-                for (int u = 0; u < TPC; ++u) {
-                    KRlo[lrow + u] = lr0[u];
-                    KRlo[lrow + u + HALF] = lr1[u];
+                *reinterpret_cast<f16x8*>(KR + drow) = yr0;
+                *reinterpret_cast<f16x8*>(KR + drow + HALF) = yr1;
+            }
+            if (lo_row) {
+                const int64_t lrow =
+                    ((int64_t)g * (a.lay.lo_pad / kBN) + e[kPlanLoTile0] + n / kBN) * ktile_elems(D) +
+                    (int64_t)(n % kBN) * kstr(D) + 8 * c;
+                *reinterpret_cast<f16x8*>(KSlo + lrow) = ls0;
+                *reinterpret_cast<f16x8*>(KSlo + lrow + HALF) = ls1;
+                if (bif) {
+                    *reinterpret_cast<f16x8*>(KRlo + lrow) = lr0;
+                    *reinterpret_cast<f16x8*>(KRlo + lrow + HALF) = lr1;
                 }
             }
-        }
-        if (krot && valid) {
-            bf16* dst = krot + ((int64_t)(start + n) * a.Hkv + g) * D + c * TPC;
-#pragma unroll
-            for (int u = 0; u < TPC; ++u) {
-                dst[u] = kb0[u];
-                dst[u + HALF] = kb1[u];
+            if (krot && valid) {
+                bf16* dst = krot + ((int64_t)(start + n) * a.Hkv + g) * D + 8 * c;
+                *reinterpret_cast<bf16x8*>(dst) = kb0;
+                *reinterpret_cast<bf16x8*>(dst + HALF) = kb1;
             }
         }
     }
 
     // ---- values: transpose each head's [kBN][D] tile through LDS ----
     // (source rows of the tile's positions shared through LDS; the first
-    // barrier of the loop publishes them)
-    if (c == 0) vrow[r] = krow;
+    // barrier of the loop publishes them).  Rows are read and the transposed
+    // tile written in 16-byte vectors: output vector (d, m) holds the keys of
+    // positions 8m .. 8m + 7 of row d in vt_perm16 order.
+    constexpr int VSS = D + 8;  // LDS row stride (halves), 16-byte aligned rows
     for (int g = 0; g < a.Hkv; ++g) {
         __syncthreads();
-        for (int idx = threadIdx.x; idx < kBN * D; idx += 256) {
-            const int rr = idx / D, dd = idx % D;
+        for (int idx = threadIdx.x; idx < kBN * (D / 8); idx += 256) {
+            const int rr = idx / (D / 8), ch = idx % (D / 8);
             const int32_t nn = n0 + rr;
-            vs[rr * (D + 2) + dd] =
-                nn < len ? v[(vrow[rr] * a.Hkv + g) * D + dd] : (bf16)0.0f;
+            bf16x8 x = bf16x8{};
+            if (nn < len) x = *reinterpret_cast<const bf16x8*>(v + (vrow[rr] * a.Hkv + g) * D + 8 * ch);
+            *reinterpret_cast<bf16x8*>(vs + rr * VSS + 8 * ch) = x;
         }
         __syncthreads();
         f16* dst = VT + ((int64_t)g * (a.lay.T_pad / kBN) + tile) * vtile_elems(D);
-        for (int idx = threadIdx.x; idx < kBN * D; idx += 256) {
-            const int dd = idx / kBN, p = idx % kBN;
-            const int key = (p & ~15) | vt_perm16(p & 15);
-            dst[dd * kVStr + p] = (f16)(float)vs[key * (D + 2) + dd];
+        for (int idx = threadIdx.x; idx < D * (kBN / 8); idx += 256) {
+            const int dd = idx / (kBN / 8), m = idx % (kBN / 8);
+            f16x8 o;
+#pragma unroll
+            for (int e8 = 0; e8 < 8; ++e8) {
+                const int p = 8 * m + e8;
+                const int key = (p & ~15) | vt_perm16(p & 15);
+                o[e8] = (f16)(float)vs[key * VSS + dd];
+            }
+            *reinterpret_cast<f16x8*>(dst + dd * kVStr + 8 * m) = o;
         }
     }
 }
