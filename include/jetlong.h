@@ -35,6 +35,10 @@
  *     documented contract the outputs are unspecified, but no kernel reads or
  *     writes outside the buffers whose sizes the host arguments describe.
  *   - Outputs must not alias inputs (except in jl_rope_apply).
+ *   - The attention entry points move tensors in 16-byte vectors: q, k, v, o,
+ *     k_rot_out and the caches or page pools must start on a 16-byte boundary
+ *     (JL_ERR_INVALID_ARGUMENT otherwise).  Workspaces start on a 256-byte
+ *     boundary.
  */
 #ifndef JETLONG_H
 #define JETLONG_H
@@ -183,7 +187,8 @@ jl_status jl_bifocal_decode_workspace(int32_t batch, int32_t max_seqlen_k, int32
  *   k_cache, v_cache  [B][S_max][Hkv][d] of dtype, read-only.
  *   seqlens_k  device int32 [B], 1 <= L_b <= max_seqlen_k <= S_max.
  *   workspace  at least jl_bifocal_decode_workspace() bytes (scratch).
- * Supported: dtype bf16 or f32, d in {64, 128}, Hq / Hkv <= 16.
+ * Supported: dtype bf16 or f32 (bf16 only for params->bifocal == 2), d in {64, 128},
+ * Hq / Hkv <= 16.
  */
 jl_status jl_bifocal_decode(void* o, float* lse, const void* q, const void* k_cache,
                             const void* v_cache, const int32_t* seqlens_k, int32_t batch,
@@ -257,9 +262,10 @@ jl_status jl_kv_quantize_fp8(void* out, const void* x, const float* scale, int64
 
 /* Bytes of device workspace the chunk calls below need for Tq query rows in
  * batch sequences of at most max_seqlen_k keys (bf16 only).  Besides the
- * key tiles it holds fp32 partials for calls whose grid is small (a 4096-row
- * chunk of 32 heads, for example): those split each row block's keys in up
- * to four shares and merge the shares in LogSumExp space. */
+ * key tiles it holds fp32 partials for calls whose grid is small (fewer than
+ * two 256-row workgroups per compute unit, e.g. a 1024-row chunk of 32
+ * heads): those split each row block's keys in up to four shares and merge
+ * the shares in LogSumExp space. */
 jl_status jl_bifocal_prefill_chunk_workspace(int64_t Tq, int32_t batch, int32_t max_seqlen_k,
                                              int32_t Hq, int32_t Hkv, int32_t d, jl_dtype dtype,
                                              size_t* bytes);

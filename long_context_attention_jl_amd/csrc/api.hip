@@ -8,6 +8,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <initializer_list>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -192,6 +193,14 @@ static jl_status check_params(const jl_params* p) {
     return JL_OK;
 }
 
+// The kernels move tensors in 16-byte vectors.
+static bool al16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+static jl_status check_aligned(std::initializer_list<const void*> ps) {
+    for (const void* p : ps)
+        if (p && !al16(p)) return fail(JL_ERR_INVALID_ARGUMENT, "tensors must be 16-byte aligned");
+    return JL_OK;
+}
+
 static jl_status check_heads(int32_t Hq, int32_t Hkv) {
     if (Hq < 1 || Hkv < 1) return fail(JL_ERR_INVALID_ARGUMENT, "Hq and Hkv must be >= 1");
     if (Hq % Hkv) return fail(JL_ERR_INVALID_ARGUMENT, "Hq must be a multiple of Hkv");
@@ -289,6 +298,8 @@ jl_status jl_bifocal_prefill(void* o, float* lse, const void* q, const void* k, 
     if (o == q || o == k || o == v || (void*)lse == q || (k_rot_out && (k_rot_out == k || k_rot_out == q || k_rot_out == v || k_rot_out == o)))
         return fail(JL_ERR_INVALID_ARGUMENT, "outputs must not alias inputs");
     if ((uintptr_t)workspace & 255) return fail(JL_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
+    st = check_aligned({o, q, k, v, k_rot_out});
+    if (st != JL_OK) return st;
     const PrefillLayout lay = prefill_layout(T, n_seqs, Hkv, d, dtype);
     if (workspace_bytes < lay.total)
         return fail(JL_ERR_WORKSPACE_TOO_SMALL,
@@ -381,6 +392,8 @@ jl_status jl_bifocal_prefill_three_call(void* o, float* lse, const void* q, cons
     if (o == q || o == k || o == v || (void*)lse == q)
         return fail(JL_ERR_INVALID_ARGUMENT, "outputs must not alias inputs");
     if ((uintptr_t)workspace & 255) return fail(JL_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
+    st = check_aligned({o, q, k, v});
+    if (st != JL_OK) return st;
     const PrefillLayout lay = prefill_layout(T, n_seqs, Hkv, d, dtype);
     const ThreeCallLayout tl = three_call_layout(lay, T, Hq, d);
     if (workspace_bytes < tl.total)
@@ -488,6 +501,10 @@ static jl_status decode_impl(const DecodeCall& c, const jl_params* params, jl_dt
     if (c.o == c.q || c.o == c.kc || c.o == c.vc)
         return fail(JL_ERR_INVALID_ARGUMENT, "outputs must not alias inputs");
     if ((uintptr_t)workspace & 255) return fail(JL_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
+    {
+        const jl_status ast = check_aligned({c.o, c.q, c.kc, c.vc});
+        if (ast != JL_OK) return ast;
+    }
     const DecodeLayout lay = decode_layout(c.batch, c.max_seqlen_k, c.Hq, c.Hkv, c.d, dtype);
     if (workspace_bytes < lay.total)
         return fail(JL_ERR_WORKSPACE_TOO_SMALL,
@@ -669,6 +686,8 @@ static jl_status chunk_call(PrefillArgs& a, const int32_t* cu_seqlens_q,
     if (a.o == a.q || a.o == a.k || a.o == a.v || (const void*)a.lse == a.q)
         return fail(JL_ERR_INVALID_ARGUMENT, "outputs must not alias inputs");
     if ((uintptr_t)workspace & 255) return fail(JL_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
+    st = check_aligned({a.o, a.q, a.k, a.v});
+    if (st != JL_OK) return st;
     const ChunkLayout cl = chunk_layout(a.T, a.n_seqs, a.max_seqlen_k, a.Hq, a.Hkv, a.d);
     const PrefillLayout& lay = cl.pl;
     if (workspace_bytes < cl.total)

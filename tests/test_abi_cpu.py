@@ -345,3 +345,17 @@ def test_fp8_decode_workspace_is_the_bf16_one():
 ])
 def test_kv_quantize_validation(args, status):
     assert jlb.lib().jl_kv_quantize_fp8(*args, None) == status
+
+
+@pytest.mark.parametrize("call,kw", [
+    (_prefill, dict(q=FAKE * 3 + 8)), (_prefill, dict(o=FAKE + 2)),
+    (_prefill, dict(krot=FAKE * 9 + 4)), (_three_call, dict(v=FAKE * 5 + 8)),
+    (_decode, dict(kc=FAKE * 4 + 8)), (_decode, dict(q=FAKE * 3 + 2)),
+    (_paged, dict(vp=FAKE * 5 + 4)), (_chunk, dict(o=FAKE + 8)),
+    (lambda **kw: _chunk(True, **kw), dict(kc=FAKE * 5 + 8)), (_fp8, dict(vc=FAKE * 5 + 8)),
+])
+def test_vector_operands_must_be_16_byte_aligned(call, kw):
+    """Every attention kernel moves q, k, v, o and the caches in 16-byte
+    vectors; a pointer off that boundary is refused on the host."""
+    assert call(**kw) == 1
+    assert b"16-byte" in jlb.lib().jl_last_error()
