@@ -908,83 +908,78 @@ __global__ __launch_bounds__(512) void decode_split_bf16_kernel(DecodeArgs a) {
         }
 }
 
-// Merge of the chunk partials in one pass: o = sum 2^(m_c - M) O_c /
-// sum 2^(m_c - M) l_c, lse = (M + log2 sum ...) ln 2 -- the LogSumExp
-// combination of [TW] §四.  Workgroup (head, sequence, 32-wide slice of d),
-// 256 threads = 32 chunk groups x 8 quads of d; each thread folds its chunks
-// (loaded together) against their common max, then the 32 groups are folded
-// through LDS.  A sequence
-// with no keys gets o = 0 and lse = -inf.
+// Merge of the chunk partials: o = sum 2^(m_c - M) O_c / sum 2^(m_c - M) l_c,
+// lse = (M + log2 sum ...) ln 2 -- the LogSumExp combination of [TW] §四.
+// Workgroup (head, sequence, 16-wide slice of d), 256 threads = 64 chunk
+// groups x 4 quads of d.  Each thread folds its chunks (loaded together)
+// against their common max; the 16 groups of a wave are folded with lane
+// shuffles and the 4 waves through LDS.  A sequence with no keys gets o = 0
+// and lse = -inf.
+struct MergeAcc {
+    float m, l;
+    f32x4 o;
+};
+// (m, l, o) of two disjoint key sets -> their union; m = -inf is the empty set
+__device__ __forceinline__ MergeAcc merge_acc(const MergeAcc& x, const MergeAcc& y) {
+    const float m = fmaxf(x.m, y.m);
+    if (m == -INFINITY) return x;
+    const float sx = __builtin_amdgcn_exp2f(x.m - m), sy = __builtin_amdgcn_exp2f(y.m - m);
+    return MergeAcc{m, sx * x.l + sy * y.l, sx * x.o + sy * y.o};
+}
+
 template <typename TOUT>
 __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
-    constexpr int NG = 32;
-    __shared__ float sm[NG][8], sl[NG][8];
-    __shared__ f32x4 so[NG][8];
+    constexpr int NG = 64, NB = 4;  // chunk groups; chunks per group per round
+    __shared__ float sm[4][4], sl[4][4];
+    __shared__ f32x4 so[4][4];
     const int head = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
-    const int g = tid >> 3, q4 = tid & 7;
-    const int x0 = 32 * blockIdx.z + 4 * q4;
+    const int g = tid >> 2, q4 = tid & 3, wave = tid >> 6;
+    const int x0 = 16 * blockIdx.z + 4 * q4;
     const float* pm = (const float*)((const char*)a.ws + a.lay.part_ml);
     const float* po = (const float*)((const char*)a.ws + a.lay.part_o);
     const int ns = a.lay.n_splits;
     const int64_t base = (int64_t)b * ns * a.Hq + head;
-    // every load of a thread is issued before any is used (one memory round
-    // trip for up to 8 chunks per thread, more chunks loop)
-    float M = -INFINITY, Ls = 0.0f;
-    f32x4 acc = {};
-    for (int s0 = g; s0 < ns; s0 += NG * 8) {
-        float2 ml[8];
-        f32x4 ov[8];
+    MergeAcc acc{-INFINITY, 0.0f, f32x4{}};
+    for (int s0 = g; s0 < ns; s0 += NG * NB) {
+        float2 ml[NB];
+        f32x4 ov[NB];
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
+        for (int k = 0; k < NB; ++k) {
             const int sp = min(s0 + NG * k, ns - 1);
             const int64_t idx = base + (int64_t)sp * a.Hq;
             ml[k] = *(const float2*)(pm + 2 * idx);
             ov[k] = *(const f32x4*)(po + idx * a.d + x0);
         }
-        float mk = -INFINITY;
 #pragma unroll
-        for (int k = 0; k < 8; ++k)
-            if (s0 + NG * k < ns) mk = fmaxf(mk, ml[k].x);
-        if (mk == -INFINITY) continue;
-        if (mk > M) {
-            const float sc = __builtin_amdgcn_exp2f(M - mk);  // 0 when M = -inf
-            Ls *= sc;
-            acc *= sc;
-            M = mk;
-        }
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            if (s0 + NG * k >= ns || ml[k].x == -INFINITY) continue;
-            const float w = __builtin_amdgcn_exp2f(ml[k].x - M);
-            Ls += w * ml[k].y;
-            acc += w * ov[k];
-        }
+        for (int k = 0; k < NB; ++k)
+            if (s0 + NG * k < ns) acc = merge_acc(acc, MergeAcc{ml[k].x, ml[k].y, ov[k]});
     }
-    sm[g][q4] = M;
-    sl[g][q4] = Ls;
-    so[g][q4] = acc;
+    // groups g of a wave differ in lane bits 2..5
+#pragma unroll
+    for (int sh = 4; sh < 64; sh <<= 1) {
+        MergeAcc y;
+        y.m = __shfl_xor(acc.m, sh);
+        y.l = __shfl_xor(acc.l, sh);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) y.o[i] = __shfl_xor(acc.o[i], sh);
+        acc = merge_acc(acc, y);
+    }
+    if ((tid & 63) < 4) {
+        sm[wave][q4] = acc.m;
+        sl[wave][q4] = acc.l;
+        so[wave][q4] = acc.o;
+    }
     __syncthreads();
-    if (g == 0) {
-        float Mt = -INFINITY;
-#pragma unroll 8
-        for (int k = 0; k < NG; ++k) Mt = fmaxf(Mt, sm[k][q4]);
-        float Lt = 0.0f;
-        f32x4 At = {};
-        if (Mt != -INFINITY) {
-#pragma unroll 8
-            for (int k = 0; k < NG; ++k) {
-                if (sm[k][q4] == -INFINITY) continue;
-                const float w = __builtin_amdgcn_exp2f(sm[k][q4] - Mt);
-                Lt += w * sl[k][q4];
-                At += w * so[k][q4];
-            }
-        }
-        const bool empty = !(Lt > 0.0f);
+    if (tid < 4) {
+#pragma unroll
+        for (int w = 1; w < 4; ++w) acc = merge_acc(acc, MergeAcc{sm[w][q4], sl[w][q4], so[w][q4]});
+        const bool empty = !(acc.l > 0.0f);
+        const float inv = empty ? 0.0f : 1.0f / acc.l;
         TOUT* o = (TOUT*)a.o + ((int64_t)b * a.Hq + head) * a.d + x0;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) o[i] = (TOUT)(empty ? 0.0f : At[i] / Lt);
+        for (int i = 0; i < 4; ++i) o[i] = (TOUT)(acc.o[i] * inv);
         if (blockIdx.z == 0 && q4 == 0)
-            a.lse[(int64_t)b * a.Hq + head] = empty ? -INFINITY : (Mt + log2f(Lt)) * kLn2;
+            a.lse[(int64_t)b * a.Hq + head] = empty ? -INFINITY : (acc.m + log2f(acc.l)) * kLn2;
     }
 }
 
@@ -1026,7 +1021,7 @@ static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t s) {
     else err = launch_decode_g<D, TIN, 16>(a, s);
     if (err != hipSuccess) return err;
     LaunchScope scope("decode_merge", s);
-    hipLaunchKernelGGL(decode_merge_kernel<TIN>, dim3(a.Hq, a.B, D / 32), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(decode_merge_kernel<TIN>, dim3(a.Hq, a.B, D / 16), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 
