@@ -338,7 +338,10 @@ void prefill_bf16_kernel(PrefillArgs a, int rb_first, int n_rb) {
 #pragma unroll
         for (int b = 0; b < 2; ++b) {
             const int32_t jb = tau * kBN + 32 * b;
-            const uint32_t cls = pure ? want : tile_class32(wlo, wr_end, jb, jb + 32, wl, bif);
+            // uniform per wave: readfirstlane keeps it (and the branches on
+            // it) in scalar registers
+            const uint32_t cls = __builtin_amdgcn_readfirstlane(
+                pure ? want : tile_class32(wlo, wr_end, jb, jb + 32, wl, bif));
             if (cls & want) do_block(base, b, cls != want, remote_phase, jb);
         }
     };
