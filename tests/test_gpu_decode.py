@@ -87,6 +87,26 @@ def test_decode_small_batched(dtype, d, Hq, Hkv):
     _check(o, lse, o_ref, lse_ref, dtype, "small d=%d" % d)
 
 
+@pytest.mark.parametrize("dtype,wgs", [(torch.float32, None), (torch.bfloat16, "2048")])
+def test_decode_merge_of_many_chunks(dtype, wgs, monkeypatch):
+    """More than 256 key chunks per sequence, so each merge thread folds
+    several rounds of partials (fp32 caches aim at 512 workgroups; the bf16
+    case raises the workgroup target through JL_DECODE_WGS)."""
+    if wgs:
+        monkeypatch.setenv("JL_DECODE_WGS", wgs)
+    B, S, Hq, Hkv, d = 1, 40000, 8, 2, 128
+    ws = jl.decode_workspace_bytes(B, S, Hq, Hkv, d, dtype)
+    n_splits = ws // (B * Hq * (d + 2) * 4)
+    say("many-chunk decode", dtype, "about", n_splits, "chunks")
+    assert n_splits > 256
+    q, kc, vc = inputs.decode_inputs(B, S, Hq, Hkv, d, seed=77, dtype=dtype)
+    p = Params(8192, 2048, 1e6, 1.0 / math.sqrt(d))
+    o, lse = _dec_gpu(q, kc.cuda(), vc.cuda(), [S], p)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = _dec_ref(q, kc, vc, [S], p)
+    _check(o, lse, o_ref, lse_ref, dtype, "many chunks %s" % dtype)
+
+
 @pytest.mark.parametrize("label,p", [
     ("G1", Params(1000, 40, 1e4, 0.1)), ("w_local0", Params(64, 0, 1e4, 0.1)),
     ("w_local_all", Params(64, 4000, 1e4, 0.1)), ("plain", Params(64, 40, 1e4, 0.1, False)),
