@@ -469,6 +469,13 @@ __device__ __forceinline__ f16x8 e4m3x8_to_f16(uint32_t w0, uint32_t w1) {
     for (int x = 0; x < 8; ++x) r[x] = (f16)f[x];
     return r;
 }
+// 8 bf16 keys as fp16 MFMA operands (exact for magnitudes in [2^-14, 65504])
+__device__ __forceinline__ f16x8 bf16x8_to_f16(const bf16x8& x) {
+    f16x8 r;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) r[i] = (f16)(float)x[i];
+    return r;
+}
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ f32x4 mfma16(f16x8 a, f16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
@@ -479,7 +486,12 @@ __device__ __forceinline__ f32x4 mfma16k16h(s16x4 a, s16x4 b, f32x4 c) {
                                                  __builtin_bit_cast(f16x4, b), c, 0, 0, 0);
 }
 
-// bf16 decode.  Same scoring as above; P V runs on MFMA.  Each wave stages
+// bf16 decode.  Same scoring as above, with QK^T on fp16 operands: the
+// query is an fp16 hi + lo pair, stored keys widen to fp16 (exact), and a
+// remote key is rotated in fp32 and rounded once to fp16 (11 significant
+// bits; a key's rounding is independent of the other keys' and averages out
+// in the softmax, unlike the query's, hence the query's lo part).  P V runs
+// on MFMA.  Each wave stages
 // its V tile in LDS and the transposing read ds_read_b64_tr_b16 hands every
 // lane its B operand (4 keys x 1 d per 16-d block) directly.  The
 // probabilities are already in the A operand layout (lane (n, c) holds keys
@@ -490,20 +502,19 @@ __device__ __forceinline__ f32x4 mfma16k16h(s16x4 a, s16x4 b, f32x4 c) {
 // PAGED: the cache is a pool of pages of 2^page_shift rows addressed through
 // a per-sequence block table (each workgroup copies its chunk's page numbers
 // to LDS, clamped to the pool, so a bad table entry cannot read outside it).
-// FP8: the cache holds OCP E4M3 codes with one scale per kv head.  With half
-// the bytes per key the remote keys' rotation would bound the kernel, so this
-// path runs on fp16 operands: codes widen exactly to fp16 (local keys, the V
-// tile in LDS) or f32 (remote keys, rotated and rounded once to fp16, 11
-// significant bits, where the bf16 path needs a hi + lo pair); the query is
-// an fp16 hi + lo pair, P is fp16.  The key scale multiplies the finished
-// scores and the value scale the partial output.
+// FP8: the cache holds OCP E4M3 codes with one scale per kv head.  Codes
+// widen exactly to fp16 (local keys, the V tile in LDS) or f32 (remote keys,
+// rotated and rounded once to fp16); P and the V tile are fp16 too.  The key
+// scale multiplies the finished scores and the value scale the partial
+// output.
 template <int D, bool BIF, int GQ, bool PAGED, bool FP8>
 __global__ __launch_bounds__(512) void decode_split_bf16_kernel(DecodeArgs a) {
     using TC = typename std::conditional<FP8, uint8_t, bf16>::type;  // cache element
     using KRAW = typename std::conditional<FP8, u32x2, bf16x8>::type;  // 8 key elements
     using VRAW = typename std::conditional<FP8, u32x4, bf16x8>::type;  // 16 bytes of a V row
-    using OT = typename std::conditional<FP8, f16, bf16>::type;         // MFMA operand element
-    using OV = typename std::conditional<FP8, f16x8, bf16x8>::type;     // 8 MFMA operands
+    using OT = f16;                                                     // QK^T operand element
+    using OV = f16x8;                                                   // 8 QK^T operands
+    using PT = typename std::conditional<FP8, f16, bf16>::type;         // P V operand element
     constexpr int HALF = D / 2;
     constexpr int NST = D / 32;          // k-steps of the QK^T product
     constexpr int NH = NST / 2;          // k-steps per RoPE half
@@ -632,7 +643,7 @@ __global__ __launch_bounds__(512) void decode_split_bf16_kernel(DecodeArgs a) {
     // the 8 key elements of a k-step as MFMA operands (exact for E4M3 codes)
     auto kop = [&](const KRAW& kr) __attribute__((always_inline)) -> OV {
         if constexpr (FP8) return e4m3x8_to_f16(kr[0], kr[1]);
-        else return kr;
+        else return bf16x8_to_f16(kr);
     };
     VRAW vA[NI], vB[NI], vC[NI];
 
@@ -757,40 +768,18 @@ __global__ __launch_bounds__(512) void decode_split_bf16_kernel(DecodeArgs a) {
                     kf1[x] = (float)kcur[s + NH][x];
                 }
             }
-            if constexpr (FP8) {
-                f16x8 h0, h1;
+            f16x8 h0, h1;
 #pragma unroll
-                for (int x = 0; x < 8; ++x) {
-                    const float2 cs = tp[32 * s + x];
-                    h0[x] = (f16)(kf0[x] * cs.x - kf1[x] * cs.y);
-                    h1[x] = (f16)(kf1[x] * cs.x + kf0[x] * cs.y);
-                }
-                acc = mfma16(h0, Q[s], acc);
-                acc = mfma16(h1, Q[s + NH], acc);
-                if constexpr (!PACK) {
-                    acc = mfma16(h0, Qlo[s], acc);
-                    acc = mfma16(h1, Qlo[s + NH], acc);
-                }
-            } else {
-                bf16x8 h0, l0, h1, l1;
-#pragma unroll
-                for (int x = 0; x < 8; ++x) {
-                    const float2 cs = tp[32 * s + x];
-                    const float y0 = kf0[x] * cs.x - kf1[x] * cs.y;
-                    const float y1 = kf1[x] * cs.x + kf0[x] * cs.y;
-                    h0[x] = (bf16)y0;
-                    l0[x] = (bf16)(y0 - (float)h0[x]);
-                    h1[x] = (bf16)y1;
-                    l1[x] = (bf16)(y1 - (float)h1[x]);
-                }
-                acc = mfma16(h0, Q[s], acc);
-                acc = mfma16(l0, Q[s], acc);
-                acc = mfma16(h1, Q[s + NH], acc);
-                acc = mfma16(l1, Q[s + NH], acc);
-                if constexpr (!PACK) {
-                    acc = mfma16(h0, Qlo[s], acc);
-                    acc = mfma16(h1, Qlo[s + NH], acc);
-                }
+            for (int x = 0; x < 8; ++x) {
+                const float2 cs = tp[32 * s + x];
+                h0[x] = (f16)(kf0[x] * cs.x - kf1[x] * cs.y);
+                h1[x] = (f16)(kf1[x] * cs.x + kf0[x] * cs.y);
+            }
+            acc = mfma16(h0, Q[s], acc);
+            acc = mfma16(h1, Q[s + NH], acc);
+            if constexpr (!PACK) {
+                acc = mfma16(h0, Qlo[s], acc);
+                acc = mfma16(h1, Qlo[s + NH], acc);
             }
         }
         return finish(acc);
@@ -829,7 +818,7 @@ __global__ __launch_bounds__(512) void decode_split_bf16_kernel(DecodeArgs a) {
         float ps = 0.0f;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const OT pb = (OT)__builtin_amdgcn_exp2f(sc[i] - m_run);
+            const PT pb = (PT)__builtin_amdgcn_exp2f(sc[i] - m_run);
             ps += (float)pb;
             pa[i] = __builtin_bit_cast(short, pb);
         }
