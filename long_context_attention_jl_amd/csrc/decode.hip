@@ -488,24 +488,23 @@ __device__ __forceinline__ f32x4 mfma16k16h(s16x4 a, s16x4 b, f32x4 c) {
 
 // bf16 decode.  Same scoring as above, with QK^T on fp16 operands: the
 // query is an fp16 hi + lo pair, stored keys widen to fp16 (exact), and a
-// remote key is rotated in fp32 and rounded once to fp16 (11 significant
-// bits; a key's rounding is independent of the other keys' and averages out
-// in the softmax, unlike the query's, hence the query's lo part).  P V runs
-// on MFMA.  Each wave stages
-// its V tile in LDS and the transposing read ds_read_b64_tr_b16 hands every
-// lane its B operand (4 keys x 1 d per 16-d block) directly.  The
-// probabilities are already in the A operand layout (lane (n, c) holds keys
-// 4c..4c+3 of query column n), rounded to bf16; the row sums use the same
-// rounded values.  K and V tiles stay two ahead in registers.  All loads are
-// unconditional (indices clamped to valid rows), so the memory stream has no
-// branches and the compiler's waits stay exact.
+// remote key is turned on packed fp16 by an fp16 (cos, sin) table, a few
+// fp16 roundings per element (a key's rounding is independent of the other
+// keys' and averages out in the softmax, unlike the query's, hence the
+// query's lo part).  P V runs on MFMA.  Each wave stages its V tile in LDS
+// and the transposing read ds_read_b64_tr_b16 hands every lane its B operand
+// (4 keys x 1 d per 16-d block) directly.  The probabilities are already in
+// the A operand layout (lane (n, c) holds keys 4c..4c+3 of query column n),
+// rounded to bf16; the row sums use the same rounded values.  K and V tiles
+// stay two ahead in registers.  All loads are unconditional (indices clamped
+// to valid rows), so the memory stream has no branches and the compiler's
+// waits stay exact.
 // PAGED: the cache is a pool of pages of 2^page_shift rows addressed through
 // a per-sequence block table (each workgroup copies its chunk's page numbers
 // to LDS, clamped to the pool, so a bad table entry cannot read outside it).
 // FP8: the cache holds OCP E4M3 codes with one scale per kv head.  Codes
-// widen exactly to fp16 (local keys, the V tile in LDS) or f32 (remote keys,
-// rotated and rounded once to fp16); P and the V tile are fp16 too.  The key
-// scale multiplies the finished scores and the value scale the partial
+// widen exactly to fp16 (keys and the V tile in LDS); P is fp16 too.  The
+// key scale multiplies the finished scores and the value scale the partial
 // output.
 template <int D, bool BIF, int GQ, bool PAGED, bool FP8>
 __global__ __launch_bounds__(512) void decode_split_bf16_kernel(DecodeArgs a) {
@@ -519,7 +518,6 @@ __global__ __launch_bounds__(512) void decode_split_bf16_kernel(DecodeArgs a) {
     constexpr int NST = D / 32;          // k-steps of the QK^T product
     constexpr int NH = NST / 2;          // k-steps per RoPE half
     constexpr bool PACK = GQ <= 8;       // hi and lo query parts in one operand
-    constexpr int TSTR = HALF + 2;       // LDS row stride of the angle table (float2)
     constexpr int ROWB = D * (int)sizeof(TC);  // bytes of one cache row of V
     constexpr int VEL = 16 / (int)sizeof(TC);  // V elements per 16-byte load
     constexpr int CPR = ROWB / 16;       // 16-byte chunks per row
@@ -528,7 +526,9 @@ __global__ __launch_bounds__(512) void decode_split_bf16_kernel(DecodeArgs a) {
     constexpr int VRS = D * 2 + 32;      // LDS row stride of a bf16 V tile (+32 spreads banks)
     constexpr int SLOT = kTile * VRS;    // bytes of one wave's V tile
     constexpr int NDB = D / 16;          // 16-wide d blocks of O
-    __shared__ float2 tab[BIF ? kStageB * TSTR : 1];  // R(-u theta_t): (cos, sin)
+    constexpr int TSTRH = D + 8;         // LDS row stride of the angle table (halves)
+    // R(-u theta_t) in fp16: row u holds the HALF cosines, then the HALF sines
+    __shared__ __align__(16) f16 tabh[BIF ? kStageB * TSTRH : 8];
     // query angles: row st < kDecodeMaxStagesB holds R(f(p) - f(jb) + jb) of
     // stage st of this chunk (remote stages), the last row R(p)
     __shared__ float2 qtab[(kDecodeMaxStagesB + 1) * HALF];
@@ -694,7 +694,8 @@ __global__ __launch_bounds__(512) void decode_split_bf16_kernel(DecodeArgs a) {
                     rope_cs_rev(-(double)(x / HALF) * (1.0 - rsc) * rv, cs, sn);
                 else
                     rope_cs_hw(-(int64_t)(x / HALF), rv, cs, sn);
-                tab[(x / HALF) * TSTR + x % HALF] = make_float2(cs, sn);
+                tabh[(x / HALF) * TSTRH + x % HALF] = (f16)cs;
+                tabh[(x / HALF) * TSTRH + HALF + x % HALF] = (f16)sn;
             }
         }
         __syncthreads();
@@ -752,29 +753,20 @@ __global__ __launch_bounds__(512) void decode_split_bf16_kernel(DecodeArgs a) {
         }
         return finish(acc);
     };
+    // A remote key turned by -u theta_t: the stored values widen exactly to
+    // fp16 and the rotation runs on packed fp16 against the fp16 table (a
+    // key's rounding is its own and averages out in the softmax).
     auto scores_remote = [&](const KRAW* kcur, int32_t u) __attribute__((always_inline)) -> f32x4 {
         f32x4 acc = {};
-        const float2* tp = tab + u * TSTR + 8 * c;
+        const f16* th = tabh + u * TSTRH + 8 * c;
 #pragma unroll
         for (int s = 0; s < NH; ++s) {
-            float kf0[8], kf1[8];
-            if constexpr (FP8) {
-                e4m3x8_to_f32(kcur[s][0], kcur[s][1], kf0);
-                e4m3x8_to_f32(kcur[s + NH][0], kcur[s + NH][1], kf1);
-            } else {
-#pragma unroll
-                for (int x = 0; x < 8; ++x) {
-                    kf0[x] = (float)kcur[s][x];
-                    kf1[x] = (float)kcur[s + NH][x];
-                }
-            }
-            f16x8 h0, h1;
-#pragma unroll
-            for (int x = 0; x < 8; ++x) {
-                const float2 cs = tp[32 * s + x];
-                h0[x] = (f16)(kf0[x] * cs.x - kf1[x] * cs.y);
-                h1[x] = (f16)(kf1[x] * cs.x + kf0[x] * cs.y);
-            }
+            const f16x8 k0 = kop(kcur[s]);
+            const f16x8 k1 = kop(kcur[s + NH]);
+            const f16x8 cs = *reinterpret_cast<const f16x8*>(th + 32 * s);
+            const f16x8 sn = *reinterpret_cast<const f16x8*>(th + HALF + 32 * s);
+            const f16x8 h0 = k0 * cs - k1 * sn;
+            const f16x8 h1 = k1 * cs + k0 * sn;
             acc = mfma16(h0, Q[s], acc);
             acc = mfma16(h1, Q[s + NH], acc);
             if constexpr (!PACK) {
