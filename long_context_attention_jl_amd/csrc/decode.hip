@@ -12,15 +12,15 @@
 // inside the window are scored as <R(p) q, K_j> on the stored values.
 //
 // Work decomposition: a workgroup owns a chunk of key positions of one
-// sequence and up to 4 kv heads (one wave each).  Per 16-key tile a wave
-// forms S^T (16 keys x the GQA group's query heads) = K Q^T on
-// v_mfma_f32_16x16x32_bf16 with the query split into bf16 hi + lo parts and
-// rotated keys split the same way (about 16 significant bits, so the scores
-// carry no visible 16-bit rounding), then accumulates P V in fp32 on the
-// vector ALU.  One tile's K and V loads stay in flight while the previous
-// tile is processed; three workgroups share a compute unit.
-// Each chunk writes (m, l, O) partials; a second kernel merges the chunks
-// exactly (max-shifted sums).
+// sequence and a group of kv heads (one wave each); each chunk writes
+// (m, l, O) partials and a second kernel merges the chunks exactly
+// (max-shifted sums).  Two split kernels:
+//  - fp32 caches (decode_split_kernel, up to 4 kv heads per workgroup): per
+//    16-key tile a wave forms S^T = K Q^T on v_mfma_f32_16x16x32_bf16 with the
+//    query and the rotated keys split into bf16 hi + lo parts (about 16
+//    significant bits), then accumulates P V in fp32 on the vector ALU;
+//  - bf16 and fp8 caches (decode_split_bf16_kernel, up to 8 kv heads): QK^T on
+//    fp16 MFMA, P V on MFMA through LDS; described above that kernel.
 #include "internal.h"
 
 namespace jl {
