@@ -188,7 +188,10 @@ jl_status jl_bifocal_decode_workspace(int32_t batch, int32_t max_seqlen_k, int32
  *   seqlens_k  device int32 [B], 1 <= L_b <= max_seqlen_k <= S_max.
  *   workspace  at least jl_bifocal_decode_workspace() bytes (scratch).
  * Supported: dtype bf16 or f32 (bf16 only for params->bifocal == 2), d in {64, 128},
- * Hq / Hkv <= 16.
+ * Hq / Hkv <= 16.  The bf16 path forms q k^T on fp16 MFMA operands and P v on
+ * bf16 ones (fp32 accumulate): the rotated query (times softmax_scale *
+ * log2 e) and the cached keys must stay below 65504 in magnitude; device
+ * data is not range-checked.
  */
 jl_status jl_bifocal_decode(void* o, float* lse, const void* q, const void* k_cache,
                             const void* v_cache, const int32_t* seqlens_k, int32_t batch,
