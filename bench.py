@@ -79,6 +79,8 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-three-call", action="store_true")
     ap.add_argument("--no-chunk", action="store_true")
+    ap.add_argument("--no-prefill-configs", action="store_true",
+                    help="skip the 64K and varlen prefill workloads")
     ap.add_argument("--no-decode-extras", action="store_true",
                     help="decode: time only the flat bf16 cache (no paged, fp8 or 16-step runs)")
     ap.add_argument("--copy-calibration", type=int, default=0,
@@ -198,6 +200,9 @@ def main():
     if not args.no_chunk:
         out["chunk"] = bench_chunk(jl, inputs, torch)
 
+    if not args.no_prefill_configs:
+        out["prefill_configs"] = bench_prefill_configs(jl, inputs, torch)
+
     if not args.no_decode:
         out["decode"] = bench_decode(jl, inputs, torch, args.decode_iters,
                                      extras=not args.no_decode_extras)
@@ -228,6 +233,46 @@ def bench_three_call(jl, torch, case, fused_ms):
     ms = (time.perf_counter() - t0) * 1e3
     return {"ms_per_step": round(ms, 3), "tokens_per_s": round(T / (ms / 1e3), 1),
             "fused_speedup": round(ms / fused_ms, 3)}
+
+
+def bench_prefill_configs(jl, inputs, torch, iters=3):
+    """The other two bf16 prefill workloads: the Qwen3-1.7B-shaped layer at
+    L = 65536 (G = 2) and four packed sequences of 8192, 32768, 49152 and 98304
+    tokens (G = 1, 1, 2, 3).  Best of `iters` warm calls, timed with events on
+    the launch stream; algorithmic FLOPs count one score per causal pair."""
+    res = {}
+    for make in (inputs.qwen3_1p7b_64k, inputs.varlen_4seq):
+        case = make()
+        T, Hq, d = case.q.shape
+        Hkv = case.k.shape[1]
+        p = case.params
+        cu = case.cu_seqlens
+        lens = [cu[i + 1] - cu[i] for i in range(len(cu) - 1)] if cu else [T]
+        q, k, v = case.q.cuda(), case.k.cuda(), case.v.cuda()
+        ws = torch.empty(jl.prefill_workspace_bytes(T, len(lens), Hq, Hkv, d, q.dtype),
+                         dtype=torch.uint8, device="cuda")
+        kw = dict(w_pretrained=p.w_pretrained, w_local=p.w_local, rope_base=p.rope_base,
+                  softmax_scale=p.softmax_scale, workspace=ws)
+        if cu:
+            kw["cu_seqlens"] = torch.tensor(cu, dtype=torch.int32, device="cuda")
+            kw["max_seqlen"] = max(lens)
+        jl.bifocal_prefill(q, k, v, **kw)
+        ts = []
+        for _ in range(iters):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            jl.bifocal_prefill(q, k, v, **kw)
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        ms = min(ts)
+        flops = sum(_flops_rows(d, Hq, 0, n) for n in lens)
+        res[case.name] = {"ms": round(ms, 3), "tokens_per_s": round(T / (ms / 1e3), 1),
+                          "tflops": round(flops / (ms / 1e3) / 1e12, 1),
+                          "frac_of_bf16_peak": round(flops / (ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+        del q, k, v, ws, case
+    return res
 
 
 def bench_chunk(jl, inputs, torch, iters=10):
