@@ -30,10 +30,10 @@ def _flops_rows(d, Hq, a, b):
     return 4.0 * d * Hq * ((b * (b + 1) - a * (a + 1)) / 2.0)
 
 
-def _profiled_traffic(summary: str):
-    """HBM bytes per launch recorded in a committed rocprofv3 counter summary
-    (FETCH_SIZE + WRITE_SIZE, scaled by a plain-copy calibration), or None when
-    the kernel's sources no longer hash to the value the counters were taken on."""
+def _profiled_field(summary: str, field: str):
+    """A figure recorded in a committed rocprofv3 summary under profiles/, or None
+    when the summary is missing or the kernel's sources no longer hash to the
+    value the counters were taken on."""
     import hashlib
 
     path = os.path.join(ROOT, "profiles", summary)
@@ -42,7 +42,7 @@ def _profiled_traffic(summary: str):
     fields = {}
     for line in open(path):
         key, sep, val = line.partition(":")
-        if sep and key.strip() in ("traffic_bytes_per_launch", "sources", "source_sha256_16"):
+        if sep and key.strip() in (field, "sources", "source_sha256_16"):
             fields[key.strip()] = val.strip()
     if len(fields) != 3:
         return None
@@ -55,7 +55,13 @@ def _profiled_traffic(summary: str):
             h.update(fh.read())
     if h.hexdigest()[:16] != fields["source_sha256_16"]:
         return None
-    return float(fields["traffic_bytes_per_launch"])
+    return float(fields[field])
+
+
+def _profiled_traffic(summary: str):
+    """HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, scaled by a plain-copy
+    calibration) from a committed counter summary, or None (see _profiled_field)."""
+    return _profiled_field(summary, "traffic_bytes_per_launch")
 
 
 def _copy_calibration(n_bytes: int, iters: int):
@@ -172,6 +178,12 @@ def main():
                      "traffic": _profiled_traffic("traffic_prefill_bf16_qwen3_L131072.md"),
                      "algorithmic_flops_per_launch": main_flops},
     }
+    # the engine clock rocprofv3 measured under this kernel: the peak scaled to it
+    sclk = _profiled_field("sclk_prefill_bf16_qwen3_L131072.md", "sclk_ghz")
+    if sclk:
+        peak_sclk = PEAK_BF16_TFLOPS * sclk / 2.4
+        out["roofline"].update({"sclk_ghz": sclk, "peak_at_sclk": round(peak_sclk, 1),
+                                "frac_at_sclk": round(achieved / peak_sclk, 4)})
     # the same prefill with the bifocal logic off (every pair under standard
     # RoPE): the overhead baseline, timed warm after the timed region
     t_plain = []
