@@ -461,6 +461,24 @@ def bench_decode(jl, inputs, torch, iters, extras=True):
     jl.profile_enable(False)
     t_bif, t_plain = min(tb), min(tp)
     nbytes = 2 * L * Hkv * d * 2
+    # measured read ceiling: the library's read-only stream over buffers of the
+    # cache's size (four rotating, as for the decode calls)
+    bufs = [torch.empty(nbytes, dtype=torch.uint8, device="cuda") for _ in range(4)]
+    part = torch.empty(256, dtype=torch.int32, device="cuda")
+
+    def run_read(n):
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        ev0.record()
+        for i in range(n):
+            jl.stream_read(bufs[i % 4], part)
+        ev1.record()
+        torch.cuda.synchronize()
+        return ev0.elapsed_time(ev1) * 1e3 / n
+
+    run_read(8)
+    t_read = min(run_read(40) for _ in range(3))
+    del bufs
     split_cnt, split_ms = prof.get("decode_split", (1, float("nan")))
     split_us = split_ms * 1e3 / max(split_cnt, 1)
     # the 16-step run: a cache filled to 32760 plus one appended token per
@@ -477,6 +495,9 @@ def bench_decode(jl, inputs, torch, iters, extras=True):
         "split_kernel_us": round(split_us, 2),
         "split_kernel_GBps": round(nbytes / (split_us * 1e-6) / 1e9, 1),
         "split_kernel_traffic": _profiled_traffic("traffic_decode_split_L131072.md"),
+        "stream_read_us": round(t_read, 2),
+        "stream_read_GBps": round(nbytes / (t_read * 1e-6) / 1e9, 1),
+        "frac_of_stream_read": round(t_read / t_bif, 4),
         "kernels": {n: {"launches": c2, "avg_us": round(ms * 1e3 / max(c2, 1), 2)}
                     for n, (c2, ms) in sorted(prof.items())},
     }

@@ -344,6 +344,17 @@ jl_status jl_debug_index_math(int64_t L, int32_t w_pretrained, int32_t w_local, 
                               uint8_t* band_out, uint8_t* tile_out, void* stream);
 
 /*
+ * Measurement aid: reads `bytes` of device memory at `src` once, as a
+ * read-only stream (256 workgroups, 16-byte loads, four in flight per thread),
+ * and writes the wrapping uint32 sum of the words each workgroup read to
+ * partial_sums (device uint32 [256]); their wrapping sum is the sum of every
+ * uint32 word of the buffer.  Timing it gives the HBM read rate the decode
+ * kernels, which read each cache byte once, are compared with.  src 16-byte
+ * aligned, bytes a positive multiple of 16 (JL_ERR_INVALID_ARGUMENT otherwise).
+ */
+jl_status jl_debug_stream_read(const void* src, size_t bytes, uint32_t* partial_sums, void* stream);
+
+/*
  * Kernel timing (profiling aid).  While enabled, every kernel the library
  * launches is bracketed by HIP events on its stream; jl_profile_read()
  * synchronizes those events and reports, per kernel name, the launch count

@@ -793,6 +793,19 @@ jl_status jl_debug_index_math(int64_t L, int32_t w_pretrained, int32_t w_local, 
     return finish(s, "jl_debug_index_math");
 }
 
+jl_status jl_debug_stream_read(const void* src, size_t bytes, uint32_t* partial_sums,
+                               void* stream) {
+    if (!src || !partial_sums) return fail(JL_ERR_INVALID_ARGUMENT, "null pointer argument");
+    if (bytes < 16 || bytes % 16) return fail(JL_ERR_INVALID_ARGUMENT, "bytes must be a positive multiple of 16");
+    if (bytes > (1ULL << 40)) return fail(JL_ERR_INVALID_ARGUMENT, "bytes above 2^40");
+    if (!al16(src) || ((uintptr_t)partial_sums & 3))
+        return fail(JL_ERR_INVALID_ARGUMENT, "src must be 16-byte and partial_sums 4-byte aligned");
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e = launch_stream_read(src, (int64_t)bytes, partial_sums, s);
+    if (e != hipSuccess) return hip_fail(e, "stream read launch");
+    return finish(s, "jl_debug_stream_read");
+}
+
 jl_status jl_profile_enable(int32_t on) {
     std::lock_guard<std::mutex> lk(g_prof_mu);
     clear_records();

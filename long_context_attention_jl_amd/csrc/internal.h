@@ -46,6 +46,8 @@ DecodeLayout decode_layout(int32_t batch, int32_t max_seqlen_k, int32_t Hq, int3
 
 RopeFreq make_rope_freq(double base, int d);
 
+constexpr int kStreamReadWgs = 256;  // workgroups (and partial sums) of the read stream
+hipError_t launch_stream_read(const void* src, int64_t bytes, uint32_t* out, hipStream_t s);
 hipError_t launch_rope_apply(void* out, const void* x, const int32_t* pos, int64_t T, int32_t H,
                              int32_t d, const RopeFreq& tab, int32_t G, int dtype,
                              hipStream_t s);

@@ -121,6 +121,8 @@ def lib() -> ctypes.CDLL:
         L.jl_kv_quantize_fp8.argtypes = [_vp, _vp, _vp, _i64, _i32, _i32, _vp]
         L.jl_debug_index_math.restype = ctypes.c_int
         L.jl_debug_index_math.argtypes = [_i64, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp]
+        L.jl_debug_stream_read.restype = ctypes.c_int
+        L.jl_debug_stream_read.argtypes = [_vp, ctypes.c_size_t, _vp, _vp]
         L.jl_profile_enable.restype = ctypes.c_int
         L.jl_profile_enable.argtypes = [_i32]
         L.jl_profile_read.restype = ctypes.c_int
@@ -520,6 +522,20 @@ def debug_index_math(L: int, w_pretrained: int, w_local: int, bifocal: bool, bm:
     torch.cuda.synchronize(device)
     return (int(G.item()), f.cpu().numpy(), band.cpu().numpy().reshape(n, n),
             tile.cpu().numpy().reshape(nti, ntj))
+
+
+def stream_read(buf: torch.Tensor, partial: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Reads every byte of the contiguous device tensor `buf` once
+    (jl_debug_stream_read); returns the 256 per-workgroup wrapping uint32 sums
+    (as int32, on the device, not synchronized)."""
+    if not buf.is_contiguous():
+        raise ValueError("buf must be contiguous")
+    nbytes = buf.numel() * buf.element_size()
+    if partial is None:
+        partial = torch.empty(256, dtype=torch.int32, device=buf.device)
+    _check(lib().jl_debug_stream_read(buf.data_ptr(), nbytes, partial.data_ptr(), _stream()),
+           "jl_debug_stream_read")
+    return partial
 
 
 def profile_enable(on: bool) -> None:

@@ -359,3 +359,11 @@ def test_vector_operands_must_be_16_byte_aligned(call, kw):
     vectors; a pointer off that boundary is refused on the host."""
     assert call(**kw) == 1
     assert b"16-byte" in jlb.lib().jl_last_error()
+
+
+@pytest.mark.parametrize("args,status", [
+    ((None, 1024, FAKE), 1), ((FAKE, 1024, None), 1), ((FAKE, 0, FAKE), 1), ((FAKE, 24, FAKE), 1),
+    ((FAKE + 8, 1024, FAKE), 1), ((FAKE, 1024, FAKE + 2), 1),
+])
+def test_stream_read_validation(args, status):
+    assert jlb.lib().jl_debug_stream_read(*args, None) == status
