@@ -27,7 +27,9 @@
  *     caller.  The library allocates no device memory, keeps no state other
  *     than a thread-local error string, and never synchronizes: work is
  *     enqueued on `stream` (a hipStream_t; NULL is the default stream) and is
- *     complete when the caller synchronizes that stream.
+ *     complete when the caller synchronizes that stream.  A call enqueues
+ *     kernels only (no memset, copy or allocation), so it can be captured in a
+ *     HIP graph and replayed; a replay reads the buffers the call was given.
  *   - Every argument is validated on the host before any HIP call.  A failing
  *     entry point launches nothing and returns a status; jl_last_error() then
  *     holds a description.  Values that live in device memory (cu_seqlens,
