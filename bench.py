@@ -12,7 +12,6 @@ Prints ONE JSON line.  Usage: python bench.py [--gpus 1] [--steps K] [--warmup W
 """
 import argparse
 import json
-import math
 import os
 import sys
 import time

@@ -16,7 +16,7 @@ from long_context_attention_jl_amd import inputs
 from long_context_attention_jl_amd import jetlong as jl
 from long_context_attention_jl_amd.inputs import Params
 
-from _parity import (check_prefill, gpu_prefill, ln_sum_exp, oracle_prefill_rows, sample_rows,
+from _parity import (check_prefill, gpu_prefill, oracle_prefill_rows, sample_rows,
                      say)
 
 pytestmark = pytest.mark.gpu
