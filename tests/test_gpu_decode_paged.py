@@ -58,13 +58,14 @@ def _oracle(q, kc, vc, lens, p):
                          rope_base=p.rope_base, softmax_scale=p.softmax_scale, bifocal=p.bifocal)
 
 
-@pytest.mark.parametrize("page", [16, 64, 256])
-def test_paged_equals_flat_and_oracle(page):
-    B, S, Hq, Hkv, d = 3, 1500, 8, 2, 128
+@pytest.mark.parametrize("page,Hq,Hkv,d", [(16, 8, 2, 128), (64, 8, 2, 128), (256, 8, 2, 128),
+                                          (32, 32, 2, 64)])
+def test_paged_equals_flat_and_oracle(page, Hq, Hkv, d):
+    B, S = 3, 1500
     lens = [1500, 1, 777]
     q, kc, vc = inputs.decode_inputs(B, S, Hq, Hkv, d, seed=page)
     p = Params(300, 100, 1e4, 1.0 / math.sqrt(d))
-    say("paged decode page=%d lens=%s" % (page, lens))
+    say("paged decode page=%d Hq=%d Hkv=%d d=%d lens=%s" % (page, Hq, Hkv, d, lens))
     o_f, l_f, o_p, l_p = _run_both(q, kc, vc, lens, p, page, seed=page)
     assert torch.equal(o_f, o_p) and torch.equal(l_f, l_p), "paged differs from flat"
     o_ref, l_ref = _oracle(q, kc, vc, lens, p)
