@@ -228,8 +228,9 @@ jl_status jl_bifocal_decode_paged(void* o, float* lse, const void* q, const void
  * the correction rotation ([TW] §三, [BT] §3.3) and the outputs are those
  * of jl_bifocal_decode on these dequantized values: the rotation is applied
  * after dequantization, so the cache format leaves the method unchanged.
- * Codes widen exactly to bf16; the key scale is folded into the query and
- * the value scale into the output.
+ * Codes widen exactly to fp16 (the MFMA operands); the key scale multiplies
+ * the finished scores, so the query's fp16 parts keep their range, and the
+ * value scale multiplies the output.
  *   q, o          bf16 [B][Hq][d]; lse float32 [B][Hq].
  *   k_cache, v_cache  uint8 [B][S_max][Hkv][d] E4M3 codes, read-only.
  *   k_scale, v_scale  device float32 [Hkv].
