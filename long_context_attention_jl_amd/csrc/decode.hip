@@ -534,6 +534,13 @@ __global__ __launch_bounds__(512) void decode_split_bf16_kernel(DecodeArgs a) {
     __shared__ float2 qtab[(kDecodeMaxStagesB + 1) * HALF];
     __shared__ __align__(16) char vs[kWavesB * SLOT];  // per wave: the V tile in use
     __shared__ int32_t ptab[PAGED ? kDecodeMaxPages : 1];  // page numbers of this chunk
+    // tiles finished per wave.  Waves w and w + 4 share a SIMD, whose issue
+    // arbiter favours the older wave: left alone, waves 0-3 finish their
+    // chunks about a fifth earlier and the younger waves then stream alone
+    // with half the loads in flight.  A wave that falls behind its partner
+    // raises its issue priority until it has caught up.
+    __shared__ int done_s[kWavesB];
+    volatile int* done = done_s;
 
     const int nw = blockDim.x >> 6;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
@@ -662,10 +669,11 @@ __global__ __launch_bounds__(512) void decode_split_bf16_kernel(DecodeArgs a) {
             qraw[s] = qok ? x : bf16x8{};
         }
     }
+    // the first tile's loads go out before the angle tables, the second's
+    // after them (the table work then waits less on the load issue queue)
     load_k(kbeg, kA);
     load_vr(kbeg, vA);
-    load_k(kbeg + kTile, kB);
-    load_vr(kbeg + kTile, vB);
+    if (threadIdx.x < kWavesB) done_s[threadIdx.x] = 0;
 
     // ---- angle tables, once per workgroup (the only barrier): the query
     // rows and the small key angles -u theta_t ----
@@ -701,6 +709,8 @@ __global__ __launch_bounds__(512) void decode_split_bf16_kernel(DecodeArgs a) {
         __syncthreads();
     }
     if (!head_ok) return;
+    load_k(kbeg + kTile, kB);
+    load_vr(kbeg + kTile, vB);
 
     // ---- query (as in the generic kernel) ----
     const float qscale = a.softmax_scale * kLog2e;
@@ -834,8 +844,10 @@ __global__ __launch_bounds__(512) void decode_split_bf16_kernel(DecodeArgs a) {
     const float invG = 1.0f / (float)G;
     int32_t jb = 0, r0 = 0;  // angle base of the stage (>= 0) and jb mod G
     bool stage_remote = false;
+    int my_done = 0;
+    const int partner = wave ^ 4;  // the other wave on this SIMD (if any)
     // one tile: issue the loads two tiles ahead, stage this tile's V in LDS,
-    // score, P V
+    // score, P V, then set this wave's priority from its lead over its partner
     auto step = [&](int32_t j0, const KRAW* kcur, const VRAW* vcur, KRAW* knext,
                     VRAW* vnext) __attribute__((always_inline)) {
         load_k(j0 + 2 * kTile, knext);
@@ -854,6 +866,12 @@ __global__ __launch_bounds__(512) void decode_split_bf16_kernel(DecodeArgs a) {
             sacc = scores_local(kcur);
         }
         process(j0, sacc, slot);
+        done[wave] = ++my_done;
+        const int other = partner < nw ? done[partner] : 0;
+        if (__builtin_amdgcn_readfirstlane(other) > my_done)
+            __builtin_amdgcn_s_setprio(3);
+        else
+            __builtin_amdgcn_s_setprio(0);
     };
 
     for (int32_t js = kbeg; js < kend; js += kStageB) {
