@@ -74,7 +74,11 @@ def test_decode_16_steps_across_g_switch():
 
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
-@pytest.mark.parametrize("d,Hq,Hkv", [(128, 8, 2), (64, 4, 4), (128, 16, 1), (64, 3, 1)])
+# (64, 12, 6): six waves, two of them with no SIMD partner in the tile-count
+# balancing; (128, 24, 12): a second head group of four waves whose other
+# four waves have no head
+@pytest.mark.parametrize("d,Hq,Hkv", [(128, 8, 2), (64, 4, 4), (128, 16, 1), (64, 3, 1), (64, 12, 6),
+                                      (128, 24, 12)])
 def test_decode_small_batched(dtype, d, Hq, Hkv):
     B, S = 3, 700
     q, kc, vc = inputs.decode_inputs(B, S, Hq, Hkv, d, seed=d + Hq, dtype=dtype)
