@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define JL_ABI_VERSION 1
+#define JL_ABI_VERSION 2
 
 typedef enum {
     JL_OK = 0,
@@ -75,6 +75,15 @@ typedef struct {
                            /*    position x / s with the real s = max(1, L / w_pretrained) */
                            /*    in place of floor(x / G).  bf16 prefill, chunked prefill */
                            /*    and decode only (JL_ERR_UNSUPPORTED elsewhere)           */
+    int32_t precise;       /* 0: fast scores (below); 1: split-precision scores for       */
+                           /*    concentrated attention (a few keys carry the softmax, so */
+                           /*    one key's score rounding reaches the LSE undiluted).     */
+                           /*    bf16 prefill: q and k as fp16 hi + lo on every row       */
+                           /*    (3 products instead of 1; rows below 2048 always do so); */
+                           /*    bf16 decode: remote keys turned in fp32 and split hi + lo */
+                           /*    (the stored keys and the query already are exact / split).*/
+                           /*    Ignored by the fp32 paths (already split); fp8 decode:   */
+                           /*    JL_ERR_UNSUPPORTED.  Must be 0 or 1.                     */
 } jl_params;
 
 /* JL_ABI_VERSION of the built library. */
@@ -108,9 +117,13 @@ jl_status jl_rope_apply(void* out, const void* x, const int32_t* positions, int6
 /*
  * Bytes of device workspace jl_bifocal_prefill needs for these sizes
  * (host pointer `bytes`).  Depends only on the arguments, never on data.
+ * `params` (host, may be NULL for the defaults) matters only through
+ * params->precise: split precision on every row needs low-part key tiles for
+ * every key.
  */
 jl_status jl_bifocal_prefill_workspace(int64_t T, int32_t n_seqs, int32_t Hq, int32_t Hkv,
-                                       int32_t d, jl_dtype dtype, size_t* bytes);
+                                       int32_t d, jl_dtype dtype, const jl_params* params,
+                                       size_t* bytes);
 
 /*
  * Causal bifocal prefill ([BT] §3.2, [TW] §四).  For query i of a sequence of
@@ -144,10 +157,11 @@ jl_status jl_bifocal_prefill(void* o, float* lse, const void* q, const void* k, 
                              const jl_params* params, jl_dtype dtype, void* k_rot_out,
                              void* workspace, size_t workspace_bytes, void* stream);
 
-/* Bytes of device workspace jl_bifocal_prefill_three_call needs (bf16 only). */
+/* Bytes of device workspace jl_bifocal_prefill_three_call needs (bf16 only);
+ * params as for jl_bifocal_prefill_workspace. */
 jl_status jl_bifocal_prefill_three_call_workspace(int64_t T, int32_t n_seqs, int32_t Hq,
                                                   int32_t Hkv, int32_t d, jl_dtype dtype,
-                                                  size_t* bytes);
+                                                  const jl_params* params, size_t* bytes);
 
 /*
  * The pages' unfused form of the same prefill ([TW] §四, [BT] §3.2): three
@@ -169,7 +183,16 @@ jl_status jl_bifocal_prefill_three_call(void* o, float* lse, const void* q, cons
                                         int32_t d, const jl_params* params, jl_dtype dtype,
                                         void* workspace, size_t workspace_bytes, void* stream);
 
-/* Bytes of device workspace jl_bifocal_decode needs for these sizes. */
+/*
+ * Bytes of device workspace jl_bifocal_decode (and the paged and fp8 decode
+ * calls) need for these sizes.  The workspace must be zero-filled before its
+ * first decode call: bf16 decode merges its key chunks inside the split
+ * kernel, the last workgroup of each group of chunks being found with
+ * counters kept at the start of the workspace.  Every decode call leaves
+ * those counters at zero again, so a workspace that only decode calls use is
+ * zeroed once (e.g. hipMemset at allocation); one shared with other entry
+ * points must be zeroed again before the next decode call.
+ */
 jl_status jl_bifocal_decode_workspace(int32_t batch, int32_t max_seqlen_k, int32_t Hq,
                                       int32_t Hkv, int32_t d, jl_dtype dtype, size_t* bytes);
 
@@ -188,7 +211,8 @@ jl_status jl_bifocal_decode_workspace(int32_t batch, int32_t max_seqlen_k, int32
  *   q          raw (un-rotated) query [B][Hq][d].
  *   k_cache, v_cache  [B][S_max][Hkv][d] of dtype, read-only.
  *   seqlens_k  device int32 [B], 1 <= L_b <= max_seqlen_k <= S_max.
- *   workspace  at least jl_bifocal_decode_workspace() bytes (scratch).
+ *   workspace  at least jl_bifocal_decode_workspace() bytes, zero-filled
+ *              before its first decode call (see there); otherwise scratch.
  * Supported: dtype bf16 or f32 (bf16 only for params->bifocal == 2), d in {64, 128},
  * Hq / Hkv <= 16.  The bf16 path forms q k^T on fp16 MFMA operands and P v on
  * bf16 ones (fp32 accumulate): the rotated query (times softmax_scale *
@@ -271,10 +295,11 @@ jl_status jl_kv_quantize_fp8(void* out, const void* x, const float* scale, int64
  * key tiles it holds fp32 partials for calls whose grid is small (fewer than
  * two 256-row workgroups per compute unit, e.g. a 1024-row chunk of 32
  * heads): those split each row block's keys in up to four shares and merge
- * the shares in LogSumExp space. */
+ * the shares in LogSumExp space.  params as for jl_bifocal_prefill_workspace
+ * (split-precision calls take no key shares). */
 jl_status jl_bifocal_prefill_chunk_workspace(int64_t Tq, int32_t batch, int32_t max_seqlen_k,
                                              int32_t Hq, int32_t Hkv, int32_t d, jl_dtype dtype,
-                                             size_t* bytes);
+                                             const jl_params* params, size_t* bytes);
 
 /*
  * Chunked prefill ([TW] §三 and [BT] §3.3 for the cache, [BT] §3.1 for G): a

@@ -99,10 +99,11 @@ LaunchScope::~LaunchScope() {
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-PrefillLayout prefill_layout(int64_t T, int32_t n_seqs, int32_t Hkv, int32_t d, int dtype) {
+PrefillLayout prefill_layout(int64_t T, int32_t n_seqs, int32_t Hkv, int32_t d, int dtype,
+                             int precise) {
     PrefillLayout L{};
     L.T_pad = (T + (int64_t)n_seqs * (kBN - 1) + kBN - 1) / kBN * kBN;
-    int64_t lo = (int64_t)n_seqs * kPreciseRows;
+    int64_t lo = precise ? T : (int64_t)n_seqs * kPreciseRows;
     if (lo > T) lo = T;
     L.lo_pad = (lo + (int64_t)n_seqs * (kBN - 1) + kBN - 1) / kBN * kBN;
     size_t off = 0;
@@ -136,12 +137,7 @@ DecodeLayout decode_layout(int32_t B, int32_t max_seqlen_k, int32_t Hq, int32_t 
     const int stage = b16 ? kDecodeStageB : 64;
     const int nw = Hkv < wmax ? Hkv : wmax;  // waves (kv heads) per decode workgroup
     const int64_t groups = (Hkv + nw - 1) / nw;
-    // JL_DECODE_WGS overrides the workgroup target for tuning
-    int64_t target = b16 ? 256 : 512;
-    if (const char* e = getenv("JL_DECODE_WGS")) {
-        const long v = strtol(e, nullptr, 10);
-        if (v >= 1 && v <= 65536) target = v;
-    }
+    const int64_t target = b16 ? 256 : 512;  // workgroups per call
     const int64_t span = (int64_t)max_seqlen_k + stage - 1;
     int64_t want = (target + (int64_t)B * groups - 1) / ((int64_t)B * groups);
     if (want < 1) want = 1;
@@ -150,11 +146,22 @@ DecodeLayout decode_layout(int32_t B, int32_t max_seqlen_k, int32_t Hq, int32_t 
     if (b16 && chunk > (int64_t)kDecodeMaxStagesB * stage) chunk = (int64_t)kDecodeMaxStagesB * stage;
     L.chunk = (int32_t)chunk;
     L.n_splits = (int32_t)((span + chunk - 1) / chunk);
+    L.groups = (int32_t)groups;
+    L.nbins = (L.n_splits + kDecodeBin - 1) / kDecodeBin;
     size_t off = 0;
+    L.tickets = off;
+    L.ticket_bytes = (size_t)B * groups * (L.nbins + 1) * sizeof(uint32_t);
+    off = align256(off + L.ticket_bytes);
     L.part_ml = off;
-    off = align256(off + (size_t)B * L.n_splits * Hq * 2 * sizeof(float));
+    off = align256(off + (size_t)B * L.n_splits * Hq * 4 * sizeof(float));
     L.part_o = off;
     off = align256(off + (size_t)B * L.n_splits * Hq * d * sizeof(float));
+    if (L.nbins > 1) {
+        L.part2_ml = off;
+        off = align256(off + (size_t)B * L.nbins * Hq * 4 * sizeof(float));
+        L.part2_o = off;
+        off = align256(off + (size_t)B * L.nbins * Hq * d * sizeof(float));
+    }
     L.total = off;
     return L;
 }
@@ -190,8 +197,13 @@ static jl_status check_params(const jl_params* p) {
         return fail(JL_ERR_INVALID_ARGUMENT, "softmax_scale must be finite and > 0");
     if (p->bifocal < 0 || p->bifocal > 2)
         return fail(JL_ERR_INVALID_ARGUMENT, "bifocal must be 0, 1 or 2");
+    if (p->precise != 0 && p->precise != 1)
+        return fail(JL_ERR_INVALID_ARGUMENT, "precise must be 0 or 1");
     return JL_OK;
 }
+
+// precise flag of an optional params pointer (workspace queries)
+static int precise_of(const jl_params* p) { return p && p->precise ? 1 : 0; }
 
 // The kernels move tensors in 16-byte vectors.
 static bool al16(const void* p) { return ((uintptr_t)p & 15) == 0; }
@@ -254,7 +266,8 @@ jl_status jl_rope_apply(void* out, const void* x, const int32_t* positions, int6
 }
 
 jl_status jl_bifocal_prefill_workspace(int64_t T, int32_t n_seqs, int32_t Hq, int32_t Hkv,
-                                       int32_t d, jl_dtype dtype, size_t* bytes) {
+                                       int32_t d, jl_dtype dtype, const jl_params* params,
+                                       size_t* bytes) {
     if (!bytes) return fail(JL_ERR_INVALID_ARGUMENT, "bytes is NULL");
     if (T < 1 || n_seqs < 1) return fail(JL_ERR_INVALID_ARGUMENT, "T and n_seqs must be >= 1");
     jl_status st = check_heads(Hq, Hkv);
@@ -263,7 +276,11 @@ jl_status jl_bifocal_prefill_workspace(int64_t T, int32_t n_seqs, int32_t Hq, in
     if (st != JL_OK) return st;
     if (T + (int64_t)n_seqs * kBN >= 2147483647LL)
         return fail(JL_ERR_UNSUPPORTED, "T + 64 * n_seqs must stay below 2^31");
-    *bytes = prefill_layout(T, n_seqs, Hkv, d, dtype).total;
+    if (params) {
+        const jl_status pst = check_params(params);
+        if (pst != JL_OK) return pst;
+    }
+    *bytes = prefill_layout(T, n_seqs, Hkv, d, dtype, precise_of(params)).total;
     g_err.clear();
     return JL_OK;
 }
@@ -300,7 +317,8 @@ jl_status jl_bifocal_prefill(void* o, float* lse, const void* q, const void* k, 
     if ((uintptr_t)workspace & 255) return fail(JL_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
     st = check_aligned({o, q, k, v, k_rot_out});
     if (st != JL_OK) return st;
-    const PrefillLayout lay = prefill_layout(T, n_seqs, Hkv, d, dtype);
+    const int precise = dtype == JL_DTYPE_BF16 ? params->precise : 0;
+    const PrefillLayout lay = prefill_layout(T, n_seqs, Hkv, d, dtype, precise);
     if (workspace_bytes < lay.total)
         return fail(JL_ERR_WORKSPACE_TOO_SMALL,
                     "workspace needs " + std::to_string(lay.total) + " bytes");
@@ -313,12 +331,13 @@ jl_status jl_bifocal_prefill(void* o, float* lse, const void* q, const void* k, 
     a.softmax_scale = params->softmax_scale;
     a.tab = make_rope_freq(params->rope_base, d);
     a.w_pretrained = params->w_pretrained;
+    a.precise = precise;
     if (params->bifocal == 2 && dtype != JL_DTYPE_BF16)
         return fail(JL_ERR_UNSUPPORTED, "continuous interpolation (bifocal = 2) is bf16 only");
 
     hipStream_t s = (hipStream_t)stream;
     hipError_t e = launch_plan((int32_t*)((char*)workspace + lay.plan), cu_seqlens, n_seqs, T,
-                               max_seqlen, params->w_pretrained, s);
+                               max_seqlen, params->w_pretrained, precise, s);
     if (e != hipSuccess) return hip_fail(e, "plan launch");
     e = launch_kv_prepass(a, dtype, s);
     if (e != hipSuccess) return hip_fail(e, "key/value pre-pass launch");
@@ -346,7 +365,8 @@ static ThreeCallLayout three_call_layout(const PrefillLayout& pl, int64_t T, int
 }
 
 jl_status jl_bifocal_prefill_three_call_workspace(int64_t T, int32_t n_seqs, int32_t Hq, int32_t Hkv,
-                                                  int32_t d, jl_dtype dtype, size_t* bytes) {
+                                                  int32_t d, jl_dtype dtype, const jl_params* params,
+                                                  size_t* bytes) {
     if (!bytes) return fail(JL_ERR_INVALID_ARGUMENT, "bytes is NULL");
     if (T < 1 || n_seqs < 1) return fail(JL_ERR_INVALID_ARGUMENT, "T and n_seqs must be >= 1");
     jl_status st = check_heads(Hq, Hkv);
@@ -354,7 +374,12 @@ jl_status jl_bifocal_prefill_three_call_workspace(int64_t T, int32_t n_seqs, int
     st = check_dtype_d(dtype, d);
     if (st != JL_OK) return st;
     if (dtype != JL_DTYPE_BF16) return fail(JL_ERR_UNSUPPORTED, "the unfused form is bf16 only");
-    *bytes = three_call_layout(prefill_layout(T, n_seqs, Hkv, d, dtype), T, Hq, d).total;
+    if (params) {
+        const jl_status pst = check_params(params);
+        if (pst != JL_OK) return pst;
+    }
+    *bytes = three_call_layout(prefill_layout(T, n_seqs, Hkv, d, dtype, precise_of(params)), T, Hq,
+                               d).total;
     g_err.clear();
     return JL_OK;
 }
@@ -394,7 +419,7 @@ jl_status jl_bifocal_prefill_three_call(void* o, float* lse, const void* q, cons
     if ((uintptr_t)workspace & 255) return fail(JL_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
     st = check_aligned({o, q, k, v});
     if (st != JL_OK) return st;
-    const PrefillLayout lay = prefill_layout(T, n_seqs, Hkv, d, dtype);
+    const PrefillLayout lay = prefill_layout(T, n_seqs, Hkv, d, dtype, params->precise);
     const ThreeCallLayout tl = three_call_layout(lay, T, Hq, d);
     if (workspace_bytes < tl.total)
         return fail(JL_ERR_WORKSPACE_TOO_SMALL,
@@ -407,10 +432,11 @@ jl_status jl_bifocal_prefill_three_call(void* o, float* lse, const void* q, cons
     a.w_local = params->w_local; a.bifocal = 1;
     a.softmax_scale = params->softmax_scale;
     a.tab = make_rope_freq(params->rope_base, d);
+    a.precise = params->precise;
 
     hipStream_t s = (hipStream_t)stream;
     hipError_t e = launch_plan((int32_t*)(ws + lay.plan), cu_seqlens, n_seqs, T, max_seqlen,
-                               params->w_pretrained, s);
+                               params->w_pretrained, params->precise, s);
     if (e != hipSuccess) return hip_fail(e, "plan launch");
     e = launch_kv_prepass(a, dtype, s);
     if (e != hipSuccess) return hip_fail(e, "key/value pre-pass launch");
@@ -524,6 +550,11 @@ static jl_status decode_impl(const DecodeCall& c, const jl_params* params, jl_dt
         a.page_shift = shift; a.bt_stride = c.bt_stride; a.n_pages = c.n_pages;
     }
     a.fp8 = c.fp8; a.k_scale = c.k_scale; a.v_scale = c.v_scale;
+    // split-precision remote keys: bf16 caches (fp32 caches are scored in
+    // split bf16 anyway; an fp8 cache's own rounding is far coarser)
+    if (params->precise && c.fp8)
+        return fail(JL_ERR_UNSUPPORTED, "split precision (precise = 1) is not offered for fp8 caches");
+    a.precise = dtype == JL_DTYPE_BF16 ? params->precise : 0;
     hipStream_t s = (hipStream_t)stream;
     hipError_t e = launch_decode(a, dtype, s);
     if (e != hipSuccess) return hip_fail(e, "decode launch");
@@ -627,10 +658,11 @@ struct ChunkLayout {
     size_t part_o, part_ml, total;
 };
 static ChunkLayout chunk_layout(int64_t Tq, int32_t batch, int32_t max_seqlen_k, int32_t Hq,
-                                int32_t Hkv, int32_t d) {
+                                int32_t Hkv, int32_t d, int precise) {
     ChunkLayout L{};
-    L.pl = prefill_layout((int64_t)batch * max_seqlen_k, batch, Hkv, d, JL_DTYPE_BF16);
-    L.kmax = chunk_split_bound((int64_t)Hq * ((Tq + kBM - 1) / kBM));
+    L.pl = prefill_layout((int64_t)batch * max_seqlen_k, batch, Hkv, d, JL_DTYPE_BF16, precise);
+    // split-precision calls run every row in one kernel without key shares
+    L.kmax = precise ? 1 : chunk_split_bound((int64_t)Hq * ((Tq + kBM - 1) / kBM));
     size_t off = align256(L.pl.total);
     if (L.kmax > 1) {
         L.part_o = off;
@@ -644,7 +676,7 @@ static ChunkLayout chunk_layout(int64_t Tq, int32_t batch, int32_t max_seqlen_k,
 
 jl_status jl_bifocal_prefill_chunk_workspace(int64_t Tq, int32_t batch, int32_t max_seqlen_k,
                                              int32_t Hq, int32_t Hkv, int32_t d, jl_dtype dtype,
-                                             size_t* bytes) {
+                                             const jl_params* params, size_t* bytes) {
     if (!bytes) return fail(JL_ERR_INVALID_ARGUMENT, "bytes is NULL");
     if (Tq < 1 || Tq >= 2147483647LL) return fail(JL_ERR_INVALID_ARGUMENT, "Tq must be in [1, 2^31)");
     jl_status st = chunk_sizes_ok(batch, max_seqlen_k);
@@ -654,7 +686,11 @@ jl_status jl_bifocal_prefill_chunk_workspace(int64_t Tq, int32_t batch, int32_t 
     st = check_dtype_d(dtype, d);
     if (st != JL_OK) return st;
     if (dtype != JL_DTYPE_BF16) return fail(JL_ERR_UNSUPPORTED, "chunked prefill is bf16 only");
-    *bytes = chunk_layout(Tq, batch, max_seqlen_k, Hq, Hkv, d).total;
+    if (params) {
+        const jl_status pst = check_params(params);
+        if (pst != JL_OK) return pst;
+    }
+    *bytes = chunk_layout(Tq, batch, max_seqlen_k, Hq, Hkv, d, precise_of(params)).total;
     g_err.clear();
     return JL_OK;
 }
@@ -688,7 +724,8 @@ static jl_status chunk_call(PrefillArgs& a, const int32_t* cu_seqlens_q,
     if ((uintptr_t)workspace & 255) return fail(JL_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
     st = check_aligned({a.o, a.q, a.k, a.v});
     if (st != JL_OK) return st;
-    const ChunkLayout cl = chunk_layout(a.T, a.n_seqs, a.max_seqlen_k, a.Hq, a.Hkv, a.d);
+    const ChunkLayout cl = chunk_layout(a.T, a.n_seqs, a.max_seqlen_k, a.Hq, a.Hkv, a.d,
+                                        params->precise);
     const PrefillLayout& lay = cl.pl;
     if (workspace_bytes < cl.total)
         return fail(JL_ERR_WORKSPACE_TOO_SMALL,
@@ -712,10 +749,11 @@ static jl_status chunk_call(PrefillArgs& a, const int32_t* cu_seqlens_q,
     a.softmax_scale = params->softmax_scale;
     a.tab = make_rope_freq(params->rope_base, a.d);
     a.w_pretrained = params->w_pretrained;
+    a.precise = params->precise;
     hipStream_t s = (hipStream_t)stream;
     hipError_t e = launch_plan_chunk((int32_t*)((char*)workspace + lay.plan), cu_seqlens_q,
                                      seqlens_k, a.n_seqs, a.T, a.max_seqlen, a.max_seqlen_k,
-                                     params->w_pretrained, s);
+                                     params->w_pretrained, params->precise, s);
     if (e != hipSuccess) return hip_fail(e, "plan launch");
     e = launch_kv_prepass(a, dtype, s);
     if (e != hipSuccess) return hip_fail(e, "key/value pre-pass launch");

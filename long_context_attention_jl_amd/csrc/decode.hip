@@ -165,16 +165,13 @@ void decode_split_kernel(DecodeArgs a) {
     const int32_t kbeg = z0 + split * a.lay.chunk;
     const int32_t kend = min(kbeg + a.lay.chunk, L);
 
-    float* pm = (float*)((char*)a.ws + a.lay.part_ml);
+    float4* pm = (float4*)((char*)a.ws + a.lay.part_ml);
     float* po = (float*)((char*)a.ws + a.lay.part_o);
     const int64_t pbase = ((int64_t)b * a.lay.n_splits + split) * a.Hq + (int64_t)kvh * grp;
 
     if (kbeg >= kend) {  // empty chunk: neutral partial
         if (head_ok) {
-            if (c == 0 && n < grp) {
-                pm[2 * (pbase + n)] = -INFINITY;
-                pm[2 * (pbase + n) + 1] = 0.0f;
-            }
+            if (c == 0 && n < grp) pm[pbase + n] = make_float4(-INFINITY, 0.0f, 0.0f, 0.0f);
             for (int x = lane; x < grp * D; x += 64) po[pbase * D + x] = 0.0f;
         }
         return;
@@ -437,16 +434,192 @@ void decode_split_kernel(DecodeArgs a) {
     // ---- partial (m, l, unnormalised O) of this chunk ----
     float l_tot = l_part + __shfl_xor(l_part, 16);
     l_tot += __shfl_xor(l_tot, 32);
-    if (c == 0 && n < grp) {
-        pm[2 * (pbase + n)] = m_run;
-        pm[2 * (pbase + n) + 1] = l_tot;
-    }
+    if (c == 0 && n < grp) pm[pbase + n] = make_float4(m_run, l_tot, l_tot, 0.0f);
 #pragma unroll
     for (int h = 0; h < GQ; ++h)
         if (h < grp) {
 #pragma unroll
             for (int x = 0; x < DPL; ++x) po[(pbase + h) * D + DPL * lane + x] = O[h][x];
         }
+}
+
+// ---------------------------------------------------------------------------
+// Merging split partials inside the split kernel ([TW] §四's LogSumExp
+// combination of partial attentions).  A partial of query head h holds
+// (m, l_o, l_lse) and the unnormalised O, all relative to 2^m (log2 units):
+// l_o sums the probabilities exactly as rounded for the P V product, so
+// O / l_o is a consistent weighted mean; l_lse sums them before rounding and
+// gives the LSE.  Merging n partials: M = max m_c, w_c = 2^(m_c - M),
+// O = sum w_c O_c, l = sum w_c l_c.
+
+// Merges partials c = 0..n-1 of the nh query heads starting at `ml` / `po`
+// (partial c of head h at ml[c * Hq + h], its O at po[(c * Hq + h) * D]),
+// kDecodeBin partials at a time with a running max.  If `final`, writes
+// o = O / l_o (TOUT) and lse = (M + log2 l_lse) ln 2 for those heads at
+// `o` / `lse`; otherwise the merged partial at out_ml[h], out_o[h * D].
+// Called by a whole workgroup; `lds` holds at least (kDecodeBin + 5) * nh
+// floats.
+template <int D>
+__device__ void merge_partials(const float4* __restrict__ ml, const float* __restrict__ po, int Hq,
+                               int n, int nh, bool final, float4* out_ml, float* out_o, void* o,
+                               bool o_f32, float* lse, float* lds) {
+    constexpr int NB = kDecodeBin;
+    constexpr int Q = D / 4;  // 4-wide d slices per head
+    float* sw = lds;                 // [NB][nh] weights within the group
+    float* sM = lds + NB * nh;       // [nh] running max
+    float* sLo = sM + nh;            // [nh] running l_o, l_lse
+    float* sLl = sLo + nh;
+    float* sA = sLl + nh;            // [nh] rescale of the running sums
+    float* sB = sA + nh;             // [nh] scale of the group's sums
+    const int tid = threadIdx.x, nt = blockDim.x;
+    const int items = nh * Q;
+    for (int base = 0; base < items; base += 2 * nt) {
+        float4 acc[2] = {make_float4(0.0f, 0.0f, 0.0f, 0.0f), make_float4(0.0f, 0.0f, 0.0f, 0.0f)};
+        for (int g0 = 0; g0 < n; g0 += NB) {
+            const int ng = min(NB, n - g0);
+            // the group's O loads go out before its weights are formed, so
+            // the two round trips overlap
+            float4 ov[2][NB];
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int it = min(base + tid + u * nt, items - 1);
+                const int h = it / Q, x = 4 * (it % Q);
+#pragma unroll
+                for (int c = 0; c < NB; ++c) {
+                    const int cc = g0 + min(c, ng - 1);
+                    ov[u][c] = *reinterpret_cast<const float4*>(po + ((int64_t)cc * Hq + h) * D + x);
+                }
+            }
+            // weights: 16 consecutive lanes per head, lane c holds partial g0 + c
+            for (int t = tid; t < nh * NB; t += nt) {
+                const int h = t / NB, c = t % NB;
+                float4 v = make_float4(-INFINITY, 0.0f, 0.0f, 0.0f);
+                if (c < ng) v = ml[(int64_t)(g0 + c) * Hq + h];
+                float Mg = v.x;
+#pragma unroll
+                for (int sh = 1; sh < NB; sh <<= 1) Mg = fmaxf(Mg, __shfl_xor(Mg, sh));
+                const float w = (v.x == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(v.x - Mg);
+                float lo = w * v.y, ll = w * v.z;
+#pragma unroll
+                for (int sh = 1; sh < NB; sh <<= 1) {
+                    lo += __shfl_xor(lo, sh);
+                    ll += __shfl_xor(ll, sh);
+                }
+                sw[c * nh + h] = w;
+                if (c == 0) {
+                    const float Mo = g0 == 0 ? -INFINITY : sM[h];
+                    const float Mn = fmaxf(Mo, Mg);
+                    const float ao = Mo == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(Mo - Mn);
+                    const float bg = Mg == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(Mg - Mn);
+                    sM[h] = Mn;
+                    sLo[h] = (g0 == 0 ? 0.0f : sLo[h]) * ao + lo * bg;
+                    sLl[h] = (g0 == 0 ? 0.0f : sLl[h]) * ao + ll * bg;
+                    sA[h] = ao;
+                    sB[h] = bg;
+                }
+            }
+            __syncthreads();
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int it = min(base + tid + u * nt, items - 1);
+                const int h = it / Q;
+                float4 gs = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+#pragma unroll
+                for (int c = 0; c < NB; ++c) {
+                    const float w = c < ng ? sw[c * nh + h] : 0.0f;
+                    gs.x += w * ov[u][c].x;
+                    gs.y += w * ov[u][c].y;
+                    gs.z += w * ov[u][c].z;
+                    gs.w += w * ov[u][c].w;
+                }
+                const float ao = sA[h], bg = sB[h];
+                acc[u].x = acc[u].x * ao + gs.x * bg;
+                acc[u].y = acc[u].y * ao + gs.y * bg;
+                acc[u].z = acc[u].z * ao + gs.z * bg;
+                acc[u].w = acc[u].w * ao + gs.w * bg;
+            }
+            __syncthreads();
+        }
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int it = base + tid + u * nt;
+            if (it >= items) continue;
+            const int h = it / Q, x = 4 * (it % Q);
+            if (!final) {
+                *reinterpret_cast<float4*>(out_o + (int64_t)h * D + x) = acc[u];
+                if (x == 0) out_ml[h] = make_float4(sM[h], sLo[h], sLl[h], 0.0f);
+                continue;
+            }
+            const float lo = sLo[h];
+            const float inv = lo > 0.0f ? 1.0f / lo : 0.0f;
+            const float4 r = make_float4(acc[u].x * inv, acc[u].y * inv, acc[u].z * inv,
+                                         acc[u].w * inv);
+            if (o_f32) {
+                *reinterpret_cast<float4*>((float*)o + (int64_t)h * D + x) = r;
+            } else {
+                const bf16x4 rb = {(bf16)r.x, (bf16)r.y, (bf16)r.z, (bf16)r.w};
+                *reinterpret_cast<bf16x4*>((bf16*)o + (int64_t)h * D + x) = rb;
+            }
+            if (x == 0) lse[h] = sLl[h] > 0.0f ? (sM[h] + log2f(sLl[h])) * kLn2 : -INFINITY;
+        }
+        __syncthreads();  // the next round rewrites the sums read above
+    }
+}
+
+// Called by every thread of a split workgroup once its partials are written:
+// draws this chunk's ticket of its bin; the workgroup holding the bin's last
+// ticket merges the bin (and, with one bin, writes the output), then draws
+// the (sequence, group) ticket; the holder of its last ticket merges the
+// bins.  A ticket holder that sees the final count resets the counter, so
+// every counter is zero again when the kernel ends.  Release and acquire
+// fences at agent scope order the partials' stores before the counter
+// update and the merger's loads after it (the compute units of different
+// XCDs do not share an L2).
+template <int D>
+__device__ void merge_by_tickets(const DecodeArgs& a, int b, int g, int split, int h0, int nh,
+                                 float* lds) {
+    __shared__ int s_last;
+    const DecodeLayout& L = a.lay;
+    uint32_t* tk = (uint32_t*)((char*)a.ws + L.tickets) + ((int64_t)b * L.groups + g) * (L.nbins + 1);
+    const int bin = split / kDecodeBin;
+    const int nin = min(kDecodeBin, L.n_splits - bin * kDecodeBin);
+    auto draw = [&](uint32_t* ctr, int count) __attribute__((always_inline)) -> bool {
+        __threadfence();
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            const uint32_t old = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED,
+                                                        __HIP_MEMORY_SCOPE_AGENT);
+            const int last = old == (uint32_t)(count - 1);
+            if (last) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            s_last = last;
+        }
+        __syncthreads();
+        const bool last = s_last != 0;
+        if (last) __threadfence();
+        return last;
+    };
+    if (!draw(tk + bin, nin)) return;
+    const float4* pm = (const float4*)((const char*)a.ws + L.part_ml);
+    const float* po = (const float*)((const char*)a.ws + L.part_o);
+    const size_t osz = a.o_f32 ? sizeof(float) : sizeof(bf16);
+    void* o = (char*)a.o + ((int64_t)b * a.Hq * D + (int64_t)h0 * D) * osz;
+    float* lse = a.lse + (int64_t)b * a.Hq + h0;
+    const int64_t c0 = (int64_t)b * L.n_splits + (int64_t)bin * kDecodeBin;
+    if (L.nbins == 1) {
+        merge_partials<D>(pm + c0 * a.Hq + h0, po + (c0 * a.Hq + h0) * D, a.Hq, nin, nh, true,
+                          nullptr, nullptr, o, a.o_f32, lse, lds);
+        return;
+    }
+    float4* pm2 = (float4*)((char*)a.ws + L.part2_ml);
+    float* po2 = (float*)((char*)a.ws + L.part2_o);
+    const int64_t c2 = (int64_t)b * L.nbins + bin;
+    merge_partials<D>(pm + c0 * a.Hq + h0, po + (c0 * a.Hq + h0) * D, a.Hq, nin, nh, false,
+                      pm2 + c2 * a.Hq + h0, po2 + (c2 * a.Hq + h0) * D, nullptr, false, nullptr,
+                      lds);
+    if (!draw(tk + L.nbins, L.nbins)) return;
+    const int64_t b0 = (int64_t)b * L.nbins;
+    merge_partials<D>(pm2 + b0 * a.Hq + h0, po2 + (b0 * a.Hq + h0) * D, a.Hq, L.nbins, nh, true,
+                      nullptr, nullptr, o, a.o_f32, lse, lds);
 }
 
 // OCP E4M3 codes (4 per 32-bit word, little-endian) widened exactly; the
@@ -506,7 +679,10 @@ __device__ __forceinline__ f32x4 mfma16k16h(s16x4 a, s16x4 b, f32x4 c) {
 // widen exactly to fp16 (keys and the V tile in LDS); P is fp16 too.  The
 // key scale multiplies the finished scores and the value scale the partial
 // output.
-template <int D, bool BIF, int GQ, bool PAGED, bool FP8>
+// PREC (split precision, bf16 caches): remote keys are turned in fp32 against
+// an fp32 table and split into fp16 hi + lo operands (two products per
+// k-step), so a dominant remote key's score carries no fp16 rounding.
+template <int D, bool BIF, int GQ, bool PAGED, bool FP8, bool PREC = false>
 __global__ __launch_bounds__(512) void decode_split_bf16_kernel(DecodeArgs a) {
     using TC = typename std::conditional<FP8, uint8_t, bf16>::type;  // cache element
     using KRAW = typename std::conditional<FP8, u32x2, bf16x8>::type;  // 8 key elements
@@ -528,7 +704,10 @@ __global__ __launch_bounds__(512) void decode_split_bf16_kernel(DecodeArgs a) {
     constexpr int NDB = D / 16;          // 16-wide d blocks of O
     constexpr int TSTRH = D + 8;         // LDS row stride of the angle table (halves)
     // R(-u theta_t) in fp16: row u holds the HALF cosines, then the HALF sines
-    __shared__ __align__(16) f16 tabh[BIF ? kStageB * TSTRH : 8];
+    __shared__ __align__(16) f16 tabh[(BIF && !PREC) ? kStageB * TSTRH : 8];
+    // the same table in fp32 for split-precision remote keys (row stride D + 4)
+    constexpr int TSTRF = D + 4;
+    __shared__ __align__(16) float tabf[(BIF && PREC) ? kStageB * TSTRF : 4];
     // query angles: row st < kDecodeMaxStagesB holds R(f(p) - f(jb) + jb) of
     // stage st of this chunk (remote stages), the last row R(p)
     __shared__ float2 qtab[(kDecodeMaxStagesB + 1) * HALF];
@@ -572,20 +751,19 @@ __global__ __launch_bounds__(512) void decode_split_bf16_kernel(DecodeArgs a) {
     const int32_t kbeg = z0 + split * a.lay.chunk;
     const int32_t kend = min(kbeg + a.lay.chunk, L);
 
-    float* pm = (float*)((char*)a.ws + a.lay.part_ml);
+    float4* pm = (float4*)((char*)a.ws + a.lay.part_ml);
     float* po = (float*)((char*)a.ws + a.lay.part_o);
     const int64_t pbase = ((int64_t)b * a.lay.n_splits + split) * a.Hq + (int64_t)kvh * grp;
+    // query heads of this workgroup (its kv heads' groups)
+    const int h0 = blockIdx.y * nw * grp;
+    const int nh = min(nw, a.Hkv - (int)blockIdx.y * nw) * grp;
 
-    if (kbeg >= kend) {  // empty chunk: neutral partial
+    if (kbeg >= kend) {  // empty chunk: neutral partial, then its ticket
         if (head_ok) {
-            if (c == 0 && n < grp) {
-                pm[2 * (pbase + n)] = -INFINITY;
-                pm[2 * (pbase + n) + 1] = 0.0f;
-            }
+            if (c == 0 && n < grp) pm[pbase + n] = make_float4(-INFINITY, 0.0f, 0.0f, 0.0f);
             for (int x = lane; x < grp * D; x += 64) po[pbase * D + x] = 0.0f;
         }
-        return;
-    }
+    } else {
 
     // every load below is unconditional (branch-free memory stream, exact
     // waits): indices are clamped to valid rows, masked keys weigh 0
@@ -702,13 +880,18 @@ __global__ __launch_bounds__(512) void decode_split_bf16_kernel(DecodeArgs a) {
                     rope_cs_rev(-(double)(x / HALF) * (1.0 - rsc) * rv, cs, sn);
                 else
                     rope_cs_hw(-(int64_t)(x / HALF), rv, cs, sn);
-                tabh[(x / HALF) * TSTRH + x % HALF] = (f16)cs;
-                tabh[(x / HALF) * TSTRH + HALF + x % HALF] = (f16)sn;
+                if constexpr (PREC) {
+                    tabf[(x / HALF) * TSTRF + x % HALF] = cs;
+                    tabf[(x / HALF) * TSTRF + HALF + x % HALF] = sn;
+                } else {
+                    tabh[(x / HALF) * TSTRH + x % HALF] = (f16)cs;
+                    tabh[(x / HALF) * TSTRH + HALF + x % HALF] = (f16)sn;
+                }
             }
         }
         __syncthreads();
     }
-    if (!head_ok) return;
+    if (head_ok) {
     load_k(kbeg + kTile, kB);
     load_vr(kbeg + kTile, vB);
 
@@ -768,6 +951,40 @@ __global__ __launch_bounds__(512) void decode_split_bf16_kernel(DecodeArgs a) {
     // key's rounding is its own and averages out in the softmax).
     auto scores_remote = [&](const KRAW* kcur, int32_t u) __attribute__((always_inline)) -> f32x4 {
         f32x4 acc = {};
+        if constexpr (PREC) {
+            const float* tf = tabf + u * TSTRF + 8 * c;
+#pragma unroll
+            for (int s = 0; s < NH; ++s) {
+                const f16x8 k0 = kop(kcur[s]);
+                const f16x8 k1 = kop(kcur[s + NH]);
+                const f32x4 ca = *reinterpret_cast<const f32x4*>(tf + 32 * s);
+                const f32x4 cb = *reinterpret_cast<const f32x4*>(tf + 32 * s + 4);
+                const f32x4 sa = *reinterpret_cast<const f32x4*>(tf + HALF + 32 * s);
+                const f32x4 sb = *reinterpret_cast<const f32x4*>(tf + HALF + 32 * s + 4);
+                f16x8 h0, l0, h1, l1;
+#pragma unroll
+                for (int x = 0; x < 8; ++x) {
+                    const float cs = x < 4 ? ca[x] : cb[x - 4];
+                    const float sn = x < 4 ? sa[x] : sb[x - 4];
+                    const float a0 = (float)k0[x], a1 = (float)k1[x];
+                    const float y0 = a0 * cs - a1 * sn;
+                    const float y1 = a1 * cs + a0 * sn;
+                    h0[x] = (f16)y0;
+                    l0[x] = (f16)(y0 - (float)h0[x]);
+                    h1[x] = (f16)y1;
+                    l1[x] = (f16)(y1 - (float)h1[x]);
+                }
+                acc = mfma16(h0, Q[s], acc);
+                acc = mfma16(l0, Q[s], acc);
+                acc = mfma16(h1, Q[s + NH], acc);
+                acc = mfma16(l1, Q[s + NH], acc);
+                if constexpr (!PACK) {
+                    acc = mfma16(h0, Qlo[s], acc);
+                    acc = mfma16(h1, Qlo[s + NH], acc);
+                }
+            }
+            return finish(acc);
+        }
         const f16* th = tabh + u * TSTRH + 8 * c;
 #pragma unroll
         for (int s = 0; s < NH; ++s) {
@@ -790,7 +1007,10 @@ __global__ __launch_bounds__(512) void decode_split_bf16_kernel(DecodeArgs a) {
     // running softmax state per query column (log2 domain; a finite floor so
     // masked keys give exp2(-inf) = 0, never NaN) and O^T blocks: lane (n, c)
     // of block bd holds O[query 4c + i][d = 16 bd + n]
-    float m_run = -1e30f, l_part = 0.0f;
+    // l_part sums the probabilities as rounded for the P V product (it
+    // normalises O), l_exact sums them before rounding (it gives the LSE: a
+    // dominant probability's rounding would otherwise enter the LSE whole)
+    float m_run = -1e30f, l_part = 0.0f, l_exact = 0.0f;
     f32x4 O[NDB];
 #pragma unroll
     for (int bd = 0; bd < NDB; ++bd) O[bd] = f32x4{};
@@ -817,14 +1037,17 @@ __global__ __launch_bounds__(512) void decode_split_bf16_kernel(DecodeArgs a) {
             m_run = mx;
         }
         s16x4 pa;
-        float ps = 0.0f;
+        float ps = 0.0f, pe = 0.0f;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const PT pb = (PT)__builtin_amdgcn_exp2f(sc[i] - m_run);
+            const float pf = __builtin_amdgcn_exp2f(sc[i] - m_run);
+            const PT pb = (PT)pf;
             ps += (float)pb;
+            pe += pf;
             pa[i] = __builtin_bit_cast(short, pb);
         }
         l_part = l_part * alpha + ps;
+        l_exact = l_exact * alpha + pe;
         if (__any(raise)) {
             // row 4c + i of O belongs to query column 4c + i
 #pragma unroll
@@ -890,13 +1113,12 @@ __global__ __launch_bounds__(512) void decode_split_bf16_kernel(DecodeArgs a) {
         step(js + 2 * kTile, kC, vC, kB, vB);
     }
 
-    // ---- partial (m, l, unnormalised O) of this chunk ----
+    // ---- partial (m, l_o, l_lse, unnormalised O) of this chunk ----
     float l_tot = l_part + __shfl_xor(l_part, 16);
     l_tot += __shfl_xor(l_tot, 32);
-    if (c == 0 && n < grp) {
-        pm[2 * (pbase + n)] = m_run;
-        pm[2 * (pbase + n) + 1] = l_tot;
-    }
+    float l_ex = l_exact + __shfl_xor(l_exact, 16);
+    l_ex += __shfl_xor(l_ex, 32);
+    if (c == 0 && n < grp) pm[pbase + n] = make_float4(m_run, l_tot, l_ex, 0.0f);
     const float vscale = FP8 && a.v_scale ? a.v_scale[kvh_c] : 1.0f;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -905,6 +1127,11 @@ __global__ __launch_bounds__(512) void decode_split_bf16_kernel(DecodeArgs a) {
             for (int bd = 0; bd < NDB; ++bd)
                 po[(pbase + 4 * c + i) * D + 16 * bd + n] = FP8 ? O[bd][i] * vscale : O[bd][i];
         }
+    }  // head_ok
+    }  // non-empty chunk
+
+    // ---- the last workgroup of the bin (and then of the sequence) merges ----
+    merge_by_tickets<D>(a, b, blockIdx.y, split, h0, nh, (float*)vs);
 }
 
 // Merge of the chunk partials: o = sum 2^(m_c - M) O_c / sum 2^(m_c - M) l_c,
@@ -946,7 +1173,8 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
         for (int k = 0; k < NB; ++k) {
             const int sp = min(s0 + NG * k, ns - 1);
             const int64_t idx = base + (int64_t)sp * a.Hq;
-            ml[k] = *(const float2*)(pm + 2 * idx);
+            const float4 v = *(const float4*)(pm + 4 * idx);
+            ml[k] = make_float2(v.x, v.y);
             ov[k] = *(const f32x4*)(po + idx * a.d + x0);
         }
 #pragma unroll
@@ -987,11 +1215,20 @@ static hipError_t launch_decode_g(const DecodeArgs& a, hipStream_t s) {
     const int wmax = sizeof(TIN) == 2 ? kWavesB : kDecodeWaves;
     const int nw = a.Hkv < wmax ? a.Hkv : wmax;
     const dim3 grid(a.lay.n_splits, (a.Hkv + nw - 1) / nw, a.B);
-    LaunchScope scope(a.bifocal ? "decode_split" : "decode_split_plain", s);
+    LaunchScope scope(a.bifocal ? (a.precise ? "decode_split_precise" : "decode_split")
+                                : "decode_split_plain", s);
     if constexpr (sizeof(TIN) == 2) {
-        // (bifocal, paged, fp8) -> one instantiation each
+        // (bifocal, paged, fp8) -> one instantiation each; split precision
+        // for bifocal bf16 caches (plain decode has no remote keys)
         const int sel = (a.bifocal ? 4 : 0) | (a.block_table ? 2 : 0) | (a.fp8 ? 1 : 0);
         const dim3 blk(64 * nw);
+        if (a.bifocal && a.precise && !a.fp8) {
+            if (a.block_table)
+                hipLaunchKernelGGL((decode_split_bf16_kernel<D, true, GQ, true, false, true>), grid, blk, 0, s, a);
+            else
+                hipLaunchKernelGGL((decode_split_bf16_kernel<D, true, GQ, false, false, true>), grid, blk, 0, s, a);
+            return hipGetLastError();
+        }
         switch (sel) {
             case 0: hipLaunchKernelGGL((decode_split_bf16_kernel<D, false, GQ, false, false>), grid, blk, 0, s, a); break;
             case 1: hipLaunchKernelGGL((decode_split_bf16_kernel<D, false, GQ, false, true>), grid, blk, 0, s, a); break;
@@ -1018,7 +1255,7 @@ static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t s) {
     if (grp <= 4) err = launch_decode_g<D, TIN, 4>(a, s);
     else if (grp <= 8) err = launch_decode_g<D, TIN, 8>(a, s);
     else err = launch_decode_g<D, TIN, 16>(a, s);
-    if (err != hipSuccess) return err;
+    if (err != hipSuccess || sizeof(TIN) == 2) return err;  // bf16: merged in the split kernel
     LaunchScope scope("decode_merge", s);
     hipLaunchKernelGGL(decode_merge_kernel<TIN>, dim3(a.Hq, a.B, D / 16), dim3(256), 0, s, a);
     return hipGetLastError();

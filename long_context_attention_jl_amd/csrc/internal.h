@@ -26,7 +26,10 @@ struct PrefillLayout {
     size_t ks32, kr32;                      // offsets (f32 path)
     size_t total;
 };
-PrefillLayout prefill_layout(int64_t T, int32_t n_seqs, int32_t Hkv, int32_t d, int dtype);
+// precise: the split-precision ("lo") key tiles cover every key, not only the
+// first kPreciseRows of each sequence
+PrefillLayout prefill_layout(int64_t T, int32_t n_seqs, int32_t Hkv, int32_t d, int dtype,
+                             int precise);
 
 // bf16 decode: positions per stage and the most stages one chunk may hold
 // (the kernel keeps one query-angle row per stage in LDS)
@@ -36,10 +39,26 @@ constexpr int kDecodeMaxStagesB = 32;
 // most this many pages
 constexpr int kDecodeMaxPages = (kDecodeMaxStagesB * kDecodeStageB + kDecodeStageB - 1) / 16 + 2;
 
+// Decode workspace.  Each (sequence, kv-head group) owns n_splits key chunks,
+// grouped in bins of up to kDecodeBin consecutive chunks.  The last workgroup
+// of a bin to finish merges the bin's partials into one level-2 partial; the
+// last bin to finish merges those into the output.  "Last" is decided with
+// counters (tickets) at the start of the workspace: one per bin plus one per
+// (sequence, group), zero before a call and reset to zero by the workgroup
+// that draws the final ticket.
+constexpr int kDecodeBin = 16;
 struct DecodeLayout {
     int32_t n_splits;
     int32_t chunk;
-    size_t part_o, part_ml, total;
+    int32_t groups;  // kv-head groups (workgroups along grid y)
+    int32_t nbins;   // bins of kDecodeBin chunks per (sequence, group)
+    size_t tickets;  // uint32 [B][groups][nbins + 1] (offset 0)
+    size_t ticket_bytes;
+    size_t part_ml;  // float4 (m, l_o, l_lse, 0) [B][n_splits][Hq]
+    size_t part_o;   // float [B][n_splits][Hq][d]: unnormalised O
+    size_t part2_ml; // level-2 partials [B][nbins][Hq] (nbins > 1)
+    size_t part2_o;  // [B][nbins][Hq][d]
+    size_t total;
 };
 DecodeLayout decode_layout(int32_t batch, int32_t max_seqlen_k, int32_t Hq, int32_t Hkv, int32_t d,
                            int dtype);
@@ -53,7 +72,7 @@ hipError_t launch_rope_apply(void* out, const void* x, const int32_t* pos, int64
                              hipStream_t s);
 
 hipError_t launch_plan(int32_t* plan, const int32_t* cu, int32_t n_seqs, int64_t T,
-                       int32_t max_seqlen, int32_t w_pretrained, hipStream_t s);
+                       int32_t max_seqlen, int32_t w_pretrained, int32_t precise, hipStream_t s);
 
 struct PrefillArgs {
     const void* q;
@@ -87,13 +106,16 @@ struct PrefillArgs {
     int64_t S_max;
     const int32_t* block_table;
     int32_t page_shift, bt_stride, n_pages;
+    // split-precision (hi + lo) scores on every row, not only the first
+    // kPreciseRows of each sequence
+    int32_t precise;
 };
 
 // Plan of a chunk call: per sequence b, C_b = cu_q[b + 1] - cu_q[b] query rows
 // at positions seqlens_k[b] - C_b .. seqlens_k[b] - 1.
 hipError_t launch_plan_chunk(int32_t* plan, const int32_t* cu_q, const int32_t* seqlens_k,
                              int32_t B, int64_t Tq, int32_t max_seqlen_q, int32_t max_seqlen_k,
-                             int32_t w_pretrained, hipStream_t s);
+                             int32_t w_pretrained, int32_t precise, hipStream_t s);
 // out[t][h][:] = E4M3(x[t][h][:] / scale[h]) (fp32 quotient, round to nearest
 // even, saturating at +-448); x bf16 [ntok][H][d]
 hipError_t launch_e4m3_quant(uint8_t* out, const void* x, const float* scale, int64_t ntok,
@@ -133,6 +155,12 @@ struct DecodeArgs {
     int32_t fp8;
     const float* k_scale;
     const float* v_scale;
+    // Single-call pieces of the unfused form (bf16, bifocal off): q_remap
+    // turns the query by R(f(p)) instead of R(p); window keeps only the keys
+    // p - j < w_local; o_f32 writes o as float32.
+    int32_t q_remap, window, o_f32;
+    // remote keys turned in fp32 and split into fp16 hi + lo operands
+    int32_t precise;
 };
 hipError_t launch_decode(const DecodeArgs& a, int dtype, hipStream_t s);
 

@@ -40,7 +40,9 @@
 // V (bf16 input, exact in fp16 within its range) and the probabilities, whose
 // row sum is taken from the same fp16 values with v_dot2_f32_f16.  Rows below
 // kPreciseRows, which see few keys, add the fp16 residuals of q and k
-// (hi * hi + hi * lo + lo * hi).
+// (hi * hi + hi * lo + lo * hi); a call that asks for split precision gets
+// that on every row (for concentrated attention, where one key's score
+// rounding enters the LSE undiluted).
 #include "internal.h"
 
 namespace jl {
@@ -116,7 +118,7 @@ void prefill_bf16_kernel(PrefillArgs a, int rb_first, int n_rb) {
     const int64_t qbase = (int64_t)start - q0;
     const int32_t row0 = (q0 / kBM + rb) * kBM;
     if (row0 >= len) return;
-    if (PRECISE != (row0 < kPreciseRows)) return;
+    if (PRECISE != (a.precise || row0 < kPreciseRows)) return;
     const int32_t row_end = min(row0 + kBM, len);
     // Which pairs and which RoPE.  Mode 0 is the bifocal softmax (remote
     // pairs remapped, local pairs standard).  Modes 1-3 are the three
@@ -444,7 +446,9 @@ hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t s) {
         total_rb = (a.max_seqlen + kBM - 1) / kBM;
         main_first = precise_rb;
     }
-    const int n_prec = total_rb < precise_rb ? total_rb : precise_rb;
+    // split precision on every row: the split-precision kernel takes all row blocks
+    const int n_prec = a.precise ? total_rb : (total_rb < precise_rb ? total_rb : precise_rb);
+    if (a.precise) main_first = total_rb;
     hipError_t err;
     if (a.d == 128) {
         err = launch_one<128, true>(a, 0, n_prec, s, "prefill_bf16_precise");

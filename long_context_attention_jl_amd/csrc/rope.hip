@@ -56,7 +56,8 @@ hipError_t launch_rope_apply(void* out, const void* x, const int32_t* pos, int64
 // breaks its contract every length is set to 0 (all kernels then do nothing)
 // and the "bad" flag is raised, so no kernel leaves its buffers.
 __global__ void plan_kernel(int32_t* __restrict__ plan, const int32_t* __restrict__ cu,
-                            int32_t n_seqs, int64_t T, int32_t max_seqlen, int32_t w_pretrained) {
+                            int32_t n_seqs, int64_t T, int32_t max_seqlen, int32_t w_pretrained,
+                            int32_t precise) {
     if (threadIdx.x != 0 || blockIdx.x != 0) return;
     bool bad = false;
     if (cu) {
@@ -81,7 +82,7 @@ __global__ void plan_kernel(int32_t* __restrict__ plan, const int32_t* __restric
         e[kPlanBad] = 0;
         e[kPlanQ0] = 0;
         pad += (len + kBN - 1) / kBN * kBN;
-        const int32_t nlo = len < kPreciseRows ? len : kPreciseRows;
+        const int32_t nlo = (precise || len < kPreciseRows) ? len : kPreciseRows;
         lo += (nlo + kBN - 1) / kBN * kBN;
     }
     int32_t* e = plan + n_seqs * kPlanFields;
@@ -97,10 +98,10 @@ __global__ void plan_kernel(int32_t* __restrict__ plan, const int32_t* __restric
 }
 
 hipError_t launch_plan(int32_t* plan, const int32_t* cu, int32_t n_seqs, int64_t T,
-                       int32_t max_seqlen, int32_t w_pretrained, hipStream_t s) {
+                       int32_t max_seqlen, int32_t w_pretrained, int32_t precise, hipStream_t s) {
     LaunchScope scope("plan", s);
     hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(64), 0, s, plan, cu, n_seqs, T, max_seqlen,
-                       w_pretrained);
+                       w_pretrained, precise);
     return hipGetLastError();
 }
 
@@ -115,7 +116,7 @@ hipError_t launch_plan(int32_t* plan, const int32_t* cu, int32_t n_seqs, int64_t
 __global__ void plan_chunk_kernel(int32_t* __restrict__ plan, const int32_t* __restrict__ cu_q,
                                   const int32_t* __restrict__ seqlens_k, int32_t B, int64_t Tq,
                                   int32_t max_seqlen_q, int32_t max_seqlen_k,
-                                  int32_t w_pretrained) {
+                                  int32_t w_pretrained, int32_t precise) {
     if (threadIdx.x != 0 || blockIdx.x != 0) return;
     bool bad = cu_q && (cu_q[0] != 0 || (int64_t)cu_q[B] != Tq);
     for (int b = 0; b < B && !bad; ++b) {
@@ -139,7 +140,7 @@ __global__ void plan_chunk_kernel(int32_t* __restrict__ plan, const int32_t* __r
         e[kPlanBad] = 0;
         e[kPlanQ0] = len - (len ? C : 0);
         pad += (len + kBN - 1) / kBN * kBN;
-        const int32_t nlo = len < kPreciseRows ? len : kPreciseRows;
+        const int32_t nlo = (precise || len < kPreciseRows) ? len : kPreciseRows;
         lo += (nlo + kBN - 1) / kBN * kBN;
     }
     int32_t* e = plan + B * kPlanFields;
@@ -156,10 +157,10 @@ __global__ void plan_chunk_kernel(int32_t* __restrict__ plan, const int32_t* __r
 
 hipError_t launch_plan_chunk(int32_t* plan, const int32_t* cu_q, const int32_t* seqlens_k,
                              int32_t B, int64_t Tq, int32_t max_seqlen_q, int32_t max_seqlen_k,
-                             int32_t w_pretrained, hipStream_t s) {
+                             int32_t w_pretrained, int32_t precise, hipStream_t s) {
     LaunchScope scope("plan", s);
     hipLaunchKernelGGL(plan_chunk_kernel, dim3(1), dim3(64), 0, s, plan, cu_q, seqlens_k, B, Tq,
-                       max_seqlen_q, max_seqlen_k, w_pretrained);
+                       max_seqlen_q, max_seqlen_k, w_pretrained, precise);
     return hipGetLastError();
 }
 
@@ -192,7 +193,8 @@ __host__ __device__ constexpr int vt_perm16(int p) {
 //   KR[g][row]  = R(f(n)) k_n         (remapped RoPE, [BT] §3.1; only if G > 1), fp16
 // In a chunk call the source rows are cache rows c_n = R(n) k_n, so
 // KS = c_n and KR = R(f(n) - n) c_n (the correction rotation of [BT] §3.3).
-//   KS_lo/KR_lo = f16(x - f16(x))     for n < kPreciseRows (split precision)
+//   KS_lo/KR_lo = f16(x - f16(x))     for n < kPreciseRows, or every n when the
+//                                     call asks for split precision on all rows
 //   VT[g][tile][d][key']              V tile transposed to fp16, keys in vt_perm16 order
 //   k_rot_out[tok][g] = KS row        (optional, the caller's cache layout)
 // Pad rows (n >= L) are written as zeros so masked keys never meet NaNs.
@@ -242,7 +244,7 @@ __global__ __launch_bounds__(256) void kv_prepass_bf16_kernel(PrefillArgs a) {
         const int r = pass * RPP + (int)threadIdx.x / TPR, c = (int)threadIdx.x % TPR;
         const int32_t n = n0 + r;
         const bool valid = n < len;
-        const bool lo_row = n < kPreciseRows;
+        const bool lo_row = n < kPreciseRows || a.precise;
         const int64_t krow = valid ? src_row(n) : 0;
         if (c == 0) vrow[r] = krow;  // published by the first barrier of the value loop
         float cs[8], sn[8], cr[8], sr[8];

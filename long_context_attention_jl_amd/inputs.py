@@ -213,3 +213,44 @@ def decode_fp8_128k():
     """The 128K decode workload (L = 131072, G = 4) on an fp8 cache."""
     q, k8, v8, ks, vs = decode_fp8_inputs(1, 131072, 32, 8, 128, seed=4)
     return q, k8, v8, ks, vs, [131072], DECODE_PARAMS
+
+
+def outlier_value_channels(d: int):
+    """The value channels with_outlier_channels makes large (by default)."""
+    return (10, d - 28)
+
+
+def with_outlier_channels(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, seed: int,
+                          k_channels=(3,), v_channels=None, k_range=(1.0e3, 3.0e4),
+                          v_range=(1.0e3, 6.0e4), q_small: float = 7.0e-5):
+    """Large-magnitude variant of seeded inputs (any shape whose last dim is d).
+
+    Every key gets, in each channel of ``k_channels``, a value of random sign
+    and magnitude uniform in ``k_range``; every value gets the same in each
+    channel of ``v_channels`` with ``v_range``.  The query channels c and
+    c + d/2 of each key channel c (the two channels a half-split RoPE pair
+    mixes) are redrawn as N(0, 1) * q_small, so the scores stay of order one
+    while the keys reach ``k_range[1]``.  Everything else is left as drawn.
+    Returns new tensors of the inputs' dtype (bf16 rounds to nearest even)."""
+    g = torch.Generator("cpu").manual_seed(seed)
+    d = q.shape[-1]
+    if v_channels is None:
+        v_channels = outlier_value_channels(d)
+    q, k, v = q.float().clone(), k.float().clone(), v.float().clone()
+
+    def big(shape, lo, hi):
+        mag = lo + (hi - lo) * torch.rand(*shape, generator=g, dtype=torch.float32)
+        sign = torch.where(torch.rand(*shape, generator=g) < 0.5, -1.0, 1.0)
+        return mag * sign
+
+    for c in k_channels:
+        k[..., c] = big(k.shape[:-1], *k_range)
+        for cq in (c, (c + d // 2) % d):
+            q[..., cq] = torch.randn(*q.shape[:-1], generator=g, dtype=torch.float32) * q_small
+    for c in v_channels:
+        v[..., c] = big(v.shape[:-1], *v_range)
+    return q, k, v
+
+
+def to_dtype(dtype, *ts):
+    return tuple(t.to(dtype) for t in ts)

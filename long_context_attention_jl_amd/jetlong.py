@@ -42,7 +42,7 @@ _STATUS = {0: "JL_OK", 1: "JL_ERR_INVALID_ARGUMENT", 2: "JL_ERR_UNSUPPORTED",
 class jl_params(ctypes.Structure):
     _fields_ = [("w_pretrained", ctypes.c_int32), ("w_local", ctypes.c_int32),
                 ("rope_base", ctypes.c_double), ("softmax_scale", ctypes.c_float),
-                ("bifocal", ctypes.c_int32)]
+                ("bifocal", ctypes.c_int32), ("precise", ctypes.c_int32)]
 
 
 _lib = None
@@ -69,6 +69,7 @@ def lib() -> ctypes.CDLL:
         L.jl_rope_apply.argtypes = [_vp, _vp, _vp, _i64, _i32, _i32, ctypes.c_double, _i32, ctypes.c_int, _vp]
         L.jl_bifocal_prefill_workspace.restype = ctypes.c_int
         L.jl_bifocal_prefill_workspace.argtypes = [_i64, _i32, _i32, _i32, _i32, ctypes.c_int,
+                                                   ctypes.POINTER(jl_params),
                                                    ctypes.POINTER(ctypes.c_size_t)]
         L.jl_bifocal_prefill.restype = ctypes.c_int
         L.jl_bifocal_prefill.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i64, _i32, _i32, _i32,
@@ -77,6 +78,7 @@ def lib() -> ctypes.CDLL:
         L.jl_bifocal_prefill_three_call_workspace.restype = ctypes.c_int
         L.jl_bifocal_prefill_three_call_workspace.argtypes = [_i64, _i32, _i32, _i32, _i32,
                                                               ctypes.c_int,
+                                                              ctypes.POINTER(jl_params),
                                                               ctypes.POINTER(ctypes.c_size_t)]
         L.jl_bifocal_prefill_three_call.restype = ctypes.c_int
         L.jl_bifocal_prefill_three_call.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i64, _i32,
@@ -96,7 +98,7 @@ def lib() -> ctypes.CDLL:
                                               ctypes.c_size_t, _vp]
         L.jl_bifocal_prefill_chunk_workspace.restype = ctypes.c_int
         L.jl_bifocal_prefill_chunk_workspace.argtypes = [_i64, _i32, _i32, _i32, _i32, _i32,
-                                                         ctypes.c_int,
+                                                         ctypes.c_int, ctypes.POINTER(jl_params),
                                                          ctypes.POINTER(ctypes.c_size_t)]
         L.jl_bifocal_prefill_chunk.restype = ctypes.c_int
         L.jl_bifocal_prefill_chunk.argtypes = [_vp, _vp, _vp, _vp, _i64, _i32, _vp, _vp, _vp,
@@ -154,15 +156,88 @@ def _dev(t: torch.Tensor, name: str) -> int:
     return t.data_ptr()
 
 
+def _expect(cond: bool, msg: str) -> None:
+    if not cond:
+        raise ValueError(msg)
+
+
+def _like(t: Optional[torch.Tensor], name: str, shape, dtype, device) -> None:
+    """An optional caller-supplied tensor must have exactly this shape, dtype
+    and device (the library writes or reads exactly that many elements)."""
+    if t is None:
+        return
+    _expect(tuple(t.shape) == tuple(shape), "%s must have shape %s, got %s"
+            % (name, tuple(shape), tuple(t.shape)))
+    _expect(t.dtype == dtype, "%s must be %s, got %s" % (name, dtype, t.dtype))
+    _expect(t.device == device, "%s must be on %s, got %s" % (name, device, t.device))
+
+
+def _rank(t: torch.Tensor, name: str, n: int) -> None:
+    _expect(t.dim() == n, "%s must have %d dimensions, got shape %s" % (name, n, tuple(t.shape)))
+
+
+def _check_qkv(q, k, v, out, lse_out, k_rot_out=None):
+    """Prefill operands: q [T, Hq, d]; k, v [T, Hkv, d] of q's dtype and device."""
+    _rank(q, "q", 3)
+    _rank(k, "k", 3)
+    T, Hq, d = q.shape
+    Hkv = k.shape[1]
+    _expect(q.dtype in (torch.bfloat16, torch.float32), "q must be bfloat16 or float32")
+    _expect(k.shape[0] == T and k.shape[2] == d, "k must be [T, Hkv, d] = [%d, Hkv, %d], got %s"
+            % (T, d, tuple(k.shape)))
+    _like(k, "k", (T, Hkv, d), q.dtype, q.device)
+    _like(v, "v", (T, Hkv, d), q.dtype, q.device)
+    _like(out, "out", (T, Hq, d), q.dtype, q.device)
+    _like(lse_out, "lse_out", (Hq, T), torch.float32, q.device)
+    _like(k_rot_out, "k_rot_out", (T, Hkv, d), q.dtype, q.device)
+
+
+def _check_cache(q, k_cache, v_cache, out, lse_out, *, batch_dim: bool, cache_dtype=None):
+    """Decode / chunk operands: caches [B', S, Hkv, d] (B' >= batch when batch_dim)
+    or page pools [n_pages, page_size, Hkv, d]; values like keys."""
+    _rank(q, "q", 3)
+    _rank(k_cache, "k_cache", 4)
+    Bq, Hq, d = q.shape
+    _expect(q.dtype in (torch.bfloat16, torch.float32), "q must be bfloat16 or float32")
+    _expect(k_cache.shape[3] == d, "the caches' last dimension must be d = %d, got %s"
+            % (d, tuple(k_cache.shape)))
+    cdt = q.dtype if cache_dtype is None else k_cache.dtype
+    if cache_dtype is not None:
+        _expect(k_cache.dtype in cache_dtype, "k_cache must be one of %s" % (cache_dtype,))
+    _like(k_cache, "k_cache", tuple(k_cache.shape), cdt, q.device)
+    _like(v_cache, "v_cache", tuple(k_cache.shape), cdt, q.device)
+    _like(out, "out", tuple(q.shape), q.dtype, q.device)
+    _expect(k_cache.shape[2] >= 1 and Hq % k_cache.shape[2] == 0,
+            "Hq = %d must be a multiple of the caches' kv heads %d" % (Hq, k_cache.shape[2]))
+    return Bq, Hq, d
+
+
+def _check_lens(n: int, batch: int, name: str) -> None:
+    _expect(n == batch, "%s needs one entry per sequence (%d), got %d" % (name, batch, n))
+
+
+def _check_block_table(bt: torch.Tensor, batch: int, device) -> None:
+    _rank(bt, "block_table", 2)
+    _expect(bt.shape[0] >= batch, "block_table needs a row per sequence (%d), got %d"
+            % (batch, bt.shape[0]))
+    _expect(bt.device == device, "block_table must be on %s" % device)
+
+
 def _stream() -> int:
     return torch.cuda.current_stream().cuda_stream
 
 
-def _params(w_pretrained, w_local, rope_base, softmax_scale, bifocal) -> jl_params:
+def _params(w_pretrained, w_local, rope_base, softmax_scale, bifocal, precise=False) -> jl_params:
     """bifocal: False / 0 plain RoPE, True / 1 the method (integer grouping in the
-    remote window), 2 continuous interpolation in the remote window."""
+    remote window), 2 continuous interpolation in the remote window.
+    precise: split-precision scores (for concentrated attention)."""
     return jl_params(int(w_pretrained), int(w_local), float(rope_base), float(softmax_scale),
-                     int(bifocal))
+                     int(bifocal), 1 if precise else 0)
+
+
+def _precise_params(precise) -> jl_params:
+    """Params carrying only the precision choice (for the workspace queries)."""
+    return jl_params(1, 0, 1.0, 1.0, 1, 1 if precise else 0)
 
 
 def abi_version() -> int:
@@ -179,7 +254,10 @@ def group_size(L: int, w_pretrained: int) -> int:
 def rope_apply(x: torch.Tensor, positions: torch.Tensor, rope_base: float, G: int = 1,
                out: Optional[torch.Tensor] = None) -> torch.Tensor:
     """out[t, h] = R(floor(positions[t] / G)) x[t, h]; x is [T, H, d] (bf16 or fp32)."""
+    _rank(x, "x", 3)
     T, H, d = x.shape
+    _expect(positions.numel() == T, "positions needs T = %d entries, got %d" % (T, positions.numel()))
+    _like(out, "out", tuple(x.shape), x.dtype, x.device)
     if out is None:
         out = torch.empty_like(x)
     pos = positions.to(device=x.device, dtype=torch.int32).contiguous()
@@ -188,19 +266,35 @@ def rope_apply(x: torch.Tensor, positions: torch.Tensor, rope_base: float, G: in
     return out
 
 
-def prefill_workspace_bytes(T: int, n_seqs: int, Hq: int, Hkv: int, d: int, dtype) -> int:
+def prefill_workspace_bytes(T: int, n_seqs: int, Hq: int, Hkv: int, d: int, dtype,
+                            precise: bool = False) -> int:
     n = ctypes.c_size_t()
     dt = JL_DTYPE_BF16 if dtype == torch.bfloat16 else JL_DTYPE_F32
-    _check(lib().jl_bifocal_prefill_workspace(T, n_seqs, Hq, Hkv, d, dt, ctypes.byref(n)),
+    pp = _precise_params(precise)
+    _check(lib().jl_bifocal_prefill_workspace(T, n_seqs, Hq, Hkv, d, dt, ctypes.byref(pp),
+                                              ctypes.byref(n)),
            "jl_bifocal_prefill_workspace")
     return n.value
 
 
-def _workspace(nbytes: int, device, ws: Optional[torch.Tensor]) -> torch.Tensor:
+def _workspace(nbytes: int, device, ws: Optional[torch.Tensor], zeroed: bool = False) -> torch.Tensor:
+    """The caller's workspace if it is large enough, else a new one (256-byte
+    aligned: torch's caching allocator aligns to at least 512 bytes).  Decode
+    workspaces hold ticket counters that must be zero before the first call;
+    every decode call leaves them zero, so a workspace kept for decode calls
+    is zeroed once, when it is made."""
     if ws is not None and ws.numel() * ws.element_size() >= nbytes:
         return ws
-    # 256-byte aligned (torch's caching allocator aligns to at least 512 bytes)
+    if zeroed:
+        return torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
     return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+
+
+def decode_workspace(B: int, max_seqlen_k: int, Hq: int, Hkv: int, d: int, dtype,
+                     device="cuda") -> torch.Tensor:
+    """A zero-filled decode workspace for these sizes, to keep across calls."""
+    return torch.zeros(max(decode_workspace_bytes(B, max_seqlen_k, Hq, Hkv, d, dtype), 256),
+                       dtype=torch.uint8, device=device)
 
 
 def _varlen(cu_seqlens, max_seqlen, T: int, dev):
@@ -219,10 +313,12 @@ def _varlen(cu_seqlens, max_seqlen, T: int, dev):
     return cu_t, cu_t.numel() - 1, max_seqlen
 
 
-def prefill_three_call_workspace_bytes(T: int, n_seqs: int, Hq: int, Hkv: int, d: int) -> int:
+def prefill_three_call_workspace_bytes(T: int, n_seqs: int, Hq: int, Hkv: int, d: int,
+                                       precise: bool = False) -> int:
     n = ctypes.c_size_t()
+    pp = _precise_params(precise)
     _check(lib().jl_bifocal_prefill_three_call_workspace(T, n_seqs, Hq, Hkv, d, JL_DTYPE_BF16,
-                                                         ctypes.byref(n)),
+                                                         ctypes.byref(pp), ctypes.byref(n)),
            "jl_bifocal_prefill_three_call_workspace")
     return n.value
 
@@ -231,21 +327,23 @@ def bifocal_prefill_three_call(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor
                                w_pretrained: int, w_local: int, rope_base: float,
                                softmax_scale: float,
                                cu_seqlens: Union[None, Sequence[int], torch.Tensor] = None,
-                               max_seqlen: Optional[int] = None,
+                               max_seqlen: Optional[int] = None, precise: bool = False,
                                workspace: Optional[torch.Tensor] = None,
                                out: Optional[torch.Tensor] = None,
                                lse_out: Optional[torch.Tensor] = None
                                ) -> Tuple[torch.Tensor, torch.Tensor]:
     """The pages' unfused form ([TW] §四): three attention calls B, A, C merged in
     LogSumExp space.  bf16 only.  Returns (o [T, Hq, d], lse [Hq, T] float32)."""
+    _check_qkv(q, k, v, out, lse_out)
     T, Hq, d = q.shape
     Hkv = k.shape[1]
     dev = q.device
     cu_t, n_seqs, max_seqlen = _varlen(cu_seqlens, max_seqlen, T, dev)
     o = out if out is not None else torch.empty_like(q)
     lse = lse_out if lse_out is not None else torch.empty((Hq, T), dtype=torch.float32, device=dev)
-    ws = _workspace(prefill_three_call_workspace_bytes(T, n_seqs, Hq, Hkv, d), dev, workspace)
-    p = _params(w_pretrained, w_local, rope_base, softmax_scale, True)
+    ws = _workspace(prefill_three_call_workspace_bytes(T, n_seqs, Hq, Hkv, d, precise), dev,
+                    workspace)
+    p = _params(w_pretrained, w_local, rope_base, softmax_scale, True, precise)
     _check(lib().jl_bifocal_prefill_three_call(
         _dev(o, "o"), _dev(lse, "lse"), _dev(q, "q"), _dev(k, "k"), _dev(v, "v"),
         None if cu_t is None else _dev(cu_t, "cu_seqlens"), n_seqs, T, int(max_seqlen), Hq, Hkv,
@@ -258,19 +356,21 @@ def bifocal_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, w_pret
                     w_local: int, rope_base: float, softmax_scale: float, bifocal: Union[bool, int] = True,
                     cu_seqlens: Union[None, Sequence[int], torch.Tensor] = None,
                     max_seqlen: Optional[int] = None, k_rot_out: Optional[torch.Tensor] = None,
+                    precise: bool = False,
                     workspace: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
                     lse_out: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
     """Causal bifocal prefill ([BT] §3.2): q [T, Hq, d], k/v [T, Hkv, d] raw.
     Returns (o [T, Hq, d], lse [Hq, T] float32)."""
+    _check_qkv(q, k, v, out, lse_out, k_rot_out)
     T, Hq, d = q.shape
     Hkv = k.shape[1]
     dev = q.device
     cu_t, n_seqs, max_seqlen = _varlen(cu_seqlens, max_seqlen, T, dev)
     o = out if out is not None else torch.empty_like(q)
     lse = lse_out if lse_out is not None else torch.empty((Hq, T), dtype=torch.float32, device=dev)
-    nbytes = prefill_workspace_bytes(T, n_seqs, Hq, Hkv, d, q.dtype)
+    nbytes = prefill_workspace_bytes(T, n_seqs, Hq, Hkv, d, q.dtype, precise)
     ws = _workspace(nbytes, dev, workspace)
-    p = _params(w_pretrained, w_local, rope_base, softmax_scale, bifocal)
+    p = _params(w_pretrained, w_local, rope_base, softmax_scale, bifocal, precise)
     _check(lib().jl_bifocal_prefill(
         _dev(o, "o"), _dev(lse, "lse"), _dev(q, "q"), _dev(k, "k"), _dev(v, "v"),
         None if cu_t is None else _dev(cu_t, "cu_seqlens"), n_seqs, T, int(max_seqlen), Hq, Hkv,
@@ -290,12 +390,17 @@ def decode_workspace_bytes(B: int, max_seqlen_k: int, Hq: int, Hkv: int, d: int,
 def bifocal_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                    seqlens_k: Union[Sequence[int], torch.Tensor], *, w_pretrained: int,
                    w_local: int, rope_base: float, softmax_scale: float, bifocal: Union[bool, int] = True,
-                   max_seqlen_k: Optional[int] = None, workspace: Optional[torch.Tensor] = None,
+                   max_seqlen_k: Optional[int] = None, precise: bool = False,
+                   workspace: Optional[torch.Tensor] = None,
                    out: Optional[torch.Tensor] = None,
                    lse_out: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
     """Bifocal decode ([TW] §三, [BT] §3.3): q [B, Hq, d] raw; caches
     [B, S_max, Hkv, d] of standard-RoPE keys.  Returns (o [B, Hq, d], lse [B, Hq])."""
-    B, Hq, d = q.shape
+    B, Hq, d = _check_cache(q, k_cache, v_cache, out, lse_out, batch_dim=True)
+    _expect(k_cache.shape[0] >= B, "the caches need a row per sequence (%d), got %d"
+            % (B, k_cache.shape[0]))
+    _like(lse_out, "lse_out", (B, Hq), torch.float32, q.device)
+    _check_lens(len(seqlens_k), B, "seqlens_k")
     S_max, Hkv = k_cache.shape[1], k_cache.shape[2]
     dev = q.device
     if isinstance(seqlens_k, torch.Tensor):
@@ -310,8 +415,8 @@ def bifocal_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor
     o = out if out is not None else torch.empty_like(q)
     lse = lse_out if lse_out is not None else torch.empty((B, Hq), dtype=torch.float32, device=dev)
     nbytes = decode_workspace_bytes(B, int(max_seqlen_k), Hq, Hkv, d, q.dtype)
-    ws = _workspace(nbytes, dev, workspace)
-    p = _params(w_pretrained, w_local, rope_base, softmax_scale, bifocal)
+    ws = _workspace(nbytes, dev, workspace, zeroed=True)
+    p = _params(w_pretrained, w_local, rope_base, softmax_scale, bifocal, precise)
     _check(lib().jl_bifocal_decode(
         _dev(o, "o"), _dev(lse, "lse"), _dev(q, "q"), _dev(k_cache, "k_cache"),
         _dev(v_cache, "v_cache"), _dev(sl, "seqlens_k"), B, int(max_seqlen_k), S_max, Hq, Hkv, d,
@@ -337,22 +442,26 @@ def bifocal_decode_paged(q: torch.Tensor, k_pages: torch.Tensor, v_pages: torch.
                          block_table: torch.Tensor, seqlens_k: Union[Sequence[int], torch.Tensor],
                          *, w_pretrained: int, w_local: int, rope_base: float,
                          softmax_scale: float, bifocal: Union[bool, int] = True,
-                         max_seqlen_k: Optional[int] = None,
+                         max_seqlen_k: Optional[int] = None, precise: bool = False,
                          workspace: Optional[torch.Tensor] = None,
                          out: Optional[torch.Tensor] = None,
                          lse_out: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
     """Bifocal decode on a paged cache: k_pages / v_pages [n_pages, page_size, Hkv, d]
     bf16, block_table [B, bt_stride] int32 (page of key j: block_table[b, j // page_size]).
     Returns (o [B, Hq, d], lse [B, Hq])."""
-    B, Hq, d = q.shape
+    B, Hq, d = _check_cache(q, k_pages, v_pages, out, lse_out, batch_dim=False)
+    _like(lse_out, "lse_out", (B, Hq), torch.float32, q.device)
+    _check_lens(len(seqlens_k), B, "seqlens_k")
+    _check_block_table(block_table, B, block_table.device)
     n_pages, page_size, Hkv = k_pages.shape[0], k_pages.shape[1], k_pages.shape[2]
     dev = q.device
     sl, max_seqlen_k = _seqlens(seqlens_k, max_seqlen_k, dev)
     bt = block_table.to(device=dev, dtype=torch.int32).contiguous()
     o = out if out is not None else torch.empty_like(q)
     lse = lse_out if lse_out is not None else torch.empty((B, Hq), dtype=torch.float32, device=dev)
-    ws = _workspace(decode_workspace_bytes(B, max_seqlen_k, Hq, Hkv, d, q.dtype), dev, workspace)
-    p = _params(w_pretrained, w_local, rope_base, softmax_scale, bifocal)
+    ws = _workspace(decode_workspace_bytes(B, max_seqlen_k, Hq, Hkv, d, q.dtype), dev, workspace,
+                    zeroed=True)
+    p = _params(w_pretrained, w_local, rope_base, softmax_scale, bifocal, precise)
     _check(lib().jl_bifocal_decode_paged(
         _dev(o, "o"), _dev(lse, "lse"), _dev(q, "q"), _dev(k_pages, "k_pages"),
         _dev(v_pages, "v_pages"), _dev(bt, "block_table"), _dev(sl, "seqlens_k"), B, max_seqlen_k,
@@ -363,16 +472,18 @@ def bifocal_decode_paged(q: torch.Tensor, k_pages: torch.Tensor, v_pages: torch.
 
 
 def prefill_chunk_workspace_bytes(Tq: int, B: int, max_seqlen_k: int, Hq: int, Hkv: int,
-                                  d: int) -> int:
+                                  d: int, precise: bool = False) -> int:
     n = ctypes.c_size_t(0)
+    pp = _precise_params(precise)
     _check(lib().jl_bifocal_prefill_chunk_workspace(Tq, B, max_seqlen_k, Hq, Hkv, d, 1,
-                                                    ctypes.byref(n)),
+                                                    ctypes.byref(pp), ctypes.byref(n)),
            "jl_bifocal_prefill_chunk_workspace")
     return n.value
 
 
 def _chunk_common(q, seqlens_k, cu_seqlens_q, max_seqlen_q, max_seqlen_k, dev, out, lse_out):
     Tq, Hq, d = q.shape
+    _like(lse_out, "lse_out", (Hq, Tq), torch.float32, q.device)
     cu, B, max_q = _varlen(cu_seqlens_q, max_seqlen_q, Tq, dev)
     sl, max_k = _seqlens(seqlens_k, max_seqlen_k, dev)
     if sl.numel() != B:
@@ -388,7 +499,7 @@ def bifocal_prefill_chunk(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch
                           w_local: int, rope_base: float, softmax_scale: float,
                           bifocal: Union[bool, int] = True, cu_seqlens_q=None,
                           max_seqlen_q: Optional[int] = None,
-                          max_seqlen_k: Optional[int] = None,
+                          max_seqlen_k: Optional[int] = None, precise: bool = False,
                           workspace: Optional[torch.Tensor] = None,
                           out: Optional[torch.Tensor] = None,
                           lse_out: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
@@ -396,14 +507,18 @@ def bifocal_prefill_chunk(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch
     rows of each sequence packed by cu_seqlens_q (None: one chunk); caches
     [B, S_max, Hkv, d] bf16 of standard-RoPE keys holding seqlens_k[b] keys,
     the chunk's own included.  Returns (o [Tq, Hq, d], lse [Hq, Tq])."""
+    _check_cache(q, k_cache, v_cache, out, None, batch_dim=True)
+    _expect(q.dtype == torch.bfloat16, "chunked prefill takes bfloat16 tensors")
+    _check_lens(len(seqlens_k), 1 if cu_seqlens_q is None else len(cu_seqlens_q) - 1, "seqlens_k")
+    _expect(k_cache.shape[0] >= len(seqlens_k), "the caches need a row per sequence")
     dev = q.device
     Hq, d = q.shape[1], q.shape[2]
     S_max, Hkv = k_cache.shape[1], k_cache.shape[2]
     cu, B, max_q, sl, max_k, o, lse = _chunk_common(q, seqlens_k, cu_seqlens_q, max_seqlen_q,
                                                     max_seqlen_k, dev, out, lse_out)
-    ws = _workspace(prefill_chunk_workspace_bytes(q.shape[0], B, max_k, Hq, Hkv, d), dev,
+    ws = _workspace(prefill_chunk_workspace_bytes(q.shape[0], B, max_k, Hq, Hkv, d, precise), dev,
                     workspace)
-    p = _params(w_pretrained, w_local, rope_base, softmax_scale, bifocal)
+    p = _params(w_pretrained, w_local, rope_base, softmax_scale, bifocal, precise)
     _check(lib().jl_bifocal_prefill_chunk(
         _dev(o, "o"), _dev(lse, "lse"), _dev(q, "q"), None if cu is None else _dev(cu, "cu"),
         q.shape[0], max_q, _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
@@ -419,21 +534,26 @@ def bifocal_prefill_chunk_paged(q: torch.Tensor, k_pages: torch.Tensor, v_pages:
                                 w_pretrained: int, w_local: int, rope_base: float,
                                 softmax_scale: float, bifocal: Union[bool, int] = True, cu_seqlens_q=None,
                                 max_seqlen_q: Optional[int] = None,
-                                max_seqlen_k: Optional[int] = None,
+                                max_seqlen_k: Optional[int] = None, precise: bool = False,
                                 workspace: Optional[torch.Tensor] = None,
                                 out: Optional[torch.Tensor] = None,
                                 lse_out: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
     """bifocal_prefill_chunk on a paged cache: k_pages / v_pages
     [n_pages, page_size, Hkv, d] bf16, block_table [B, bt_stride] int32."""
+    _check_cache(q, k_pages, v_pages, out, None, batch_dim=False)
+    _expect(q.dtype == torch.bfloat16, "chunked prefill takes bfloat16 tensors")
+    nb = 1 if cu_seqlens_q is None else len(cu_seqlens_q) - 1
+    _check_lens(len(seqlens_k), nb, "seqlens_k")
+    _check_block_table(block_table, nb, block_table.device)
     dev = q.device
     Hq, d = q.shape[1], q.shape[2]
     n_pages, page_size, Hkv = k_pages.shape[0], k_pages.shape[1], k_pages.shape[2]
     cu, B, max_q, sl, max_k, o, lse = _chunk_common(q, seqlens_k, cu_seqlens_q, max_seqlen_q,
                                                     max_seqlen_k, dev, out, lse_out)
     bt = block_table.to(device=dev, dtype=torch.int32).contiguous()
-    ws = _workspace(prefill_chunk_workspace_bytes(q.shape[0], B, max_k, Hq, Hkv, d), dev,
+    ws = _workspace(prefill_chunk_workspace_bytes(q.shape[0], B, max_k, Hq, Hkv, d, precise), dev,
                     workspace)
-    p = _params(w_pretrained, w_local, rope_base, softmax_scale, bifocal)
+    p = _params(w_pretrained, w_local, rope_base, softmax_scale, bifocal, precise)
     _check(lib().jl_bifocal_prefill_chunk_paged(
         _dev(o, "o"), _dev(lse, "lse"), _dev(q, "q"), None if cu is None else _dev(cu, "cu"),
         q.shape[0], max_q, _dev(k_pages, "k_pages"), _dev(v_pages, "v_pages"),
@@ -458,6 +578,10 @@ def _scale(x, H: int, dev) -> torch.Tensor:
 
 def kv_quantize_fp8(x: torch.Tensor, scale, out: Optional[torch.Tensor] = None) -> torch.Tensor:
     """E4M3 codes (uint8) of x / scale[h] for a bf16 cache block x [..., H, d]."""
+    _expect(x.dim() >= 2 and x.dtype == torch.bfloat16, "x must be a bfloat16 [..., H, d] tensor")
+    if out is not None:
+        _expect(tuple(out.shape) == tuple(x.shape) and out.device == x.device,
+                "out must have x's shape %s and device" % (tuple(x.shape),))
     H, d = x.shape[-2], x.shape[-1]
     sc = _scale(scale, H, x.device)
     o = out if out is not None else torch.empty(x.shape, dtype=torch.uint8, device=x.device)
@@ -478,7 +602,16 @@ def bifocal_decode_fp8(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Te
     """Bifocal decode on an fp8 (E4M3) cache with per-kv-head scales.  Flat
     caches [B, S_max, Hkv, d]; with ``block_table`` page pools
     [n_pages, page_size, Hkv, d].  Returns (o [B, Hq, d], lse [B, Hq])."""
-    B, Hq, d = q.shape
+    B, Hq, d = _check_cache(q, k_cache, v_cache, out, lse_out, batch_dim=block_table is None,
+                            cache_dtype=(torch.uint8, torch.float8_e4m3fn))
+    _expect(q.dtype == torch.bfloat16, "fp8 decode takes bfloat16 queries")
+    _like(lse_out, "lse_out", (B, Hq), torch.float32, q.device)
+    _check_lens(len(seqlens_k), B, "seqlens_k")
+    if block_table is None:
+        _expect(k_cache.shape[0] >= B, "the caches need a row per sequence (%d), got %d"
+                % (B, k_cache.shape[0]))
+    else:
+        _check_block_table(block_table, B, block_table.device)
     dev = q.device
     Hkv = k_cache.shape[2]
     sl, max_seqlen_k = _seqlens(seqlens_k, max_seqlen_k, dev)
@@ -486,7 +619,7 @@ def bifocal_decode_fp8(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Te
     o = out if out is not None else torch.empty_like(q)
     lse = lse_out if lse_out is not None else torch.empty((B, Hq), dtype=torch.float32, device=dev)
     ws = _workspace(decode_workspace_bytes(B, max_seqlen_k, Hq, Hkv, d, torch.bfloat16), dev,
-                    workspace)
+                    workspace, zeroed=True)
     p = _params(w_pretrained, w_local, rope_base, softmax_scale, bifocal)
     if block_table is None:
         _check(lib().jl_bifocal_decode_fp8(

@@ -35,7 +35,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert jlb.abi_version() == 1
+    assert jlb.abi_version() == 2
     L = jlb.lib()
     assert L.jl_status_string(0) == b"JL_OK"
     assert L.jl_status_string(4) == b"JL_ERR_HIP"
@@ -57,10 +57,11 @@ def test_group_size_rejects():
 
 
 def _params(**kw):
-    d = dict(w_pretrained=32768, w_local=2048, rope_base=1e6, softmax_scale=0.088, bifocal=1)
+    d = dict(w_pretrained=32768, w_local=2048, rope_base=1e6, softmax_scale=0.088, bifocal=1,
+             precise=0)
     d.update(kw)
     return jlb.jl_params(d["w_pretrained"], d["w_local"], d["rope_base"], d["softmax_scale"],
-                         d["bifocal"])
+                         d["bifocal"], d["precise"])
 
 
 def _prefill(**kw):
@@ -84,6 +85,7 @@ def _prefill(**kw):
     (dict(params=_params(rope_base=0.0)), 1), (dict(params=_params(softmax_scale=0.0)), 1),
     (dict(params=_params(softmax_scale=float("inf"))), 1), (dict(params=_params(bifocal=3)), 1),
     (dict(params=_params(bifocal=-1)), 1), (dict(params=_params(bifocal=2), dtype=0), 2),
+    (dict(params=_params(precise=2)), 1), (dict(params=_params(precise=-1)), 1),
     (dict(ws_bytes=1000), 3), (dict(ws=FAKE * 8 + 4), 1), (dict(o=FAKE * 3), 1),
     (dict(krot=FAKE * 4), 1), (dict(cu=FAKE * 9, n_seqs=70000, T=1 << 20, max_seqlen=1024), 2),
 ])
@@ -120,24 +122,24 @@ def test_three_call_workspace_query():
     n = ctypes.c_size_t()
     m = ctypes.c_size_t()
     L = jlb.lib()
-    assert L.jl_bifocal_prefill_three_call_workspace(4096, 1, 32, 8, 128, 1, ctypes.byref(n)) == 0
-    assert L.jl_bifocal_prefill_workspace(4096, 1, 32, 8, 128, 1, ctypes.byref(m)) == 0
+    assert L.jl_bifocal_prefill_three_call_workspace(4096, 1, 32, 8, 128, 1, None, ctypes.byref(n)) == 0
+    assert L.jl_bifocal_prefill_workspace(4096, 1, 32, 8, 128, 1, None, ctypes.byref(m)) == 0
     # the three calls' bf16 outputs and fp32 LSEs come on top of the prefill workspace
     assert n.value >= m.value + 3 * (4096 * 32 * 128 * 2 + 32 * 4096 * 4)
-    assert L.jl_bifocal_prefill_three_call_workspace(4096, 1, 32, 8, 128, 0, ctypes.byref(n)) == 2
+    assert L.jl_bifocal_prefill_three_call_workspace(4096, 1, 32, 8, 128, 0, None, ctypes.byref(n)) == 2
 
 
 def test_prefill_workspace_query():
     n = ctypes.c_size_t()
     L = jlb.lib()
-    assert L.jl_bifocal_prefill_workspace(131072, 1, 32, 8, 128, 1, ctypes.byref(n)) == 0
+    assert L.jl_bifocal_prefill_workspace(131072, 1, 32, 8, 128, 1, None, ctypes.byref(n)) == 0
     # three bf16 key/value layouts of the padded sequence dominate
     assert n.value >= 3 * 8 * 131072 * 128 * 2
-    assert L.jl_bifocal_prefill_workspace(512, 1, 1, 1, 64, 0, ctypes.byref(n)) == 0
+    assert L.jl_bifocal_prefill_workspace(512, 1, 1, 1, 64, 0, None, ctypes.byref(n)) == 0
     assert n.value >= 2 * 512 * 64 * 4
-    assert L.jl_bifocal_prefill_workspace(0, 1, 1, 1, 64, 0, ctypes.byref(n)) == 1
-    assert L.jl_bifocal_prefill_workspace(10, 1, 3, 2, 64, 0, ctypes.byref(n)) == 1
-    assert L.jl_bifocal_prefill_workspace(10, 1, 1, 1, 80, 0, ctypes.byref(n)) == 2
+    assert L.jl_bifocal_prefill_workspace(0, 1, 1, 1, 64, 0, None, ctypes.byref(n)) == 1
+    assert L.jl_bifocal_prefill_workspace(10, 1, 3, 2, 64, 0, None, ctypes.byref(n)) == 1
+    assert L.jl_bifocal_prefill_workspace(10, 1, 1, 1, 80, 0, None, ctypes.byref(n)) == 2
 
 
 def _decode(**kw):
@@ -270,24 +272,24 @@ def test_chunk_workspace_query():
     x Tq x Hq x (d + 2) fp32."""
     n = ctypes.c_size_t(0)
     L = jlb.lib()
-    assert L.jl_bifocal_prefill_workspace(131072, 1, 32, 8, 128, 1, ctypes.byref(n)) == 0
+    assert L.jl_bifocal_prefill_workspace(131072, 1, 32, 8, 128, 1, None, ctypes.byref(n)) == 0
     base = n.value
     # 32768 rows of 32 heads: 4096 row blocks >= 1024 workgroups, no split
-    assert L.jl_bifocal_prefill_chunk_workspace(32768, 1, 131072, 32, 8, 128, 1, ctypes.byref(n)) == 0
+    assert L.jl_bifocal_prefill_chunk_workspace(32768, 1, 131072, 32, 8, 128, 1, None, ctypes.byref(n)) == 0
     assert n.value == base
     # 4096 rows: 512 row-block workgroups, two per compute unit: no split
-    assert L.jl_bifocal_prefill_chunk_workspace(4096, 1, 131072, 32, 8, 128, 1, ctypes.byref(n)) == 0
+    assert L.jl_bifocal_prefill_chunk_workspace(4096, 1, 131072, 32, 8, 128, 1, None, ctypes.byref(n)) == 0
     assert n.value == base
     # 1024 rows: 128 workgroups -> up to 4 shares
-    assert L.jl_bifocal_prefill_chunk_workspace(1024, 1, 131072, 32, 8, 128, 1, ctypes.byref(n)) == 0
+    assert L.jl_bifocal_prefill_chunk_workspace(1024, 1, 131072, 32, 8, 128, 1, None, ctypes.byref(n)) == 0
     assert base + 4 * 1024 * 32 * 130 * 4 <= n.value < base + 4 * 1024 * 32 * 130 * 4 + 1024
     # one row: capped at 4 shares
-    assert L.jl_bifocal_prefill_chunk_workspace(1, 1, 131072, 32, 8, 128, 1, ctypes.byref(n)) == 0
+    assert L.jl_bifocal_prefill_chunk_workspace(1, 1, 131072, 32, 8, 128, 1, None, ctypes.byref(n)) == 0
     assert base + 4 * 32 * 130 * 4 <= n.value < base + 4 * 32 * 130 * 4 + 1024
-    assert L.jl_bifocal_prefill_chunk_workspace(1, 1, 131072, 32, 8, 128, 0, ctypes.byref(n)) == 2
-    assert L.jl_bifocal_prefill_chunk_workspace(1, 0, 10, 32, 8, 128, 1, ctypes.byref(n)) == 1
-    assert L.jl_bifocal_prefill_chunk_workspace(0, 1, 10, 32, 8, 128, 1, ctypes.byref(n)) == 1
-    assert L.jl_bifocal_prefill_chunk_workspace(1, 1, 10, 32, 8, 128, 1, None) == 1
+    assert L.jl_bifocal_prefill_chunk_workspace(1, 1, 131072, 32, 8, 128, 0, None, ctypes.byref(n)) == 2
+    assert L.jl_bifocal_prefill_chunk_workspace(1, 0, 10, 32, 8, 128, 1, None, ctypes.byref(n)) == 1
+    assert L.jl_bifocal_prefill_chunk_workspace(0, 1, 10, 32, 8, 128, 1, None, ctypes.byref(n)) == 1
+    assert L.jl_bifocal_prefill_chunk_workspace(1, 1, 10, 32, 8, 128, 1, None, None) == 1
 
 
 def _fp8(paged=False, **kw):
@@ -367,3 +369,136 @@ def test_vector_operands_must_be_16_byte_aligned(call, kw):
 ])
 def test_stream_read_validation(args, status):
     assert jlb.lib().jl_debug_stream_read(*args, None) == status
+
+
+# ---- the Python binding checks every tensor against q before any call --------
+# (CPU tensors: the shape/dtype checks run before the device check, so no
+# pointer reaches the library.)
+
+def _t(*shape, dtype=None):
+    import torch
+    return torch.zeros(*shape, dtype=dtype or torch.bfloat16)
+
+
+_PF = dict(w_pretrained=64, w_local=8, rope_base=1e4, softmax_scale=0.1)
+
+
+@pytest.mark.parametrize("case", [
+    "k_dtype", "v_shape", "k_head_dim", "k_tokens", "out_dtype", "out_shape", "lse_dtype",
+    "lse_shape", "k_rot_shape", "k_rot_dtype",
+])
+def test_binding_prefill_rejects_mismatched_tensors(case):
+    import torch
+    q, k, v = _t(100, 4, 64), _t(100, 2, 64), _t(100, 2, 64)
+    extra = {}
+    if case == "k_dtype":
+        k = _t(100, 2, 64, dtype=torch.float32)
+    elif case == "v_shape":
+        v = _t(100, 1, 64)
+    elif case == "k_head_dim":
+        k = _t(100, 2, 128)
+    elif case == "k_tokens":
+        k = _t(99, 2, 64)
+    elif case == "out_dtype":
+        extra["out"] = _t(100, 4, 64, dtype=torch.float32)
+    elif case == "out_shape":
+        extra["out"] = _t(100, 4, 32)
+    elif case == "lse_dtype":
+        extra["lse_out"] = _t(4, 100)
+    elif case == "lse_shape":
+        extra["lse_out"] = _t(100, 4, dtype=torch.float32)
+    elif case == "k_rot_shape":
+        extra["k_rot_out"] = _t(100, 4, 64)
+    elif case == "k_rot_dtype":
+        extra["k_rot_out"] = _t(100, 2, 64, dtype=torch.float32)
+    with pytest.raises(ValueError):
+        jlb.bifocal_prefill(q, k, v, **_PF, **extra)
+    if case != "k_rot_shape" and case != "k_rot_dtype":
+        with pytest.raises(ValueError):
+            jlb.bifocal_prefill_three_call(q, k, v, **_PF, **extra)
+
+
+@pytest.mark.parametrize("case", [
+    "cache_batch", "cache_dtype", "cache_head_dim", "v_shape", "out_dtype", "lse_shape",
+    "seqlens_count", "heads",
+])
+def test_binding_decode_rejects_mismatched_tensors(case):
+    import torch
+    q, kc, vc = _t(2, 4, 64), _t(2, 50, 2, 64), _t(2, 50, 2, 64)
+    lens, extra = [50, 10], {}
+    if case == "cache_batch":
+        kc, vc = _t(1, 50, 2, 64), _t(1, 50, 2, 64)
+    elif case == "cache_dtype":
+        kc = _t(2, 50, 2, 64, dtype=torch.float32)
+    elif case == "cache_head_dim":
+        kc, vc = _t(2, 50, 2, 128), _t(2, 50, 2, 128)
+    elif case == "v_shape":
+        vc = _t(2, 40, 2, 64)
+    elif case == "out_dtype":
+        extra["out"] = _t(2, 4, 64, dtype=torch.float32)
+    elif case == "lse_shape":
+        extra["lse_out"] = _t(4, 2, dtype=torch.float32)
+    elif case == "seqlens_count":
+        lens = [50]
+    elif case == "heads":
+        kc, vc = _t(2, 50, 3, 64), _t(2, 50, 3, 64)
+    with pytest.raises(ValueError):
+        jlb.bifocal_decode(q, kc, vc, lens, **_PF, **extra)
+
+
+def test_binding_paged_chunk_fp8_and_quantize_reject_mismatched_tensors():
+    import torch
+    q = _t(2, 4, 64)
+    kp, vp = _t(8, 16, 2, 64), _t(8, 16, 2, 64)
+    bt = torch.zeros(1, 8, dtype=torch.int32)  # one row for two sequences
+    with pytest.raises(ValueError):
+        jlb.bifocal_decode_paged(q, kp, vp, bt, [16, 16], **_PF)
+    with pytest.raises(ValueError):  # values of another page size
+        jlb.bifocal_decode_paged(q, kp, _t(8, 32, 2, 64), torch.zeros(2, 8, dtype=torch.int32),
+                                 [16, 16], **_PF)
+    with pytest.raises(ValueError):  # chunk caches with too few rows
+        jlb.bifocal_prefill_chunk(_t(10, 4, 64), _t(1, 50, 2, 64), _t(1, 50, 2, 64), [50, 50],
+                                  cu_seqlens_q=[0, 5, 10], **_PF)
+    with pytest.raises(ValueError):  # chunk of fp32 queries
+        jlb.bifocal_prefill_chunk(_t(10, 4, 64, dtype=torch.float32),
+                                  _t(1, 50, 2, 64, dtype=torch.float32),
+                                  _t(1, 50, 2, 64, dtype=torch.float32), [50], **_PF)
+    u8 = torch.zeros(2, 50, 2, 64, dtype=torch.uint8)
+    with pytest.raises(ValueError):  # a bf16 cache where codes are expected
+        jlb.bifocal_decode_fp8(q, _t(2, 50, 2, 64), u8, [1.0, 1.0], [1.0, 1.0], [50, 50], **_PF)
+    with pytest.raises(ValueError):  # fp32 queries on the fp8 path
+        jlb.bifocal_decode_fp8(_t(2, 4, 64, dtype=torch.float32), u8, u8, [1.0, 1.0],
+                               [1.0, 1.0], [50, 50], **_PF)
+    with pytest.raises(ValueError):  # quantize output of the wrong shape
+        jlb.kv_quantize_fp8(_t(5, 2, 64), [1.0, 1.0], out=torch.zeros(5, 2, 32, dtype=torch.uint8))
+    with pytest.raises(ValueError):  # rope positions of the wrong length
+        jlb.rope_apply(_t(5, 2, 64), torch.arange(4), 1e4)
+
+
+def test_precise_workspaces_cover_every_key():
+    """Split precision on every row needs low-part key tiles for every key, so
+    its prefill and chunk workspaces are larger; the default ones are unchanged
+    by a NULL or default params pointer; a bad precise value is refused."""
+    L = jlb.lib()
+    a, b, c = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
+    d0, d1 = _params(), _params(precise=1)
+    assert L.jl_bifocal_prefill_workspace(131072, 1, 32, 8, 128, 1, None, ctypes.byref(a)) == 0
+    assert L.jl_bifocal_prefill_workspace(131072, 1, 32, 8, 128, 1, ctypes.byref(d0),
+                                          ctypes.byref(b)) == 0
+    assert L.jl_bifocal_prefill_workspace(131072, 1, 32, 8, 128, 1, ctypes.byref(d1),
+                                          ctypes.byref(c)) == 0
+    assert a.value == b.value and c.value > a.value
+    # the low-part tiles of every key: 2 copies x 8 heads x 131072 keys x (128 + 8) halves
+    assert c.value - a.value >= 2 * 8 * (131072 - 2048) * 136 * 2
+    assert L.jl_bifocal_prefill_chunk_workspace(1024, 1, 131072, 32, 8, 128, 1, ctypes.byref(d1),
+                                                ctypes.byref(c)) == 0
+    assert L.jl_bifocal_prefill_workspace(10, 1, 1, 1, 64, 1, ctypes.byref(_params(precise=3)),
+                                          ctypes.byref(c)) == 1
+
+
+def test_precise_fp8_decode_is_unsupported():
+    p = _params(precise=1)
+    st = jlb.lib().jl_bifocal_decode_fp8(FAKE, FAKE * 2, FAKE * 3, FAKE * 4, FAKE * 5, FAKE * 6,
+                                         FAKE * 7, FAKE * 9, 1, 1024, 1024, 32, 8, 128,
+                                         ctypes.byref(p), FAKE * 8, 1 << 40, None)
+    assert st == jlb.JL_ERR_UNSUPPORTED

@@ -11,7 +11,7 @@ from long_context_attention_jl_amd import inputs
 from long_context_attention_jl_amd import jetlong as jl
 from long_context_attention_jl_amd.inputs import Params
 
-from _parity import TOL_BF16_LSE, TOL_BF16_O, TOL_F32_LSE, TOL_F32_O, say
+from _parity import TOL_BF16_LSE, TOL_BF16_O, TOL_F32_LSE, TOL_F32_O, check_decode, say
 
 pytestmark = pytest.mark.gpu
 
@@ -39,6 +39,10 @@ def _check(o, lse, o_ref, lse_ref, dtype, label):
         assert do <= TOL_BF16_O and dl <= TOL_BF16_LSE, label
 
 
+def _plain(p):
+    return Params(p.w_pretrained, p.w_local, p.rope_base, p.softmax_scale, bifocal=False)
+
+
 def test_decode_128k_workload():
     """32 q heads, 8 kv heads, d=128, cache of 131071 keys + the new token (L = 131072, G = 4)."""
     c = inputs.decode_128k()
@@ -49,13 +53,54 @@ def test_decode_128k_workload():
     torch.cuda.synchronize()
     assert torch.equal(kc, k_before), "the cache must never be rewritten"
     o_ref, lse_ref = _dec_ref(c.q, c.k_cache, c.v_cache, c.seqlens, c.params)
-    _check(o, lse, o_ref, lse_ref, torch.bfloat16, c.name)
     # discrimination: bifocal differs from plain attention by far more than the error
-    p0 = Params(c.params.w_pretrained, c.params.w_local, c.params.rope_base,
-                c.params.softmax_scale, bifocal=False)
-    o_pl, _ = _dec_ref(c.q, c.k_cache, c.v_cache, c.seqlens, p0)
-    err = np.linalg.norm(o.float().cpu().double().numpy() - o_ref)
-    assert np.linalg.norm(o_ref - o_pl) >= 10 * err
+    o_pl, _ = _dec_ref(c.q, c.k_cache, c.v_cache, c.seqlens, _plain(c.params))
+    check_decode(o, lse, o_ref, lse_ref, torch.bfloat16, c.name, o_plain=o_pl)
+
+
+def test_decode_128k_peaky():
+    """The 128K decode with the query scaled by 4: a concentrated softmax, so
+    the remote keys' fp16 correction rotation and the band edge show in o."""
+    c = inputs.decode_128k()
+    q = (c.q.float() * 4.0).to(torch.bfloat16)
+    say("case", c.name, "q x4")
+    o_ref, lse_ref = _dec_ref(q, c.k_cache, c.v_cache, c.seqlens, c.params)
+    o_pl, _ = _dec_ref(q, c.k_cache, c.v_cache, c.seqlens, _plain(c.params))
+    kc, vc = c.k_cache.cuda(), c.v_cache.cuda()
+    for precise in (True, False):  # split-precision remote keys meet every bar
+        o, lse = _dec_gpu(q, kc, vc, c.seqlens, c.params, precise=precise)
+        torch.cuda.synchronize()
+        check_decode(o, lse, o_ref, lse_ref, torch.bfloat16,
+                     c.name + " q x4" + (" precise" if precise else ""), o_plain=o_pl,
+                     check_lse=precise)
+
+
+@pytest.mark.parametrize("S", [131072, 3000])
+def test_decode_large_magnitude_channels(S):
+    """Cached keys with an outlier channel of magnitude 1e3..3e4 and values with
+    outlier channels up to 6e4 (the fp16 operand range ends at 65504); the
+    query is small in the channels the key outlier rotates into, so scores
+    stay of order one.  The value channels' bar scales with their magnitude."""
+    # the short cache takes a smaller pretraining window so that G > 1 there too
+    p = inputs.DECODE_PARAMS if S > 65536 else Params(1024, 300, 1e6, 1.0 / math.sqrt(128))
+    q, kc, vc = inputs.decode_inputs(1, S, 32, 8, 128, seed=404)
+    q, kc, vc = inputs.with_outlier_channels(q, kc, vc, seed=405, q_small=7.0e-4)
+    q, kc, vc = inputs.to_dtype(torch.bfloat16, q, kc, vc)
+    scale = np.ones(128)
+    vmax = vc.float().abs().amax(dim=(0, 1, 2)).double().numpy()
+    for ch in inputs.outlier_value_channels(128):
+        scale[ch] = vmax[ch]
+    say("decode outliers S=%d max|k|=%.0f max|v|=%.0f" % (
+        S, kc.float().abs().max().item(), vc.float().abs().max().item()))
+    o_ref, lse_ref = _dec_ref(q, kc, vc, [S], p)
+    o_pl, _ = _dec_ref(q, kc, vc, [S], _plain(p))
+    kd, vd = kc.cuda(), vc.cuda()
+    for precise in (True, False):
+        o, lse = _dec_gpu(q, kd, vd, [S], p, precise=precise)
+        torch.cuda.synchronize()
+        check_decode(o, lse, o_ref, lse_ref, torch.bfloat16,
+                     "decode outliers S=%d%s" % (S, " precise" if precise else ""),
+                     o_plain=o_pl, o_scale=scale, check_lse=precise)
 
 
 def test_decode_16_steps_across_g_switch():
@@ -65,11 +110,14 @@ def test_decode_16_steps_across_g_switch():
     kc, vc = kc_h.cuda(), vc_h.cuda()
     snapshot = kc.clone()
     for step, (q, L) in enumerate(zip(queries, lens)):
-        say("step", step, "L", L, "G", oracle.group_size(L, p.w_pretrained))
+        G = oracle.group_size(L, p.w_pretrained)
+        say("step", step, "L", L, "G", G)
         o, lse = _dec_gpu(q, kc, vc, [L], p, max_seqlen_k=L)
         torch.cuda.synchronize()
         o_ref, lse_ref = _dec_ref(q, kc_h, vc_h, [L], p)
-        _check(o, lse, o_ref, lse_ref, torch.bfloat16, "step %d L=%d" % (step, L))
+        o_pl = _dec_ref(q, kc_h, vc_h, [L], _plain(p))[0] if G > 1 else None
+        check_decode(o, lse, o_ref, lse_ref, torch.bfloat16, "step %d L=%d" % (step, L),
+                     o_plain=o_pl)
     assert torch.equal(kc, snapshot)
 
 
@@ -91,14 +139,12 @@ def test_decode_small_batched(dtype, d, Hq, Hkv):
     _check(o, lse, o_ref, lse_ref, dtype, "small d=%d" % d)
 
 
-@pytest.mark.parametrize("dtype,wgs", [(torch.float32, None), (torch.bfloat16, "2048")])
-def test_decode_merge_of_many_chunks(dtype, wgs, monkeypatch):
-    """More than 256 key chunks per sequence, so each merge thread folds
-    several rounds of partials (fp32 caches aim at 512 workgroups; the bf16
-    case raises the workgroup target through JL_DECODE_WGS)."""
-    if wgs:
-        monkeypatch.setenv("JL_DECODE_WGS", wgs)
-    B, S, Hq, Hkv, d = 1, 40000, 8, 2, 128
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_decode_merge_of_many_chunks(dtype):
+    """More than 256 key chunks per sequence (a 400000-key cache of two kv heads:
+    bf16 chunks hold at most 32 stages of 48 positions, fp32 ones aim at 512
+    workgroups), so the partials are folded over several rounds."""
+    B, S, Hq, Hkv, d = 1, 400000, 8, 2, 128
     ws = jl.decode_workspace_bytes(B, S, Hq, Hkv, d, dtype)
     n_splits = ws // (B * Hq * (d + 2) * 4)
     say("many-chunk decode", dtype, "about", n_splits, "chunks")
@@ -109,6 +155,36 @@ def test_decode_merge_of_many_chunks(dtype, wgs, monkeypatch):
     torch.cuda.synchronize()
     o_ref, lse_ref = _dec_ref(q, kc, vc, [S], p)
     _check(o, lse, o_ref, lse_ref, dtype, "many chunks %s" % dtype)
+
+
+@pytest.mark.parametrize("d,Hq,Hkv", [(128, 8, 2), (64, 16, 1), (128, 24, 12)])
+def test_decode_precise_small_batched(d, Hq, Hkv):
+    """Split-precision remote keys (precise = 1), flat and paged caches."""
+    B, S = 3, 700
+    q, kc, vc = inputs.decode_inputs(B, S, Hq, Hkv, d, seed=d + Hq + 5)
+    lens = [700, 1, 333]
+    p = Params(100, 50, 1e4, 1.0 / math.sqrt(d))
+    say("precise decode", d, Hq, Hkv)
+    o, lse = _dec_gpu(q, kc.cuda(), vc.cuda(), lens, p, precise=True)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = _dec_ref(q, kc, vc, lens, p)
+    check_decode(o, lse, o_ref, lse_ref, torch.bfloat16, "precise d=%d" % d)
+    # the same cache as pages of 64 rows in order
+    page = 64
+    npg = (S + page - 1) // page
+    kp = torch.zeros(B * npg * page, Hkv, d, dtype=kc.dtype)
+    vp = torch.zeros_like(kp)
+    for b in range(B):
+        kp[b * npg * page:b * npg * page + S] = kc[b]
+        vp[b * npg * page:b * npg * page + S] = vc[b]
+    bt = torch.arange(B * npg, dtype=torch.int32).view(B, npg)
+    o2, l2 = jl.bifocal_decode_paged(q.cuda(), kp.view(-1, page, Hkv, d).cuda(),
+                                     vp.view(-1, page, Hkv, d).cuda(), bt.cuda(), lens,
+                                     w_pretrained=p.w_pretrained, w_local=p.w_local,
+                                     rope_base=p.rope_base, softmax_scale=p.softmax_scale,
+                                     precise=True, max_seqlen_k=S)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2) and torch.equal(lse, l2)
 
 
 @pytest.mark.parametrize("label,p", [

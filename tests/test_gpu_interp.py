@@ -13,7 +13,7 @@ from long_context_attention_jl_amd import inputs
 from long_context_attention_jl_amd import jetlong as jl
 from long_context_attention_jl_amd.inputs import Params
 
-from _parity import TOL_BF16_LSE, TOL_BF16_O, check_prefill, say
+from _parity import TOL_BF16_LSE, TOL_BF16_O, block_rows, check_decode, check_prefill, say
 
 pytestmark = pytest.mark.gpu
 
@@ -40,14 +40,23 @@ def test_interp_prefill_full(T, Hq, Hkv, d, w_pre, w_local):
     check_prefill(o, lse, o_ref, l_ref, rows, torch.bfloat16, "interp T=%d" % T, o_plain=o_int)
 
 
-def test_interp_prefill_128k_sampled():
+def test_interp_prefill_128k_every_workgroup():
+    """The 128K layer with continuous interpolation: one row of every 256-row
+    block plus the band-edge rows; every fourth row also under integer
+    grouping, which the result must be told apart from."""
     c = inputs.qwen3_8b_128k()
     say("interp prefill", c.name)
     o, lse = jl.bifocal_prefill(c.q.cuda(), c.k.cuda(), c.v.cuda(), **_kw(c.params))
     torch.cuda.synchronize()
-    rows = [0, 5, 2047, 2048, 4097, 40001, 65537, 100003, 131069, 131071]
+    rows = sorted(set(block_rows(c.T)) | {0, 5, 2046, 2047, 2048, 2049, 4097, 40001, 65537,
+                                          100003, 131069, 131071})
     o_ref, l_ref = oracle.prefill(c.q, c.k, c.v, rows=rows, **_kw(c.params))
-    check_prefill(o, lse, o_ref, l_ref, rows, torch.bfloat16, c.name + " interp")
+    o_int = o_ref.copy()
+    o_int[::4], _ = oracle.prefill(c.q, c.k, c.v, rows=rows[::4], **_kw(c.params, 1))
+    mask = np.zeros(len(rows), dtype=bool)
+    mask[::4] = True
+    check_prefill(o, lse, o_ref, l_ref, rows, torch.bfloat16, c.name + " interp",
+                  o_plain=o_int, disc_rows=mask)
 
 
 def test_interp_chunk():

@@ -16,8 +16,8 @@ from long_context_attention_jl_amd import inputs
 from long_context_attention_jl_amd import jetlong as jl
 from long_context_attention_jl_amd.inputs import Params
 
-from _parity import (check_prefill, gpu_prefill, oracle_prefill_rows, sample_rows,
-                     say)
+from _parity import (block_rows, check_prefill, gpu_prefill, oracle_prefill_rows,
+                     sample_rows, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -40,7 +40,8 @@ def test_tiny_f32_workload_full():
     o, lse = gpu_prefill(jl, c.q, c.k, c.v, c.params)
     rows = list(range(c.T))
     o_ref, lse_ref = oracle_prefill_rows(c.q, c.k, c.v, c.params, rows)
-    check_prefill(o, lse, o_ref, lse_ref, rows, torch.float32, c.name)
+    o_pl, _ = oracle_prefill_rows(c.q, c.k, c.v, c.params, rows, bifocal=False)
+    check_prefill(o, lse, o_ref, lse_ref, rows, torch.float32, c.name, o_plain=o_pl)
 
 
 @pytest.mark.parametrize("T,Hq,Hkv,d,w_pre,w_local", [
@@ -52,6 +53,23 @@ def test_tiny_f32_workload_full():
 def test_bf16_small_full(T, Hq, Hkv, d, w_pre, w_local):
     p = Params(w_pre, w_local, 1e4, 1.0 / math.sqrt(d))
     _full_case(T, Hq, Hkv, d, p, seed=T + d)
+
+
+@pytest.mark.parametrize("T,Hq,Hkv,d,w_pre,w_local,cu", [
+    (3000, 4, 1, 128, 1024, 300, None),              # rows >= 2048 in split precision too
+    (2600, 2, 2, 64, 700, 2200, None),
+    (3563, 4, 2, 128, 256, 90, [0, 300, 301, 1000, 3500, 3563]),
+])
+def test_bf16_precise_full(T, Hq, Hkv, d, w_pre, w_local, cu):
+    """Split precision on every row (precise = 1): every row against the oracle."""
+    p = Params(w_pre, w_local, 1e4, 1.0 / math.sqrt(d))
+    q, k, v = inputs.prefill_inputs(T, Hq, Hkv, d, seed=T + d + 1)
+    say("precise T=%d d=%d cu=%s" % (T, d, cu))
+    o, lse = gpu_prefill(jl, q, k, v, p, cu=cu, precise=True)
+    torch.cuda.synchronize()
+    rows = list(range(T))
+    o_ref, lse_ref = oracle_prefill_rows(q, k, v, p, rows, cu=cu)
+    check_prefill(o, lse, o_ref, lse_ref, rows, torch.bfloat16, "precise T=%d" % T)
 
 
 @pytest.mark.parametrize("T,d", [(700, 128), (2300, 64)])
@@ -149,38 +167,79 @@ def test_k_rot_out_is_standard_rope():
     assert np.abs(got - ref).max() <= 2.0 ** -8 * np.abs(ref).max()
 
 
-# ---- the named long-context workloads at full size (sampled rows) -------------
+# ---- the named long-context workloads at full size --------------------------
+# One row of every 256-row block of every sequence (every prefill workgroup,
+# since all heads are compared), plus the band-edge, split-precision and
+# group-boundary rows; the oracle computes them one by one.
 
-def _sampled(case, label, discrimination=False):
-    say("workload", case.name)
-    o, lse = gpu_prefill(jl, case.q, case.k, case.v, case.params, cu=case.cu_seqlens)
-    torch.cuda.synchronize()
-    rows = []
+def _rows_of(case, every=1, n_strided=12):
+    """(rows, mask of rows whose sequence has G > 1)."""
+    rows, big = [], []
     cu = case.cu_seqlens or [0, case.T]
     for a, b in zip(cu[:-1], cu[1:]):
-        G = oracle.group_size(b - a, case.params.w_pretrained)
-        rows += [a + r for r in sample_rows(b - a, case.params.w_local, G, n_strided=12)]
+        L = b - a
+        G = oracle.group_size(L, case.params.w_pretrained)
+        r = set(block_rows(L, a)[::every])
+        r.update(a + x for x in sample_rows(L, case.params.w_local, G, n_strided=n_strided))
+        r = sorted(r)
+        rows += r
+        big += [G > 1] * len(r)
+    return rows, np.array(big, dtype=bool)
+
+
+def _plain_on(case, rows, mask, o_ref):
+    """The oracle's plain-RoPE output on the rows of `mask` (o_ref elsewhere)."""
+    o_plain = o_ref.copy()
+    sel = [r for r, m in zip(rows, mask) if m]
+    if sel:
+        o_pl, _ = oracle_prefill_rows(case.q, case.k, case.v, case.params, sel,
+                                      cu=case.cu_seqlens, bifocal=False)
+        o_plain[mask] = o_pl
+    return o_plain
+
+
+def _full_size(case, label, every=1, o_scale=None, modes=(False,)):
+    """modes: the precise flags to run; the fast path (False) on concentrated
+    attention has its LSE recorded, not asserted (see check_prefill)."""
+    rows, mask = _rows_of(case, every)
+    say("workload", case.name, label, "- comparing %d rows x %d heads" % (len(rows), case.q.shape[1]))
     o_ref, lse_ref = oracle_prefill_rows(case.q, case.k, case.v, case.params, rows,
                                          cu=case.cu_seqlens)
-    o_plain = None
-    if discrimination:
-        o_plain, _ = oracle_prefill_rows(case.q, case.k, case.v, case.params, rows,
-                                         cu=case.cu_seqlens, bifocal=False)
-    check_prefill(o, lse, o_ref, lse_ref, rows, case.q.dtype, label, o_plain=o_plain)
-    return o, lse
+    o_plain = _plain_on(case, rows, mask, o_ref)
+    out = None
+    for precise in modes:
+        o, lse = gpu_prefill(jl, case.q, case.k, case.v, case.params, cu=case.cu_seqlens,
+                             precise=precise)
+        torch.cuda.synchronize()
+        strict = precise or len(modes) == 1
+        check_prefill(o, lse, o_ref, lse_ref, rows, case.q.dtype,
+                      label + (" precise" if precise else ""), o_plain=o_plain, disc_rows=mask,
+                      o_scale=o_scale, check_lse=strict)
+        out = (o, lse) if out is None else out
+        del o, lse
+    return out
 
 
-def test_qwen3_1p7b_65536_sampled():
-    _sampled(inputs.qwen3_1p7b_64k(), "qwen3_1p7b_L65536")
+def test_qwen3_1p7b_65536_every_workgroup():
+    _full_size(inputs.qwen3_1p7b_64k(), "qwen3_1p7b_L65536")
 
 
-def test_qwen3_8b_131072_sampled():
-    _sampled(inputs.qwen3_8b_128k(), "qwen3_8b_L131072", discrimination=True)
+def test_qwen3_8b_131072_every_workgroup():
+    _full_size(inputs.qwen3_8b_128k(), "qwen3_8b_L131072")
 
 
-def test_varlen_4seq_sampled_and_g1_sequences_plain():
+def test_qwen3_8b_131072_peaky():
+    """The 128K layer with q scaled by 4 (scores of standard deviation 4: the
+    softmax concentrates on a few keys, so the fp16 probabilities and the
+    band edge show at the output level).  One row of every 512-row block."""
+    c = inputs.qwen3_8b_128k()
+    c.q = (c.q.float() * 4.0).to(torch.bfloat16)
+    _full_size(c, "qwen3_8b_L131072 q x4", every=2, modes=(True, False))
+
+
+def test_varlen_4seq_every_workgroup_and_g1_sequences_plain():
     c = inputs.varlen_4seq()
-    o, lse = _sampled(c, "varlen_4seq")
+    o, lse = _full_size(c, "varlen_4seq")
     # sequences with G = 1 equal plain RoPE causal attention
     p0 = Params(c.params.w_pretrained, c.params.w_local, c.params.rope_base,
                 c.params.softmax_scale, bifocal=False)
@@ -192,3 +251,55 @@ def test_varlen_4seq_sampled_and_g1_sequences_plain():
     # and the G > 1 sequences differ from plain attention
     a, b = c.cu_seqlens[3], c.cu_seqlens[4]
     assert (lse[:, a:b] - l0[:, a:b]).abs().max().item() > 1e-3
+
+
+def _outlier_case(T, Hq, Hkv, d, seed, params, q_scale, q_small):
+    q, k, v = inputs.prefill_inputs(T, Hq, Hkv, d, seed=seed, q_scale=q_scale)
+    q, k, v = inputs.with_outlier_channels(q, k, v, seed=seed + 1, q_small=q_small)
+    q, k, v = inputs.to_dtype(torch.bfloat16, q, k, v)
+    scale = np.ones(d)
+    vmax = v.float().abs().amax(dim=(0, 1)).double().numpy()
+    for c in inputs.outlier_value_channels(d):
+        scale[c] = vmax[c]
+    return q, k, v, scale
+
+
+@pytest.mark.parametrize("T,Hq,Hkv,d,w_pre,w_local", [
+    (3000, 4, 2, 128, 1024, 300),  # both kernels (rows below and above 2048), ragged tail
+    (1300, 2, 1, 64, 400, 100),
+])
+def test_large_magnitude_channels_full(T, Hq, Hkv, d, w_pre, w_local):
+    """Keys with an outlier channel up to 3e4 and values with outlier channels
+    up to 6e4 (near the fp16 operand limit of 65504), every row compared.
+    The value channels' bar scales with their magnitude (attention is linear
+    in v channel by channel).  Split precision meets every bar; the fast path
+    meets the output bars (its LSE error is recorded)."""
+    p = Params(w_pre, w_local, 1e4, 1.0)
+    q, k, v, scale = _outlier_case(T, Hq, Hkv, d, 40 + d, p, 1.0 / math.sqrt(d), 7.0e-5)
+    say("outliers T=%d d=%d max|k|=%.0f max|v|=%.0f" % (
+        T, d, k.float().abs().max().item(), v.float().abs().max().item()))
+    rows = list(range(T))
+    o_ref, lse_ref = oracle_prefill_rows(q, k, v, p, rows)
+    o_pl, _ = oracle_prefill_rows(q, k, v, p, rows, bifocal=False)
+    for precise in (True, False):
+        o, lse = gpu_prefill(jl, q, k, v, p, precise=precise)
+        torch.cuda.synchronize()
+        check_prefill(o, lse, o_ref, lse_ref, rows, torch.bfloat16,
+                      "outliers T=%d%s" % (T, " precise" if precise else ""), o_plain=o_pl,
+                      o_scale=scale, check_lse=precise)
+
+
+def test_large_magnitude_channels_128k():
+    """The 128K layer's shape with outlier key and value channels: one row of
+    every 1024-row block plus the band-edge rows."""
+    base = inputs.qwen3_8b_128k()
+    q, k, v = inputs.with_outlier_channels(base.q, base.k, base.v, seed=303, q_small=7.0e-5)
+    q, k, v = inputs.to_dtype(torch.bfloat16, q, k, v)
+    case = inputs.PrefillCase(base.name + "_outliers", q, k, v, None, base.params)
+    del base
+    scale = np.ones(q.shape[2])
+    vmax = v.float().abs().amax(dim=(0, 1)).double().numpy()
+    for c in inputs.outlier_value_channels(q.shape[2]):
+        scale[c] = vmax[c]
+    _full_size(case, "qwen3_8b_L131072 outlier channels", every=4, o_scale=scale,
+               modes=(True, False))

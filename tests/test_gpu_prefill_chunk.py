@@ -161,3 +161,18 @@ def test_chunk_1024_rows_key_split_128k():
     rows = [0, 1, 255, 256, 511, 700, 1022, 1023]
     o_ref, lse_ref = _oracle(q, kc, vc, [131072], None, p, rows=rows)
     check_prefill(o, lse, o_ref, lse_ref, rows, torch.bfloat16, "chunk1024 split")
+
+
+def test_chunk_precise_full_rows_and_key_split_off():
+    """Split precision (precise = 1) on a chunk whose rows cross 2048 and on a
+    1024-row chunk of a long cache (which would otherwise split its keys in
+    shares): every row against the oracle."""
+    for L, C, Hq, Hkv, d, w_pre, w_local in ((3100, 1500, 4, 2, 128, 1000, 300),
+                                              (9000, 1024, 32, 8, 128, 2048, 700)):
+        p = Params(w_pre, w_local, 1e4, 1.0 / math.sqrt(d))
+        q, kc, vc, _ = inputs.chunk_inputs([C], [L], L, Hq, Hkv, d, seed=L + C + 3)
+        say("precise chunk L=%d C=%d" % (L, C))
+        o, lse = _gpu(q, kc, vc, [L], None, p, precise=True)
+        o_ref, lse_ref = _oracle(q, kc, vc, [L], None, p)
+        check_prefill(o, lse, o_ref, lse_ref, list(range(C)), torch.bfloat16,
+                      "precise chunk L=%d C=%d" % (L, C))

@@ -13,7 +13,7 @@ from long_context_attention_jl_amd import inputs
 from long_context_attention_jl_amd import jetlong as jl
 from long_context_attention_jl_amd.inputs import Params
 
-from _parity import check_prefill, oracle_prefill_rows, sample_rows, say
+from _parity import block_rows, check_prefill, oracle_prefill_rows, sample_rows, say
 
 pytestmark = pytest.mark.gpu
 
@@ -77,14 +77,21 @@ def test_three_call_varlen_small():
     check_prefill(o, lse, o_ref, lse_ref, rows, torch.bfloat16, "three-call varlen")
 
 
-def test_three_call_qwen3_8b_131072_sampled():
-    """The 128K layer (G = 4) in the benchmark's shape: sampled rows against the
-    oracle."""
+def test_three_call_qwen3_8b_131072_every_workgroup():
+    """The 128K layer (G = 4) in the benchmark's shape: one row of every
+    256-row block (every workgroup of the three calls) plus the band-edge and
+    group-boundary rows, against the oracle's direct form."""
     c = inputs.qwen3_8b_128k()
     p = c.params
     say("three-call", c.name)
     o, lse = _three(c.q, c.k, c.v, p)
     torch.cuda.synchronize()
-    rows = sample_rows(c.T, p.w_local, 4, n_strided=24)
+    rows = sorted(set(block_rows(c.T)) | set(sample_rows(c.T, p.w_local, 4, n_strided=24)))
     o_ref, lse_ref = oracle_prefill_rows(c.q, c.k, c.v, p, rows)
-    check_prefill(o, lse, o_ref, lse_ref, rows, torch.bfloat16, "three-call " + c.name)
+    o_pl, _ = oracle_prefill_rows(c.q, c.k, c.v, p, rows[::4], bifocal=False)
+    o_plain = o_ref.copy()
+    o_plain[::4] = o_pl
+    mask = np.zeros(len(rows), dtype=bool)
+    mask[::4] = True
+    check_prefill(o, lse, o_ref, lse_ref, rows, torch.bfloat16, "three-call " + c.name,
+                  o_plain=o_plain, disc_rows=mask)
