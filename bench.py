@@ -371,7 +371,7 @@ def bench_decode(jl, inputs, torch, iters, extras=True):
     copies = [(c.k_cache.cuda(), c.v_cache.cuda()) for _ in range(4)]
     q = c.q.cuda()
     sl = torch.tensor(c.seqlens, dtype=torch.int32, device="cuda")
-    ws = torch.zeros(jl.decode_workspace_bytes(B, L, Hq, Hkv, d, q.dtype), dtype=torch.uint8,
+    ws = torch.empty(jl.decode_workspace_bytes(B, L, Hq, Hkv, d, q.dtype), dtype=torch.uint8,
                      device="cuda")
     o = torch.empty_like(q)
     lse = torch.empty((B, Hq), dtype=torch.float32, device="cuda")
@@ -511,7 +511,7 @@ def bench_decode(jl, inputs, torch, iters, extras=True):
 
     queries, kc16, vc16, lens16, p16 = inputs.decode_16step_cache()
     copies16 = [(kc16.cuda(), vc16.cuda()) for _ in range(4)]
-    ws16 = torch.zeros(jl.decode_workspace_bytes(1, max(lens16), Hq, Hkv, d, q.dtype),
+    ws16 = torch.empty(jl.decode_workspace_bytes(1, max(lens16), Hq, Hkv, d, q.dtype),
                        dtype=torch.uint8, device="cuda")
 
     def run16(qs, L16, bifocal, n):

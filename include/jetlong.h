@@ -183,16 +183,8 @@ jl_status jl_bifocal_prefill_three_call(void* o, float* lse, const void* q, cons
                                         int32_t d, const jl_params* params, jl_dtype dtype,
                                         void* workspace, size_t workspace_bytes, void* stream);
 
-/*
- * Bytes of device workspace jl_bifocal_decode (and the paged and fp8 decode
- * calls) need for these sizes.  The workspace must be zero-filled before its
- * first decode call: bf16 decode merges its key chunks inside the split
- * kernel, the last workgroup of each group of chunks being found with
- * counters kept at the start of the workspace.  Every decode call leaves
- * those counters at zero again, so a workspace that only decode calls use is
- * zeroed once (e.g. hipMemset at allocation); one shared with other entry
- * points must be zeroed again before the next decode call.
- */
+/* Bytes of device workspace jl_bifocal_decode (and the paged and fp8 decode
+ * calls) need for these sizes: the split partials of the key chunks. */
 jl_status jl_bifocal_decode_workspace(int32_t batch, int32_t max_seqlen_k, int32_t Hq,
                                       int32_t Hkv, int32_t d, jl_dtype dtype, size_t* bytes);
 
@@ -211,8 +203,7 @@ jl_status jl_bifocal_decode_workspace(int32_t batch, int32_t max_seqlen_k, int32
  *   q          raw (un-rotated) query [B][Hq][d].
  *   k_cache, v_cache  [B][S_max][Hkv][d] of dtype, read-only.
  *   seqlens_k  device int32 [B], 1 <= L_b <= max_seqlen_k <= S_max.
- *   workspace  at least jl_bifocal_decode_workspace() bytes, zero-filled
- *              before its first decode call (see there); otherwise scratch.
+ *   workspace  at least jl_bifocal_decode_workspace() bytes (scratch).
  * Supported: dtype bf16 or f32 (bf16 only for params->bifocal == 2), d in {64, 128},
  * Hq / Hkv <= 16.  The bf16 path forms q k^T on fp16 MFMA operands and P v on
  * bf16 ones (fp32 accumulate): the rotated query (times softmax_scale *

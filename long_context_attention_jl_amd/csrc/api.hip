@@ -146,22 +146,11 @@ DecodeLayout decode_layout(int32_t B, int32_t max_seqlen_k, int32_t Hq, int32_t 
     if (b16 && chunk > (int64_t)kDecodeMaxStagesB * stage) chunk = (int64_t)kDecodeMaxStagesB * stage;
     L.chunk = (int32_t)chunk;
     L.n_splits = (int32_t)((span + chunk - 1) / chunk);
-    L.groups = (int32_t)groups;
-    L.nbins = (L.n_splits + kDecodeBin - 1) / kDecodeBin;
     size_t off = 0;
-    L.tickets = off;
-    L.ticket_bytes = (size_t)B * groups * (L.nbins + 1) * sizeof(uint32_t);
-    off = align256(off + L.ticket_bytes);
     L.part_ml = off;
     off = align256(off + (size_t)B * L.n_splits * Hq * 4 * sizeof(float));
     L.part_o = off;
     off = align256(off + (size_t)B * L.n_splits * Hq * d * sizeof(float));
-    if (L.nbins > 1) {
-        L.part2_ml = off;
-        off = align256(off + (size_t)B * L.nbins * Hq * 4 * sizeof(float));
-        L.part2_o = off;
-        off = align256(off + (size_t)B * L.nbins * Hq * d * sizeof(float));
-    }
     L.total = off;
     return L;
 }

@@ -443,185 +443,6 @@ void decode_split_kernel(DecodeArgs a) {
         }
 }
 
-// ---------------------------------------------------------------------------
-// Merging split partials inside the split kernel ([TW] §四's LogSumExp
-// combination of partial attentions).  A partial of query head h holds
-// (m, l_o, l_lse) and the unnormalised O, all relative to 2^m (log2 units):
-// l_o sums the probabilities exactly as rounded for the P V product, so
-// O / l_o is a consistent weighted mean; l_lse sums them before rounding and
-// gives the LSE.  Merging n partials: M = max m_c, w_c = 2^(m_c - M),
-// O = sum w_c O_c, l = sum w_c l_c.
-
-// Merges partials c = 0..n-1 of the nh query heads starting at `ml` / `po`
-// (partial c of head h at ml[c * Hq + h], its O at po[(c * Hq + h) * D]),
-// kDecodeBin partials at a time with a running max.  If `final`, writes
-// o = O / l_o (TOUT) and lse = (M + log2 l_lse) ln 2 for those heads at
-// `o` / `lse`; otherwise the merged partial at out_ml[h], out_o[h * D].
-// Called by a whole workgroup; `lds` holds at least (kDecodeBin + 5) * nh
-// floats.
-template <int D>
-__device__ void merge_partials(const float4* __restrict__ ml, const float* __restrict__ po, int Hq,
-                               int n, int nh, bool final, float4* out_ml, float* out_o, void* o,
-                               bool o_f32, float* lse, float* lds) {
-    constexpr int NB = kDecodeBin;
-    constexpr int Q = D / 4;  // 4-wide d slices per head
-    float* sw = lds;                 // [NB][nh] weights within the group
-    float* sM = lds + NB * nh;       // [nh] running max
-    float* sLo = sM + nh;            // [nh] running l_o, l_lse
-    float* sLl = sLo + nh;
-    float* sA = sLl + nh;            // [nh] rescale of the running sums
-    float* sB = sA + nh;             // [nh] scale of the group's sums
-    const int tid = threadIdx.x, nt = blockDim.x;
-    const int items = nh * Q;
-    for (int base = 0; base < items; base += 2 * nt) {
-        float4 acc[2] = {make_float4(0.0f, 0.0f, 0.0f, 0.0f), make_float4(0.0f, 0.0f, 0.0f, 0.0f)};
-        for (int g0 = 0; g0 < n; g0 += NB) {
-            const int ng = min(NB, n - g0);
-            // the group's O loads go out before its weights are formed, so
-            // the two round trips overlap
-            float4 ov[2][NB];
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                const int it = min(base + tid + u * nt, items - 1);
-                const int h = it / Q, x = 4 * (it % Q);
-#pragma unroll
-                for (int c = 0; c < NB; ++c) {
-                    const int cc = g0 + min(c, ng - 1);
-                    ov[u][c] = *reinterpret_cast<const float4*>(po + ((int64_t)cc * Hq + h) * D + x);
-                }
-            }
-            // weights: 16 consecutive lanes per head, lane c holds partial g0 + c
-            for (int t = tid; t < nh * NB; t += nt) {
-                const int h = t / NB, c = t % NB;
-                float4 v = make_float4(-INFINITY, 0.0f, 0.0f, 0.0f);
-                if (c < ng) v = ml[(int64_t)(g0 + c) * Hq + h];
-                float Mg = v.x;
-#pragma unroll
-                for (int sh = 1; sh < NB; sh <<= 1) Mg = fmaxf(Mg, __shfl_xor(Mg, sh));
-                const float w = (v.x == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(v.x - Mg);
-                float lo = w * v.y, ll = w * v.z;
-#pragma unroll
-                for (int sh = 1; sh < NB; sh <<= 1) {
-                    lo += __shfl_xor(lo, sh);
-                    ll += __shfl_xor(ll, sh);
-                }
-                sw[c * nh + h] = w;
-                if (c == 0) {
-                    const float Mo = g0 == 0 ? -INFINITY : sM[h];
-                    const float Mn = fmaxf(Mo, Mg);
-                    const float ao = Mo == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(Mo - Mn);
-                    const float bg = Mg == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(Mg - Mn);
-                    sM[h] = Mn;
-                    sLo[h] = (g0 == 0 ? 0.0f : sLo[h]) * ao + lo * bg;
-                    sLl[h] = (g0 == 0 ? 0.0f : sLl[h]) * ao + ll * bg;
-                    sA[h] = ao;
-                    sB[h] = bg;
-                }
-            }
-            __syncthreads();
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                const int it = min(base + tid + u * nt, items - 1);
-                const int h = it / Q;
-                float4 gs = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-#pragma unroll
-                for (int c = 0; c < NB; ++c) {
-                    const float w = c < ng ? sw[c * nh + h] : 0.0f;
-                    gs.x += w * ov[u][c].x;
-                    gs.y += w * ov[u][c].y;
-                    gs.z += w * ov[u][c].z;
-                    gs.w += w * ov[u][c].w;
-                }
-                const float ao = sA[h], bg = sB[h];
-                acc[u].x = acc[u].x * ao + gs.x * bg;
-                acc[u].y = acc[u].y * ao + gs.y * bg;
-                acc[u].z = acc[u].z * ao + gs.z * bg;
-                acc[u].w = acc[u].w * ao + gs.w * bg;
-            }
-            __syncthreads();
-        }
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int it = base + tid + u * nt;
-            if (it >= items) continue;
-            const int h = it / Q, x = 4 * (it % Q);
-            if (!final) {
-                *reinterpret_cast<float4*>(out_o + (int64_t)h * D + x) = acc[u];
-                if (x == 0) out_ml[h] = make_float4(sM[h], sLo[h], sLl[h], 0.0f);
-                continue;
-            }
-            const float lo = sLo[h];
-            const float inv = lo > 0.0f ? 1.0f / lo : 0.0f;
-            const float4 r = make_float4(acc[u].x * inv, acc[u].y * inv, acc[u].z * inv,
-                                         acc[u].w * inv);
-            if (o_f32) {
-                *reinterpret_cast<float4*>((float*)o + (int64_t)h * D + x) = r;
-            } else {
-                const bf16x4 rb = {(bf16)r.x, (bf16)r.y, (bf16)r.z, (bf16)r.w};
-                *reinterpret_cast<bf16x4*>((bf16*)o + (int64_t)h * D + x) = rb;
-            }
-            if (x == 0) lse[h] = sLl[h] > 0.0f ? (sM[h] + log2f(sLl[h])) * kLn2 : -INFINITY;
-        }
-        __syncthreads();  // the next round rewrites the sums read above
-    }
-}
-
-// Called by every thread of a split workgroup once its partials are written:
-// draws this chunk's ticket of its bin; the workgroup holding the bin's last
-// ticket merges the bin (and, with one bin, writes the output), then draws
-// the (sequence, group) ticket; the holder of its last ticket merges the
-// bins.  A ticket holder that sees the final count resets the counter, so
-// every counter is zero again when the kernel ends.  Release and acquire
-// fences at agent scope order the partials' stores before the counter
-// update and the merger's loads after it (the compute units of different
-// XCDs do not share an L2).
-template <int D>
-__device__ void merge_by_tickets(const DecodeArgs& a, int b, int g, int split, int h0, int nh,
-                                 float* lds) {
-    __shared__ int s_last;
-    const DecodeLayout& L = a.lay;
-    uint32_t* tk = (uint32_t*)((char*)a.ws + L.tickets) + ((int64_t)b * L.groups + g) * (L.nbins + 1);
-    const int bin = split / kDecodeBin;
-    const int nin = min(kDecodeBin, L.n_splits - bin * kDecodeBin);
-    auto draw = [&](uint32_t* ctr, int count) __attribute__((always_inline)) -> bool {
-        __threadfence();
-        __syncthreads();
-        if (threadIdx.x == 0) {
-            const uint32_t old = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED,
-                                                        __HIP_MEMORY_SCOPE_AGENT);
-            const int last = old == (uint32_t)(count - 1);
-            if (last) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            s_last = last;
-        }
-        __syncthreads();
-        const bool last = s_last != 0;
-        if (last) __threadfence();
-        return last;
-    };
-    if (!draw(tk + bin, nin)) return;
-    const float4* pm = (const float4*)((const char*)a.ws + L.part_ml);
-    const float* po = (const float*)((const char*)a.ws + L.part_o);
-    const size_t osz = a.o_f32 ? sizeof(float) : sizeof(bf16);
-    void* o = (char*)a.o + ((int64_t)b * a.Hq * D + (int64_t)h0 * D) * osz;
-    float* lse = a.lse + (int64_t)b * a.Hq + h0;
-    const int64_t c0 = (int64_t)b * L.n_splits + (int64_t)bin * kDecodeBin;
-    if (L.nbins == 1) {
-        merge_partials<D>(pm + c0 * a.Hq + h0, po + (c0 * a.Hq + h0) * D, a.Hq, nin, nh, true,
-                          nullptr, nullptr, o, a.o_f32, lse, lds);
-        return;
-    }
-    float4* pm2 = (float4*)((char*)a.ws + L.part2_ml);
-    float* po2 = (float*)((char*)a.ws + L.part2_o);
-    const int64_t c2 = (int64_t)b * L.nbins + bin;
-    merge_partials<D>(pm + c0 * a.Hq + h0, po + (c0 * a.Hq + h0) * D, a.Hq, nin, nh, false,
-                      pm2 + c2 * a.Hq + h0, po2 + (c2 * a.Hq + h0) * D, nullptr, false, nullptr,
-                      lds);
-    if (!draw(tk + L.nbins, L.nbins)) return;
-    const int64_t b0 = (int64_t)b * L.nbins;
-    merge_partials<D>(pm2 + b0 * a.Hq + h0, po2 + (b0 * a.Hq + h0) * D, a.Hq, L.nbins, nh, true,
-                      nullptr, nullptr, o, a.o_f32, lse, lds);
-}
-
 // OCP E4M3 codes (4 per 32-bit word, little-endian) widened exactly; the
 // hardware conversion v_cvt_pk_f32_fp8 reads E4M3 in this format on gfx950.
 __device__ __forceinline__ void e4m3x8_to_f32(uint32_t w0, uint32_t w1, float* f) {
@@ -754,16 +575,13 @@ __global__ __launch_bounds__(512) void decode_split_bf16_kernel(DecodeArgs a) {
     float4* pm = (float4*)((char*)a.ws + a.lay.part_ml);
     float* po = (float*)((char*)a.ws + a.lay.part_o);
     const int64_t pbase = ((int64_t)b * a.lay.n_splits + split) * a.Hq + (int64_t)kvh * grp;
-    // query heads of this workgroup (its kv heads' groups)
-    const int h0 = blockIdx.y * nw * grp;
-    const int nh = min(nw, a.Hkv - (int)blockIdx.y * nw) * grp;
-
-    if (kbeg >= kend) {  // empty chunk: neutral partial, then its ticket
+    if (kbeg >= kend) {  // empty chunk: neutral partial
         if (head_ok) {
             if (c == 0 && n < grp) pm[pbase + n] = make_float4(-INFINITY, 0.0f, 0.0f, 0.0f);
             for (int x = lane; x < grp * D; x += 64) po[pbase * D + x] = 0.0f;
         }
-    } else {
+        return;
+    }
 
     // every load below is unconditional (branch-free memory stream, exact
     // waits): indices are clamped to valid rows, masked keys weigh 0
@@ -891,7 +709,7 @@ __global__ __launch_bounds__(512) void decode_split_bf16_kernel(DecodeArgs a) {
         }
         __syncthreads();
     }
-    if (head_ok) {
+    if (!head_ok) return;
     load_k(kbeg + kTile, kB);
     load_vr(kbeg + kTile, vB);
 
@@ -1127,22 +945,26 @@ __global__ __launch_bounds__(512) void decode_split_bf16_kernel(DecodeArgs a) {
             for (int bd = 0; bd < NDB; ++bd)
                 po[(pbase + 4 * c + i) * D + 16 * bd + n] = FP8 ? O[bd][i] * vscale : O[bd][i];
         }
-    }  // head_ok
-    }  // non-empty chunk
-
-    // ---- the last workgroup of the bin (and then of the sequence) merges ----
-    merge_by_tickets<D>(a, b, blockIdx.y, split, h0, nh, (float*)vs);
 }
 
-// Merge of the chunk partials: o = sum 2^(m_c - M) O_c / sum 2^(m_c - M) l_c,
-// lse = (M + log2 sum ...) ln 2 -- the LogSumExp combination of [TW] §四.
-// Workgroup (head, sequence, 16-wide slice of d), 256 threads = 64 chunk
-// groups x 4 quads of d.  Each thread folds its chunks (loaded together)
-// against their common max; the 16 groups of a wave are folded with lane
-// shuffles and the 4 waves through LDS.  A sequence with no keys gets o = 0
-// and lse = -inf.
+// Merge of the chunk partials ([TW] §四's LogSumExp combination): with m_c
+// in log2 units, o = sum 2^(m_c - M) O_c / sum 2^(m_c - M) lo_c and
+// lse = (M + log2 sum 2^(m_c - M) ll_c) ln 2, where lo_c sums a chunk's
+// probabilities as its P V product used them (so o is a consistent weighted
+// mean) and ll_c sums them before any rounding (bf16 caches; the two agree
+// for fp32 caches).  Workgroup (head, sequence, 16-wide slice of d), 256
+// threads = 64 chunk groups x 4 quads of d.  Each thread folds its chunks
+// (loaded together) against their common max; the 16 groups of a wave are
+// folded with lane shuffles and the 4 waves through LDS.  A sequence with no
+// keys gets o = 0 and lse = -inf.
+//
+// A merge inside the split kernel (the last workgroup of each group of
+// chunks merging them, found with counters) was measured slower: the
+// compute units of different XCDs do not share an L2, so handing partials
+// across XCDs costs L2 write-back / invalidate or uncached loads on the
+// critical path, more than this launch costs.
 struct MergeAcc {
-    float m, l;
+    float m, lo, ll;
     f32x4 o;
 };
 // (m, l, o) of two disjoint key sets -> their union; m = -inf is the empty set
@@ -1150,63 +972,65 @@ __device__ __forceinline__ MergeAcc merge_acc(const MergeAcc& x, const MergeAcc&
     const float m = fmaxf(x.m, y.m);
     if (m == -INFINITY) return x;
     const float sx = __builtin_amdgcn_exp2f(x.m - m), sy = __builtin_amdgcn_exp2f(y.m - m);
-    return MergeAcc{m, sx * x.l + sy * y.l, sx * x.o + sy * y.o};
+    return MergeAcc{m, sx * x.lo + sy * y.lo, sx * x.ll + sy * y.ll, sx * x.o + sy * y.o};
 }
 
 template <typename TOUT>
 __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
     constexpr int NG = 64, NB = 4;  // chunk groups; chunks per group per round
-    __shared__ float sm[4][4], sl[4][4];
+    __shared__ float sm[4][4], slo[4][4], sll[4][4];
     __shared__ f32x4 so[4][4];
     const int head = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
     const int g = tid >> 2, q4 = tid & 3, wave = tid >> 6;
     const int x0 = 16 * blockIdx.z + 4 * q4;
-    const float* pm = (const float*)((const char*)a.ws + a.lay.part_ml);
+    const float4* pm = (const float4*)((const char*)a.ws + a.lay.part_ml);
     const float* po = (const float*)((const char*)a.ws + a.lay.part_o);
     const int ns = a.lay.n_splits;
     const int64_t base = (int64_t)b * ns * a.Hq + head;
-    MergeAcc acc{-INFINITY, 0.0f, f32x4{}};
+    MergeAcc acc{-INFINITY, 0.0f, 0.0f, f32x4{}};
     for (int s0 = g; s0 < ns; s0 += NG * NB) {
-        float2 ml[NB];
+        float4 ml[NB];
         f32x4 ov[NB];
 #pragma unroll
         for (int k = 0; k < NB; ++k) {
             const int sp = min(s0 + NG * k, ns - 1);
             const int64_t idx = base + (int64_t)sp * a.Hq;
-            const float4 v = *(const float4*)(pm + 4 * idx);
-            ml[k] = make_float2(v.x, v.y);
+            ml[k] = pm[idx];
             ov[k] = *(const f32x4*)(po + idx * a.d + x0);
         }
 #pragma unroll
         for (int k = 0; k < NB; ++k)
-            if (s0 + NG * k < ns) acc = merge_acc(acc, MergeAcc{ml[k].x, ml[k].y, ov[k]});
+            if (s0 + NG * k < ns) acc = merge_acc(acc, MergeAcc{ml[k].x, ml[k].y, ml[k].z, ov[k]});
     }
     // groups g of a wave differ in lane bits 2..5
 #pragma unroll
     for (int sh = 4; sh < 64; sh <<= 1) {
         MergeAcc y;
         y.m = __shfl_xor(acc.m, sh);
-        y.l = __shfl_xor(acc.l, sh);
+        y.lo = __shfl_xor(acc.lo, sh);
+        y.ll = __shfl_xor(acc.ll, sh);
 #pragma unroll
         for (int i = 0; i < 4; ++i) y.o[i] = __shfl_xor(acc.o[i], sh);
         acc = merge_acc(acc, y);
     }
     if ((tid & 63) < 4) {
         sm[wave][q4] = acc.m;
-        sl[wave][q4] = acc.l;
+        slo[wave][q4] = acc.lo;
+        sll[wave][q4] = acc.ll;
         so[wave][q4] = acc.o;
     }
     __syncthreads();
     if (tid < 4) {
 #pragma unroll
-        for (int w = 1; w < 4; ++w) acc = merge_acc(acc, MergeAcc{sm[w][q4], sl[w][q4], so[w][q4]});
-        const bool empty = !(acc.l > 0.0f);
-        const float inv = empty ? 0.0f : 1.0f / acc.l;
+        for (int w = 1; w < 4; ++w)
+            acc = merge_acc(acc, MergeAcc{sm[w][q4], slo[w][q4], sll[w][q4], so[w][q4]});
+        const float inv = acc.lo > 0.0f ? 1.0f / acc.lo : 0.0f;
         TOUT* o = (TOUT*)a.o + ((int64_t)b * a.Hq + head) * a.d + x0;
 #pragma unroll
         for (int i = 0; i < 4; ++i) o[i] = (TOUT)(acc.o[i] * inv);
         if (blockIdx.z == 0 && q4 == 0)
-            a.lse[(int64_t)b * a.Hq + head] = empty ? -INFINITY : (acc.m + log2f(acc.l)) * kLn2;
+            a.lse[(int64_t)b * a.Hq + head] =
+                acc.ll > 0.0f ? (acc.m + log2f(acc.ll)) * kLn2 : -INFINITY;
     }
 }
 
@@ -1255,9 +1079,12 @@ static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t s) {
     if (grp <= 4) err = launch_decode_g<D, TIN, 4>(a, s);
     else if (grp <= 8) err = launch_decode_g<D, TIN, 8>(a, s);
     else err = launch_decode_g<D, TIN, 16>(a, s);
-    if (err != hipSuccess || sizeof(TIN) == 2) return err;  // bf16: merged in the split kernel
+    if (err != hipSuccess) return err;
     LaunchScope scope("decode_merge", s);
-    hipLaunchKernelGGL(decode_merge_kernel<TIN>, dim3(a.Hq, a.B, D / 16), dim3(256), 0, s, a);
+    if (a.o_f32)  // float32 output (the unfused decode's intermediates)
+        hipLaunchKernelGGL(decode_merge_kernel<float>, dim3(a.Hq, a.B, D / 16), dim3(256), 0, s, a);
+    else
+        hipLaunchKernelGGL(decode_merge_kernel<TIN>, dim3(a.Hq, a.B, D / 16), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 

@@ -39,25 +39,13 @@ constexpr int kDecodeMaxStagesB = 32;
 // most this many pages
 constexpr int kDecodeMaxPages = (kDecodeMaxStagesB * kDecodeStageB + kDecodeStageB - 1) / 16 + 2;
 
-// Decode workspace.  Each (sequence, kv-head group) owns n_splits key chunks,
-// grouped in bins of up to kDecodeBin consecutive chunks.  The last workgroup
-// of a bin to finish merges the bin's partials into one level-2 partial; the
-// last bin to finish merges those into the output.  "Last" is decided with
-// counters (tickets) at the start of the workspace: one per bin plus one per
-// (sequence, group), zero before a call and reset to zero by the workgroup
-// that draws the final ticket.
-constexpr int kDecodeBin = 16;
+// Decode workspace: per (sequence, key chunk, query head) a partial
+// (m, l_o, l_lse) and the unnormalised O, merged by a second kernel.
 struct DecodeLayout {
     int32_t n_splits;
     int32_t chunk;
-    int32_t groups;  // kv-head groups (workgroups along grid y)
-    int32_t nbins;   // bins of kDecodeBin chunks per (sequence, group)
-    size_t tickets;  // uint32 [B][groups][nbins + 1] (offset 0)
-    size_t ticket_bytes;
     size_t part_ml;  // float4 (m, l_o, l_lse, 0) [B][n_splits][Hq]
-    size_t part_o;   // float [B][n_splits][Hq][d]: unnormalised O
-    size_t part2_ml; // level-2 partials [B][nbins][Hq] (nbins > 1)
-    size_t part2_o;  // [B][nbins][Hq][d]
+    size_t part_o;   // float [B][n_splits][Hq][d]
     size_t total;
 };
 DecodeLayout decode_layout(int32_t batch, int32_t max_seqlen_k, int32_t Hq, int32_t Hkv, int32_t d,

@@ -277,24 +277,11 @@ def prefill_workspace_bytes(T: int, n_seqs: int, Hq: int, Hkv: int, d: int, dtyp
     return n.value
 
 
-def _workspace(nbytes: int, device, ws: Optional[torch.Tensor], zeroed: bool = False) -> torch.Tensor:
-    """The caller's workspace if it is large enough, else a new one (256-byte
-    aligned: torch's caching allocator aligns to at least 512 bytes).  Decode
-    workspaces hold ticket counters that must be zero before the first call;
-    every decode call leaves them zero, so a workspace kept for decode calls
-    is zeroed once, when it is made."""
+def _workspace(nbytes: int, device, ws: Optional[torch.Tensor]) -> torch.Tensor:
     if ws is not None and ws.numel() * ws.element_size() >= nbytes:
         return ws
-    if zeroed:
-        return torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
+    # 256-byte aligned (torch's caching allocator aligns to at least 512 bytes)
     return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
-
-
-def decode_workspace(B: int, max_seqlen_k: int, Hq: int, Hkv: int, d: int, dtype,
-                     device="cuda") -> torch.Tensor:
-    """A zero-filled decode workspace for these sizes, to keep across calls."""
-    return torch.zeros(max(decode_workspace_bytes(B, max_seqlen_k, Hq, Hkv, d, dtype), 256),
-                       dtype=torch.uint8, device=device)
 
 
 def _varlen(cu_seqlens, max_seqlen, T: int, dev):
@@ -415,7 +402,7 @@ def bifocal_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor
     o = out if out is not None else torch.empty_like(q)
     lse = lse_out if lse_out is not None else torch.empty((B, Hq), dtype=torch.float32, device=dev)
     nbytes = decode_workspace_bytes(B, int(max_seqlen_k), Hq, Hkv, d, q.dtype)
-    ws = _workspace(nbytes, dev, workspace, zeroed=True)
+    ws = _workspace(nbytes, dev, workspace)
     p = _params(w_pretrained, w_local, rope_base, softmax_scale, bifocal, precise)
     _check(lib().jl_bifocal_decode(
         _dev(o, "o"), _dev(lse, "lse"), _dev(q, "q"), _dev(k_cache, "k_cache"),
@@ -459,8 +446,7 @@ def bifocal_decode_paged(q: torch.Tensor, k_pages: torch.Tensor, v_pages: torch.
     bt = block_table.to(device=dev, dtype=torch.int32).contiguous()
     o = out if out is not None else torch.empty_like(q)
     lse = lse_out if lse_out is not None else torch.empty((B, Hq), dtype=torch.float32, device=dev)
-    ws = _workspace(decode_workspace_bytes(B, max_seqlen_k, Hq, Hkv, d, q.dtype), dev, workspace,
-                    zeroed=True)
+    ws = _workspace(decode_workspace_bytes(B, max_seqlen_k, Hq, Hkv, d, q.dtype), dev, workspace)
     p = _params(w_pretrained, w_local, rope_base, softmax_scale, bifocal, precise)
     _check(lib().jl_bifocal_decode_paged(
         _dev(o, "o"), _dev(lse, "lse"), _dev(q, "q"), _dev(k_pages, "k_pages"),
@@ -619,7 +605,7 @@ def bifocal_decode_fp8(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Te
     o = out if out is not None else torch.empty_like(q)
     lse = lse_out if lse_out is not None else torch.empty((B, Hq), dtype=torch.float32, device=dev)
     ws = _workspace(decode_workspace_bytes(B, max_seqlen_k, Hq, Hkv, d, torch.bfloat16), dev,
-                    workspace, zeroed=True)
+                    workspace)
     p = _params(w_pretrained, w_local, rope_base, softmax_scale, bifocal)
     if block_table is None:
         _check(lib().jl_bifocal_decode_fp8(

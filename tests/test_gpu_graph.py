@@ -51,7 +51,7 @@ def test_graph_decode():
     q, kc, vc = inputs.decode_inputs(B, S, Hq, Hkv, d, seed=41)
     q, kc, vc = q.cuda(), kc.cuda(), vc.cuda()
     sl = torch.tensor([3000, 1777], dtype=torch.int32, device="cuda")
-    ws = torch.zeros(jl.decode_workspace_bytes(B, S, Hq, Hkv, d, q.dtype), dtype=torch.uint8,
+    ws = torch.empty(jl.decode_workspace_bytes(B, S, Hq, Hkv, d, q.dtype), dtype=torch.uint8,
                      device="cuda")
     o = torch.empty_like(q)
     lse = torch.empty((B, Hq), dtype=torch.float32, device="cuda")
