@@ -217,6 +217,28 @@ jl_status jl_bifocal_decode(void* o, float* lse, const void* q, const void* k_ca
                             size_t workspace_bytes, void* stream);
 
 /*
+ * jl_bifocal_decode without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Same arguments, results and kernels as
+ * jl_bifocal_decode; the split partials live in a static device array of
+ * the library (32 MiB per device, held until the
+ * process ends).  Sizes whose decode workspace (jl_bifocal_decode_workspace)
+ * exceeds 32 MiB return JL_ERR_WORKSPACE_TOO_SMALL before any HIP call (at
+ * 128K keys with 32 query heads a batch of 1 needs about 4.3 MB).  The first
+ * call on a device looks up that device's copy of the array; `stream` must
+ * belong to the current device (JL_ERR_INVALID_ARGUMENT otherwise).  Every
+ * call on a device shares its array: calls that overlap on one device (on
+ * different streams, or from several threads) race and must be serialized
+ * by the caller.  The array keeps the last call's partials, which need no
+ * clearing (every call writes each partial it reads).  Allocates nothing.
+ */
+jl_status jl_bifocal_decode_noalloc(void* o, float* lse, const void* q, const void* k_cache,
+                                    const void* v_cache, const int32_t* seqlens_k, int32_t batch,
+                                    int32_t max_seqlen_k, int64_t S_max, int32_t Hq, int32_t Hkv,
+                                    int32_t d, const jl_params* params, jl_dtype dtype,
+                                    void* stream);
+
+/*
  * jl_bifocal_decode on a paged KV cache (the layout serving systems keep):
  * k_pages, v_pages are pools of n_pages pages, each [page_size][Hkv][d] bf16
  * holding standard-RoPE keys (values) at their original positions; key j of

@@ -479,9 +479,14 @@ struct DecodeCall {
     int32_t Hq, Hkv, d;
 };
 
+static jl_status scratch_of_device(void* stream, void** out);
+
+// static_scratch: `workspace` is a placeholder; once every check has passed
+// (the size against workspace_bytes included) the library's own scratch
+// array of the current device takes its place.
 static jl_status decode_impl(const DecodeCall& c, const jl_params* params, jl_dtype dtype,
                              void* workspace, size_t workspace_bytes, void* stream,
-                             const char* where) {
+                             const char* where, bool static_scratch = false) {
     if (!c.o || !c.lse || !c.q || !c.kc || !c.vc || !c.seqlens_k || !workspace)
         return fail(JL_ERR_INVALID_ARGUMENT, "null pointer argument");
     jl_status st = check_params(params);
@@ -523,7 +528,11 @@ static jl_status decode_impl(const DecodeCall& c, const jl_params* params, jl_dt
     const DecodeLayout lay = decode_layout(c.batch, c.max_seqlen_k, c.Hq, c.Hkv, c.d, dtype);
     if (workspace_bytes < lay.total)
         return fail(JL_ERR_WORKSPACE_TOO_SMALL,
-                    "workspace needs " + std::to_string(lay.total) + " bytes");
+                    static_scratch
+                        ? "these sizes need " + std::to_string(lay.total) +
+                              " bytes of scratch; the library's static scratch holds " +
+                              std::to_string(workspace_bytes) + " (use jl_bifocal_decode)"
+                        : "workspace needs " + std::to_string(lay.total) + " bytes");
     DecodeArgs a{};
     a.q = c.q; a.kc = c.kc; a.vc = c.vc; a.o = c.o; a.lse = c.lse; a.seqlens = c.seqlens_k;
     a.ws = workspace; a.lay = lay;
@@ -544,6 +553,10 @@ static jl_status decode_impl(const DecodeCall& c, const jl_params* params, jl_dt
     if (params->precise && c.fp8)
         return fail(JL_ERR_UNSUPPORTED, "split precision (precise = 1) is not offered for fp8 caches");
     a.precise = dtype == JL_DTYPE_BF16 ? params->precise : 0;
+    if (static_scratch) {
+        const jl_status sst = scratch_of_device(stream, &a.ws);
+        if (sst != JL_OK) return sst;
+    }
     hipStream_t s = (hipStream_t)stream;
     hipError_t e = launch_decode(a, dtype, s);
     if (e != hipSuccess) return hip_fail(e, "decode launch");
@@ -558,6 +571,53 @@ jl_status jl_bifocal_decode(void* o, float* lse, const void* q, const void* k_ca
     DecodeCall c{o, lse, q, k_cache, v_cache, seqlens_k, batch, max_seqlen_k, S_max,
                  nullptr, 0, 0, 0, 0, nullptr, nullptr, Hq, Hkv, d};
     return decode_impl(c, params, dtype, workspace, workspace_bytes, stream, "jl_bifocal_decode");
+}
+
+// ---------------------------------------------------------------------------
+// Decode with library-owned scratch, for callers that cannot allocate.  The
+// split partials live in a file-scope device array; each device holds its
+// own copy, whose address is looked up once per device.  Every call writes
+// each partial it later reads, so nothing in the array needs clearing.
+constexpr size_t kDecodeScratchBytes = (size_t)32 << 20;
+static __device__ __align__(256) char scratch[kDecodeScratchBytes];
+static std::mutex g_scratch_mu;
+constexpr int kMaxDevices = 64;
+static void* g_scratch_ptr[kMaxDevices];
+
+static jl_status scratch_of_device(void* stream, void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (stream) {
+        hipDevice_t sdev = 0;
+        e = hipStreamGetDevice((hipStream_t)stream, &sdev);
+        if (e != hipSuccess) return hip_fail(e, "hipStreamGetDevice");
+        if ((int)sdev != dev)
+            return fail(JL_ERR_INVALID_ARGUMENT, "the stream belongs to another device than the current one");
+    }
+    if (dev < 0 || dev >= kMaxDevices) return fail(JL_ERR_UNSUPPORTED, "device index above 63");
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return JL_OK;
+}
+
+jl_status jl_bifocal_decode_noalloc(void* o, float* lse, const void* q, const void* k_cache,
+                                    const void* v_cache, const int32_t* seqlens_k, int32_t batch,
+                                    int32_t max_seqlen_k, int64_t S_max, int32_t Hq, int32_t Hkv,
+                                    int32_t d, const jl_params* params, jl_dtype dtype,
+                                    void* stream) {
+    DecodeCall c{o, lse, q, k_cache, v_cache, seqlens_k, batch, max_seqlen_k, S_max,
+                 nullptr, 0, 0, 0, 0, nullptr, nullptr, Hq, Hkv, d};
+    // a placeholder that passes the null and alignment checks; replaced by
+    // the device's scratch once the sizes are known to fit
+    return decode_impl(c, params, dtype, (void*)(uintptr_t)256, kDecodeScratchBytes, stream,
+                       "jl_bifocal_decode_noalloc", true);
 }
 
 jl_status jl_bifocal_decode_paged(void* o, float* lse, const void* q, const void* k_pages,

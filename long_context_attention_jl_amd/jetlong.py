@@ -91,6 +91,10 @@ def lib() -> ctypes.CDLL:
         L.jl_bifocal_decode.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i64, _i32, _i32,
                                         _i32, ctypes.POINTER(jl_params), ctypes.c_int, _vp,
                                         ctypes.c_size_t, _vp]
+        L.jl_bifocal_decode_noalloc.restype = ctypes.c_int
+        L.jl_bifocal_decode_noalloc.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i64,
+                                                _i32, _i32, _i32, ctypes.POINTER(jl_params),
+                                                ctypes.c_int, _vp]
         L.jl_bifocal_decode_paged.restype = ctypes.c_int
         L.jl_bifocal_decode_paged.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32,
                                               _i64, _i32, _i32, _i32, _i32,
@@ -410,6 +414,28 @@ def bifocal_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor
         ctypes.byref(p), _dtype(q), _dev(ws, "workspace"), ws.numel() * ws.element_size(),
         _stream()), "jl_bifocal_decode")
     return o, lse
+
+
+def bifocal_decode_noalloc(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                           seqlens_k: torch.Tensor, out: torch.Tensor, lse_out: torch.Tensor, *,
+                           w_pretrained: int, w_local: int, rope_base: float,
+                           softmax_scale: float, max_seqlen_k: int,
+                           bifocal: Union[bool, int] = True, precise: bool = False) -> None:
+    """bifocal_decode on the library's static scratch (jl_bifocal_decode_noalloc):
+    no workspace, and no allocation here either -- seqlens_k (int32, on the
+    device), out and lse_out are the caller's.  Calls that overlap on one
+    device race on that scratch."""
+    B, Hq, d = _check_cache(q, k_cache, v_cache, out, lse_out, batch_dim=True)
+    _expect(k_cache.shape[0] >= B, "the caches need a row per sequence")
+    _like(lse_out, "lse_out", (B, Hq), torch.float32, q.device)
+    _expect(seqlens_k.dtype == torch.int32 and seqlens_k.numel() == B,
+            "seqlens_k must be an int32 device tensor with one entry per sequence")
+    p = _params(w_pretrained, w_local, rope_base, softmax_scale, bifocal, precise)
+    _check(lib().jl_bifocal_decode_noalloc(
+        _dev(out, "out"), _dev(lse_out, "lse_out"), _dev(q, "q"), _dev(k_cache, "k_cache"),
+        _dev(v_cache, "v_cache"), _dev(seqlens_k, "seqlens_k"), B, int(max_seqlen_k),
+        k_cache.shape[1], Hq, k_cache.shape[2], d, ctypes.byref(p), _dtype(q), _stream()),
+        "jl_bifocal_decode_noalloc")
 
 
 def _seqlens(seqlens_k, max_seqlen_k, dev):

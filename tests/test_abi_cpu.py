@@ -502,3 +502,19 @@ def test_precise_fp8_decode_is_unsupported():
                                          FAKE * 7, FAKE * 9, 1, 1024, 1024, 32, 8, 128,
                                          ctypes.byref(p), FAKE * 8, 1 << 40, None)
     assert st == jlb.JL_ERR_UNSUPPORTED
+
+
+def test_noalloc_decode_rejects_sizes_beyond_its_scratch():
+    """jl_bifocal_decode_noalloc keeps its partials in a 32 MiB static device
+    array: a batch whose partials exceed it is refused before any HIP call,
+    with the size in the message (fake pointers are never touched)."""
+    p = _params()
+    st = jlb.lib().jl_bifocal_decode_noalloc(FAKE, FAKE * 2, FAKE * 3, FAKE * 4, FAKE * 5,
+                                            FAKE * 6, 64, 131072, 131072, 32, 8, 128,
+                                            ctypes.byref(p), 1, None)
+    assert st == jlb.JL_ERR_WORKSPACE_TOO_SMALL
+    assert b"static scratch" in jlb.lib().jl_last_error()
+    st = jlb.lib().jl_bifocal_decode_noalloc(FAKE, FAKE * 2, FAKE * 3, FAKE * 4, FAKE * 5,
+                                            None, 1, 4096, 4096, 32, 8, 128, ctypes.byref(p), 1,
+                                            None)
+    assert st == jlb.JL_ERR_INVALID_ARGUMENT
