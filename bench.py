@@ -435,6 +435,39 @@ def bench_decode(jl, inputs, torch, iters, extras=True):
         torch.cuda.synchronize()
         return ev0.elapsed_time(ev1) * 1e3 / n
 
+    # the pages' unfused generation step on the same caches: the keys turned
+    # to remapped RoPE, three attention calls and the LogSumExp merge
+    ws3 = torch.empty(jl.decode_three_call_workspace_bytes(B, L, Hq, Hkv, d, p.w_local),
+                      dtype=torch.uint8, device="cuda")
+
+    def run_three(n):
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        ev0.record()
+        for i in range(n):
+            kc, vc = copies[i % 4]
+            jl.bifocal_decode_three_call(q, kc, vc, sl, max_seqlen_k=L, w_pretrained=p.w_pretrained,
+                                         w_local=p.w_local, rope_base=p.rope_base,
+                                         softmax_scale=p.softmax_scale, workspace=ws3, out=o,
+                                         lse_out=lse)
+        ev1.record()
+        torch.cuda.synchronize()
+        return ev0.elapsed_time(ev1) * 1e3 / n
+
+    def run_precise(n):
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        ev0.record()
+        for i in range(n):
+            kc, vc = copies[i % 4]
+            jl.bifocal_decode(q, kc, vc, sl, max_seqlen_k=L, w_pretrained=p.w_pretrained,
+                              w_local=p.w_local, rope_base=p.rope_base,
+                              softmax_scale=p.softmax_scale, precise=True, workspace=ws,
+                              out=o, lse_out=lse)
+        ev1.record()
+        torch.cuda.synchronize()
+        return ev0.elapsed_time(ev1) * 1e3 / n
+
     run(True, 10)
     run(False, 10)
     if extras:
@@ -502,6 +535,14 @@ def bench_decode(jl, inputs, torch, iters, extras=True):
     }
     if not extras:
         return res
+    run_three(4)
+    t3 = min(run_three(10) for _ in range(3))
+    run_precise(4)
+    tpr = min(run_precise(20) for _ in range(3))
+    res["three_call_us_per_token"] = round(t3, 2)
+    res["three_call_over_fused"] = round(t3 / t_bif, 3)
+    res["precise_us_per_token"] = round(tpr, 2)
+    del ws3
     res["interp_us_per_token"] = round(min(t2), 2)
     res["paged_us_per_token"] = {"page_%d" % page: round(min(t), 2) for page, t in tpg.items()}
     res["fp8"] = {"us_per_token": round(min(t8b), 2), "plain_us_per_token": round(min(t8p), 2),

@@ -171,8 +171,9 @@ jl_status jl_bifocal_prefill_three_call_workspace(int64_t T, int32_t n_seqs, int
  *     C: the local pairs under remapped RoPE,
  * combined as Z = e^lse_B - e^lse_C + e^lse_A and
  * o = (e^lse_B o_B - e^lse_C o_C + e^lse_A o_A) / Z (the remote mass
- * e^lse_B - e^lse_C clamped at 0).  Up to rounding this equals
- * jl_bifocal_prefill; it exists to compare the two forms on the device.
+ * e^lse_B - e^lse_C clamped at 0), from the calls' fp32 outputs.  Up to
+ * rounding this equals jl_bifocal_prefill; it exists to compare the two
+ * forms on the device.
  * Arguments as for jl_bifocal_prefill (no k_rot_out); params->bifocal must
  * be 1; dtype must be JL_DTYPE_BF16 (else JL_ERR_UNSUPPORTED).  The three
  * calls' outputs live in the workspace.
@@ -237,6 +238,40 @@ jl_status jl_bifocal_decode_noalloc(void* o, float* lse, const void* q, const vo
                                     int32_t max_seqlen_k, int64_t S_max, int32_t Hq, int32_t Hkv,
                                     int32_t d, const jl_params* params, jl_dtype dtype,
                                     void* stream);
+
+/* Bytes of device workspace jl_bifocal_decode_three_call needs (bf16 only):
+ * a remapped copy of the cache's keys [batch][max_seqlen_k][Hkv][d], the three
+ * calls' fp32 outputs and the split partials.  params->w_local sizes the
+ * local calls' partials. */
+jl_status jl_bifocal_decode_three_call_workspace(int32_t batch, int32_t max_seqlen_k, int32_t Hq,
+                                                 int32_t Hkv, int32_t d, jl_dtype dtype,
+                                                 const jl_params* params, size_t* bytes);
+
+/*
+ * The pages' unfused form of a generation step ([TW] §四, [BT] §3.2), the
+ * counterpart of jl_bifocal_prefill_three_call: three separate attention
+ * calls over the cache and a LogSumExp merge.  Because the cache holds
+ * standard-RoPE keys ([TW] §三), call B first needs every key turned to
+ * remapped RoPE: the call writes R(f(j) - j) k_cache[b][j] for all j < L_b
+ * into the workspace ([BT] §3.3's correction, applied to the whole cache and
+ * stored), then runs
+ *     B: the query R(f(p)) q against every remapped key,
+ *     A: R(p) q against the stored keys with p - j < w_local,
+ *     C: R(f(p)) q against the remapped keys with p - j < w_local,
+ * each a plain decode with fp32 output, and merges
+ * o = (e^lse_B o_B - e^lse_C o_C + e^lse_A o_A) / Z, Z = e^lse_B - e^lse_C +
+ * e^lse_A (the remote mass clamped at 0).  Up to rounding this equals
+ * jl_bifocal_decode; it exists to measure the two forms on the device.
+ * Arguments as for jl_bifocal_decode (flat bf16 caches, read-only);
+ * params->bifocal must be 1 and params->precise 0 (JL_ERR_INVALID_ARGUMENT
+ * / JL_ERR_UNSUPPORTED otherwise).
+ */
+jl_status jl_bifocal_decode_three_call(void* o, float* lse, const void* q, const void* k_cache,
+                                       const void* v_cache, const int32_t* seqlens_k,
+                                       int32_t batch, int32_t max_seqlen_k, int64_t S_max,
+                                       int32_t Hq, int32_t Hkv, int32_t d,
+                                       const jl_params* params, jl_dtype dtype, void* workspace,
+                                       size_t workspace_bytes, void* stream);
 
 /*
  * jl_bifocal_decode on a paged KV cache (the layout serving systems keep):

@@ -341,7 +341,8 @@ struct ThreeCallLayout {
 };
 static ThreeCallLayout three_call_layout(const PrefillLayout& pl, int64_t T, int32_t Hq, int32_t d) {
     ThreeCallLayout L{};
-    const size_t ob = align256((size_t)T * Hq * d * 2), lb = align256((size_t)Hq * T * 4);
+    // fp32 outputs of the three calls
+    const size_t ob = align256((size_t)T * Hq * d * 4), lb = align256((size_t)Hq * T * 4);
     size_t off = align256(pl.total);
     L.oA = off; off += ob;
     L.oB = off; off += ob;
@@ -430,6 +431,7 @@ jl_status jl_bifocal_prefill_three_call(void* o, float* lse, const void* q, cons
     e = launch_kv_prepass(a, dtype, s);
     if (e != hipSuccess) return hip_fail(e, "key/value pre-pass launch");
     const size_t oofs[3] = {tl.oB, tl.oA, tl.oC}, lofs[3] = {tl.lB, tl.lA, tl.lC};
+    a.o_f32 = 1;
     for (int c = 0; c < 3; ++c) {  // modes 1 (B), 2 (A), 3 (C)
         a.mode = c + 1;
         a.o = ws + oofs[c];
@@ -437,9 +439,10 @@ jl_status jl_bifocal_prefill_three_call(void* o, float* lse, const void* q, cons
         e = launch_prefill_bf16(a, s);
         if (e != hipSuccess) return hip_fail(e, "prefill launch");
     }
-    e = launch_three_call_merge(ws + tl.oA, ws + tl.oB, ws + tl.oC, (const float*)(ws + tl.lA),
+    e = launch_three_call_merge((const float*)(ws + tl.oA), (const float*)(ws + tl.oB),
+                                (const float*)(ws + tl.oC), (const float*)(ws + tl.lA),
                                 (const float*)(ws + tl.lB), (const float*)(ws + tl.lC), o, lse, T,
-                                Hq, d, s);
+                                Hq, d, 1, T, s);
     if (e != hipSuccess) return hip_fail(e, "merge launch");
     return finish(s, "jl_bifocal_prefill_three_call");
 }
@@ -561,6 +564,126 @@ static jl_status decode_impl(const DecodeCall& c, const jl_params* params, jl_dt
     hipError_t e = launch_decode(a, dtype, s);
     if (e != hipSuccess) return hip_fail(e, "decode launch");
     return finish(s, where);
+}
+
+// The unfused decode: the cache turned to remapped RoPE, the three calls'
+// fp32 outputs and LSEs, and one decode workspace the calls take in turn.
+struct DecodeThreeLayout {
+    DecodeLayout full, win;  // call B (all keys); calls A and C (the local window)
+    size_t kr, oA, oB, oC, lA, lB, lC, dec, total;
+};
+static DecodeThreeLayout decode_three_layout(int32_t B, int32_t max_seqlen_k, int32_t Hq,
+                                             int32_t Hkv, int32_t d, int32_t w_local) {
+    DecodeThreeLayout L{};
+    L.full = decode_layout(B, max_seqlen_k, Hq, Hkv, d, JL_DTYPE_BF16);
+    const int32_t wk = w_local < 1 ? 1 : (w_local < max_seqlen_k ? w_local : max_seqlen_k);
+    L.win = decode_layout(B, wk, Hq, Hkv, d, JL_DTYPE_BF16);
+    const size_t ob = align256((size_t)B * Hq * d * 4), lb = align256((size_t)B * Hq * 4);
+    size_t off = 0;
+    L.kr = off; off = align256(off + (size_t)B * max_seqlen_k * Hkv * d * 2);
+    L.oA = off; off += ob;
+    L.oB = off; off += ob;
+    L.oC = off; off += ob;
+    L.lA = off; off += lb;
+    L.lB = off; off += lb;
+    L.lC = off; off += lb;
+    L.dec = off;
+    off += L.full.total > L.win.total ? L.full.total : L.win.total;
+    L.total = align256(off);
+    return L;
+}
+
+jl_status jl_bifocal_decode_three_call_workspace(int32_t batch, int32_t max_seqlen_k, int32_t Hq,
+                                                 int32_t Hkv, int32_t d, jl_dtype dtype,
+                                                 const jl_params* params, size_t* bytes) {
+    if (!bytes) return fail(JL_ERR_INVALID_ARGUMENT, "bytes is NULL");
+    jl_status st = check_params(params);
+    if (st != JL_OK) return st;
+    if (batch < 1 || max_seqlen_k < 1)
+        return fail(JL_ERR_INVALID_ARGUMENT, "batch and max_seqlen_k must be >= 1");
+    st = check_heads(Hq, Hkv);
+    if (st != JL_OK) return st;
+    st = check_dtype_d(dtype, d);
+    if (st != JL_OK) return st;
+    if (dtype != JL_DTYPE_BF16) return fail(JL_ERR_UNSUPPORTED, "the unfused decode is bf16 only");
+    *bytes = decode_three_layout(batch, max_seqlen_k, Hq, Hkv, d, params->w_local).total;
+    g_err.clear();
+    return JL_OK;
+}
+
+jl_status jl_bifocal_decode_three_call(void* o, float* lse, const void* q, const void* k_cache,
+                                       const void* v_cache, const int32_t* seqlens_k,
+                                       int32_t batch, int32_t max_seqlen_k, int64_t S_max,
+                                       int32_t Hq, int32_t Hkv, int32_t d,
+                                       const jl_params* params, jl_dtype dtype, void* workspace,
+                                       size_t workspace_bytes, void* stream) {
+    if (!o || !lse || !q || !k_cache || !v_cache || !seqlens_k || !workspace)
+        return fail(JL_ERR_INVALID_ARGUMENT, "null pointer argument");
+    jl_status st = check_params(params);
+    if (st != JL_OK) return st;
+    if (params->bifocal != 1) return fail(JL_ERR_INVALID_ARGUMENT, "the unfused form needs bifocal = 1");
+    if (params->precise) return fail(JL_ERR_UNSUPPORTED, "the unfused decode has no split-precision mode");
+    if (batch < 1 || max_seqlen_k < 1)
+        return fail(JL_ERR_INVALID_ARGUMENT, "batch and max_seqlen_k must be >= 1");
+    if (batch > 65535) return fail(JL_ERR_UNSUPPORTED, "batch above 65535");
+    if (S_max < max_seqlen_k) return fail(JL_ERR_INVALID_ARGUMENT, "S_max < max_seqlen_k");
+    st = check_heads(Hq, Hkv);
+    if (st != JL_OK) return st;
+    if (Hq / Hkv > 16) return fail(JL_ERR_UNSUPPORTED, "decode supports Hq / Hkv <= 16");
+    st = check_dtype_d(dtype, d);
+    if (st != JL_OK) return st;
+    if (dtype != JL_DTYPE_BF16) return fail(JL_ERR_UNSUPPORTED, "the unfused decode is bf16 only");
+    if (S_max > (1LL << 40) / ((int64_t)batch * Hkv * d))
+        return fail(JL_ERR_INVALID_ARGUMENT, "cache too large");
+    if (o == q || o == k_cache || o == v_cache)
+        return fail(JL_ERR_INVALID_ARGUMENT, "outputs must not alias inputs");
+    if ((uintptr_t)workspace & 255) return fail(JL_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
+    st = check_aligned({o, q, k_cache, v_cache});
+    if (st != JL_OK) return st;
+    const DecodeThreeLayout tl = decode_three_layout(batch, max_seqlen_k, Hq, Hkv, d, params->w_local);
+    if (workspace_bytes < tl.total)
+        return fail(JL_ERR_WORKSPACE_TOO_SMALL, "workspace needs " + std::to_string(tl.total) + " bytes");
+    char* ws = (char*)workspace;
+    DecodeArgs a{};
+    a.q = q; a.seqlens = seqlens_k; a.B = batch; a.max_seqlen_k = max_seqlen_k;
+    a.Hq = Hq; a.Hkv = Hkv; a.d = d;
+    a.w_pretrained = params->w_pretrained; a.w_local = params->w_local;
+    a.bifocal = 0;  // each call is a plain attention call over its keys
+    a.softmax_scale = params->softmax_scale;
+    a.tab = make_rope_freq(params->rope_base, d);
+    a.ws = ws + tl.dec;
+    a.o_f32 = 1;
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e = launch_cache_remap(ws + tl.kr, k_cache, seqlens_k, batch, max_seqlen_k, S_max,
+                                      Hkv, d, params->w_pretrained, a.tab, s);
+    if (e != hipSuccess) return hip_fail(e, "cache remap launch");
+    struct Call {
+        const void* kc;
+        int64_t S_max;
+        int32_t q_remap, window;
+        size_t o, l;
+    };
+    const Call calls[3] = {
+        {ws + tl.kr, max_seqlen_k, 1, 0, tl.oB, tl.lB},  // B: every key, remapped RoPE
+        {k_cache, S_max, 0, 1, tl.oA, tl.lA},           // A: the local window, standard RoPE
+        {ws + tl.kr, max_seqlen_k, 1, 1, tl.oC, tl.lC},  // C: the local window, remapped RoPE
+    };
+    for (const Call& c : calls) {
+        // keys from the caller's cache or the remapped copy, values always
+        // from the caller's cache (rows per sequence S_max)
+        a.kc = c.kc; a.vc = v_cache; a.S_max = S_max; a.S_max_k = c.S_max;
+        a.q_remap = c.q_remap; a.window = c.window;
+        a.lay = c.window ? tl.win : tl.full;
+        a.o = ws + c.o; a.lse = (float*)(ws + c.l);
+        e = launch_decode(a, JL_DTYPE_BF16, s);
+        if (e != hipSuccess) return hip_fail(e, "decode launch");
+    }
+    e = launch_three_call_merge((const float*)(ws + tl.oA), (const float*)(ws + tl.oB),
+                                (const float*)(ws + tl.oC), (const float*)(ws + tl.lA),
+                                (const float*)(ws + tl.lB), (const float*)(ws + tl.lC), o, lse,
+                                batch, Hq, d, Hq, 1, s);
+    if (e != hipSuccess) return hip_fail(e, "merge launch");
+    return finish(s, "jl_bifocal_decode_three_call");
 }
 
 jl_status jl_bifocal_decode(void* o, float* lse, const void* q, const void* k_cache,

@@ -569,7 +569,9 @@ __global__ __launch_bounds__(512) void decode_split_bf16_kernel(DecodeArgs a) {
         const int32_t m = (rem_last + 1) % kStageB;
         z0 = m ? m - kStageB : 0;
     }
-    const int32_t kbeg = z0 + split * a.lay.chunk;
+    // a single local call of the unfused form sees only keys p - j < w_local
+    const int32_t kwin = a.window ? max(L - a.w_local, 0) : 0;
+    const int32_t kbeg = kwin + z0 + split * a.lay.chunk;
     const int32_t kend = min(kbeg + a.lay.chunk, L);
 
     float4* pm = (float4*)((char*)a.ws + a.lay.part_ml);
@@ -587,7 +589,8 @@ __global__ __launch_bounds__(512) void decode_split_bf16_kernel(DecodeArgs a) {
     // waits): indices are clamped to valid rows, masked keys weigh 0
     const int kvh_c = min(kvh, a.Hkv - 1);
     const int64_t boff = PAGED ? 0 : (int64_t)b * a.S_max * a.Hkv * D;
-    const TC* kc = (const TC*)a.kc + boff + (int64_t)kvh_c * D;
+    const int64_t boff_k = PAGED ? 0 : (int64_t)b * (a.S_max_k ? a.S_max_k : a.S_max) * a.Hkv * D;
+    const TC* kc = (const TC*)a.kc + boff_k + (int64_t)kvh_c * D;
     const TC* vc = (const TC*)a.vc + boff + (int64_t)kvh_c * D;
     const int64_t rstride = (int64_t)a.Hkv * D;
     char* const slot = vs + wave * SLOT;
@@ -687,7 +690,7 @@ __global__ __launch_bounds__(512) void decode_split_bf16_kernel(DecodeArgs a) {
                 else
                     rope_cs_hw((int64_t)fp - remap(jbs, G) + jbs, rv, cs, sn);
             } else {
-                rope_cs_hw(p, rv, cs, sn);
+                rope_cs_hw(a.q_remap ? fp : p, rv, cs, sn);
             }
             qtab[(st < nst ? st : QLOC) * HALF + x % HALF] = make_float2(cs, sn);
         }
@@ -1085,6 +1088,119 @@ static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t s) {
         hipLaunchKernelGGL(decode_merge_kernel<float>, dim3(a.Hq, a.B, D / 16), dim3(256), 0, s, a);
     else
         hipLaunchKernelGGL(decode_merge_kernel<TIN>, dim3(a.Hq, a.B, D / 16), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// The pages' unfused generation step ([TW] §四, [BT] §3.2): the cache holds
+// standard-RoPE keys, so call B (every key under remapped RoPE) first needs
+// the whole cache turned to remapped RoPE: out[b][j] = R(f(j) - j) k[b][j]
+// for j < L_b, G = G(L_b) -- the correction rotation of [BT] §3.3 applied
+// to every key and stored.  One thread per (sequence, row, 8 pairs), the
+// angles shared by all kv heads; rows j >= L_b are not written.
+template <int D>
+__global__ __launch_bounds__(256) void cache_remap_kernel(bf16* __restrict__ out,
+                                                          const bf16* __restrict__ kc,
+                                                          const int32_t* __restrict__ seqlens,
+                                                          int32_t B, int32_t max_seqlen_k,
+                                                          int64_t S_max, int32_t Hkv,
+                                                          int32_t w_pretrained, RopeFreq tab) {
+    constexpr int HALF = D / 2, NC = HALF / 8;
+    const int64_t item = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (item >= (int64_t)B * max_seqlen_k * NC) return;
+    const int c = (int)(item % NC);
+    const int64_t row = item / NC;
+    const int b = (int)(row / max_seqlen_k);
+    const int32_t j = (int32_t)(row % max_seqlen_k);
+    int32_t L = seqlens[b];
+    L = L < 0 ? 0 : (L > max_seqlen_k ? max_seqlen_k : L);
+    if (j >= L) return;
+    const int32_t G = (int32_t)group_size(L, w_pretrained);
+    const int32_t ang = remap(j, G) - j;
+    float cs[8], sn[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) rope_cs(ang, rope_rev(tab, 8 * c + u), cs[u], sn[u]);
+    for (int g = 0; g < Hkv; ++g) {
+        const bf16* src = kc + (((int64_t)b * S_max + j) * Hkv + g) * D + 8 * c;
+        bf16* dst = out + (((int64_t)b * max_seqlen_k + j) * Hkv + g) * D + 8 * c;
+        const bf16x8 x0 = *reinterpret_cast<const bf16x8*>(src);
+        const bf16x8 x1 = *reinterpret_cast<const bf16x8*>(src + HALF);
+        bf16x8 y0, y1;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const float a0 = (float)x0[u], a1 = (float)x1[u];
+            y0[u] = (bf16)(a0 * cs[u] - a1 * sn[u]);
+            y1[u] = (bf16)(a1 * cs[u] + a0 * sn[u]);
+        }
+        *reinterpret_cast<bf16x8*>(dst) = y0;
+        *reinterpret_cast<bf16x8*>(dst + HALF) = y1;
+    }
+}
+
+hipError_t launch_cache_remap(void* out, const void* kc, const int32_t* seqlens, int32_t B,
+                              int32_t max_seqlen_k, int64_t S_max, int32_t Hkv, int32_t d,
+                              int32_t w_pretrained, const RopeFreq& tab, hipStream_t s) {
+    const int64_t items = (int64_t)B * max_seqlen_k * (d / 16);
+    const dim3 grid((unsigned)((items + 255) / 256));
+    LaunchScope scope("cache_remap", s);
+    if (d == 128)
+        hipLaunchKernelGGL(cache_remap_kernel<128>, grid, dim3(256), 0, s, (bf16*)out,
+                           (const bf16*)kc, seqlens, B, max_seqlen_k, S_max, Hkv, w_pretrained, tab);
+    else
+        hipLaunchKernelGGL(cache_remap_kernel<64>, grid, dim3(256), 0, s, (bf16*)out,
+                           (const bf16*)kc, seqlens, B, max_seqlen_k, S_max, Hkv, w_pretrained, tab);
+    return hipGetLastError();
+}
+
+// LogSumExp combination of the pages' three unfused calls ([TW] §四, [BT]
+// §3.2): with B every causal pair under remapped RoPE, A the local pairs
+// under standard RoPE and C the local pairs under remapped RoPE,
+//   Z = e^lse_B - e^lse_C + e^lse_A,  o = (e^lse_B o_B - e^lse_C o_C + e^lse_A o_A) / Z.
+// B and C hold the same local pairs, so the remote mass e^lse_B - e^lse_C is
+// taken relative to e^lse_B and clamped at 0 (rows with no remote key give 0
+// up to rounding); a clamped remote part contributes nothing.  The three
+// calls' outputs are fp32, so the difference e^lse_B o_B - e^lse_C o_C does
+// not cancel rounded values.  Row r, head h: o at (r Hq + h) d, lse at
+// r * ls_r + h * ls_h (prefill [Hq][T]: ls_r = 1, ls_h = T; decode [B][Hq]:
+// ls_r = Hq, ls_h = 1).  One wave per (row, head); lse is the natural log,
+// and lse_B is finite for every row that has a key (its own key is in B).
+__global__ __launch_bounds__(256) void three_call_merge_kernel(
+    const float* __restrict__ oA, const float* __restrict__ oB, const float* __restrict__ oC,
+    const float* __restrict__ lA, const float* __restrict__ lB, const float* __restrict__ lC,
+    bf16* __restrict__ o, float* __restrict__ lse, int64_t rows, int Hq, int d, int64_t ls_r,
+    int64_t ls_h) {
+    const int64_t r = blockIdx.x;
+    const int head = blockIdx.y * 4 + (int)(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (head >= Hq) return;
+    const int64_t li = r * ls_r + (int64_t)head * ls_h;
+    const float la = lA[li], lb = lB[li], lc = lC[li];
+    const int64_t base = (r * Hq + head) * d;
+    if (!(lb > -INFINITY)) {  // a row with no key (an empty decode sequence)
+        for (int x = lane; x < d; x += 64) o[base + x] = (bf16)0.0f;
+        if (lane == 0) lse[li] = -INFINITY;
+        return;
+    }
+    const float ec = expf(lc - lb);
+    const float rem = fmaxf(0.0f, 1.0f - ec);  // remote mass / e^lse_B
+    const float loc = expf(la - lb);           // local mass / e^lse_B
+    const float z = rem + loc;
+    const float wB = rem > 0.0f ? 1.0f / z : 0.0f;
+    const float wC = rem > 0.0f ? ec / z : 0.0f;
+    const float wA = loc / z;
+    for (int x = lane; x < d; x += 64)
+        o[base + x] = (bf16)(wB * oB[base + x] - wC * oC[base + x] + wA * oA[base + x]);
+    if (lane == 0) lse[li] = lb + logf(z);
+}
+
+hipError_t launch_three_call_merge(const float* oA, const float* oB, const float* oC,
+                                   const float* lA, const float* lB, const float* lC, void* o,
+                                   float* lse, int64_t rows, int32_t Hq, int32_t d, int64_t ls_r,
+                                   int64_t ls_h, hipStream_t s) {
+    LaunchScope scope("three_call_merge", s);
+    hipLaunchKernelGGL(three_call_merge_kernel, dim3((unsigned)rows, (unsigned)((Hq + 3) / 4)),
+                       dim3(256), 0, s, oA, oB, oC, lA, lB, lC, (bf16*)o, lse, rows, (int)Hq,
+                       (int)d, ls_r, ls_h);
     return hipGetLastError();
 }
 

@@ -97,6 +97,8 @@ struct PrefillArgs {
     // split-precision (hi + lo) scores on every row, not only the first
     // kPreciseRows of each sequence
     int32_t precise;
+    // o is written as float32 (the unfused form's separate calls)
+    int32_t o_f32;
 };
 
 // Plan of a chunk call: per sequence b, C_b = cu_q[b + 1] - cu_q[b] query rows
@@ -109,10 +111,16 @@ hipError_t launch_plan_chunk(int32_t* plan, const int32_t* cu_q, const int32_t* 
 hipError_t launch_e4m3_quant(uint8_t* out, const void* x, const float* scale, int64_t ntok,
                              int32_t H, int32_t d, hipStream_t s);
 hipError_t launch_kv_prepass(const PrefillArgs& a, int dtype, hipStream_t s);
-// O = the LogSumExp combination of the three unfused calls B + A - C
-hipError_t launch_three_call_merge(const void* oA, const void* oB, const void* oC, const float* lA,
-                                   const float* lB, const float* lC, void* o, float* lse,
-                                   int64_t T, int32_t Hq, int32_t d, hipStream_t s);
+// O = the LogSumExp combination of the three unfused calls B + A - C (fp32
+// outputs of the calls, bf16 o); lse of row r, head h at r * ls_r + h * ls_h
+hipError_t launch_three_call_merge(const float* oA, const float* oB, const float* oC,
+                                   const float* lA, const float* lB, const float* lC, void* o,
+                                   float* lse, int64_t rows, int32_t Hq, int32_t d, int64_t ls_r,
+                                   int64_t ls_h, hipStream_t s);
+// out[b][j] = R(f(j) - j) k_cache[b][j] for j < L_b (bf16 [B][max_seqlen_k][Hkv][d])
+hipError_t launch_cache_remap(void* out, const void* kc, const int32_t* seqlens, int32_t B,
+                              int32_t max_seqlen_k, int64_t S_max, int32_t Hkv, int32_t d,
+                              int32_t w_pretrained, const RopeFreq& tab, hipStream_t s);
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t s);
 // combines the key-split partials of the main rows (positions >= 2048) of a
 // chunk call into o and lse
@@ -147,6 +155,9 @@ struct DecodeArgs {
     // turns the query by R(f(p)) instead of R(p); window keeps only the keys
     // p - j < w_local; o_f32 writes o as float32.
     int32_t q_remap, window, o_f32;
+    // rows per sequence of the key cache when they differ from the value
+    // cache's S_max (the unfused form's remapped copy of the keys); 0: S_max
+    int64_t S_max_k;
     // remote keys turned in fp32 and split into fp16 hi + lo operands
     int32_t precise;
 };

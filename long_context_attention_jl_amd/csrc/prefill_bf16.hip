@@ -408,16 +408,29 @@ void prefill_bf16_kernel(PrefillArgs a, int rb_first, int n_rb) {
     // a row with no key of the call (the local calls with w_local = 0): o = 0, lse = -inf
     const bool none = !(l_run > 0.0f);
     const float inv = none ? 0.0f : 1.0f / l_run;
-    bf16* op = (bf16*)a.o + ((qbase + myrow) * a.Hq + head) * D;
+    const int64_t oofs = ((qbase + myrow) * a.Hq + head) * D;
+    if (a.o_f32) {  // the unfused form's separate calls keep fp32 outputs
+        float* op = (float*)a.o + oofs;
 #pragma unroll
-    for (int db = 0; db < C::ND; ++db)
+        for (int db = 0; db < C::ND; ++db)
 #pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-            bf16x4 w;
+            for (int g4 = 0; g4 < 4; ++g4) {
+                const f32x4 w = {O[db][4 * g4] * inv, O[db][4 * g4 + 1] * inv,
+                                 O[db][4 * g4 + 2] * inv, O[db][4 * g4 + 3] * inv};
+                *reinterpret_cast<f32x4*>(op + 32 * db + 8 * g4 + 4 * hh) = w;
+            }
+    } else {
+        bf16* op = (bf16*)a.o + oofs;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) w[r] = (bf16)(O[db][4 * g4 + r] * inv);
-            *reinterpret_cast<bf16x4*>(op + 32 * db + 8 * g4 + 4 * hh) = w;
-        }
+        for (int db = 0; db < C::ND; ++db)
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+                bf16x4 w;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) w[r] = (bf16)(O[db][4 * g4 + r] * inv);
+                *reinterpret_cast<bf16x4*>(op + 32 * db + 8 * g4 + 4 * hh) = w;
+            }
+    }
     if (hh == 0) a.lse[(int64_t)head * a.T + qbase + myrow] = none ? -INFINITY : (m_run + log2f(l_run)) * kLn2;
 }
 
@@ -514,47 +527,6 @@ hipError_t launch_chunk_merge(const PrefillArgs& a, hipStream_t s) {
     LaunchScope scope("chunk_merge", s);
     hipLaunchKernelGGL(chunk_merge_kernel, dim3((unsigned)a.T, (unsigned)((a.Hq + 3) / 4)),
                        dim3(256), 0, s, a);
-    return hipGetLastError();
-}
-
-// LogSumExp combination of the pages' three unfused calls ([TW] §四, [BT]
-// §3.2): with B every causal pair under remapped RoPE, A the local pairs under
-// standard RoPE and C the local pairs under remapped RoPE,
-//   Z = e^lse_B - e^lse_C + e^lse_A,  o = (e^lse_B o_B - e^lse_C o_C + e^lse_A o_A) / Z.
-// B and C hold the same local pairs, so the remote mass e^lse_B - e^lse_C is
-// computed relative to e^lse_B and clamped at 0 (rows with no remote key give
-// 0 up to rounding); a clamped remote part contributes nothing.  One wave per
-// (token, head); lse is the natural log, lse_B is finite for every row (its
-// own key is always in B).
-__global__ __launch_bounds__(256) void three_call_merge_kernel(
-    const bf16* __restrict__ oA, const bf16* __restrict__ oB, const bf16* __restrict__ oC,
-    const float* __restrict__ lA, const float* __restrict__ lB, const float* __restrict__ lC,
-    bf16* __restrict__ o, float* __restrict__ lse, int64_t T, int Hq, int d) {
-    const int64_t tok = blockIdx.x;
-    const int head = blockIdx.y * 4 + (int)(threadIdx.x >> 6);
-    const int lane = threadIdx.x & 63;
-    if (head >= Hq) return;
-    const int64_t li = (int64_t)head * T + tok;
-    const float la = lA[li], lb = lB[li], lc = lC[li];
-    const float rem = fmaxf(0.0f, 1.0f - expf(lc - lb));  // remote mass / e^lse_B
-    const float loc = expf(la - lb);                      // local mass / e^lse_B
-    const float z = rem + loc;
-    const float wB = rem > 0.0f ? 1.0f / z : 0.0f;
-    const float wC = rem > 0.0f ? expf(lc - lb) / z : 0.0f;
-    const float wA = loc / z;
-    const int64_t base = (tok * Hq + head) * d;
-    for (int x = lane; x < d; x += 64)
-        o[base + x] = (bf16)(wB * (float)oB[base + x] - wC * (float)oC[base + x] + wA * (float)oA[base + x]);
-    if (lane == 0) lse[li] = lb + logf(z);
-}
-
-hipError_t launch_three_call_merge(const void* oA, const void* oB, const void* oC, const float* lA,
-                                   const float* lB, const float* lC, void* o, float* lse,
-                                   int64_t T, int32_t Hq, int32_t d, hipStream_t s) {
-    LaunchScope scope("three_call_merge", s);
-    hipLaunchKernelGGL(three_call_merge_kernel, dim3((unsigned)T, (unsigned)((Hq + 3) / 4)), dim3(256), 0, s,
-                       (const bf16*)oA, (const bf16*)oB, (const bf16*)oC, lA, lB, lC, (bf16*)o, lse,
-                       T, (int)Hq, (int)d);
     return hipGetLastError();
 }
 

@@ -95,6 +95,15 @@ def lib() -> ctypes.CDLL:
         L.jl_bifocal_decode_noalloc.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i64,
                                                 _i32, _i32, _i32, ctypes.POINTER(jl_params),
                                                 ctypes.c_int, _vp]
+        L.jl_bifocal_decode_three_call_workspace.restype = ctypes.c_int
+        L.jl_bifocal_decode_three_call_workspace.argtypes = [_i32, _i32, _i32, _i32, _i32,
+                                                             ctypes.c_int,
+                                                             ctypes.POINTER(jl_params),
+                                                             ctypes.POINTER(ctypes.c_size_t)]
+        L.jl_bifocal_decode_three_call.restype = ctypes.c_int
+        L.jl_bifocal_decode_three_call.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i64,
+                                                   _i32, _i32, _i32, ctypes.POINTER(jl_params),
+                                                   ctypes.c_int, _vp, ctypes.c_size_t, _vp]
         L.jl_bifocal_decode_paged.restype = ctypes.c_int
         L.jl_bifocal_decode_paged.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32,
                                               _i64, _i32, _i32, _i32, _i32,
@@ -436,6 +445,48 @@ def bifocal_decode_noalloc(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torc
         _dev(v_cache, "v_cache"), _dev(seqlens_k, "seqlens_k"), B, int(max_seqlen_k),
         k_cache.shape[1], Hq, k_cache.shape[2], d, ctypes.byref(p), _dtype(q), _stream()),
         "jl_bifocal_decode_noalloc")
+
+
+def decode_three_call_workspace_bytes(B: int, max_seqlen_k: int, Hq: int, Hkv: int, d: int,
+                                      w_local: int) -> int:
+    n = ctypes.c_size_t()
+    p = jl_params(1, int(w_local), 1.0, 1.0, 1, 0)
+    _check(lib().jl_bifocal_decode_three_call_workspace(B, max_seqlen_k, Hq, Hkv, d, JL_DTYPE_BF16,
+                                                        ctypes.byref(p), ctypes.byref(n)),
+           "jl_bifocal_decode_three_call_workspace")
+    return n.value
+
+
+def bifocal_decode_three_call(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                              seqlens_k: Union[Sequence[int], torch.Tensor], *,
+                              w_pretrained: int, w_local: int, rope_base: float,
+                              softmax_scale: float, max_seqlen_k: Optional[int] = None,
+                              workspace: Optional[torch.Tensor] = None,
+                              out: Optional[torch.Tensor] = None,
+                              lse_out: Optional[torch.Tensor] = None
+                              ) -> Tuple[torch.Tensor, torch.Tensor]:
+    """The pages' unfused generation step ([TW] §四): the cache's keys turned to
+    remapped RoPE, three attention calls B, A, C and the LogSumExp merge.  bf16
+    caches [B, S_max, Hkv, d].  Returns (o [B, Hq, d], lse [B, Hq])."""
+    B, Hq, d = _check_cache(q, k_cache, v_cache, out, lse_out, batch_dim=True)
+    _expect(q.dtype == torch.bfloat16, "the unfused decode takes bfloat16 tensors")
+    _expect(k_cache.shape[0] >= B, "the caches need a row per sequence")
+    _like(lse_out, "lse_out", (B, Hq), torch.float32, q.device)
+    _check_lens(len(seqlens_k), B, "seqlens_k")
+    S_max, Hkv = k_cache.shape[1], k_cache.shape[2]
+    dev = q.device
+    sl, max_seqlen_k = _seqlens(seqlens_k, max_seqlen_k, dev)
+    p = _params(w_pretrained, w_local, rope_base, softmax_scale, True)
+    ws = _workspace(decode_three_call_workspace_bytes(B, max_seqlen_k, Hq, Hkv, d, w_local), dev,
+                    workspace)
+    o = out if out is not None else torch.empty_like(q)
+    lse = lse_out if lse_out is not None else torch.empty((B, Hq), dtype=torch.float32, device=dev)
+    _check(lib().jl_bifocal_decode_three_call(
+        _dev(o, "o"), _dev(lse, "lse"), _dev(q, "q"), _dev(k_cache, "k_cache"),
+        _dev(v_cache, "v_cache"), _dev(sl, "seqlens_k"), B, max_seqlen_k, S_max, Hq, Hkv, d,
+        ctypes.byref(p), JL_DTYPE_BF16, _dev(ws, "workspace"), ws.numel() * ws.element_size(),
+        _stream()), "jl_bifocal_decode_three_call")
+    return o, lse
 
 
 def _seqlens(seqlens_k, max_seqlen_k, dev):

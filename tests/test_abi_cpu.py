@@ -518,3 +518,42 @@ def test_noalloc_decode_rejects_sizes_beyond_its_scratch():
                                             None, 1, 4096, 4096, 32, 8, 128, ctypes.byref(p), 1,
                                             None)
     assert st == jlb.JL_ERR_INVALID_ARGUMENT
+
+
+def _dec3(**kw):
+    a = dict(o=FAKE, lse=FAKE * 2, q=FAKE * 3, kc=FAKE * 4, vc=FAKE * 5, sl=FAKE * 6, B=1,
+             max_k=4096, S_max=4096, Hq=32, Hkv=8, d=128, params=_params(), dtype=1,
+             ws=FAKE * 8, ws_bytes=1 << 40, stream=None)
+    a.update(kw)
+    p = a["params"]
+    return jlb.lib().jl_bifocal_decode_three_call(
+        a["o"], a["lse"], a["q"], a["kc"], a["vc"], a["sl"], a["B"], a["max_k"], a["S_max"],
+        a["Hq"], a["Hkv"], a["d"], None if p is None else ctypes.byref(p), a["dtype"], a["ws"],
+        a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(o=None), 1), (dict(sl=None), 1), (dict(ws=None), 1), (dict(params=None), 1),
+    (dict(params=_params(bifocal=0)), 1), (dict(params=_params(bifocal=2)), 1),
+    (dict(params=_params(precise=1)), 2), (dict(dtype=0), 2), (dict(B=0), 1),
+    (dict(S_max=100), 1), (dict(Hq=30), 1), (dict(Hq=64, Hkv=2), 2), (dict(d=96), 2),
+    (dict(ws_bytes=4096), 3), (dict(ws=FAKE * 8 + 8), 1), (dict(o=FAKE * 3), 1),
+    (dict(q=FAKE * 3 + 8), 1),
+])
+def test_three_call_decode_validation(kw, status):
+    assert _dec3(**kw) == status
+
+
+def test_three_call_decode_workspace_query():
+    L = jlb.lib()
+    n, m = ctypes.c_size_t(), ctypes.c_size_t()
+    p = _params()
+    assert L.jl_bifocal_decode_three_call_workspace(1, 131072, 32, 8, 128, 1, ctypes.byref(p),
+                                                    ctypes.byref(n)) == 0
+    # at least the remapped copy of the keys (bf16) and the decode partials
+    assert L.jl_bifocal_decode_workspace(1, 131072, 32, 8, 128, 1, ctypes.byref(m)) == 0
+    assert n.value >= 131072 * 8 * 128 * 2 + m.value
+    assert L.jl_bifocal_decode_three_call_workspace(1, 100, 32, 8, 128, 0, ctypes.byref(p),
+                                                    ctypes.byref(n)) == 2
+    assert L.jl_bifocal_decode_three_call_workspace(1, 100, 32, 8, 128, 1, None,
+                                                    ctypes.byref(n)) == 1

@@ -95,3 +95,25 @@ def test_three_call_qwen3_8b_131072_every_workgroup():
     mask[::4] = True
     check_prefill(o, lse, o_ref, lse_ref, rows, torch.bfloat16, "three-call " + c.name,
                   o_plain=o_plain, disc_rows=mask)
+
+
+def test_three_call_tiny_remote_mass_full():
+    """w_local just below L: the last rows have only a few remote keys, so the
+    remote part e^lse_B o_B - e^lse_C o_C is a small difference of two nearly
+    equal terms.  The calls' fp32 outputs keep it accurate; every row against
+    the oracle."""
+    T, Hq, Hkv, d = 3000, 4, 2, 128
+    p = Params(1000, 2990, 1e4, 1.0 / math.sqrt(d))
+    q, k, v = inputs.prefill_inputs(T, Hq, Hkv, d, seed=77)
+    o, lse = _three(q, k, v, p)
+    torch.cuda.synchronize()
+    rows = list(range(T))
+    o_ref, lse_ref = oracle_prefill_rows(q, k, v, p, rows)
+    check_prefill(o, lse, o_ref, lse_ref, rows, torch.bfloat16, "three-call tiny remote mass")
+    # the rows that have remote keys differ from plain attention by more than the error
+    tail = list(range(2990, T))
+    o_pl, _ = oracle_prefill_rows(q, k, v, p, tail, bifocal=False)
+    idx = torch.as_tensor(tail, device=o.device)
+    err = np.linalg.norm(o.index_select(0, idx).float().cpu().double().numpy() - o_ref[2990:])
+    say("tiny remote mass: |o_bif - o_plain| = %.3g, |o_gpu - o_bif| = %.3g" % (
+        np.linalg.norm(o_ref[2990:] - o_pl), err))
