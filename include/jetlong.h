@@ -24,12 +24,19 @@
  *   - Scores are softmax_scale * <q_rot, k_rot>; lse is the natural log of the
  *     sum of exp(score) over the keys of a row.
  *   - All pointers except those marked "host" are device pointers owned by the
- *     caller.  The library allocates no device memory, keeps no state other
- *     than a thread-local error string, and never synchronizes: work is
- *     enqueued on `stream` (a hipStream_t; NULL is the default stream) and is
- *     complete when the caller synchronizes that stream.  A call enqueues
- *     kernels only (no memset, copy or allocation), so it can be captured in a
- *     HIP graph and replayed; a replay reads the buffers the call was given.
+ *     caller.  The library allocates no device memory and never synchronizes:
+ *     work is enqueued on `stream` (a hipStream_t; NULL is the default stream)
+ *     and is complete when the caller synchronizes that stream.  A call
+ *     enqueues kernels only (no memset, copy or allocation), so it can be
+ *     captured in a HIP graph and replayed; a replay reads the buffers the
+ *     call was given.  State the library keeps: a thread-local error string;
+ *     the kernel-timing record while jl_profile_enable(1) is in force
+ *     (process-wide, see there); the static scratch of
+ *     jl_bifocal_decode_noalloc (one array per device).  Workspace sizes and
+ *     launch shapes depend only on the arguments.  Two environment variables
+ *     are read for debugging only: JL_LOG (print failures to stderr) and
+ *     JL_DEBUG_SYNC (synchronize the stream after each call and report its
+ *     errors); neither changes results or sizes.
  *   - Every argument is validated on the host before any HIP call.  A failing
  *     entry point launches nothing and returns a status; jl_last_error() then
  *     holds a description.  Values that live in device memory (cu_seqlens,
@@ -149,7 +156,9 @@ jl_status jl_bifocal_prefill_workspace(int64_t T, int32_t n_seqs, int32_t Hq, in
  * The bf16 path forms q k^T and P v on fp16 MFMA operands (fp32 accumulate):
  * inputs must be finite and the rotated q (times softmax_scale * log2 e), the
  * rotated k and v must stay below 65504 in magnitude.  Device data is not
- * range-checked; values outside that range give inf/NaN outputs.
+ * range-checked and operands are not clamped: a row that scores an operand
+ * beyond that range gets a non-finite o or lse (rows that never see it are
+ * unaffected), so such input shows rather than giving a quietly wrong value.
  */
 jl_status jl_bifocal_prefill(void* o, float* lse, const void* q, const void* k, const void* v,
                              const int32_t* cu_seqlens, int32_t n_seqs, int64_t T,
@@ -431,11 +440,16 @@ jl_status jl_debug_index_math(int64_t L, int32_t w_pretrained, int32_t w_local, 
 jl_status jl_debug_stream_read(const void* src, size_t bytes, uint32_t* partial_sums, void* stream);
 
 /*
- * Kernel timing (profiling aid).  While enabled, every kernel the library
- * launches is bracketed by HIP events on its stream; jl_profile_read()
- * synchronizes those events and reports, per kernel name, the launch count
- * and the summed duration in milliseconds.  Enabling or disabling clears the
- * record.  Host pointers; `names` receives static strings.
+ * Kernel timing (profiling aid, off by default).  While enabled, every kernel
+ * the library launches is bracketed by HIP events recorded on its stream;
+ * jl_profile_read() synchronizes those events and reports, per kernel name,
+ * the launch count and the summed duration in milliseconds, then clears the
+ * record.  Enabling or disabling clears it too.  The record is one
+ * process-wide list guarded by a mutex (calls from several threads are
+ * safe, their launches share it); the events come from a pool that grows on
+ * demand (hipEventCreate, host-side only) and is reused.  While enabled,
+ * entry points are no longer free of state and should not be captured in a
+ * HIP graph.  Host pointers; `names` receives static strings.
  */
 jl_status jl_profile_enable(int32_t on);
 jl_status jl_profile_read(const char** names, int32_t* counts, double* total_ms, int32_t capacity,

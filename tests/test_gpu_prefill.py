@@ -303,3 +303,24 @@ def test_large_magnitude_channels_128k():
         scale[c] = vmax[c]
     _full_size(case, "qwen3_8b_L131072 outlier channels", every=4, o_scale=scale,
                modes=(True, False))
+
+
+def test_operands_beyond_fp16_range_are_not_clamped():
+    """The bf16 path's MFMA operands are fp16: a rotated key beyond 65504 is
+    not clamped to a finite value.  A row that scores it comes out
+    non-finite, so the failure shows; rows that never see that key are
+    unaffected and match the oracle."""
+    T, d, jbad = 300, 64, 200
+    p = Params(128, 32, 1e4, 1.0)
+    q, k, v = inputs.prefill_inputs(T, 1, 1, d, seed=99, q_scale=1.0 / math.sqrt(d))
+    q[jbad, 0, :] = 0.0
+    q[jbad, 0, 0] = 1.0  # the row at jbad scores its own key with standard RoPE: q . k
+    k[jbad, 0, :] = 0.0
+    k[jbad, 0, 0] = 1.0e5  # bf16 99840: beyond fp16 once rotated into either channel
+    o, lse = gpu_prefill(jl, q, k, v, p)
+    torch.cuda.synchronize()
+    row_ok = torch.isfinite(o.float()).all(dim=(1, 2)) & torch.isfinite(lse).all(dim=0)
+    assert not bool(row_ok[jbad]), "a row scoring an out-of-range key must not look finite"
+    rows = list(range(jbad))
+    o_ref, lse_ref = oracle_prefill_rows(q, k, v, p, rows)
+    check_prefill(o, lse, o_ref, lse_ref, rows, torch.bfloat16, "rows before the bad key")
