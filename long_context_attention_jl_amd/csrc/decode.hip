@@ -443,25 +443,18 @@ void decode_split_kernel(DecodeArgs a) {
         }
 }
 
-// OCP E4M3 codes (4 per 32-bit word, little-endian) widened exactly; the
-// hardware conversion v_cvt_pk_f32_fp8 reads E4M3 in this format on gfx950.
-__device__ __forceinline__ void e4m3x8_to_f32(uint32_t w0, uint32_t w1, float* f) {
-    const float2v a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w0, false);
-    const float2v b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w0, true);
-    const float2v c = __builtin_amdgcn_cvt_pk_f32_fp8((int)w1, false);
-    const float2v d = __builtin_amdgcn_cvt_pk_f32_fp8((int)w1, true);
-    f[0] = a[0]; f[1] = a[1]; f[2] = b[0]; f[3] = b[1];
-    f[4] = c[0]; f[5] = c[1]; f[6] = d[0]; f[7] = d[1];
-}
-// the same as fp16 (an E4M3 value has 4 significant bits and an exponent in
-// [-9, 8]: fp16 holds it exactly)
+// 8 OCP E4M3 codes (4 per 32-bit word, little-endian) as fp16: an E4M3
+// value has 4 significant bits and an exponent in [-9, 8], so fp16 holds it
+// exactly.  gfx950's v_cvt_scalef32_pk_f16_fp8 widens two codes straight to
+// packed fp16 (times a power-of-two scale, here 1), four instructions for 8
+// codes; NaN codes stay NaN.
 __device__ __forceinline__ f16x8 e4m3x8_to_f16(uint32_t w0, uint32_t w1) {
-    float f[8];
-    e4m3x8_to_f32(w0, w1, f);
-    f16x8 r;
-#pragma unroll
-    for (int x = 0; x < 8; ++x) r[x] = (f16)f[x];
-    return r;
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    const h2 a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.0f, false);
+    const h2 b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.0f, true);
+    const h2 c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.0f, false);
+    const h2 d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.0f, true);
+    return f16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 // 8 bf16 keys as fp16 MFMA operands (exact for magnitudes in [2^-14, 65504])
 __device__ __forceinline__ f16x8 bf16x8_to_f16(const bf16x8& x) {

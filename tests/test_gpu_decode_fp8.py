@@ -47,6 +47,34 @@ def test_quantize_bit_exact(ntok, H, d):
     assert sat.any() and (ref[sat] & 0x7F == 0x7E).all()
 
 
+@pytest.mark.parametrize("bifocal", [True, False])
+def test_fp8_every_code_widens_exactly(bifocal):
+    """A one-key decode returns the key's value row times the value scale
+    exactly (the one probability is 1).  The value rows hold all 256 codes
+    (kv head 0 codes 0..127, head 1 codes 128..255), so the output is the
+    E4M3 value of every code (NaN for the two NaN codes), checked against the
+    oracle's decoder."""
+    Hq, Hkv, d = 8, 2, 128
+    g = torch.Generator("cpu").manual_seed(5)
+    q = torch.randn(1, Hq, d, generator=g).to(torch.bfloat16)
+    k8 = torch.zeros(1, 4, Hkv, d, dtype=torch.uint8)
+    k8[0, 0] = torch.randint(0, 0x70, (Hkv, d), generator=g, dtype=torch.uint8)
+    v8 = torch.zeros(1, 4, Hkv, d, dtype=torch.uint8)
+    v8[0, 0] = torch.arange(256, dtype=torch.int32).reshape(Hkv, d).to(torch.uint8)
+    ones = torch.ones(Hkv)
+    p = Params(64, 16, 1e4, 1.0 / math.sqrt(d), bifocal=bifocal)
+    say("fp8 every code bifocal=%s" % bifocal)
+    o, _ = jl.bifocal_decode_fp8(q.cuda(), k8.cuda(), v8.cuda(), ones, ones, [1], **_kw(p))
+    torch.cuda.synchronize()
+    want = np.array([oracle.e4m3_value(c) for c in range(256)]).reshape(Hkv, d)
+    got = o.float().cpu().double().numpy()[0].reshape(Hkv, Hq // Hkv, d)
+    for h in range(Hkv):
+        for r in range(Hq // Hkv):
+            assert np.array_equal(np.isnan(got[h, r]), np.isnan(want[h])), (h, r)
+            ok = ~np.isnan(want[h])
+            assert np.array_equal(got[h, r][ok], want[h][ok]), (h, r)
+
+
 @pytest.mark.parametrize("B,S,Hq,Hkv,d,lens,w_pre,w_local", [
     (3, 1500, 8, 2, 128, [1500, 1, 777], 300, 100),   # mixed lengths, G = 5, 3, 1
     (1, 2600, 16, 2, 128, [2600], 700, 2200),          # GQA 8, window wider than a chunk
