@@ -526,6 +526,9 @@ __global__ __launch_bounds__(512) void decode_split_bf16_kernel(DecodeArgs a) {
     // stage st of this chunk (remote stages), the last row R(p)
     __shared__ float2 qtab[(kDecodeMaxStagesB + 1) * HALF];
     __shared__ __align__(16) char vs[kWavesB * SLOT];  // per wave: the V tile in use
+    // per wave (PACK): the turned query, fp16 hi rows then lo rows
+    constexpr int QRS = D + 8;  // row stride (halves)
+    __shared__ __align__(16) f16 qs[PACK ? kWavesB * 2 * GQ * QRS : 8];
     __shared__ int32_t ptab[PAGED ? kDecodeMaxPages : 1];  // page numbers of this chunk
     // tiles finished per wave.  Waves w and w + 4 share a SIMD, whose issue
     // arbiter favours the older wave: left alone, waves 0-3 finish their
@@ -647,18 +650,37 @@ __global__ __launch_bounds__(512) void decode_split_bf16_kernel(DecodeArgs a) {
     VRAW vA[NI], vB[NI], vC[NI];
 
     KRAW kA[NST], kB[NST], kC[NST];
-    // query first (unconditional loads from a clamped head; other lanes zeroed)
-    const int hq = PACK ? (n & (GQ - 1)) : n;
-    const bool qlo = PACK && n >= GQ;
-    bf16x8 qraw[NST];
+    // query first (unconditional loads from a clamped head; heads past the
+    // group are zeroed).  With PACK each stage's query rotation is done once
+    // per element: lane l turns QPL pairs (i, i + HALF) of head qh and writes
+    // the fp16 hi and lo parts to its wave's rows of qs (hi rows 0..GQ-1, lo
+    // rows GQ..2GQ-1), from which every lane reads its MFMA operand: column
+    // n < GQ the hi part of head n, column GQ + h the lo part of head h
+    // (columns from 2 GQ on repeat the first ones; their scores are never
+    // used).  Without PACK (16 heads) the lanes' operand elements are all
+    // distinct and each lane turns its own.
+    constexpr int QPL = PACK ? GQ * HALF / 64 : 1;  // pairs per lane
+    const int qh = PACK ? lane / (64 / GQ) : n;
+    const int qi0 = PACK ? (lane % (64 / GQ)) * QPL : 0;
+    float qf[PACK ? 2 * QPL : 1];  // PACK: elements i and i + HALF of the lane's pairs
+    bf16x8 qraw[PACK ? 1 : NST];
     {
-        const bool qok = hq < grp && (!PACK || n < 2 * GQ);
-        const int hq_c = min(hq, grp - 1);
-        const bf16* qp = (const bf16*)a.q + ((int64_t)b * a.Hq + kvh_c * grp + hq_c) * D + 8 * c;
+        const bool qok = qh < grp;
+        const int qh_c = min(qh, grp - 1);
+        const bf16* qp = (const bf16*)a.q + ((int64_t)b * a.Hq + kvh_c * grp + qh_c) * D;
+        if constexpr (PACK) {
 #pragma unroll
-        for (int s = 0; s < NST; ++s) {
-            const bf16x8 x = *reinterpret_cast<const bf16x8*>(qp + 32 * s);
-            qraw[s] = qok ? x : bf16x8{};
+            for (int k = 0; k < QPL; ++k) {
+                const float x0 = (float)qp[qi0 + k], x1 = (float)qp[HALF + qi0 + k];
+                qf[k] = qok ? x0 : 0.0f;
+                qf[QPL + k] = qok ? x1 : 0.0f;
+            }
+        } else {
+#pragma unroll
+            for (int s = 0; s < NST; ++s) {
+                const bf16x8 x = *reinterpret_cast<const bf16x8*>(qp + 8 * c + 32 * s);
+                qraw[s] = qok ? x : bf16x8{};
+            }
         }
     }
     // the first tile's loads go out before the angle tables, the second's
@@ -715,27 +737,47 @@ __global__ __launch_bounds__(512) void decode_split_bf16_kernel(DecodeArgs a) {
     OV Q[NST];
     OV Qlo[PACK ? 1 : NST];
     auto rotate_q = [&](int row) __attribute__((always_inline)) {
-        const float2* qt = qtab + row * HALF + 8 * c;
+        if constexpr (PACK) {
+            typedef _Float16 QV __attribute__((ext_vector_type(QPL)));
+            const float2* qt = qtab + row * HALF + qi0;
+            QV h0, h1, l0, l1;
 #pragma unroll
-        for (int s = 0; s < NH; ++s)
-#pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const float2 cs = qt[32 * s + u];
-                const float x0 = (float)qraw[s][u], x1 = (float)qraw[s + NH][u];
+            for (int k = 0; k < QPL; ++k) {
+                const float2 cs = qt[k];
+                const float x0 = qf[k], x1 = qf[QPL + k];
                 const float y0 = (x0 * cs.x - x1 * cs.y) * qscale;
                 const float y1 = (x1 * cs.x + x0 * cs.y) * qscale;
-                const OT h0 = (OT)y0, h1 = (OT)y1;
-                const OT l0 = (OT)(y0 - (float)h0), l1 = (OT)(y1 - (float)h1);
-                if constexpr (PACK) {
-                    Q[s][u] = qlo ? l0 : h0;
-                    Q[s + NH][u] = qlo ? l1 : h1;
-                } else {
+                h0[k] = (OT)y0;
+                h1[k] = (OT)y1;
+                l0[k] = (OT)(y0 - (float)h0[k]);
+                l1[k] = (OT)(y1 - (float)h1[k]);
+            }
+            // the wave writes, then reads its own rows: LDS keeps its order
+            f16* w = qs + wave * (2 * GQ * QRS);
+            *reinterpret_cast<QV*>(w + qh * QRS + qi0) = h0;
+            *reinterpret_cast<QV*>(w + qh * QRS + HALF + qi0) = h1;
+            *reinterpret_cast<QV*>(w + (GQ + qh) * QRS + qi0) = l0;
+            *reinterpret_cast<QV*>(w + (GQ + qh) * QRS + HALF + qi0) = l1;
+            const f16* r = w + (n & (2 * GQ - 1)) * QRS + 8 * c;
+#pragma unroll
+            for (int s = 0; s < NST; ++s) Q[s] = *reinterpret_cast<const f16x8*>(r + 32 * s);
+        } else {
+            const float2* qt = qtab + row * HALF + 8 * c;
+#pragma unroll
+            for (int s = 0; s < NH; ++s)
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const float2 cs = qt[32 * s + u];
+                    const float x0 = (float)qraw[s][u], x1 = (float)qraw[s + NH][u];
+                    const float y0 = (x0 * cs.x - x1 * cs.y) * qscale;
+                    const float y1 = (x1 * cs.x + x0 * cs.y) * qscale;
+                    const OT h0 = (OT)y0, h1 = (OT)y1;
                     Q[s][u] = h0;
                     Q[s + NH][u] = h1;
-                    Qlo[s][u] = l0;
-                    Qlo[s + NH][u] = l1;
+                    Qlo[s][u] = (OT)(y0 - (float)h0);
+                    Qlo[s + NH][u] = (OT)(y1 - (float)h1);
                 }
-            }
+        }
     };
     bool q_local = false;
 
