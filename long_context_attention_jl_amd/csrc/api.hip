@@ -144,6 +144,12 @@ DecodeLayout decode_layout(int32_t B, int32_t max_seqlen_k, int32_t Hq, int32_t 
     int64_t chunk = (span + want - 1) / want;
     chunk = (chunk + stage - 1) / stage * stage;
     if (b16 && chunk > (int64_t)kDecodeMaxStagesB * stage) chunk = (int64_t)kDecodeMaxStagesB * stage;
+    if (b16) {  // the kernel's byte offsets within a chunk (plus loads ahead) stay 32-bit
+        const int64_t rowb = (int64_t)Hkv * d * 2;
+        int64_t cap = ((int64_t)INT32_MAX / rowb - 64) / stage * stage;
+        if (cap < stage) cap = stage;
+        if (chunk > cap) chunk = cap;
+    }
     L.chunk = (int32_t)chunk;
     L.n_splits = (int32_t)((span + chunk - 1) / chunk);
     size_t off = 0;

@@ -473,6 +473,20 @@ __device__ __forceinline__ f32x4 mfma16k16h(s16x4 a, s16x4 b, f32x4 c) {
                                                  __builtin_bit_cast(f16x4, b), c, 0, 0, 0);
 }
 
+// Buffer resource word 3 for raw (unstructured) buffers on gfx9-family
+// chips: 32-bit data format, no swizzle; out-of-range loads return zeros.
+constexpr int kBufferRsrcWord3 = 0x00020000;
+// 8 or 16 bytes at byte offset off of a raw buffer (zeros past its range)
+template <typename T>
+__device__ __forceinline__ T buffer_load(__amdgpu_buffer_rsrc_t r, int32_t off) {
+    if constexpr (sizeof(T) == 8) {
+        return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+    } else {
+        static_assert(sizeof(T) == 16, "8- or 16-byte loads");
+        return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+    }
+}
+
 // bf16 decode.  Same scoring as above, with QK^T on fp16 operands: the
 // query is an fp16 hi + lo pair, stored keys widen to fp16 (exact), and a
 // remote key is turned on packed fp16 by an fp16 (cos, sin) table, a few
@@ -484,15 +498,16 @@ __device__ __forceinline__ f32x4 mfma16k16h(s16x4 a, s16x4 b, f32x4 c) {
 // the A operand layout (lane (n, c) holds keys 4c..4c+3 of query column n),
 // rounded to bf16; the row sums use the same rounded values.  K and V tiles
 // stay two ahead in registers.  All loads are unconditional (indices clamped
-// to valid rows), so the memory stream has no branches and the compiler's
-// waits stay exact.
+// to the chunk's rows, or flat caches read through buffer resources that
+// return zeros outside them), so the memory stream has no branches and the
+// compiler's waits stay exact.
 // PAGED: the cache is a pool of pages of 2^page_shift rows addressed through
 // a per-sequence block table (each workgroup copies its chunk's page numbers
 // to LDS, clamped to the pool, so a bad table entry cannot read outside it).
 // FP8: the cache holds OCP E4M3 codes with one scale per kv head.  Codes
 // widen exactly to fp16 (keys and the V tile in LDS); P is fp16 too.  The
-// key scale multiplies the finished scores and the value scale the partial
-// output.
+// key scale enters the query's scale and the value scale multiplies the
+// partial output.
 // PREC (split precision, bf16 caches): remote keys are turned in fp32 against
 // an fp32 table and split into fp16 hi + lo operands (two products per
 // k-step), so a dominant remote key's score carries no fp16 rounding.
@@ -582,7 +597,12 @@ __global__ __launch_bounds__(512) void decode_split_bf16_kernel(DecodeArgs a) {
     }
 
     // every load below is unconditional (branch-free memory stream, exact
-    // waits): indices are clamped to valid rows, masked keys weigh 0
+    // waits) and reads only rows of the chunk: the key index is clamped into
+    // [klo, kend), or (BUF: flat caches, up to 8 query heads per kv head,
+    // where the registers allow) the loads go through buffer resources whose
+    // range ends with row kend - 1, so that rows outside the chunk read as
+    // zeros.  Masked keys weigh 0 either way.
+    constexpr bool BUF = !PAGED && PACK;
     const int kvh_c = min(kvh, a.Hkv - 1);
     const int64_t boff = PAGED ? 0 : (int64_t)b * a.S_max * a.Hkv * D;
     const int64_t boff_k = PAGED ? 0 : (int64_t)b * (a.S_max_k ? a.S_max_k : a.S_max) * a.Hkv * D;
@@ -609,13 +629,28 @@ __global__ __launch_bounds__(512) void decode_split_bf16_kernel(DecodeArgs a) {
             return j;
         }
     };
-    // K of key j0 + n into registers (keys outside the chunk read a row
-    // inside it; their scores are masked)
+    // BUF: resources based at row klo of this kv head (offsets in bytes from
+    // there, 32-bit: a chunk spans at most a few MB), one add per load group
+    // and tile in place of clamping and 64-bit row arithmetic
+    constexpr int ES = (int)sizeof(TC);
+    const int32_t rsb = (int32_t)rstride * ES;  // bytes between rows
+    const int32_t nrec = (kend - klo - 1) * rsb + D * ES;
+    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(kc + (int64_t)klo * rstride), (short)0, BUF ? nrec : 0, kBufferRsrcWord3);
+    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(vc + (int64_t)klo * rstride), (short)0, BUF ? nrec : 0, kBufferRsrcWord3);
+    // K of key j0 + n into registers (keys outside the chunk: masked)
     auto load_k = [&](int32_t j0, KRAW* kd) __attribute__((always_inline)) {
-        const int32_t kj = min(max(j0 + n, klo), khi);
+        if constexpr (!BUF) {
+            const int32_t kj = min(max(j0 + n, klo), khi);
 #pragma unroll
-        for (int s = 0; s < NST; ++s)
-            kd[s] = *reinterpret_cast<const KRAW*>(kc + row_of(kj) * rstride + 32 * s + 8 * c);
+            for (int s = 0; s < NST; ++s)
+                kd[s] = *reinterpret_cast<const KRAW*>(kc + row_of(kj) * rstride + 32 * s + 8 * c);
+        } else {
+            const int32_t off = (j0 - klo + n) * rsb + 8 * c * ES;
+#pragma unroll
+            for (int s = 0; s < NST; ++s) kd[s] = buffer_load<KRAW>(rk, off + 32 * s * ES);
+        }
     };
     // V tiles are staged in registers two tiles ahead (load r of a lane
     // reads 16 bytes of key RPI r + lane / CPR, so one load instruction
@@ -625,8 +660,12 @@ __global__ __launch_bounds__(512) void decode_split_bf16_kernel(DecodeArgs a) {
         const int q = lane / CPR, ch = lane % CPR;
 #pragma unroll
         for (int r = 0; r < NI; ++r) {
-            const int32_t key = min(max(j0 + RPI * r + q, klo), khi);
-            vd[r] = *reinterpret_cast<const VRAW*>(vc + row_of(key) * rstride + VEL * ch);
+            if constexpr (!BUF) {
+                const int32_t key = min(max(j0 + RPI * r + q, klo), khi);
+                vd[r] = *reinterpret_cast<const VRAW*>(vc + row_of(key) * rstride + VEL * ch);
+            } else {
+                vd[r] = buffer_load<VRAW>(rv, (j0 - klo + RPI * r + q) * rsb + 16 * ch);
+            }
         }
     };
     auto store_vr = [&](const VRAW* vsrc, char* dst) __attribute__((always_inline)) {
@@ -732,8 +771,9 @@ __global__ __launch_bounds__(512) void decode_split_bf16_kernel(DecodeArgs a) {
     load_vr(kbeg + kTile, vB);
 
     // ---- query (as in the generic kernel) ----
-    const float qscale = a.softmax_scale * kLog2e;
+    // fp8: the key scale enters the query's scale (a score is linear in k)
     const float kscale = FP8 && a.k_scale ? a.k_scale[kvh_c] : 1.0f;
+    const float qscale = a.softmax_scale * kLog2e * kscale;
     OV Q[NST];
     OV Qlo[PACK ? 1 : NST];
     auto rotate_q = [&](int row) __attribute__((always_inline)) {
@@ -785,10 +825,6 @@ __global__ __launch_bounds__(512) void decode_split_bf16_kernel(DecodeArgs a) {
         if constexpr (PACK) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) acc[i] += __shfl_xor(acc[i], GQ);
-        }
-        if constexpr (FP8) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) acc[i] *= kscale;
         }
         return acc;
     };
