@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define JL_ABI_VERSION 2
+#define JL_ABI_VERSION 3
 
 typedef enum {
     JL_OK = 0,
@@ -91,6 +91,15 @@ typedef struct {
                            /*    (the stored keys and the query already are exact / split).*/
                            /*    Ignored by the fp32 paths (already split); fp8 decode:   */
                            /*    JL_ERR_UNSUPPORTED.  Must be 0 or 1.                     */
+    int32_t reuse_images;  /* chunk calls only (ignored elsewhere); 0 or 1.  1: the      */
+                           /*    caller keeps the workspace from one chunk call to the    */
+                           /*    next on the same caches and changes no cache row below   */
+                           /*    the lengths an earlier call saw; key/value images that   */
+                           /*    call built are then reused while they still hold (same   */
+                           /*    caches, sizes and parameters, same G, for bifocal 2 the  */
+                           /*    same L), and only the new rows are turned.  0: rebuild   */
+                           /*    (the first call of every prefill: a workspace may hold   */
+                           /*    images of other caches that sat at the same addresses).  */
 } jl_params;
 
 /* JL_ABI_VERSION of the built library. */
@@ -348,11 +357,15 @@ jl_status jl_kv_quantize_fp8(void* out, const void* x, const float* scale, int64
                              int32_t H, int32_t d, void* stream);
 
 /* Bytes of device workspace the chunk calls below need for Tq query rows in
- * batch sequences of at most max_seqlen_k keys (bf16 only).  Besides the
- * key tiles it holds fp32 partials for calls whose grid is small (fewer than
- * two 256-row workgroups per compute unit, e.g. a 1024-row chunk of 32
- * heads): those split each row block's keys in up to four shares and merge
- * the shares in LogSumExp space.  params as for jl_bifocal_prefill_workspace
+ * batch sequences of at most max_seqlen_k keys (bf16 only).  It holds the
+ * fp16 images of the cache's key and value tiles (each sequence a fixed
+ * stretch of max_seqlen_k keys), a small record of what they were built for
+ * (see jl_params.reuse_images), and fp32 partials for calls whose grid is
+ * small (fewer than two 256-row workgroups per compute unit, e.g. a 1024-row
+ * chunk of 32 heads): those split each row block's keys in up to four shares
+ * and merge the shares in LogSumExp space.  The images and the record sit at
+ * the same offsets for every Tq, so a workspace sized for the largest chunk
+ * serves every chunk size.  params as for jl_bifocal_prefill_workspace
  * (split-precision calls take no key shares). */
 jl_status jl_bifocal_prefill_chunk_workspace(int64_t Tq, int32_t batch, int32_t max_seqlen_k,
                                              int32_t Hq, int32_t Hkv, int32_t d, jl_dtype dtype,
@@ -379,6 +392,13 @@ jl_status jl_bifocal_prefill_chunk_workspace(int64_t Tq, int32_t batch, int32_t 
  *   k_cache, v_cache  [batch][S_max][Hkv][d] bf16, read-only.
  *   seqlens_k     device int32 [batch], C_b <= L_b <= max_seqlen_k <= S_max.
  *   workspace     at least jl_bifocal_prefill_chunk_workspace() bytes.
+ *                 Each call turns the cache rows [0, L_b) into fp16 images
+ *                 (remote keys to remapped RoPE) in the workspace; with
+ *                 params->reuse_images = 1 it turns only the rows past the
+ *                 whole 64-key tiles an earlier call on this workspace built
+ *                 and that still hold (a chunked prefill then turns each
+ *                 row about once).  The first call of a prefill passes 0.
+ *                 Calls that share a workspace must not overlap.
  * If the device arrays break their contract nothing is read or written
  * outside the buffers and o, lse are left unwritten.  bf16 only; d in
  * {64, 128}; rotated q and k must stay below 65504 in magnitude (fp16 MFMA

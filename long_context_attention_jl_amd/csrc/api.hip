@@ -194,6 +194,8 @@ static jl_status check_params(const jl_params* p) {
         return fail(JL_ERR_INVALID_ARGUMENT, "bifocal must be 0, 1 or 2");
     if (p->precise != 0 && p->precise != 1)
         return fail(JL_ERR_INVALID_ARGUMENT, "precise must be 0 or 1");
+    if (p->reuse_images != 0 && p->reuse_images != 1)
+        return fail(JL_ERR_INVALID_ARGUMENT, "reuse_images must be 0 or 1");
     return JL_OK;
 }
 
@@ -818,11 +820,15 @@ static jl_status chunk_sizes_ok(int32_t batch, int32_t max_seqlen_k) {
     return JL_OK;
 }
 
-// Workspace of a chunk call: the prefill layout for the cache keys, then the
-// key-split partials.  A call whose main-rows grid holds fewer than
-// kChunkTargetWgs workgroups (two per compute unit) splits each row block's key tiles in up to
-// kChunkMaxSplit shares; the partials are sized for the most shares Tq
-// query rows can need (every row block holds at most 256 of them).
+// Workspace of a chunk call: the prefill layout for the cache keys (each
+// sequence a fixed stretch of max_seqlen_k keys), the record of the images it
+// holds, then the key-split partials.  The images and the record sit at
+// offsets that depend on batch, max_seqlen_k, Hkv, d and the precise flag
+// only, so that calls with other chunk sizes find them.  A call whose
+// main-rows grid holds fewer than kChunkTargetWgs workgroups (two per compute
+// unit) splits each row block's key tiles in up to kChunkMaxSplit shares; the
+// partials are sized for the most shares Tq query rows can need (every row
+// block holds at most 256 of them).
 constexpr int kChunkTargetWgs = 512;  // two workgroups per compute unit
 constexpr int kChunkMaxSplit = 4;
 static int chunk_split_bound(int64_t wgs) {
@@ -833,7 +839,7 @@ static int chunk_split_bound(int64_t wgs) {
 struct ChunkLayout {
     PrefillLayout pl;
     int kmax;
-    size_t part_o, part_ml, total;
+    size_t state, part_o, part_ml, total;
 };
 static ChunkLayout chunk_layout(int64_t Tq, int32_t batch, int32_t max_seqlen_k, int32_t Hq,
                                 int32_t Hkv, int32_t d, int precise) {
@@ -842,6 +848,8 @@ static ChunkLayout chunk_layout(int64_t Tq, int32_t batch, int32_t max_seqlen_k,
     // split-precision calls run every row in one kernel without key shares
     L.kmax = precise ? 1 : chunk_split_bound((int64_t)Hq * ((Tq + kBM - 1) / kBM));
     size_t off = align256(L.pl.total);
+    L.state = off;
+    off = align256(off + image_state_bytes(batch));
     if (L.kmax > 1) {
         L.part_o = off;
         off = align256(off + (size_t)L.kmax * Tq * Hq * d * sizeof(float));
@@ -871,6 +879,25 @@ jl_status jl_bifocal_prefill_chunk_workspace(int64_t Tq, int32_t batch, int32_t 
     *bytes = chunk_layout(Tq, batch, max_seqlen_k, Hq, Hkv, d, precise_of(params)).total;
     g_err.clear();
     return JL_OK;
+}
+
+// FNV-1a over everything a chunk call's key/value images depend on besides
+// the cache rows and the lengths: the caches (and block table) by address,
+// their geometry, the layout's sizes and the parameters the rotations use.
+static uint64_t image_fingerprint(const PrefillArgs& a, const jl_params* p) {
+    uint64_t h = 0xcbf29ce484222325ULL;
+    auto mix = [&](const void* x, size_t n) {
+        const unsigned char* c = (const unsigned char*)x;
+        for (size_t i = 0; i < n; ++i) h = (h ^ c[i]) * 0x100000001b3ULL;
+    };
+    const uintptr_t ptrs[3] = {(uintptr_t)a.k, (uintptr_t)a.v, (uintptr_t)a.block_table};
+    const int64_t ints[10] = {a.S_max, a.page_shift, a.n_pages, a.bt_stride, a.Hkv, a.d,
+                              a.n_seqs, a.max_seqlen_k, p->bifocal, p->precise};
+    mix(ptrs, sizeof(ptrs));
+    mix(ints, sizeof(ints));
+    mix(&p->rope_base, sizeof(p->rope_base));
+    mix(&p->w_pretrained, sizeof(p->w_pretrained));
+    return h;
 }
 
 // Shared checks and launches of the flat and paged chunk calls.
@@ -929,9 +956,13 @@ static jl_status chunk_call(PrefillArgs& a, const int32_t* cu_seqlens_q,
     a.w_pretrained = params->w_pretrained;
     a.precise = params->precise;
     hipStream_t s = (hipStream_t)stream;
-    hipError_t e = launch_plan_chunk((int32_t*)((char*)workspace + lay.plan), cu_seqlens_q,
-                                     seqlens_k, a.n_seqs, a.T, a.max_seqlen, a.max_seqlen_k,
-                                     params->w_pretrained, params->precise, s);
+    // the plan also rewrites the image record; the pre-pass launched next
+    // builds what the record then claims
+    hipError_t e = launch_plan_chunk((int32_t*)((char*)workspace + lay.plan),
+                                     (char*)workspace + cl.state, image_fingerprint(a, params),
+                                     params->reuse_images, cu_seqlens_q, seqlens_k, a.n_seqs, a.T,
+                                     a.max_seqlen, a.max_seqlen_k, params->w_pretrained,
+                                     params->precise, params->bifocal, s);
     if (e != hipSuccess) return hip_fail(e, "plan launch");
     e = launch_kv_prepass(a, dtype, s);
     if (e != hipSuccess) return hip_fail(e, "key/value pre-pass launch");

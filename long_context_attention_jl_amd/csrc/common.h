@@ -35,7 +35,7 @@ constexpr int kBM = kWaveRows * kWaves;  // 256 query rows per workgroup
 // path: those rows see few keys, so the LSE inherits the rounding of a single
 // score almost undiluted.  Keys they read are < kPreciseRows as well.
 constexpr int kPreciseRows = 2048;
-constexpr int kPlanFields = 9;      // int32 fields per sequence in the plan
+constexpr int kPlanFields = 10;     // int32 fields per sequence in the plan
 
 // Key and value tiles are stored in the workspace exactly as they sit in LDS
 // (rows padded by 8 halves against bank conflicts), so the prefill kernel
@@ -55,9 +55,22 @@ enum PlanField {
     kPlanTile0 = 5,   // kPlanPadOff / kBN
     kPlanLoTile0 = 6, // kPlanLoOff / kBN
     kPlanBad = 7,     // nonzero in entry n_seqs if cu_seqlens broke its contract
-    kPlanQ0 = 8       // position of the first query row: 0, or L_s - C_s for a chunk of
+    kPlanQ0 = 8,      // position of the first query row: 0, or L_s - C_s for a chunk of
                       // C_s new rows appended to a cache
+    kPlanKeep = 9     // chunk calls: leading key tiles whose workspace images an earlier
+                      // call built and that are still valid (the pre-pass skips them)
 };
+
+// Record of the key/value images a chunk call leaves in its workspace (read
+// by the next call that opts into reusing them): uint64 magic word, uint64
+// fingerprint of everything the images depend on besides the cache rows and
+// the lengths, then int32 [batch][2]: the key count L and group size G each
+// sequence's images were built for (L = 0: none).  Every image row below L
+// was built from the cache rows that call saw.
+constexpr uint64_t kImageMagic = 0x4a4c494d47535431ULL;
+__host__ __device__ constexpr size_t image_state_bytes(int32_t batch) {
+    return 16 + 8 * (size_t)batch;
+}
 
 // ---------------------------------------------------------------------------
 // Index math ([BT] §3.1, [TW] §二).  Integer only, so host and device agree

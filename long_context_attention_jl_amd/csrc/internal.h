@@ -103,9 +103,10 @@ struct PrefillArgs {
 
 // Plan of a chunk call: per sequence b, C_b = cu_q[b + 1] - cu_q[b] query rows
 // at positions seqlens_k[b] - C_b .. seqlens_k[b] - 1.
-hipError_t launch_plan_chunk(int32_t* plan, const int32_t* cu_q, const int32_t* seqlens_k,
+hipError_t launch_plan_chunk(int32_t* plan, void* image_state, uint64_t fingerprint, int32_t reuse,
+                             const int32_t* cu_q, const int32_t* seqlens_k,
                              int32_t B, int64_t Tq, int32_t max_seqlen_q, int32_t max_seqlen_k,
-                             int32_t w_pretrained, int32_t precise, hipStream_t s);
+                             int32_t w_pretrained, int32_t precise, int32_t bifocal, hipStream_t s);
 // out[t][h][:] = E4M3(x[t][h][:] / scale[h]) (fp32 quotient, round to nearest
 // even, saturating at +-448); x bf16 [ntok][H][d]
 hipError_t launch_e4m3_quant(uint8_t* out, const void* x, const float* scale, int64_t ntok,

@@ -42,7 +42,8 @@ _STATUS = {0: "JL_OK", 1: "JL_ERR_INVALID_ARGUMENT", 2: "JL_ERR_UNSUPPORTED",
 class jl_params(ctypes.Structure):
     _fields_ = [("w_pretrained", ctypes.c_int32), ("w_local", ctypes.c_int32),
                 ("rope_base", ctypes.c_double), ("softmax_scale", ctypes.c_float),
-                ("bifocal", ctypes.c_int32), ("precise", ctypes.c_int32)]
+                ("bifocal", ctypes.c_int32), ("precise", ctypes.c_int32),
+                ("reuse_images", ctypes.c_int32)]
 
 
 _lib = None
@@ -240,17 +241,20 @@ def _stream() -> int:
     return torch.cuda.current_stream().cuda_stream
 
 
-def _params(w_pretrained, w_local, rope_base, softmax_scale, bifocal, precise=False) -> jl_params:
+def _params(w_pretrained, w_local, rope_base, softmax_scale, bifocal, precise=False,
+            reuse_images=False) -> jl_params:
     """bifocal: False / 0 plain RoPE, True / 1 the method (integer grouping in the
     remote window), 2 continuous interpolation in the remote window.
-    precise: split-precision scores (for concentrated attention)."""
+    precise: split-precision scores (for concentrated attention).
+    reuse_images: chunk calls keep the key/value images of earlier calls on
+    the same workspace while they hold."""
     return jl_params(int(w_pretrained), int(w_local), float(rope_base), float(softmax_scale),
-                     int(bifocal), 1 if precise else 0)
+                     int(bifocal), 1 if precise else 0, 1 if reuse_images else 0)
 
 
 def _precise_params(precise) -> jl_params:
     """Params carrying only the precision choice (for the workspace queries)."""
-    return jl_params(1, 0, 1.0, 1.0, 1, 1 if precise else 0)
+    return jl_params(1, 0, 1.0, 1.0, 1, 1 if precise else 0, 0)
 
 
 def abi_version() -> int:
@@ -563,13 +567,21 @@ def bifocal_prefill_chunk(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch
                           bifocal: Union[bool, int] = True, cu_seqlens_q=None,
                           max_seqlen_q: Optional[int] = None,
                           max_seqlen_k: Optional[int] = None, precise: bool = False,
+                          reuse_images: bool = False,
                           workspace: Optional[torch.Tensor] = None,
                           out: Optional[torch.Tensor] = None,
                           lse_out: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
     """Chunked prefill ([TW] §三, [BT] §3.1, §3.3): q [Tq, Hq, d] raw, the new
     rows of each sequence packed by cu_seqlens_q (None: one chunk); caches
     [B, S_max, Hkv, d] bf16 of standard-RoPE keys holding seqlens_k[b] keys,
-    the chunk's own included.  Returns (o [Tq, Hq, d], lse [Hq, Tq])."""
+    the chunk's own included.  reuse_images (with a workspace the caller
+    keeps across the chunks of a prefill, sized for the largest chunk, and
+    the same max_seqlen_k every call): cache rows already turned by an
+    earlier call are not turned again.  The first chunk of a prefill passes
+    False (the workspace may hold images of other caches).
+    Returns (o [Tq, Hq, d], lse [Hq, Tq])."""
+    _expect(workspace is not None or not reuse_images,
+            "reuse_images needs a workspace the caller keeps between calls")
     _check_cache(q, k_cache, v_cache, out, None, batch_dim=True)
     _expect(q.dtype == torch.bfloat16, "chunked prefill takes bfloat16 tensors")
     _check_lens(len(seqlens_k), 1 if cu_seqlens_q is None else len(cu_seqlens_q) - 1, "seqlens_k")
@@ -581,7 +593,7 @@ def bifocal_prefill_chunk(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch
                                                     max_seqlen_k, dev, out, lse_out)
     ws = _workspace(prefill_chunk_workspace_bytes(q.shape[0], B, max_k, Hq, Hkv, d, precise), dev,
                     workspace)
-    p = _params(w_pretrained, w_local, rope_base, softmax_scale, bifocal, precise)
+    p = _params(w_pretrained, w_local, rope_base, softmax_scale, bifocal, precise, reuse_images)
     _check(lib().jl_bifocal_prefill_chunk(
         _dev(o, "o"), _dev(lse, "lse"), _dev(q, "q"), None if cu is None else _dev(cu, "cu"),
         q.shape[0], max_q, _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
@@ -598,11 +610,14 @@ def bifocal_prefill_chunk_paged(q: torch.Tensor, k_pages: torch.Tensor, v_pages:
                                 softmax_scale: float, bifocal: Union[bool, int] = True, cu_seqlens_q=None,
                                 max_seqlen_q: Optional[int] = None,
                                 max_seqlen_k: Optional[int] = None, precise: bool = False,
+                                reuse_images: bool = False,
                                 workspace: Optional[torch.Tensor] = None,
                                 out: Optional[torch.Tensor] = None,
                                 lse_out: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
     """bifocal_prefill_chunk on a paged cache: k_pages / v_pages
     [n_pages, page_size, Hkv, d] bf16, block_table [B, bt_stride] int32."""
+    _expect(workspace is not None or not reuse_images,
+            "reuse_images needs a workspace the caller keeps between calls")
     _check_cache(q, k_pages, v_pages, out, None, batch_dim=False)
     _expect(q.dtype == torch.bfloat16, "chunked prefill takes bfloat16 tensors")
     nb = 1 if cu_seqlens_q is None else len(cu_seqlens_q) - 1
@@ -616,7 +631,7 @@ def bifocal_prefill_chunk_paged(q: torch.Tensor, k_pages: torch.Tensor, v_pages:
     bt = block_table.to(device=dev, dtype=torch.int32).contiguous()
     ws = _workspace(prefill_chunk_workspace_bytes(q.shape[0], B, max_k, Hq, Hkv, d, precise), dev,
                     workspace)
-    p = _params(w_pretrained, w_local, rope_base, softmax_scale, bifocal, precise)
+    p = _params(w_pretrained, w_local, rope_base, softmax_scale, bifocal, precise, reuse_images)
     _check(lib().jl_bifocal_prefill_chunk_paged(
         _dev(o, "o"), _dev(lse, "lse"), _dev(q, "q"), None if cu is None else _dev(cu, "cu"),
         q.shape[0], max_q, _dev(k_pages, "k_pages"), _dev(v_pages, "v_pages"),

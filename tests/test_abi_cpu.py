@@ -35,7 +35,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert jlb.abi_version() == 2
+    assert jlb.abi_version() == 3
     L = jlb.lib()
     assert L.jl_status_string(0) == b"JL_OK"
     assert L.jl_status_string(4) == b"JL_ERR_HIP"
@@ -58,10 +58,10 @@ def test_group_size_rejects():
 
 def _params(**kw):
     d = dict(w_pretrained=32768, w_local=2048, rope_base=1e6, softmax_scale=0.088, bifocal=1,
-             precise=0)
+             precise=0, reuse_images=0)
     d.update(kw)
     return jlb.jl_params(d["w_pretrained"], d["w_local"], d["rope_base"], d["softmax_scale"],
-                         d["bifocal"], d["precise"])
+                         d["bifocal"], d["precise"], d["reuse_images"])
 
 
 def _prefill(**kw):
@@ -86,6 +86,7 @@ def _prefill(**kw):
     (dict(params=_params(softmax_scale=float("inf"))), 1), (dict(params=_params(bifocal=3)), 1),
     (dict(params=_params(bifocal=-1)), 1), (dict(params=_params(bifocal=2), dtype=0), 2),
     (dict(params=_params(precise=2)), 1), (dict(params=_params(precise=-1)), 1),
+    (dict(params=_params(reuse_images=2)), 1),
     (dict(ws_bytes=1000), 3), (dict(ws=FAKE * 8 + 4), 1), (dict(o=FAKE * 3), 1),
     (dict(krot=FAKE * 4), 1), (dict(cu=FAKE * 9, n_seqs=70000, T=1 << 20, max_seqlen=1024), 2),
 ])
@@ -267,13 +268,13 @@ def test_chunk_paged_validation(kw, status):
 
 
 def test_chunk_workspace_query():
-    """A large chunk needs the prefill workspace of its keys; a grid of fewer than
-    two workgroups per compute unit adds the key-split partials: up to 4 shares
-    x Tq x Hq x (d + 2) fp32."""
+    """A large chunk needs the prefill workspace of its keys plus the 256-byte
+    record of the images; a grid of fewer than two workgroups per compute unit
+    adds the key-split partials: up to 4 shares x Tq x Hq x (d + 2) fp32."""
     n = ctypes.c_size_t(0)
     L = jlb.lib()
     assert L.jl_bifocal_prefill_workspace(131072, 1, 32, 8, 128, 1, None, ctypes.byref(n)) == 0
-    base = n.value
+    base = n.value + 256
     # 32768 rows of 32 heads: 4096 row blocks >= 1024 workgroups, no split
     assert L.jl_bifocal_prefill_chunk_workspace(32768, 1, 131072, 32, 8, 128, 1, None, ctypes.byref(n)) == 0
     assert n.value == base

@@ -176,3 +176,115 @@ def test_chunk_precise_full_rows_and_key_split_off():
         o_ref, lse_ref = _oracle(q, kc, vc, [L], None, p)
         check_prefill(o, lse, o_ref, lse_ref, list(range(C)), torch.bfloat16,
                       "precise chunk L=%d C=%d" % (L, C))
+
+
+def _ws(Tq, B, max_k, Hq, Hkv, d, precise=False):
+    return torch.empty(jl.prefill_chunk_workspace_bytes(Tq, B, max_k, Hq, Hkv, d, precise),
+                       dtype=torch.uint8, device="cuda")
+
+
+def _chunk_step(q, kc, vc, lens, chunks, p, ws, reuse, max_k, **extra):
+    cu = [0]
+    for c in chunks:
+        cu.append(cu[-1] + c)
+    o, lse = jl.bifocal_prefill_chunk(q, kc, vc, lens, cu_seqlens_q=cu, max_seqlen_k=max_k,
+                                      workspace=ws, reuse_images=reuse, **_kw(p), **extra)
+    torch.cuda.synchronize()
+    return o.clone(), lse.clone(), cu
+
+
+def test_chunk_reuse_images_across_a_chunked_prefill():
+    """Two sequences grow over five chunk calls on one kept workspace with
+    reuse_images: G changes between calls (1 -> 2 -> 3 for the first, w_pretrained
+    1024), the second sequence skips a call (no new rows: its images must
+    survive) and then resumes.  Every call equals a call that rebuilds all
+    images on a fresh workspace, bit for bit; the last also meets the oracle."""
+    Hq, Hkv, d, S, max_k = 8, 2, 128, 2700, 2700
+    p = Params(1024, 256, 1e4, 1.0 / math.sqrt(d))
+    steps = [([700, 1100], [700, 1100]), ([1400, 1500], [700, 400]), ([2100, 1500], [700, 0]),
+             ([2400, 1800], [300, 300]), ([2600, 1900], [200, 100])]
+    _, kc, vc, _ = inputs.chunk_inputs([1], [S, S], S, Hq, Hkv, d, seed=71)
+    g = torch.Generator("cpu").manual_seed(72)
+    kcd, vcd = kc.cuda(), vc.cuda()
+    ws = _ws(max(sum(c) for _, c in steps), 2, max_k, Hq, Hkv, d)
+    for i, (lens, chunks) in enumerate(steps):
+        q = (torch.randn(sum(chunks), Hq, d, generator=g)).to(torch.bfloat16)
+        say("reuse step %d lens=%s chunks=%s" % (i, lens, chunks))
+        # the first call of a prefill rebuilds: the workspace may hold images
+        # of other caches that happened to sit at the same addresses
+        o_r, l_r, cu = _chunk_step(q.cuda(), kcd, vcd, lens, chunks, p, ws, i > 0, max_k)
+        o_f, l_f, _ = _chunk_step(q.cuda(), kcd, vcd, lens, chunks, p,
+                                  _ws(sum(chunks), 2, max_k, Hq, Hkv, d), False, max_k)
+        assert torch.equal(o_r, o_f) and torch.equal(l_r, l_f), "step %d" % i
+    o_ref, lse_ref = _oracle(q, kc, vc, lens, cu, p)
+    check_prefill(o_r, l_r, o_ref, lse_ref, list(range(sum(chunks))), torch.bfloat16,
+                  "chunk reuse last step")
+
+
+@pytest.mark.parametrize("case", ["other_cache", "rewritten_rows_no_reuse", "interp", "paged",
+                                  "precise"])
+def test_chunk_reuse_images_invalidation(case):
+    """Images are rebuilt whenever they may not hold: another cache (same
+    shapes) under reuse_images, rows rewritten in place with reuse_images off,
+    continuous interpolation (bifocal 2) at a new length; and kept on paged
+    caches and with split precision.  Each call equals a fresh rebuild."""
+    Hq, Hkv, d, L0, L1, max_k = 4, 2, 128, 1300, 1900, 2000
+    p = Params(600, 200, 1e4, 1.0 / math.sqrt(d), bifocal=2 if case == "interp" else 1)
+    extra = dict(precise=True) if case == "precise" else {}
+    _, kc, vc, _ = inputs.chunk_inputs([1], [max_k], max_k, Hq, Hkv, d, seed=73)
+    g = torch.Generator("cpu").manual_seed(74)
+    q0 = torch.randn(L0 - 100, Hq, d, generator=g).to(torch.bfloat16).cuda()
+    q1 = torch.randn(L1 - L0, Hq, d, generator=g).to(torch.bfloat16).cuda()
+    kcd, vcd = kc.cuda(), vc.cuda()
+    pre = case == "precise"
+    ws = _ws(L0, 1, max_k, Hq, Hkv, d, pre)
+    say("reuse invalidation", case)
+
+    if case == "paged":  # one pool for every call (the images name it by address)
+        pools = [t.cuda() for t in _paginate(kc, vc, [max_k], 64, seed=5)]
+
+    def run(kk, vv, q, L, wsx, reuse):
+        if case == "paged":
+            kp, vp, bt = pools
+            o, lse = jl.bifocal_prefill_chunk_paged(q, kp, vp, bt, [L], max_seqlen_k=max_k,
+                                                    workspace=wsx, reuse_images=reuse,
+                                                    **_kw(p), **extra)
+        else:
+            o, lse = jl.bifocal_prefill_chunk(q, kk, vv, [L], max_seqlen_k=max_k, workspace=wsx,
+                                              reuse_images=reuse, **_kw(p), **extra)
+        torch.cuda.synchronize()
+        return o.clone(), lse.clone()
+
+    run(kcd, vcd, q0, L0, ws, False)
+    if case == "other_cache":
+        kcd, vcd = (kcd * 0.5).contiguous(), (vcd + 1.0).contiguous()
+        reuse = True
+    elif case == "rewritten_rows_no_reuse":
+        kcd[:, :500] *= -1.0
+        reuse = False
+    else:
+        reuse = True
+    o_r, l_r = run(kcd, vcd, q1, L1, ws, reuse)
+    o_f, l_f = run(kcd, vcd, q1, L1, _ws(L1 - L0, 1, max_k, Hq, Hkv, d, pre), False)
+    assert torch.equal(o_r, o_f) and torch.equal(l_r, l_f), case
+    if case in ("other_cache", "rewritten_rows_no_reuse", "interp"):
+        o_ref, lse_ref = _oracle(q1.cpu(), kcd.cpu(), vcd.cpu(), [L1], None, p)
+        check_prefill(o_r, l_r, o_ref, lse_ref, list(range(L1 - L0)), torch.bfloat16,
+                      "reuse " + case)
+
+
+def test_chunk_reuse_images_1024_rows_128k():
+    """The benchmark's chunked step: 1024 rows at L = 131072 after a call that
+    built the images of the first 130048 keys (same G = 4) on the kept
+    workspace; equals a rebuild bit for bit."""
+    q, kc, vc, _ = inputs.chunk_inputs([2048], [131072], 131072, 32, 8, 128, seed=67)
+    p = inputs.DECODE_PARAMS
+    L = 131072
+    qd, kcd, vcd = q.cuda(), kc.cuda(), vc.cuda()
+    ws = _ws(1024, 1, L, 32, 8, 128)
+    say("chunk reuse 1024 rows on 131072 keys")
+    _chunk_step(qd[:1024].contiguous(), kcd, vcd, [L - 1024], [1024], p, ws, False, L)
+    o_r, l_r, _ = _chunk_step(qd[1024:].contiguous(), kcd, vcd, [L], [1024], p, ws, True, L)
+    o_f, l_f, _ = _chunk_step(qd[1024:].contiguous(), kcd, vcd, [L], [1024], p,
+                              _ws(1024, 1, L, 32, 8, 128), False, L)
+    assert torch.equal(o_r, o_f) and torch.equal(l_r, l_f)
