@@ -161,6 +161,16 @@ DecodeLayout decode_layout(int32_t B, int32_t max_seqlen_k, int32_t Hq, int32_t 
     return L;
 }
 
+bool decode_interleave(bool paged, int32_t Hq, int32_t Hkv, int32_t d, int32_t max_seqlen_k,
+                       int32_t elem_bytes) {
+    if (paged || Hq / Hkv > 8) return false;
+    // loads reach past L by up to a stride of n_splits stages (at most the
+    // sequence's span plus a chunk) and two tiles; negative offsets (stages
+    // starting below 0) stay above -2^31 as well
+    const int64_t rows = 2 * ((int64_t)max_seqlen_k + (int64_t)(kDecodeMaxStagesB + 4) * kDecodeStageB);
+    return rows * Hkv * d * elem_bytes < (int64_t)INT32_MAX;
+}
+
 RopeFreq make_rope_freq(double base, int d) {
     RopeFreq f;
     f.c = -2.0 * log2(base) / (double)d;
@@ -564,6 +574,8 @@ static jl_status decode_impl(const DecodeCall& c, const jl_params* params, jl_dt
     if (params->precise && c.fp8)
         return fail(JL_ERR_UNSUPPORTED, "split precision (precise = 1) is not offered for fp8 caches");
     a.precise = dtype == JL_DTYPE_BF16 ? params->precise : 0;
+    a.ilv = dtype == JL_DTYPE_BF16 &&
+            decode_interleave(paged, c.Hq, c.Hkv, c.d, c.max_seqlen_k, c.fp8 ? 1 : 2);
     if (static_scratch) {
         const jl_status sst = scratch_of_device(stream, &a.ws);
         if (sst != JL_OK) return sst;
@@ -661,6 +673,7 @@ jl_status jl_bifocal_decode_three_call(void* o, float* lse, const void* q, const
     a.tab = make_rope_freq(params->rope_base, d);
     a.ws = ws + tl.dec;
     a.o_f32 = 1;
+    a.ilv = decode_interleave(false, Hq, Hkv, d, max_seqlen_k, 2);
     hipStream_t s = (hipStream_t)stream;
     hipError_t e = launch_cache_remap(ws + tl.kr, k_cache, seqlens_k, batch, max_seqlen_k, S_max,
                                       Hkv, d, params->w_pretrained, a.tab, s);

@@ -573,22 +573,41 @@ __global__ __launch_bounds__(512) void decode_split_bf16_kernel(DecodeArgs a) {
     // -(j - jb)(1 - 1/s) and the table is indexed by j - jb
     const bool interp = BIF && a.bifocal == 2;
     const double rsc = interp ? (double)a.w_pretrained / (double)max(L, 1) : 1.0;
-    // chunks start at z0 + split * chunk, z0 in (-kStageB, 0], so that the
-    // first local key starts a stage; positions below 0 are masked
+    // stages of kStageB positions start at sbase = z0 (+ kwin), z0 in
+    // (-kStageB, 0], so that the first local key starts a stage; positions
+    // below 0 are masked.  A single local call of the unfused form sees only
+    // keys p - j < w_local (kwin).  NS stages cover [sbase, L).
     int32_t z0 = 0;
     if (bif && rem_last >= 0) {
         const int32_t m = (rem_last + 1) % kStageB;
         z0 = m ? m - kStageB : 0;
     }
-    // a single local call of the unfused form sees only keys p - j < w_local
     const int32_t kwin = a.window ? max(L - a.w_local, 0) : 0;
-    const int32_t kbeg = kwin + z0 + split * a.lay.chunk;
-    const int32_t kend = min(kbeg + a.lay.chunk, L);
+    const int32_t sbase = kwin + z0;
+    const int32_t NS = L > sbase ? (L - sbase + kStageB - 1) / kStageB : 0;
+    // Stages of this workgroup.  ILV (flat caches, up to 8 query heads per
+    // kv head, byte offsets within 32 bits; set by the host): stages split,
+    // split + n_splits, ..., so that at any moment the workgroups read
+    // neighbouring stages, one contiguous front of the cache, which HBM
+    // serves faster than one stream per workgroup.  Otherwise chunk /
+    // kStageB consecutive stages (the chunk [kbeg, kend)).
+    constexpr bool BUF = !PAGED && PACK;
+    const bool ilv = BUF && a.ilv;
+    const int32_t cps = a.lay.chunk / kStageB;
+    const int32_t sfirst = ilv ? split : split * cps;
+    const int32_t sstep = ilv ? a.lay.n_splits : 1;
+    const int32_t nst = ilv ? (NS > split ? (NS - split + sstep - 1) / sstep : 0)
+                            : max(0, min(cps, NS - sfirst));
+    auto js_of = [&](int32_t k) __attribute__((always_inline)) -> int32_t {
+        return sbase + (sfirst + k * sstep) * kStageB;
+    };
+    const int32_t kbeg = js_of(0);
+    const int32_t kend = ilv ? L : min(kbeg + a.lay.chunk, L);
 
     float4* pm = (float4*)((char*)a.ws + a.lay.part_ml);
     float* po = (float*)((char*)a.ws + a.lay.part_o);
     const int64_t pbase = ((int64_t)b * a.lay.n_splits + split) * a.Hq + (int64_t)kvh * grp;
-    if (kbeg >= kend) {  // empty chunk: neutral partial
+    if (nst <= 0) {  // no stage: neutral partial
         if (head_ok) {
             if (c == 0 && n < grp) pm[pbase + n] = make_float4(-INFINITY, 0.0f, 0.0f, 0.0f);
             for (int x = lane; x < grp * D; x += 64) po[pbase * D + x] = 0.0f;
@@ -600,9 +619,8 @@ __global__ __launch_bounds__(512) void decode_split_bf16_kernel(DecodeArgs a) {
     // waits) and reads only rows of the chunk: the key index is clamped into
     // [klo, kend), or (BUF: flat caches, up to 8 query heads per kv head,
     // where the registers allow) the loads go through buffer resources whose
-    // range ends with row kend - 1, so that rows outside the chunk read as
-    // zeros.  Masked keys weigh 0 either way.
-    constexpr bool BUF = !PAGED && PACK;
+    // range ends with row kend - 1, so that other rows read as zeros.
+    // Masked keys weigh 0 either way.
     const int kvh_c = min(kvh, a.Hkv - 1);
     const int64_t boff = PAGED ? 0 : (int64_t)b * a.S_max * a.Hkv * D;
     const int64_t boff_k = PAGED ? 0 : (int64_t)b * (a.S_max_k ? a.S_max_k : a.S_max) * a.Hkv * D;
@@ -629,16 +647,18 @@ __global__ __launch_bounds__(512) void decode_split_bf16_kernel(DecodeArgs a) {
             return j;
         }
     };
-    // BUF: resources based at row klo of this kv head (offsets in bytes from
-    // there, 32-bit: a chunk spans at most a few MB), one add per load group
-    // and tile in place of clamping and 64-bit row arithmetic
+    // BUF: resources based at row rb (klo, or row 0 with ILV) of this kv
+    // head, offsets in bytes from there (32-bit: a chunk spans a few MB; with
+    // ILV the host checked the sequence's span), one add per load group and
+    // tile in place of clamping and 64-bit row arithmetic
     constexpr int ES = (int)sizeof(TC);
     const int32_t rsb = (int32_t)rstride * ES;  // bytes between rows
-    const int32_t nrec = (kend - klo - 1) * rsb + D * ES;
+    const int32_t rb = ilv ? 0 : klo;
+    const int32_t nrec = (kend - rb - 1) * rsb + D * ES;
     const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(kc + (int64_t)klo * rstride), (short)0, BUF ? nrec : 0, kBufferRsrcWord3);
+        (void*)(kc + (int64_t)rb * rstride), (short)0, BUF ? nrec : 0, kBufferRsrcWord3);
     const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(vc + (int64_t)klo * rstride), (short)0, BUF ? nrec : 0, kBufferRsrcWord3);
+        (void*)(vc + (int64_t)rb * rstride), (short)0, BUF ? nrec : 0, kBufferRsrcWord3);
     // K of key j0 + n into registers (keys outside the chunk: masked)
     auto load_k = [&](int32_t j0, KRAW* kd) __attribute__((always_inline)) {
         if constexpr (!BUF) {
@@ -647,7 +667,7 @@ __global__ __launch_bounds__(512) void decode_split_bf16_kernel(DecodeArgs a) {
             for (int s = 0; s < NST; ++s)
                 kd[s] = *reinterpret_cast<const KRAW*>(kc + row_of(kj) * rstride + 32 * s + 8 * c);
         } else {
-            const int32_t off = (j0 - klo + n) * rsb + 8 * c * ES;
+            const int32_t off = (j0 - rb + n) * rsb + 8 * c * ES;
 #pragma unroll
             for (int s = 0; s < NST; ++s) kd[s] = buffer_load<KRAW>(rk, off + 32 * s * ES);
         }
@@ -664,7 +684,7 @@ __global__ __launch_bounds__(512) void decode_split_bf16_kernel(DecodeArgs a) {
                 const int32_t key = min(max(j0 + RPI * r + q, klo), khi);
                 vd[r] = *reinterpret_cast<const VRAW*>(vc + row_of(key) * rstride + VEL * ch);
             } else {
-                vd[r] = buffer_load<VRAW>(rv, (j0 - klo + RPI * r + q) * rsb + 16 * ch);
+                vd[r] = buffer_load<VRAW>(rv, (j0 - rb + RPI * r + q) * rsb + 16 * ch);
             }
         }
     };
@@ -733,12 +753,13 @@ __global__ __launch_bounds__(512) void decode_split_bf16_kernel(DecodeArgs a) {
     constexpr int QLOC = kDecodeMaxStagesB;  // row of R(p)
     {
         const double rv = rope_rev(a.tab, threadIdx.x % HALF);  // blockDim is a multiple of HALF
-        const int nst = min((kend - kbeg + kStageB - 1) / kStageB, (int32_t)kDecodeMaxStagesB);
-        for (int x = threadIdx.x; x < (nst + 1) * HALF; x += blockDim.x) {
+        // (the layout keeps nst <= kDecodeMaxStagesB; the bound keeps LDS safe)
+        const int nq = min(nst, (int32_t)kDecodeMaxStagesB);
+        for (int x = threadIdx.x; x < (nq + 1) * HALF; x += blockDim.x) {
             const int st = x / HALF;
             float cs, sn;
-            if (st < nst) {
-                const int32_t jbs = max(kbeg + kStageB * st, 0);
+            if (st < nq) {
+                const int32_t jbs = max(js_of(st), 0);
                 if (interp)  // R(p / s - jb / s + jb)
                     rope_cs_rev(((double)(p - jbs) * rsc + (double)jbs) * rv, cs, sn);
                 else
@@ -746,7 +767,7 @@ __global__ __launch_bounds__(512) void decode_split_bf16_kernel(DecodeArgs a) {
             } else {
                 rope_cs_hw(a.q_remap ? fp : p, rv, cs, sn);
             }
-            qtab[(st < nst ? st : QLOC) * HALF + x % HALF] = make_float2(cs, sn);
+            qtab[(st < nq ? st : QLOC) * HALF + x % HALF] = make_float2(cs, sn);
         }
         if (BIF && bif) {
             for (int x = threadIdx.x; x < kStageB * HALF; x += blockDim.x) {
@@ -911,13 +932,14 @@ __global__ __launch_bounds__(512) void decode_split_bf16_kernel(DecodeArgs a) {
     const int vkey = 4 * c + (n >> 2);
     const int voff = vkey * VRS + (n & 3) * 8;
 
+    int32_t kmask = 0;  // keys from here on are masked (end of the stage in use, or L)
     auto process = [&](int32_t j0, const f32x4& sacc, const char* slot) __attribute__((always_inline)) {
         const bool col = n < GQ;  // lanes of packed lo parts carry no scores
         float sc[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int32_t kk = j0 + 4 * c + i;
-            sc[i] = (col && kk >= 0 && kk < kend) ? sacc[i] : -INFINITY;
+            sc[i] = (col && kk >= 0 && kk < kmask) ? sacc[i] : -INFINITY;
         }
         float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
         mx = fmaxf(mx, __shfl_xor(mx, 16));
@@ -963,10 +985,10 @@ __global__ __launch_bounds__(512) void decode_split_bf16_kernel(DecodeArgs a) {
     const int partner = wave ^ 4;  // the other wave on this SIMD (if any)
     // one tile: issue the loads two tiles ahead, stage this tile's V in LDS,
     // score, P V, then set this wave's priority from its lead over its partner
-    auto step = [&](int32_t j0, const KRAW* kcur, const VRAW* vcur, KRAW* knext,
-                    VRAW* vnext) __attribute__((always_inline)) {
-        load_k(j0 + 2 * kTile, knext);
-        load_vr(j0 + 2 * kTile, vnext);
+    auto step = [&](int32_t j0, const KRAW* kcur, const VRAW* vcur, KRAW* knext, VRAW* vnext,
+                    int32_t jpre) __attribute__((always_inline)) {
+        load_k(jpre, knext);
+        load_vr(jpre, vnext);
         store_vr(vcur, slot);  // the same wave writes then reads: LDS keeps its order
         f32x4 sacc;
         if (BIF && stage_remote) {
@@ -989,20 +1011,23 @@ __global__ __launch_bounds__(512) void decode_split_bf16_kernel(DecodeArgs a) {
             __builtin_amdgcn_s_setprio(0);
     };
 
-    for (int32_t js = kbeg; js < kend; js += kStageB) {
+    for (int32_t k = 0; k < nst; ++k) {
+        const int32_t js = js_of(k), jn = js_of(k + 1);
+        kmask = min(js + kStageB, kend);
         stage_remote = BIF && bif && js <= rem_last;
         jb = max(js, 0);
         const int32_t fjb = remap(jb, G);
         r0 = jb - fjb * G;
         if (stage_remote || !q_local) {
-            rotate_q(stage_remote ? (js - kbeg) / kStageB : QLOC);
+            rotate_q(stage_remote ? k : QLOC);
             q_local = !stage_remote;
         }
-        // tiles js, js + 16, js + 32 sit in (kA, vA), (kB, vB), (kC, vC);
-        // tiles past kend are fully masked
-        step(js, kA, vA, kC, vC);
-        step(js + kTile, kB, vB, kA, vA);
-        step(js + 2 * kTile, kC, vC, kB, vB);
+        // tiles js, js + 16, js + 32 sit in (kA, vA), (kB, vB), (kC, vC); each
+        // step loads the tile two ahead (the next stage's first two in the
+        // last two steps); tiles past kmask are fully masked
+        step(js, kA, vA, kC, vC, js + 2 * kTile);
+        step(js + kTile, kB, vB, kA, vA, jn);
+        step(js + 2 * kTile, kC, vC, kB, vB, jn + kTile);
     }
 
     // ---- partial (m, l_o, l_lse, unnormalised O) of this chunk ----

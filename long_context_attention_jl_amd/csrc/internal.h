@@ -161,7 +161,16 @@ struct DecodeArgs {
     int64_t S_max_k;
     // remote keys turned in fp32 and split into fp16 hi + lo operands
     int32_t precise;
+    // workgroup `split` takes the stages split, split + n_splits, ... of its
+    // sequence (flat caches whose rows, plus three tiles, span less than
+    // 2^31 bytes per sequence; see decode_interleave) instead of one chunk
+    int32_t ilv;
 };
+// Whether the bf16 decode kernels may interleave stages across workgroups:
+// flat caches, up to 8 query heads per kv head, and byte offsets of a
+// sequence's rows within 32 bits.
+bool decode_interleave(bool paged, int32_t Hq, int32_t Hkv, int32_t d, int32_t max_seqlen_k,
+                       int32_t elem_bytes);
 hipError_t launch_decode(const DecodeArgs& a, int dtype, hipStream_t s);
 
 hipError_t launch_debug_index(int64_t L, int32_t w_pretrained, int32_t w_local, int32_t bifocal,

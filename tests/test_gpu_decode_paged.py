@@ -1,7 +1,10 @@
 """GPU parity of jl_bifocal_decode_paged: the cache pool is the flat cache's
 rows scattered over shuffled pages, so the paged decode must give the flat
-decode's results exactly (same arithmetic, other addresses) and match the
-fp64 oracle."""
+decode's results (same arithmetic, other addresses) and match the fp64
+oracle.  Where both assign the keys to workgroups alike (short caches: one
+stage per workgroup) they agree bit for bit; on long flat caches the
+workgroups take interleaved stages, so the partial sums group differently
+and the two agree to rounding."""
 import math
 
 import numpy as np
@@ -53,6 +56,16 @@ def _run_both(q, kc, vc, lens, p, page, seed):
     return o_f, l_f, o_p, l_p
 
 
+def _close_to_flat(o_f, l_f, o_p, l_p, label):
+    """Paged against flat with another grouping of the partial sums: the
+    outputs may differ by the rounding of their last bits only."""
+    do = (o_f.float() - o_p.float()).abs().max().item()
+    dl = (l_f - l_p).abs().max().item()
+    say("%s: paged vs flat max|dO|=%.3g max|dLSE|=%.3g" % (label, do, dl))
+    assert do <= 2.0 ** -7 * max(o_f.float().abs().max().item(), 1e-3), label  # one bf16 ulp
+    assert dl <= 1e-5 * max(l_f.abs().max().item(), 1.0), label
+
+
 def _oracle(q, kc, vc, lens, p):
     return oracle.decode(q, kc, vc, lens, w_pretrained=p.w_pretrained, w_local=p.w_local,
                          rope_base=p.rope_base, softmax_scale=p.softmax_scale, bifocal=p.bifocal)
@@ -81,7 +94,7 @@ def test_paged_128k_and_g_switch():
     p = c.params
     say("paged decode", c.name)
     o_f, l_f, o_p, l_p = _run_both(c.q, c.k_cache, c.v_cache, c.seqlens, p, 64, seed=1)
-    assert torch.equal(o_f, o_p) and torch.equal(l_f, l_p)
+    _close_to_flat(o_f, l_f, o_p, l_p, "paged 128K")
     o_ref, l_ref = _oracle(c.q, c.k_cache, c.v_cache, c.seqlens, p)
     dl = np.abs(l_p.cpu().double().numpy() - l_ref).max()
     say("paged 128K: max|dLSE|=%.3g" % dl)
@@ -89,4 +102,4 @@ def test_paged_128k_and_g_switch():
     queries, kc, vc, lens, p = inputs.decode_16step_cache()
     for step in (7, 8):  # L = 32768 (G = 1) and 32769 (G = 2)
         o_f, l_f, o_p, l_p = _run_both(queries[step], kc, vc, [lens[step]], p, 64, seed=step)
-        assert torch.equal(o_f, o_p) and torch.equal(l_f, l_p), "step %d" % step
+        _close_to_flat(o_f, l_f, o_p, l_p, "step %d" % step)
