@@ -252,5 +252,31 @@ def with_outlier_channels(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, 
     return q, k, v
 
 
+def sink_channels(d: int, n_pairs: int = 4):
+    """The RoPE channels of the n_pairs lowest-frequency pairs (t, t + d/2),
+    t = d/2 - n_pairs .. d/2 - 1: their angles stay small at every position
+    of the workloads, so a score through them hardly depends on position."""
+    half = d // 2
+    return [t for t in range(half - n_pairs, half)] + [t + half for t in range(half - n_pairs, half)]
+
+
+def with_sink_key(q: torch.Tensor, k: torch.Tensor, *, first_keys, q_add: float, k_value: float,
+                  n_pairs: int = 4):
+    """Attention-sink variant of seeded inputs: every query gets q_add added in
+    the sink channels (sink_channels(d, n_pairs)), and the keys at the rows in
+    first_keys (the first key of each sequence, or of a cache) get k_value in
+    those channels, every head.  Each query then scores that key about
+    2 n_pairs q_add k_value (times the softmax scale) above its other keys,
+    whatever its position: one key carries most of every softmax.  Returns
+    new float32 tensors (q's and k's shapes)."""
+    q = q.float().clone()
+    k = k.float().clone()
+    ch = sink_channels(q.shape[-1], n_pairs)
+    q[..., ch] += q_add
+    for r in first_keys:
+        k[r][..., ch] = k_value
+    return q, k
+
+
 def to_dtype(dtype, *ts):
     return tuple(t.to(dtype) for t in ts)

@@ -75,6 +75,24 @@ def test_decode_128k_peaky():
                      check_lse=precise)
 
 
+def test_decode_128k_sink_key():
+    """The 128K decode with an attention sink: the query scores cache key 0
+    about 13 above the other keys (through the lowest-frequency RoPE pairs),
+    so one remote key carries about three quarters of the softmax.  Split precision meets
+    every bar, the fast path the output bars (its LSE is recorded)."""
+    c = inputs.decode_128k()
+    q, kc = inputs.with_sink_key(c.q, c.k_cache, first_keys=[(0, 0)], q_add=3.0, k_value=6.1)
+    q, kc = inputs.to_dtype(torch.bfloat16, q, kc)
+    say("case", c.name, "sink key")
+    o_ref, lse_ref = _dec_ref(q, kc, c.v_cache, c.seqlens, c.params)
+    kcd, vcd = kc.cuda(), c.v_cache.cuda()
+    for precise in (True, False):
+        o, lse = _dec_gpu(q, kcd, vcd, c.seqlens, c.params, precise=precise)
+        torch.cuda.synchronize()
+        check_decode(o, lse, o_ref, lse_ref, torch.bfloat16,
+                     c.name + " sink" + (" precise" if precise else ""), check_lse=precise)
+
+
 @pytest.mark.parametrize("S", [131072, 3000])
 def test_decode_large_magnitude_channels(S):
     """Cached keys with an outlier channel of magnitude 1e3..3e4 and values with

@@ -198,14 +198,16 @@ def _plain_on(case, rows, mask, o_ref):
     return o_plain
 
 
-def _full_size(case, label, every=1, o_scale=None, modes=(False,)):
+def _full_size(case, label, every=1, o_scale=None, modes=(False,), disc=True):
     """modes: the precise flags to run; the fast path (False) on concentrated
-    attention has its LSE recorded, not asserted (see check_prefill)."""
+    attention has its LSE recorded, not asserted (see check_prefill).
+    disc=False skips the discrimination ratio (inputs on which bifocal and
+    plain attention nearly agree)."""
     rows, mask = _rows_of(case, every)
     say("workload", case.name, label, "- comparing %d rows x %d heads" % (len(rows), case.q.shape[1]))
     o_ref, lse_ref = oracle_prefill_rows(case.q, case.k, case.v, case.params, rows,
                                          cu=case.cu_seqlens)
-    o_plain = _plain_on(case, rows, mask, o_ref)
+    o_plain = _plain_on(case, rows, mask, o_ref) if disc else None
     out = None
     for precise in modes:
         o, lse = gpu_prefill(jl, case.q, case.k, case.v, case.params, cu=case.cu_seqlens,
@@ -251,6 +253,41 @@ def test_varlen_4seq_every_workgroup_and_g1_sequences_plain():
     # and the G > 1 sequences differ from plain attention
     a, b = c.cu_seqlens[3], c.cu_seqlens[4]
     assert (lse[:, a:b] - l0[:, a:b]).abs().max().item() > 1e-3
+
+
+def test_sink_key_full():
+    """An attention sink: every query scores key 0 about 9 above the other keys
+    (through the lowest-frequency RoPE pairs, so at every position), so key 0
+    carries about three quarters of a long row's softmax -- a remote key for
+    the rows past the local window.  Every row; split precision meets every bar, the fast
+    path the output bars (its LSE is recorded).  Bifocal and plain attention
+    nearly agree here (both are dominated by the same key), so there is no
+    discrimination ratio."""
+    p = Params(1024, 300, 1e4, 1.0)
+    q, k, v = inputs.prefill_inputs(3000, 4, 2, 128, seed=61, q_scale=1.0 / math.sqrt(128))
+    q, k = inputs.with_sink_key(q, k, first_keys=[0], q_add=0.4, k_value=2.8)
+    q, k, v = inputs.to_dtype(torch.bfloat16, q, k, v)
+    say("sink key T=3000")
+    rows = list(range(3000))
+    o_ref, lse_ref = oracle_prefill_rows(q, k, v, p, rows)
+    for precise in (True, False):
+        o, lse = gpu_prefill(jl, q, k, v, p, precise=precise)
+        torch.cuda.synchronize()
+        check_prefill(o, lse, o_ref, lse_ref, rows, torch.bfloat16,
+                      "sink T=3000" + (" precise" if precise else ""), check_lse=precise)
+
+
+def test_sink_key_128k():
+    """The 128K layer with an attention sink at key 0 (as test_sink_key_full,
+    scored about 13 above the rest, about three quarters of the mass of the
+    last rows): one row of every 1024-row block plus the band-edge rows, both
+    precisions."""
+    base = inputs.qwen3_8b_128k()
+    q, k = inputs.with_sink_key(base.q, base.k, first_keys=[0], q_add=0.5, k_value=3.25)
+    q, k = inputs.to_dtype(torch.bfloat16, q, k)
+    case = inputs.PrefillCase(base.name + "_sink", q, k, base.v, None, base.params)
+    del base
+    _full_size(case, "qwen3_8b_L131072 sink", every=4, modes=(True, False), disc=False)
 
 
 def _outlier_case(T, Hq, Hkv, d, seed, params, q_scale, q_small):
