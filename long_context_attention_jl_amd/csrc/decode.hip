@@ -11,10 +11,11 @@
 // the key the correction f(j) - j, applied in registers ([BT] §3.3).  Keys
 // inside the window are scored as <R(p) q, K_j> on the stored values.
 //
-// Work decomposition: a workgroup owns a chunk of key positions of one
-// sequence and a group of kv heads (one wave each); each chunk writes
-// (m, l, O) partials and a second kernel merges the chunks exactly
-// (max-shifted sums).  Two split kernels:
+// Work decomposition: a workgroup owns a set of key positions of one
+// sequence (a chunk, or for the bf16 kernel on flat caches every n_splits-th
+// stage) and a group of kv heads (one wave each); each workgroup writes
+// (m, l, O) partials and a second kernel merges them exactly (max-shifted
+// sums).  Two split kernels:
 //  - fp32 caches (decode_split_kernel, up to 4 kv heads per workgroup): per
 //    16-key tile a wave forms S^T = K Q^T on v_mfma_f32_16x16x32_bf16 with the
 //    query and the rotated keys split into bf16 hi + lo parts (about 16
@@ -538,7 +539,7 @@ __global__ __launch_bounds__(512) void decode_split_bf16_kernel(DecodeArgs a) {
     constexpr int TSTRF = D + 4;
     __shared__ __align__(16) float tabf[(BIF && PREC) ? kStageB * TSTRF : 4];
     // query angles: row st < kDecodeMaxStagesB holds R(f(p) - f(jb) + jb) of
-    // stage st of this chunk (remote stages), the last row R(p)
+    // this workgroup's stage st (remote stages), the last row R(p)
     __shared__ float2 qtab[(kDecodeMaxStagesB + 1) * HALF];
     __shared__ __align__(16) char vs[kWavesB * SLOT];  // per wave: the V tile in use
     // per wave (PACK): the turned query, fp16 hi rows then lo rows
@@ -616,11 +617,12 @@ __global__ __launch_bounds__(512) void decode_split_bf16_kernel(DecodeArgs a) {
     }
 
     // every load below is unconditional (branch-free memory stream, exact
-    // waits) and reads only rows of the chunk: the key index is clamped into
-    // [klo, kend), or (BUF: flat caches, up to 8 query heads per kv head,
-    // where the registers allow) the loads go through buffer resources whose
-    // range ends with row kend - 1, so that other rows read as zeros.
-    // Masked keys weigh 0 either way.
+    // waits) and reads only rows of this workgroup's range [klo, kend) (the
+    // chunk, or with ILV the whole sequence): the key index is clamped into
+    // it, or (BUF: flat caches, up to 8 query heads per kv head, where the
+    // registers allow) the loads go through buffer resources whose range ends
+    // with row kend - 1, so that other rows read as zeros.  Masked keys weigh
+    // 0 either way.
     const int kvh_c = min(kvh, a.Hkv - 1);
     const int64_t boff = PAGED ? 0 : (int64_t)b * a.S_max * a.Hkv * D;
     const int64_t boff_k = PAGED ? 0 : (int64_t)b * (a.S_max_k ? a.S_max_k : a.S_max) * a.Hkv * D;
@@ -1030,7 +1032,7 @@ __global__ __launch_bounds__(512) void decode_split_bf16_kernel(DecodeArgs a) {
         step(js + 2 * kTile, kC, vC, kB, vB, jn + kTile);
     }
 
-    // ---- partial (m, l_o, l_lse, unnormalised O) of this chunk ----
+    // ---- partial (m, l_o, l_lse, unnormalised O) of this workgroup's stages ----
     float l_tot = l_part + __shfl_xor(l_part, 16);
     l_tot += __shfl_xor(l_tot, 32);
     float l_ex = l_exact + __shfl_xor(l_exact, 16);
