@@ -218,6 +218,20 @@ def main():
         torch.cuda.synchronize()
         t_interp.append((time.perf_counter() - t0) * 1e3)
     out["prefill_interp_ms"] = round(min(t_interp), 3)
+    # split precision on every row (q and k as fp16 hi + lo, three products)
+    ws_p = torch.empty(jl.prefill_workspace_bytes(T, 1, Hq, Hkv, d, q.dtype, precise=True),
+                       dtype=torch.uint8, device="cuda")
+    kw_p = dict(kw, workspace=ws_p)
+    jl.bifocal_prefill(q, k, v, precise=True, **kw_p)
+    t_prec = []
+    for _ in range(2):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        jl.bifocal_prefill(q, k, v, precise=True, **kw_p)
+        torch.cuda.synchronize()
+        t_prec.append((time.perf_counter() - t0) * 1e3)
+    out["prefill_precise_ms"] = round(min(t_prec), 3)
+    del ws_p
     del o, lse
 
     if not args.no_three_call:
