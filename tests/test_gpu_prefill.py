@@ -78,6 +78,18 @@ def test_f32_small_full(T, d):
     _full_case(T, 2, 1, d, p, dtype=torch.float32, seed=7)
 
 
+def test_f32_varlen_edges_and_settings():
+    """The fp32 kernel across its row blocks and phases: packed sequences of
+    lengths 300, 1, 699, 2500 and 63 (G = 2, 1, 3, 10, 1), then the degenerate
+    windows (every key remote, every key local, plain RoPE), every row."""
+    cu = [0, 300, 301, 1000, 3500, 3563]
+    _full_case(cu[-1], 4, 2, 128, Params(256, 90, 1e4, 1.0 / math.sqrt(128)), dtype=torch.float32,
+               seed=9, cu=cu)
+    for p in (Params(300, 0, 1e4, 0.125), Params(300, 5000, 1e4, 0.125),
+              Params(300, 64, 1e4, 0.125, bifocal=False)):
+        _full_case(1100, 2, 1, 64, p, dtype=torch.float32, seed=10)
+
+
 @pytest.mark.parametrize("label,params", [
     ("G1", Params(4096, 64, 1e4, 0.125)),          # L <= w_pretrained: plain RoPE
     ("w_local0", Params(300, 0, 1e4, 0.125)),      # every key remote (call B alone)
