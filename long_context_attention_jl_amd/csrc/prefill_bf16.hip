@@ -224,11 +224,16 @@ void prefill_bf16_kernel(PrefillArgs a, int rb_first, int n_rb) {
     const bf16* KRlg = (const bf16*)((const char*)a.ws + a.lay.kr_lo) + ((int64_t)g * ntl + e[kPlanLoTile0]) * C::KSLOT;
 
     // global -> LDS DMA of one tile image: each wave instruction moves 64 x 16
-    // contiguous bytes (tile sizes are whole 1 KB rounds)
+    // contiguous bytes (tile sizes are whole 1 KB rounds).  Only waves 0-3
+    // issue copies.  Wave w and wave w + 4 share a SIMD, and the issue arbiter
+    // favours the older one, which finishes its blocks first and then idles
+    // at the tile barrier; a copy instruction adds latency to the issuing
+    // wave's own chain, so it goes where there is slack.
     auto dma = [&](const bf16* src, bf16* dst, int elems)  __attribute__((always_inline)) {
-        for (int c0 = wave * 64; c0 < elems / 8; c0 += 512)
-            __builtin_amdgcn_global_load_lds((const void*)(src + (int64_t)(c0 + lane) * 8),
-                                             (void*)(dst + c0 * 8), 16, 0, 0);
+        if (wave < 4)
+            for (int c0 = wave * 64; c0 < elems / 8; c0 += 256)
+                __builtin_amdgcn_global_load_lds((const void*)(src + (int64_t)(c0 + lane) * 8),
+                                                 (void*)(dst + c0 * 8), 16, 0, 0);
     };
     // key tiles of the phase's RoPE (remapped tiles equal the standard ones
     // when G = 1, and the pre-pass then writes only those)
