@@ -843,7 +843,6 @@ static jl_status chunk_sizes_ok(int32_t batch, int32_t max_seqlen_k) {
 // partials are sized for the most shares Tq query rows can need (every row
 // block holds at most 256 of them).
 constexpr int kChunkTargetWgs = 512;  // two workgroups per compute unit
-constexpr int kChunkMaxSplit = 4;
 static int chunk_split_bound(int64_t wgs) {
     if (wgs < 1) wgs = 1;
     const int64_t k = (kChunkTargetWgs + wgs - 1) / wgs;

@@ -18,6 +18,9 @@ struct LaunchScope {
     int slot_;
 };
 
+// most key shares a chunk call splits a row block's tiles into
+constexpr int kChunkMaxSplit = 4;
+
 // Byte layout of the prefill workspace; every region starts 256-byte aligned.
 struct PrefillLayout {
     int64_t T_pad;    // padded key rows (multiple of kBN)

@@ -482,11 +482,15 @@ hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t s) {
 // ([TW] §四's merge of partial attentions): with m_k in log2 units,
 //   Z = sum_k 2^(m_k - M) l_k,  o = sum_k 2^(m_k - M) O_k / Z,
 //   lse = (M + log2 Z) ln 2,  M = max_k m_k.
-// One wave per (token, head).  A token is looked up in the plan (its
-// sequence and position); rows of a block below the split-precision bound
-// were written directly by that kernel and are skipped, as are tokens of
-// no sequence (a broken plan has every length 0).
+// One wave per (token, head); lane l holds elements [D/64 * l, D/64 * (l + 1))
+// of the row, read from each share as one vector.  A token is looked up in
+// the plan (its sequence and position); rows of a block below the
+// split-precision bound were written directly by that kernel and are
+// skipped, as are tokens of no sequence (a broken plan has every length 0).
+template <int D>
 __global__ __launch_bounds__(256) void chunk_merge_kernel(PrefillArgs a) {
+    constexpr int E = D / 64;
+    using vecE = float __attribute__((ext_vector_type(E)));
     const int64_t tok = blockIdx.x;
     const int head = blockIdx.y * 4 + (int)(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
@@ -504,34 +508,51 @@ __global__ __launch_bounds__(256) void chunk_merge_kernel(PrefillArgs a) {
     const int32_t pos = q0 + (int32_t)(tok - e[kPlanStart]);
     if (pos - pos % kBM < kPreciseRows) return;
     const int K = a.ksplit;
+    // every share's row vector is in flight before the weights are known
+    vecE ov[kChunkMaxSplit];
+    float2 ml[kChunkMaxSplit];
+#pragma unroll
+    for (int k = 0; k < kChunkMaxSplit; ++k) {
+        if (k < K) {
+            ml[k] = a.part_ml[((int64_t)k * a.Hq + head) * a.T + tok];
+            ov[k] = *reinterpret_cast<const vecE*>(a.part_o + (((int64_t)k * a.T + tok) * a.Hq + head) * D + E * lane);
+        }
+    }
     float M = -INFINITY;
-    for (int k = 0; k < K; ++k) M = fmaxf(M, a.part_ml[((int64_t)k * a.Hq + head) * a.T + tok].x);
+#pragma unroll
+    for (int k = 0; k < kChunkMaxSplit; ++k)
+        if (k < K) M = fmaxf(M, ml[k].x);
+    // a share with no key of the row (l = 0) carries no weight
     float Z = 0.0f;
-    float w[8];
-    for (int k = 0; k < K; ++k) {
-        const float2 ml = a.part_ml[((int64_t)k * a.Hq + head) * a.T + tok];
-        w[k] = (M == -INFINITY || ml.x == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(ml.x - M) * ml.y;
-        w[k] = ml.y > 0.0f ? w[k] : 0.0f;
-        Z += w[k];
+#pragma unroll
+    for (int k = 0; k < kChunkMaxSplit; ++k) {
+        if (k < K) {
+            const float w = (M == -INFINITY || ml[k].x == -INFINITY) ? 0.0f
+                                                                     : __builtin_amdgcn_exp2f(ml[k].x - M) * ml[k].y;
+            Z += ml[k].y > 0.0f ? w : 0.0f;
+        }
     }
     const bool none = !(Z > 0.0f);
-    bf16* o = (bf16*)a.o + (tok * a.Hq + head) * (int64_t)a.d;
-    for (int x = lane; x < a.d; x += 64) {
-        float acc = 0.0f;
-        for (int k = 0; k < K; ++k) {
-            const float2 ml = a.part_ml[((int64_t)k * a.Hq + head) * a.T + tok];
-            const float wk = (none || ml.y <= 0.0f) ? 0.0f : __builtin_amdgcn_exp2f(ml.x - M);
-            acc += wk * a.part_o[(((int64_t)k * a.T + tok) * a.Hq + head) * a.d + x];
+    vecE acc = {};
+#pragma unroll
+    for (int k = 0; k < kChunkMaxSplit; ++k) {
+        if (k < K) {
+            const float wk = (none || ml[k].y <= 0.0f) ? 0.0f : __builtin_amdgcn_exp2f(ml[k].x - M);
+            acc += wk * ov[k];
         }
-        o[x] = (bf16)(none ? 0.0f : acc / Z);
     }
+    bf16* o = (bf16*)a.o + (tok * a.Hq + head) * (int64_t)D + E * lane;
+#pragma unroll
+    for (int i = 0; i < E; ++i) o[i] = (bf16)(none ? 0.0f : acc[i] / Z);
     if (lane == 0) a.lse[(int64_t)head * a.T + tok] = none ? -INFINITY : (M + log2f(Z)) * kLn2;
 }
 
 hipError_t launch_chunk_merge(const PrefillArgs& a, hipStream_t s) {
     LaunchScope scope("chunk_merge", s);
-    hipLaunchKernelGGL(chunk_merge_kernel, dim3((unsigned)a.T, (unsigned)((a.Hq + 3) / 4)),
-                       dim3(256), 0, s, a);
+    if (a.ksplit > kChunkMaxSplit) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)a.T, (unsigned)((a.Hq + 3) / 4));
+    if (a.d == 128) hipLaunchKernelGGL(chunk_merge_kernel<128>, grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL(chunk_merge_kernel<64>, grid, dim3(256), 0, s, a);
     return hipGetLastError();
 }
 
