@@ -361,8 +361,8 @@ jl_status jl_kv_quantize_fp8(void* out, const void* x, const float* scale, int64
  * fp16 images of the cache's key and value tiles (each sequence a fixed
  * stretch of max_seqlen_k keys), a small record of what they were built for
  * (see jl_params.reuse_images), and fp32 partials for calls whose grid is
- * small (fewer than two 256-row workgroups per compute unit, e.g. a 1024-row
- * chunk of 32 heads): those split each row block's keys in up to four shares
+ * small (fewer 256-row workgroups than compute units, e.g. a 1024-row chunk
+ * of 32 heads): those split each row block's keys in up to four shares
  * and merge the shares in LogSumExp space.  The images and the record sit at
  * the same offsets for every Tq, so a workspace sized for the largest chunk
  * serves every chunk size.  params as for jl_bifocal_prefill_workspace

@@ -838,11 +838,11 @@ static jl_status chunk_sizes_ok(int32_t batch, int32_t max_seqlen_k) {
 // holds, then the key-split partials.  The images and the record sit at
 // offsets that depend on batch, max_seqlen_k, Hkv, d and the precise flag
 // only, so that calls with other chunk sizes find them.  A call whose
-// main-rows grid holds fewer than kChunkTargetWgs workgroups (two per compute
+// main-rows grid holds fewer than kChunkTargetWgs workgroups (one per compute
 // unit) splits each row block's key tiles in up to kChunkMaxSplit shares; the
 // partials are sized for the most shares Tq query rows can need (every row
 // block holds at most 256 of them).
-constexpr int kChunkTargetWgs = 512;  // two workgroups per compute unit
+constexpr int kChunkTargetWgs = 256;  // one workgroup per compute unit
 static int chunk_split_bound(int64_t wgs) {
     if (wgs < 1) wgs = 1;
     const int64_t k = (kChunkTargetWgs + wgs - 1) / wgs;

@@ -269,7 +269,7 @@ def test_chunk_paged_validation(kw, status):
 
 def test_chunk_workspace_query():
     """A large chunk needs the prefill workspace of its keys plus the 256-byte
-    record of the images; a grid of fewer than two workgroups per compute unit
+    record of the images; a grid of fewer workgroups than compute units (256)
     adds the key-split partials: up to 4 shares x Tq x Hq x (d + 2) fp32."""
     n = ctypes.c_size_t(0)
     L = jlb.lib()
@@ -278,12 +278,18 @@ def test_chunk_workspace_query():
     # 32768 rows of 32 heads: 4096 row blocks >= 1024 workgroups, no split
     assert L.jl_bifocal_prefill_chunk_workspace(32768, 1, 131072, 32, 8, 128, 1, None, ctypes.byref(n)) == 0
     assert n.value == base
-    # 4096 rows: 512 row-block workgroups, two per compute unit: no split
+    # 4096 and 2048 rows: 512 and 256 row-block workgroups, at least one per
+    # compute unit: no split
     assert L.jl_bifocal_prefill_chunk_workspace(4096, 1, 131072, 32, 8, 128, 1, None, ctypes.byref(n)) == 0
     assert n.value == base
-    # 1024 rows: 128 workgroups -> up to 4 shares
+    assert L.jl_bifocal_prefill_chunk_workspace(2048, 1, 131072, 32, 8, 128, 1, None, ctypes.byref(n)) == 0
+    assert n.value == base
+    # 1024 rows: 128 workgroups -> 2 shares
     assert L.jl_bifocal_prefill_chunk_workspace(1024, 1, 131072, 32, 8, 128, 1, None, ctypes.byref(n)) == 0
-    assert base + 4 * 1024 * 32 * 130 * 4 <= n.value < base + 4 * 1024 * 32 * 130 * 4 + 1024
+    assert base + 2 * 1024 * 32 * 130 * 4 <= n.value < base + 2 * 1024 * 32 * 130 * 4 + 1024
+    # 512 rows: 64 workgroups -> 4 shares
+    assert L.jl_bifocal_prefill_chunk_workspace(512, 1, 131072, 32, 8, 128, 1, None, ctypes.byref(n)) == 0
+    assert base + 4 * 512 * 32 * 130 * 4 <= n.value < base + 4 * 512 * 32 * 130 * 4 + 1024
     # one row: capped at 4 shares
     assert L.jl_bifocal_prefill_chunk_workspace(1, 1, 131072, 32, 8, 128, 1, None, ctypes.byref(n)) == 0
     assert base + 4 * 32 * 130 * 4 <= n.value < base + 4 * 32 * 130 * 4 + 1024
