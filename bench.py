@@ -88,6 +88,9 @@ def main():
                     help="skip the 64K and varlen prefill workloads")
     ap.add_argument("--no-decode-extras", action="store_true",
                     help="decode: time only the flat bf16 cache (no paged, fp8 or 16-step runs)")
+    ap.add_argument("--prefill-input", choices=("randn", "constant", "zeros"), default="randn",
+                    help="inputs of the timed 128K prefill steps (low-entropy inputs only to "
+                         "profile the engine clock; the headline is randn)")
     ap.add_argument("--copy-calibration", type=int, default=0,
                     help="only run a plain device copy of this many bytes (counter calibration)")
     args = ap.parse_args()
@@ -114,6 +117,9 @@ def main():
     Hkv = case.k.shape[1]
     p = case.params
     q, k, v = case.q.cuda(), case.k.cuda(), case.v.cuda()
+    if args.prefill_input != "randn":
+        fill = (0.01, 0.02, 0.03) if args.prefill_input == "constant" else (0.0, 0.0, 0.0)
+        q, k, v = (torch.full_like(x, f) for x, f in zip((q, k, v), fill))
     o = torch.empty_like(q)
     lse = torch.empty((Hq, T), dtype=torch.float32, device="cuda")
     ws = torch.empty(jl.prefill_workspace_bytes(T, 1, Hq, Hkv, d, q.dtype), dtype=torch.uint8,
@@ -173,7 +179,8 @@ def main():
         "dtype": "f16",
         "io_dtype": "bf16",
         "arithmetic": "fp16 MFMA operands, fp32 accumulate; bf16 inputs and outputs",
-        "data": "synthetic (seeded N(0,1); q scaled by 1/sqrt(128))",
+        "data": ("synthetic (seeded N(0,1); q scaled by 1/sqrt(128))" if args.prefill_input == "randn"
+                 else "synthetic, %s q, k, v (clock profiling only)" % args.prefill_input),
         "config": {"workload": "qwen3_8b_L131072_prefill", "L": T, "Hq": Hq, "Hkv": Hkv,
                    "head_dim": d, "w_pretrained": p.w_pretrained, "w_local": p.w_local,
                    "G": 4, "rope_base": p.rope_base, "softmax_scale": p.softmax_scale,
@@ -232,6 +239,23 @@ def main():
         t_prec.append((time.perf_counter() - t0) * 1e3)
     out["prefill_precise_ms"] = round(min(t_prec), 3)
     del ws_p
+    # context: the same call on low-entropy inputs runs the identical
+    # instruction stream and work; the engine clock is power-limited, and the
+    # operands' switching activity is part of the power
+    low = {}
+    for name, fill in (("constant", (0.01, 0.02, 0.03)), ("zeros", (0.0, 0.0, 0.0))):
+        qz, kz, vz = (torch.full_like(x, f) for x, f in zip((q, k, v), fill))
+        jl.bifocal_prefill(qz, kz, vz, **kw)
+        t_low = []
+        for _ in range(2):
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            jl.bifocal_prefill(qz, kz, vz, **kw)
+            torch.cuda.synchronize()
+            t_low.append((time.perf_counter() - t0) * 1e3)
+        low[name] = round(min(t_low), 3)
+        del qz, kz, vz
+    out["prefill_low_entropy_ms"] = low
     del o, lse
 
     if not args.no_three_call:
