@@ -257,6 +257,35 @@ def main():
         del qz, kz, vz
     out["prefill_low_entropy_ms"] = low
     del o, lse
+    # the matrix-core stream (jl_debug_mfma_stream: 32x32x16 fp16 MFMAs and
+    # nothing else) on N(0,1) and on constant operands: the rate the matrix
+    # cores sustain on such data under the chip's power limit.  The timed calls
+    # last 30-100 ms each, as long as a prefill call, because a short burst
+    # runs at a clock the power limit does not yet hold it to.
+    ms_frac = {}
+    gen = torch.Generator("cpu").manual_seed(11)
+    n_ops = jl.MFMA_STREAM_OPERAND_BYTES // 2
+    outm = torch.empty(256 * 512, dtype=torch.float32, device="cuda")
+    for name, ops in (("randn", torch.randn(n_ops, generator=gen).to(torch.float16)),
+                      ("constant", torch.full((n_ops,), 0.01, dtype=torch.float16))):
+        opsd = ops.cuda()
+        jl.mfma_stream(opsd, 20000, outm)
+
+        def t_ms(iters):
+            ev0 = torch.cuda.Event(enable_timing=True)
+            ev1 = torch.cuda.Event(enable_timing=True)
+            ev0.record()
+            jl.mfma_stream(opsd, iters, outm)
+            ev1.record()
+            torch.cuda.synchronize()
+            return ev0.elapsed_time(ev1)
+
+        t_lo, t_hi = min(t_ms(20000) for _ in range(2)), min(t_ms(60000) for _ in range(2))
+        rate = 256 * 8 * 40000 * 32 * 32768.0 / ((t_hi - t_lo) * 1e-3) / 1e12
+        ms_frac[name] = round(rate / PEAK_BF16_TFLOPS, 4)
+        del opsd
+    out["mfma_stream_frac_of_peak"] = ms_frac
+    out["roofline"]["frac_of_mfma_stream_randn"] = round(achieved / (ms_frac["randn"] * PEAK_BF16_TFLOPS), 4)
 
     if not args.no_three_call:
         out["three_call"] = bench_three_call(jl, torch, case, ms_per_step)

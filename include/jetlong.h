@@ -460,6 +460,23 @@ jl_status jl_debug_index_math(int64_t L, int32_t w_pretrained, int32_t w_local, 
 jl_status jl_debug_stream_read(const void* src, size_t bytes, uint32_t* partial_sums, void* stream);
 
 /*
+ * Measurement aid: a stream of 32 x 32 x 16 fp16 MFMAs (the instruction the
+ * bf16 prefill's QK^T and P V run on) and nothing else, on operands the caller
+ * provides.  256 workgroups of 512 threads (two waves per SIMD); thread t of
+ * workgroup b reads 16 fp16 x 8 vectors at byte offset (b * 512 + t) * 256 of
+ * `operands` as eight (A, B) operand pairs, runs `iters` iterations of 32
+ * MFMAs (four independent accumulator chains of 8) and writes the sum of its
+ * 64 fp32 accumulator elements to out[b * 512 + t] (device float [131072]).
+ * One call performs 256 * 8 * iters * 32 MFMAs of 32768 flops each.  The
+ * engine clock is power-limited and the operands' switching activity is part
+ * of the power, so timing this on operands drawn like a workload's gives the
+ * matrix-core rate those data allow.  operands 16-byte aligned, operand_bytes
+ * >= 33554432, iters in [1, 2^24] (JL_ERR_INVALID_ARGUMENT otherwise).
+ */
+jl_status jl_debug_mfma_stream(const void* operands, size_t operand_bytes, int32_t iters,
+                               float* out, void* stream);
+
+/*
  * Kernel timing (profiling aid, off by default).  While enabled, every kernel
  * the library launches is bracketed by HIP events recorded on its stream;
  * jl_profile_read() synchronizes those events and reports, per kernel name,

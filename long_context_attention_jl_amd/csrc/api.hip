@@ -1065,6 +1065,21 @@ jl_status jl_debug_stream_read(const void* src, size_t bytes, uint32_t* partial_
     return finish(s, "jl_debug_stream_read");
 }
 
+jl_status jl_debug_mfma_stream(const void* operands, size_t operand_bytes, int32_t iters,
+                               float* out, void* stream) {
+    if (!operands || !out) return fail(JL_ERR_INVALID_ARGUMENT, "null pointer argument");
+    if (operand_bytes < kMfmaStreamOperandBytes)
+        return fail(JL_ERR_INVALID_ARGUMENT,
+                    "operand_bytes must be at least " + std::to_string(kMfmaStreamOperandBytes));
+    if (iters < 1 || iters > (1 << 24)) return fail(JL_ERR_INVALID_ARGUMENT, "iters must be in [1, 2^24]");
+    if (!al16(operands) || ((uintptr_t)out & 3))
+        return fail(JL_ERR_INVALID_ARGUMENT, "operands must be 16-byte and out 4-byte aligned");
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e = launch_mfma_stream(operands, iters, out, s);
+    if (e != hipSuccess) return hip_fail(e, "mfma stream launch");
+    return finish(s, "jl_debug_mfma_stream");
+}
+
 jl_status jl_profile_enable(int32_t on) {
     std::lock_guard<std::mutex> lk(g_prof_mu);
     clear_records();

@@ -58,6 +58,10 @@ RopeFreq make_rope_freq(double base, int d);
 
 constexpr int kStreamReadWgs = 256;  // workgroups (and partial sums) of the read stream
 hipError_t launch_stream_read(const void* src, int64_t bytes, uint32_t* out, hipStream_t s);
+// matrix-core stream: 256 workgroups x 512 threads, each thread 16 fp16 x 8 operand vectors
+constexpr int kMfmaStreamWgs = 256;
+constexpr size_t kMfmaStreamOperandBytes = (size_t)kMfmaStreamWgs * 512 * 16 * 16;
+hipError_t launch_mfma_stream(const void* operands, int32_t iters, float* out, hipStream_t s);
 hipError_t launch_rope_apply(void* out, const void* x, const int32_t* pos, int64_t T, int32_t H,
                              int32_t d, const RopeFreq& tab, int32_t G, int dtype,
                              hipStream_t s);

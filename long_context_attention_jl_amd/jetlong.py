@@ -139,6 +139,8 @@ def lib() -> ctypes.CDLL:
         L.jl_debug_index_math.argtypes = [_i64, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp]
         L.jl_debug_stream_read.restype = ctypes.c_int
         L.jl_debug_stream_read.argtypes = [_vp, ctypes.c_size_t, _vp, _vp]
+        L.jl_debug_mfma_stream.restype = ctypes.c_int
+        L.jl_debug_mfma_stream.argtypes = [_vp, ctypes.c_size_t, _i32, _vp, _vp]
         L.jl_profile_enable.restype = ctypes.c_int
         L.jl_profile_enable.argtypes = [_i32]
         L.jl_profile_read.restype = ctypes.c_int
@@ -747,6 +749,26 @@ def stream_read(buf: torch.Tensor, partial: Optional[torch.Tensor] = None) -> to
     _check(lib().jl_debug_stream_read(buf.data_ptr(), nbytes, partial.data_ptr(), _stream()),
            "jl_debug_stream_read")
     return partial
+
+
+MFMA_STREAM_OPERAND_BYTES = 256 * 512 * 16 * 16
+
+
+def mfma_stream(operands: torch.Tensor, iters: int, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Runs the matrix-core stream (jl_debug_mfma_stream) on the contiguous
+    fp16 device tensor `operands` (at least MFMA_STREAM_OPERAND_BYTES bytes);
+    returns the 131072 per-thread accumulator sums (fp32, on the device, not
+    synchronized).  One call performs 256 * 8 * iters * 32 MFMAs of 32768 flops."""
+    if operands.dtype != torch.float16 or not operands.is_contiguous():
+        raise ValueError("operands must be a contiguous float16 tensor")
+    nbytes = operands.numel() * operands.element_size()
+    if out is None:
+        out = torch.empty(256 * 512, dtype=torch.float32, device=operands.device)
+    if out.dtype != torch.float32 or out.numel() < 256 * 512 or out.device != operands.device:
+        raise ValueError("out must be a float32 tensor of at least 131072 elements on the operands' device")
+    _check(lib().jl_debug_mfma_stream(operands.data_ptr(), nbytes, int(iters), out.data_ptr(), _stream()),
+           "jl_debug_mfma_stream")
+    return out
 
 
 def profile_enable(on: bool) -> None:

@@ -378,6 +378,15 @@ def test_stream_read_validation(args, status):
     assert jlb.lib().jl_debug_stream_read(*args, None) == status
 
 
+@pytest.mark.parametrize("args,status", [
+    ((None, 1 << 25, 1, FAKE), 1), ((FAKE, 1 << 25, 1, None), 1), ((FAKE, (1 << 25) - 16, 1, FAKE), 1),
+    ((FAKE, 1 << 25, 0, FAKE), 1), ((FAKE, 1 << 25, (1 << 24) + 1, FAKE), 1),
+    ((FAKE + 8, 1 << 25, 1, FAKE), 1), ((FAKE, 1 << 25, 1, FAKE + 2), 1),
+])
+def test_mfma_stream_validation(args, status):
+    assert jlb.lib().jl_debug_mfma_stream(*args, None) == status
+
+
 # ---- the Python binding checks every tensor against q before any call --------
 # (CPU tensors: the shape/dtype checks run before the device check, so no
 # pointer reaches the library.)
