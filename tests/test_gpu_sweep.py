@@ -209,3 +209,43 @@ def test_chunk_sweep(case):
     torch.cuda.synchronize()
     o_ref, l_ref = oracle.prefill_chunk(q, kc, vc, lens, cu_seqlens_q=cu, **kw)
     check_prefill(o, lse, o_ref, l_ref, list(range(sum(chunks))), torch.bfloat16, "sweep chunk %d" % i)
+
+
+def _three_cases(n=12, seed=5):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        lens = [int(x) for x in rng.integers(1, 2600, size=int(rng.integers(1, 3)))]
+        Hkv = int(rng.choice([1, 2, 4]))
+        Hq = Hkv * int(rng.choice([1, 2, 4]))
+        d = int(rng.choice([64, 128]))
+        w_pre = int(rng.integers(8, 2000))
+        w_local = int(rng.integers(0, 2600))
+        out.append((i, lens, Hq, Hkv, d, w_pre, w_local))
+    return out
+
+
+@pytest.mark.parametrize("case", _three_cases(), ids=lambda c: "t%d" % c[0])
+def test_three_call_sweep(case):
+    """The pages' unfused form (three calls and the LogSumExp merge), prefill
+    and decode, against the oracle's direct definition."""
+    i, lens, Hq, Hkv, d, w_pre, w_local = case
+    T = sum(lens)
+    cu = [0] + [int(x) for x in np.cumsum(lens)]
+    kw = dict(w_pretrained=w_pre, w_local=w_local, rope_base=1e4, softmax_scale=1.0)
+    say("sweep three-call %d: lens=%s Hq=%d Hkv=%d d=%d w_pre=%d w_local=%d"
+        % (i, lens, Hq, Hkv, d, w_pre, w_local))
+    q, k, v = inputs.prefill_inputs(T, Hq, Hkv, d, seed=400 + i, q_scale=1.0 / math.sqrt(d))
+    o, lse = jl.bifocal_prefill_three_call(q.cuda(), k.cuda(), v.cuda(), cu_seqlens=cu, **kw)
+    torch.cuda.synchronize()
+    rows = list(range(T))
+    o_ref, l_ref = oracle.prefill(q, k, v, cu_seqlens=cu, rows=rows, **kw)
+    check_prefill(o, lse, o_ref, l_ref, rows, torch.bfloat16, "sweep three-call prefill %d" % i)
+    # decode: one query per sequence against caches of the same lengths
+    B, S = len(lens), max(lens)
+    qd, kc, vc = inputs.decode_inputs(B, S, Hq, Hkv, d, seed=500 + i)
+    kwd = dict(kw, softmax_scale=1.0 / math.sqrt(d))
+    od, ld = jl.bifocal_decode_three_call(qd.cuda(), kc.cuda(), vc.cuda(), lens, **kwd)
+    torch.cuda.synchronize()
+    od_ref, ld_ref = oracle.decode(qd, kc, vc, lens, **kwd)
+    check_decode(od, ld, od_ref, ld_ref, torch.bfloat16, "sweep three-call decode %d" % i)
