@@ -37,13 +37,22 @@ constexpr int kBM = kWaveRows * kWaves;  // 256 query rows per workgroup
 constexpr int kPreciseRows = 2048;
 constexpr int kPlanFields = 10;     // int32 fields per sequence in the plan
 
-// Key and value tiles are stored in the workspace exactly as they sit in LDS
-// (rows padded by 8 halves against bank conflicts), so the prefill kernel
-// fills LDS with flat global->LDS DMA copies.
-__host__ __device__ constexpr int kstr(int d) { return d + 8; }       // K row stride (halves)
-constexpr int kVStr = kBN + 8;                                        // V^T row stride (halves)
-__host__ __device__ constexpr int ktile_elems(int d) { return kBN * kstr(d); }
-__host__ __device__ constexpr int vtile_elems(int d) { return d * kVStr; }
+// Key and value tiles are stored in the workspace exactly as they sit in LDS,
+// so the prefill kernel fills LDS with flat global->LDS DMA copies.  A tile is
+// stored in 16-byte pieces (8 halves), piece-major: piece c of every row, the
+// rows in order, then piece c + 1.  An MFMA operand read (lane = one row's
+// piece, 32 rows x 2 pieces) then covers 16 consecutive rows of one piece as
+// one contiguous 256-byte stretch, which meets every LDS bank once: no
+// padding, and every piece a lane reads sits at a compile-time offset from
+// its first one.
+//   K tile   [d / 8 pieces][kBN keys][8]   (piece c: elements 8c .. 8c + 7)
+//   V^T tile [kBN / 8 pieces][d rows][8]   (piece c: keys 8c .. 8c + 7)
+__host__ __device__ constexpr int ktile_elems(int d) { return kBN * d; }
+__host__ __device__ constexpr int vtile_elems(int d) { return d * kBN; }
+// element offset of piece c of key row r in a K tile
+__host__ __device__ constexpr int kt_off(int r, int c) { return (c * kBN + r) * 8; }
+// element offset of piece c (keys 8c ..) of row dd in a V^T tile of head size d
+__host__ __device__ constexpr int vt_off(int d, int dd, int c) { return (c * d + dd) * 8; }
 
 // Plan fields (per sequence s, written by the plan kernel).
 enum PlanField {

@@ -54,16 +54,15 @@ constexpr float kLn2 = 0.6931471805599453f;
 
 template <int D, bool PRECISE>
 struct Cfg {
-    static constexpr int KSTR = D + 8;         // LDS row stride of a K tile (halves)
-    static constexpr int VSTR = kBN + 8;       // LDS row stride of a V^T tile
-    static constexpr int KSLOT = kBN * KSTR;   // elements
-    static constexpr int VSLOT = D * VSTR;
+    // tiles in LDS: K [D/8 pieces][kBN keys][8], V^T [kBN/8 pieces][D rows][8]
+    static constexpr int KSLOT = ktile_elems(D);  // elements
+    static constexpr int VSLOT = vtile_elems(D);
     static constexpr int NK = PRECISE ? 2 : 1; // K of the current phase (+ its lo part)
     static constexpr int BUF = NK * KSLOT + VSLOT;
     static constexpr int NS = D / 16;          // k-steps of a QK^T product
     static constexpr int ND = D / 32;          // 32-row blocks of O^T
     static constexpr int QROWS = 128;          // query rows staged per prologue round
-    static_assert(QROWS * KSTR <= BUF, "query staging must fit in one tile buffer");
+    static_assert(QROWS * D <= BUF, "query staging must fit in one tile buffer");
     static_assert(KSLOT % 512 == 0 && VSLOT % 512 == 0, "tiles are whole 1 KB DMA rounds");
 };
 
@@ -168,9 +167,10 @@ void prefill_bf16_kernel(PrefillArgs a, int rb_first, int n_rb) {
 
     // ---- rotated, scaled queries as MFMA B operands ----
     // The workgroup rotates 128 rows at a time into LDS (thread (t, r) does
-    // pair t of rows r, r + 512/(D/2), ...); each wave then reads its operand
-    // registers, lane (qr, hh) holding d = 16*st + 8*hh + u, as 16-byte
-    // vectors.  Both LDS buffers are idle whenever this runs.
+    // pair t of rows r, r + 512/(D/2), ...), in 16-byte pieces laid out like a
+    // K tile ([D/8][QROWS][8]); each wave then reads its operand registers,
+    // lane (qr, hh) holding d = 16*st + 8*hh + u, as 16-byte vectors.  Both
+    // LDS buffers are idle whenever this runs.
     f16x8 Qc[C::NS], Qcl[C::NS];
     const float qscale = a.softmax_scale * kLog2e;
     auto stage_q = [&](bool remapped)  __attribute__((always_inline)) {
@@ -196,15 +196,16 @@ void prefill_bf16_kernel(PrefillArgs a, int rb_first, int n_rb) {
                 if (remapped && interp) rope_cs_hw(row, rv * rsc, c, sn);
                 else rope_cs_hw(remapped ? remap(row, G) : row, rv, c, sn);
                 const float y0 = (x0 * c - x1 * sn) * qscale, y1 = (x1 * c + x0 * sn) * qscale;
-                qimg[r * C::KSTR + t] = lo ? (f16)(y0 - (float)(f16)y0) : (f16)y0;
-                qimg[r * C::KSTR + t + HALF] = lo ? (f16)(y1 - (float)(f16)y1) : (f16)y1;
+                qimg[((t >> 3) * C::QROWS + r) * 8 + (t & 7)] = lo ? (f16)(y0 - (float)(f16)y0) : (f16)y0;
+                qimg[(((t + HALF) >> 3) * C::QROWS + r) * 8 + (t & 7)] =
+                    lo ? (f16)(y1 - (float)(f16)y1) : (f16)y1;
             }
             __syncthreads();
             if ((wave * kWaveRows) / C::QROWS == half_rows) {
-                const int qoff = ((wave * kWaveRows) % C::QROWS + qr) * C::KSTR + 8 * hh;
+                const int qoff = (hh * C::QROWS + (wave * kWaveRows) % C::QROWS + qr) * 8;
 #pragma unroll
                 for (int st = 0; st < C::NS; ++st) {
-                    const f16x8 v = *reinterpret_cast<const f16x8*>(qimg + qoff + 16 * st);
+                    const f16x8 v = *reinterpret_cast<const f16x8*>(qimg + qoff + 16 * C::QROWS * st);
                     if (!lo) Qc[st] = v;
                     if constexpr (PRECISE) {
                         if (lo) Qcl[st] = v;
@@ -261,10 +262,11 @@ void prefill_bf16_kernel(PrefillArgs a, int rb_first, int n_rb) {
     // in log2 units: sums stay exact relative to the max they use, p stays
     // below 2^8, and most blocks skip rescaling O), then O^T += V^T P^T.
     auto do_block = [&](const bf16* base, int b, bool masked, bool remote_phase, int32_t jb)  __attribute__((always_inline)) {
-        const bf16* kp = base + (32 * b + qr) * C::KSTR + 8 * hh;
+        // piece 2 st + hh of key row 32 b + qr
+        const bf16* kp = base + kt_off(32 * b + qr, hh);
         f16x8 kv[C::NS];
 #pragma unroll
-        for (int st = 0; st < C::NS; ++st) kv[st] = *reinterpret_cast<const f16x8*>(kp + 16 * st);
+        for (int st = 0; st < C::NS; ++st) kv[st] = *reinterpret_cast<const f16x8*>(kp + kt_off(0, 2 * st));
         // the K operands are in flight before the score chain starts
         __builtin_amdgcn_sched_barrier(0);
         f32x16 Sb = negm;
@@ -273,18 +275,19 @@ void prefill_bf16_kernel(PrefillArgs a, int rb_first, int n_rb) {
             Sb = mfma32h(kv[st], Qc[st], Sb);
             if constexpr (PRECISE) {
                 Sb = mfma32h(kv[st], Qcl[st], Sb);
-                const f16x8 kl = *reinterpret_cast<const f16x8*>(kp + C::KSLOT + 16 * st);
+                const f16x8 kl = *reinterpret_cast<const f16x8*>(kp + C::KSLOT + kt_off(0, 2 * st));
                 Sb = mfma32h(kl, Qc[st], Sb);
             }
         }
         // the V operands are read while the score chain and the softmax run
-        const bf16* vb = base + C::NK * C::KSLOT + qr * C::VSTR + 32 * b + 8 * hh;
+        // piece 4 b + hh + 2 u (keys 32 b + 8 hh + 16 u ..) of row qr + 32 db
+        const bf16* vb = base + C::NK * C::KSLOT + vt_off(D, qr, 4 * b + hh);
         f16x8 vv[2][C::ND];
 #pragma unroll
         for (int u = 0; u < 2; ++u)
 #pragma unroll
             for (int db = 0; db < C::ND; ++db)
-                vv[u][db] = *reinterpret_cast<const f16x8*>(vb + 32 * db * C::VSTR + 16 * u);
+                vv[u][db] = *reinterpret_cast<const f16x8*>(vb + vt_off(D, 32 * db, 2 * u));
         __builtin_amdgcn_sched_barrier(0);
         if (masked) {
 #pragma unroll

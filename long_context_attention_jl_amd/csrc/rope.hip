@@ -273,8 +273,8 @@ __global__ __launch_bounds__(256) void kv_prepass_bf16_kernel(PrefillArgs a) {
     };
 
     // ---- keys: thread (r, c) rotates pairs [8c, 8c + 8) of row r: one
-    // 16-byte vector in each RoPE half (tile rows are 16-byte aligned:
-    // kstr(D) * 2 = 16 * 17); 256 / (D / 16) rows per pass ----
+    // 16-byte vector in each RoPE half, that is tile pieces c and
+    // c + D / 16; 256 / (D / 16) rows per pass ----
     constexpr int TPR = D / 16;          // threads per key row
     constexpr int RPP = 256 / TPR;       // rows per pass
     // remote position: f(n) = floor(n / G), or n / s with s = len / w_pretrained
@@ -334,37 +334,25 @@ __global__ __launch_bounds__(256) void kv_prepass_bf16_kernel(PrefillArgs a) {
                     lr1[u] = (f16)(r1 - (float)yr1[u]);
                 }
             }
-            // tile image: row r of tile `tile`, stride kstr(D)
-            const int64_t drow = ((int64_t)g * (a.lay.T_pad / kBN) + tile) * ktile_elems(D) +
-                                 (int64_t)r * kstr(D) + 8 * c;
-            *reinterpret_cast<f16x8*>(KS + drow) = ys0;
-            *reinterpret_cast<f16x8*>(KS + drow + HALF) = ys1;
+            // tile image: pieces c and c + TPR of row r of tile `tile` (the
+            // eight lanes of one piece write one whole 128-byte line)
+            const int64_t dt = ((int64_t)g * (a.lay.T_pad / kBN) + tile) * ktile_elems(D);
+            const int o0 = kt_off(r, c), o1 = kt_off(r, c + TPR);
+            *reinterpret_cast<f16x8*>(KS + dt + o0) = ys0;
+            *reinterpret_cast<f16x8*>(KS + dt + o1) = ys1;
             if (bif) {
-                *reinterpret_cast<f16x8*>(KR + drow) = yr0;
-                *reinterpret_cast<f16x8*>(KR + drow + HALF) = yr1;
-            }
-            // the row's 16-byte pad is written too: every cache line of a tile
-            // image is then written whole, which spares the memory a
-            // read-modify-write of partly written lines (about 30 % of this
-            // kernel's time)
-            const bool pad = c == TPR - 1;
-            if (pad) {  // drow + HALF + 8 = the row's element D (8c = HALF - 8 here)
-                *reinterpret_cast<f16x8*>(KS + drow + HALF + 8) = f16x8{};
-                if (bif) *reinterpret_cast<f16x8*>(KR + drow + HALF + 8) = f16x8{};
+                *reinterpret_cast<f16x8*>(KR + dt + o0) = yr0;
+                *reinterpret_cast<f16x8*>(KR + dt + o1) = yr1;
             }
             if (lo_row) {
-                const int64_t lrow =
-                    ((int64_t)g * (a.lay.lo_pad / kBN) + e[kPlanLoTile0] + n / kBN) * ktile_elems(D) +
-                    (int64_t)(n % kBN) * kstr(D) + 8 * c;
-                *reinterpret_cast<f16x8*>(KSlo + lrow) = ls0;
-                *reinterpret_cast<f16x8*>(KSlo + lrow + HALF) = ls1;
+                const int64_t lt =
+                    ((int64_t)g * (a.lay.lo_pad / kBN) + e[kPlanLoTile0] + n / kBN) * ktile_elems(D);
+                const int l0 = kt_off(n % kBN, c), l1 = kt_off(n % kBN, c + TPR);
+                *reinterpret_cast<f16x8*>(KSlo + lt + l0) = ls0;
+                *reinterpret_cast<f16x8*>(KSlo + lt + l1) = ls1;
                 if (bif) {
-                    *reinterpret_cast<f16x8*>(KRlo + lrow) = lr0;
-                    *reinterpret_cast<f16x8*>(KRlo + lrow + HALF) = lr1;
-                }
-                if (pad) {
-                    *reinterpret_cast<f16x8*>(KSlo + lrow + HALF + 8) = f16x8{};
-                    if (bif) *reinterpret_cast<f16x8*>(KRlo + lrow + HALF + 8) = f16x8{};
+                    *reinterpret_cast<f16x8*>(KRlo + lt + l0) = lr0;
+                    *reinterpret_cast<f16x8*>(KRlo + lt + l1) = lr1;
                 }
             }
             if (krot && valid) {
@@ -392,8 +380,10 @@ __global__ __launch_bounds__(256) void kv_prepass_bf16_kernel(PrefillArgs a) {
         }
         __syncthreads();
         f16* dst = VT + ((int64_t)g * (a.lay.T_pad / kBN) + tile) * vtile_elems(D);
+        // consecutive threads take consecutive rows dd of one piece m: a wave
+        // writes 1 KB contiguous
         for (int idx = threadIdx.x; idx < D * (kBN / 8); idx += 256) {
-            const int dd = idx / (kBN / 8), m = idx % (kBN / 8);
+            const int dd = idx % D, m = idx / D;
             f16x8 o;
 #pragma unroll
             for (int e8 = 0; e8 < 8; ++e8) {
@@ -401,9 +391,7 @@ __global__ __launch_bounds__(256) void kv_prepass_bf16_kernel(PrefillArgs a) {
                 const int key = (p & ~15) | vt_perm16(p & 15);
                 o[e8] = (f16)(float)vs[key * VSS + dd];
             }
-            *reinterpret_cast<f16x8*>(dst + dd * kVStr + 8 * m) = o;
-            if (m == kBN / 8 - 1)  // the row's pad, as for the key tiles
-                *reinterpret_cast<f16x8*>(dst + dd * kVStr + kBN) = f16x8{};
+            *reinterpret_cast<f16x8*>(dst + vt_off(D, dd, m)) = o;
         }
     }
 }

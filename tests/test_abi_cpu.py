@@ -504,8 +504,8 @@ def test_precise_workspaces_cover_every_key():
     assert L.jl_bifocal_prefill_workspace(131072, 1, 32, 8, 128, 1, ctypes.byref(d1),
                                           ctypes.byref(c)) == 0
     assert a.value == b.value and c.value > a.value
-    # the low-part tiles of every key: 2 copies x 8 heads x 131072 keys x (128 + 8) halves
-    assert c.value - a.value >= 2 * 8 * (131072 - 2048) * 136 * 2
+    # the low-part tiles of every key: 2 copies x 8 heads x 131072 keys x 128 halves
+    assert c.value - a.value >= 2 * 8 * (131072 - 2048) * 128 * 2
     assert L.jl_bifocal_prefill_chunk_workspace(1024, 1, 131072, 32, 8, 128, 1, ctypes.byref(d1),
                                                 ctypes.byref(c)) == 0
     assert L.jl_bifocal_prefill_workspace(10, 1, 1, 1, 64, 1, ctypes.byref(_params(precise=3)),
