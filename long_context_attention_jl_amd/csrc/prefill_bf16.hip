@@ -303,9 +303,14 @@ void prefill_bf16_kernel(PrefillArgs a, int rb_first, int n_rb) {
         float mx = -INFINITY;
 #pragma unroll
         for (int i = 0; i < 16; ++i) mx = fmaxf(mx, Sb[i]);
-        mx = max_other_half(mx) + m_c;
-        const bool raise = mx > m_run + 8.0f;
-        if (__any(raise)) {
+        // A row's max is raised when its max score exceeds m_run + 8.  The
+        // lane half that holds that score sees the same test on its own 16
+        // scores, so the wave enters the branch exactly when some row must
+        // raise; the row max over both halves is formed only there.
+        const float thr = m_run + 8.0f;
+        if (__any(mx + m_c > thr)) {
+            mx = max_other_half(mx) + m_c;
+            const bool raise = mx > thr;
             const float m_new = raise ? mx : m_run;
             const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
             const float d = m_new - m_c;
