@@ -251,6 +251,7 @@ void prefill_bf16_kernel(PrefillArgs a, int rb_first, int n_rb) {
     // current phase yet give exp2(-inf - m) = 0, never NaN.
     float m_run = -1e30f, l_run = 0.0f;
     float m_c = 0.0f;  // what the score accumulators start from (negated)
+    float thr_c = m_run + 8.0f - m_c;  // raise threshold on s - m_c
     f32x16 negm = {};  // -m_c in every element: the C operand of a block's first MFMA
     f32x16 O[C::ND];
 #pragma unroll
@@ -304,13 +305,14 @@ void prefill_bf16_kernel(PrefillArgs a, int rb_first, int n_rb) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) mx = fmaxf(mx, Sb[i]);
         // A row's max is raised when its max score exceeds m_run + 8.  The
-        // lane half that holds that score sees the same test on its own 16
-        // scores, so the wave enters the branch exactly when some row must
-        // raise; the row max over both halves is formed only there.
-        const float thr = m_run + 8.0f;
-        if (__any(mx + m_c > thr)) {
+        // lane half that holds that score sees the test on its own 16 scores
+        // (against the threshold kept relative to m_c), so the wave enters
+        // the branch when some row must raise; the row max over both halves
+        // is formed only there.  A lane that enters without raising keeps
+        // its state exactly (alpha = 1, d = 0).
+        if (__any(mx > thr_c)) {
             mx = max_other_half(mx) + m_c;
-            const bool raise = mx > thr;
+            const bool raise = mx > m_run + 8.0f;
             const float m_new = raise ? mx : m_run;
             const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
             const float d = m_new - m_c;
@@ -318,6 +320,7 @@ void prefill_bf16_kernel(PrefillArgs a, int rb_first, int n_rb) {
             for (int i = 0; i < 16; ++i) Sb[i] -= d;
             m_run = m_new;
             m_c = m_new > -1e29f ? m_new : 0.0f;
+            thr_c = m_run + 8.0f - m_c;
 #pragma unroll
             for (int i = 0; i < 16; ++i) negm[i] = -m_c;
             l_run *= alpha;
