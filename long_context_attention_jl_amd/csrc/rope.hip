@@ -234,6 +234,7 @@ __host__ __device__ constexpr int vt_perm16(int p) {
 //   KS_lo/KR_lo = f16(x - f16(x))     for n < kPreciseRows, or every n when the
 //                                     call asks for split precision on all rows
 //   VT[g][tile][d][key']              V tile transposed to fp16, keys in vt_perm16 order
+// Every tile is written in the piece-major image layout (kt_off, vt_off).
 //   k_rot_out[tok][g] = KS row        (optional, the caller's cache layout)
 // Pad rows (n >= L) are written as zeros so masked keys never meet NaNs.
 template <int D>
