@@ -307,9 +307,11 @@ void prefill_bf16_kernel(PrefillArgs a, int rb_first, int n_rb) {
         // A row's max is raised when its max score exceeds m_run + 8.  The
         // lane half that holds that score sees the test on its own 16 scores
         // (against the threshold kept relative to m_c), so the wave enters
-        // the branch when some row must raise; the row max over both halves
-        // is formed only there.  A lane that enters without raising keeps
-        // its state exactly (alpha = 1, d = 0).
+        // the branch when some row must raise, up to the rounding of the two
+        // forms of the test (a row that skips a raise by rounding keeps
+        // probabilities a rounding step above 2^8, which fp16 holds); the row
+        // max over both halves is formed only there.  A lane that enters
+        // without raising keeps its state exactly (alpha = 1, d = 0).
         if (__any(mx > thr_c)) {
             mx = max_other_half(mx) + m_c;
             const bool raise = mx > m_run + 8.0f;
