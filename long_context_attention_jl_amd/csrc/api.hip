@@ -128,7 +128,7 @@ PrefillLayout prefill_layout(int64_t T, int32_t n_seqs, int32_t Hkv, int32_t d, 
 }
 
 DecodeLayout decode_layout(int32_t B, int32_t max_seqlen_k, int32_t Hq, int32_t Hkv, int32_t d,
-                           int dtype) {
+                           int dtype, int target_wg) {
     DecodeLayout L{};
     // bf16: 8-wave workgroups (one per compute unit), 48-position stages;
     // fp32: 4-wave workgroups (two per compute unit), 64-position stages
@@ -137,7 +137,8 @@ DecodeLayout decode_layout(int32_t B, int32_t max_seqlen_k, int32_t Hq, int32_t 
     const int stage = b16 ? kDecodeStageB : 64;
     const int nw = Hkv < wmax ? Hkv : wmax;  // waves (kv heads) per decode workgroup
     const int64_t groups = (Hkv + nw - 1) / nw;
-    const int64_t target = b16 ? 256 : 512;  // workgroups per call
+    // workgroups per call (one 8-wave bf16 workgroup per compute unit)
+    const int64_t target = target_wg > 0 ? target_wg : (b16 ? 256 : 512);
     const int64_t span = (int64_t)max_seqlen_k + stage - 1;
     int64_t want = (target + (int64_t)B * groups - 1) / ((int64_t)B * groups);
     if (want < 1) want = 1;
@@ -576,6 +577,12 @@ static jl_status decode_impl(const DecodeCall& c, const jl_params* params, jl_dt
     a.precise = dtype == JL_DTYPE_BF16 ? params->precise : 0;
     a.ilv = dtype == JL_DTYPE_BF16 &&
             decode_interleave(paged, c.Hq, c.Hkv, c.d, c.max_seqlen_k, c.fp8 ? 1 : 2);
+    // Flat bf16 caches of 64K keys and more run faster on fewer, longer
+    // workgroups (192 against 256 at L = 131072: fewer partials to write and
+    // merge, fewer table prologues per byte); shorter caches and fp8 caches
+    // keep 256.  Fewer splits need less workspace than the size checked above.
+    if (a.ilv && !c.fp8 && c.max_seqlen_k >= 65536)
+        a.lay = decode_layout(c.batch, c.max_seqlen_k, c.Hq, c.Hkv, c.d, dtype, kDecodeLongTargetWG);
     if (static_scratch) {
         const jl_status sst = scratch_of_device(stream, &a.ws);
         if (sst != JL_OK) return sst;

@@ -51,8 +51,12 @@ struct DecodeLayout {
     size_t part_o;   // float [B][n_splits][Hq][d]
     size_t total;
 };
+// target_wg: workgroups per call to aim at (0: the default, 256 for bf16);
+// a smaller target never needs more workspace than the default.
 DecodeLayout decode_layout(int32_t batch, int32_t max_seqlen_k, int32_t Hq, int32_t Hkv, int32_t d,
-                           int dtype);
+                           int dtype, int target_wg = 0);
+// workgroup target of flat bf16 decode at max_seqlen_k >= 65536
+constexpr int kDecodeLongTargetWG = 192;
 
 RopeFreq make_rope_freq(double base, int d);
 
