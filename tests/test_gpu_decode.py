@@ -250,3 +250,18 @@ def test_rope_apply_builds_the_cache_the_oracle_expects():
     torch.cuda.synchronize()
     o_ref, lse_ref = _dec_ref(q, kc[None].cpu(), v[None], [S], p)
     _check(o, lse, o_ref, lse_ref, torch.bfloat16, "rope_apply cache")
+
+
+@pytest.mark.parametrize("L", [65535, 65536])
+def test_decode_workgroup_target_boundary(L):
+    """Flat bf16 caches of 65536 keys and more launch on the smaller workgroup
+    target: 65535 keys take the default split and 65536 the smaller one.  Both
+    against the oracle over every head, plus a batch of two where only the
+    longer sequence reaches the boundary (max_seqlen_k decides the split)."""
+    p = inputs.DECODE_PARAMS
+    q, kc, vc = inputs.decode_inputs(2, L, 32, 8, 128, seed=L)
+    lens = [L, L // 3]
+    o, lse = _dec_gpu(q, kc.cuda(), vc.cuda(), lens, p, max_seqlen_k=L)
+    o_ref, lse_ref = _dec_ref(q, kc, vc, lens, p)
+    o_pl, _ = _dec_ref(q, kc, vc, lens, _plain(p))
+    check_decode(o, lse, o_ref, lse_ref, torch.bfloat16, "decode boundary L=%d" % L, o_plain=o_pl)
